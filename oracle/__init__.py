@@ -1,0 +1,158 @@
+"""fp64 CPU oracle of the DeepSeekMoE layer forward.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this package.  The layer's own code never
+imports it, and it shares no code with the HIP library.
+
+oracle.c holds the definition (routing, SwiGLU experts, shared experts,
+residual) in plain double-precision loops; ref_np.py is a second,
+independent numpy float64 formulation used to cross-check it on small
+shapes; cost.py holds the parameter/MAC accounting of one expert and the
+expert-hit entropy diagnostic.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+NO_RESIDUAL = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("K", ctypes.c_int32), ("Ks", ctypes.c_int32),
+                ("Is", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.oracle_route.restype = i32
+        L.oracle_route.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_forward.restype = i32
+        L.oracle_forward.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, i32]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a, shape):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    assert a.shape == tuple(shape), (a.shape, shape)
+    return a
+
+
+def _ptr_table(stack, n, shape):
+    """Per-expert pointer table from a [n, ...] stack or a list of n arrays."""
+    keep = []
+    tbl = (ctypes.c_void_p * max(n, 1))()
+    for i in range(n):
+        a = _u16(stack[i], shape)
+        keep.append(a)
+        tbl[i] = a.ctypes.data
+    return tbl, keep
+
+
+def route(x_rows, C, bias, K, nthreads=0, return_probs=False):
+    """Routing (affinity, softmax, top-K) of the given token rows.
+
+    x_rows: uint16 bf16 bits [n, d]; C: [E, d]; bias: float32 [E] or None.
+    Returns idx int32 [n, K], gate float64 [n, K], margin float64 [n]
+    (and probs [n, E] when asked)."""
+    x_rows = np.ascontiguousarray(x_rows)
+    n, d = x_rows.shape
+    E = C.shape[0]
+    C = _u16(C, (E, d))
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    sh = _Shape(n, d, E, 0, K, 0, 0, 0)
+    idx = np.zeros((n, K), np.int32)
+    gate = np.zeros((n, K), np.float64)
+    margin = np.zeros(n, np.float64)
+    probs = np.zeros((n, E), np.float64) if return_probs else None
+    lib().oracle_route(ctypes.byref(sh), _ptr(x_rows), n, _ptr(C), _ptr(b), _ptr(idx),
+                       _ptr(gate), _ptr(margin), _ptr(probs), int(nthreads))
+    return (idx, gate, margin, probs) if return_probs else (idx, gate, margin)
+
+
+def forward(x_rows, C, bias, w1, w3, w2, ws1, ws3, ws2, K, no_residual=False,
+            forced_idx=None, nthreads=0):
+    """Layer forward of the given token rows, in fp64.
+
+    x_rows: [n, d] bf16 bits.  w1/w3: per routed expert [I, d] (a [E, I, d]
+    stack or a list, entries may be None for experts never selected when
+    forced_idx names the experts); w2: [d, I] each.  ws*: likewise for the
+    K_s shared experts.  Returns a dict with out, shared, routed ([n, d]
+    float64), idx, gate, margin and the thread count used."""
+    x_rows = np.ascontiguousarray(x_rows)
+    n, d = x_rows.shape
+    E = C.shape[0]
+    C = _u16(C, (E, d))
+    Ks = 0 if ws1 is None else len(ws1)
+    I = next(a.shape[0] for a in w1 if a is not None) if E else 0
+    Is = ws1[0].shape[0] if Ks else 0
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+
+    keep = []
+    tw = []
+    zero_i = np.zeros((I, d), np.uint16)
+    zero_o = np.zeros((d, I), np.uint16)
+    for stack, shp, z in ((w1, (I, d), zero_i), (w3, (I, d), zero_i), (w2, (d, I), zero_o)):
+        lst = [z if stack[e] is None else stack[e] for e in range(E)]
+        t, k = _ptr_table(lst, E, shp)
+        tw.append(t)
+        keep.append(k)
+    ts = []
+    for stack, shp in ((ws1, (Is, d)), (ws3, (Is, d)), (ws2, (d, Is))):
+        t, k = _ptr_table(stack if Ks else [], Ks, shp)
+        ts.append(t)
+        keep.append(k)
+
+    fi = None
+    if forced_idx is not None:
+        fi = np.ascontiguousarray(forced_idx, dtype=np.int32)
+        assert fi.shape == (n, K)
+        assert fi.size == 0 or (fi.min() >= 0 and fi.max() < E)
+
+    sh = _Shape(n, d, E, I, K, Ks, Is, NO_RESIDUAL if no_residual else 0)
+    out = np.zeros((n, d), np.float64)
+    shared = np.zeros((n, d), np.float64)
+    routed = np.zeros((n, d), np.float64)
+    idx = np.zeros((n, K), np.int32)
+    gate = np.zeros((n, K), np.float64)
+    margin = np.zeros(n, np.float64)
+    used = lib().oracle_forward(ctypes.byref(sh), _ptr(x_rows), n, _ptr(C), _ptr(b),
+                                tw[0], tw[1], tw[2], ts[0], ts[1], ts[2], _ptr(fi),
+                                _ptr(out), _ptr(shared), _ptr(routed), _ptr(idx), _ptr(gate),
+                                _ptr(margin), int(nthreads))
+    return dict(out=out, shared=shared, routed=routed, idx=idx, gate=gate, margin=margin,
+                threads=int(used))

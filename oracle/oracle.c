@@ -1,0 +1,225 @@
+/*
+ * fp64 CPU oracle of the DeepSeekMoE layer forward.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may load or call this file; the layer itself never
+ * does, and this file shares no code, header or table with the HIP library.
+ *
+ * What it computes, step by step, for every requested token t (all
+ * arithmetic in IEEE double, plain sequential loops, bf16 inputs widened
+ * exactly):
+ *
+ *   1. affinity  l_e = sum_j x[t,j] * C[e,j] + b_e       (b_e = 0 without bias)
+ *      The token-to-centroid inner product of the generic top-K MoE gate
+ *      ("DeepSeekMoE 深度解读报告", section 3.1, Eq. 3-5 as described there).
+ *   2. score     s_e = exp(l_e - max l) / sum_f exp(l_f - max l)
+ *      softmax over the N*m routed experts only; shared experts never enter
+ *      the gate (same page, sections 2.3 and 3.1).
+ *   3. selection K rounds of argmax over the experts not yet taken, strict
+ *      '>' so that the lower index wins a tie.  gate_k = s_{e_k}; the other
+ *      experts get 0 and no renormalisation follows (section 3.1: keep the
+ *      top scores, zero the rest).  margin = s_(K) - s_(K+1), +inf when
+ *      K == E or K == 0.
+ *   4. expert    FFN_W(x) = W2 (silu(W1 x) * (W3 x)), silu(z) = z/(1+e^-z),
+ *      W1, W3 of shape [inter, d] and W2 of shape [d, inter], no bias
+ *      (the Expert module printed on the youleyou page, "DeepSeek MoE模型优化
+ *      与未来演进及字节超稀疏内存技术").
+ *   5. output    out = x + sum_{s<K_s} FFN_{shared s}(x) + sum_k gate_k FFN_{e_k}(x)
+ *      (shared experts isolated and always active, section 2.3 / 3.1 of the
+ *      report; the residual term is dropped when ORACLE_NO_RESIDUAL is set).
+ *
+ * Fine-grained segmentation (section 2.2) enters only through the shape:
+ * E = N*m routed experts, each of inter-dim I = I_std/m.
+ *
+ * Tokens are independent; OpenMP runs them on separate threads without
+ * changing any token's order of operations.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_NO_RESIDUAL 1u
+
+typedef struct {
+    int32_t T, d, E, I, K, Ks, Is;
+    uint32_t flags;
+} oracle_shape;
+
+static double widen(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Steps 1-3 for one token.  x_t: [d] widened.  probs: [E] scratch/out. */
+static void route_token(const oracle_shape* s, const double* x_t,
+                        const uint16_t* C, const float* bias,
+                        double* logits, double* probs, uint8_t* taken,
+                        int32_t* idx, double* gate, double* margin) {
+    const int d = s->d, E = s->E, K = s->K;
+    for (int e = 0; e < E; ++e) {
+        double acc = 0.0;
+        const uint16_t* c = C + (size_t)e * d;
+        for (int j = 0; j < d; ++j) acc += x_t[j] * widen(c[j]);
+        logits[e] = acc + (bias ? (double)bias[e] : 0.0);
+    }
+    double mx = logits[0];
+    for (int e = 1; e < E; ++e)
+        if (logits[e] > mx) mx = logits[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) {
+        probs[e] = exp(logits[e] - mx);
+        z += probs[e];
+    }
+    for (int e = 0; e < E; ++e) probs[e] /= z;
+
+    memset(taken, 0, (size_t)E);
+    for (int k = 0; k < K; ++k) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (!taken[e] && (best < 0 || probs[e] > probs[best])) best = e;
+        taken[best] = 1;
+        idx[k] = best;
+        gate[k] = probs[best];
+    }
+    if (K == 0 || K == E) {
+        *margin = INFINITY;
+    } else {
+        int next = -1;
+        for (int e = 0; e < E; ++e)
+            if (!taken[e] && (next < 0 || probs[e] > probs[next])) next = e;
+        *margin = probs[idx[K - 1]] - probs[next];
+    }
+}
+
+/* Step 4: y = W2 (silu(W1 x) * W3 x) for one token. h: [inter] scratch. */
+static void expert_ffn(int d, int inter, const uint16_t* w1, const uint16_t* w3,
+                       const uint16_t* w2, const double* x_t, double* h, double* y) {
+    for (int i = 0; i < inter; ++i) {
+        double a = 0.0, b = 0.0;
+        const uint16_t* r1 = w1 + (size_t)i * d;
+        const uint16_t* r3 = w3 + (size_t)i * d;
+        for (int j = 0; j < d; ++j) {
+            a += widen(r1[j]) * x_t[j];
+            b += widen(r3[j]) * x_t[j];
+        }
+        h[i] = silu(a) * b;
+    }
+    for (int o = 0; o < d; ++o) {
+        double acc = 0.0;
+        const uint16_t* r2 = w2 + (size_t)o * inter;
+        for (int i = 0; i < inter; ++i) acc += widen(r2[i]) * h[i];
+        y[o] = acc;
+    }
+}
+
+/* Routing only (steps 1-3) for n_tokens tokens; x_rows holds their rows
+ * ([n_tokens, d], bf16).  probs_out may be NULL, else [n_tokens, E]. */
+int32_t oracle_route(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
+                     const uint16_t* C, const float* bias,
+                     int32_t* idx_out, double* gate_out, double* margin_out,
+                     double* probs_out, int32_t nthreads) {
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+#pragma omp parallel num_threads(nthreads)
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double* xt = malloc(sizeof(double) * (size_t)s->d);
+        double* lg = malloc(sizeof(double) * (size_t)s->E);
+        double* pr = malloc(sizeof(double) * (size_t)s->E);
+        uint8_t* tk = malloc((size_t)s->E);
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t i = 0; i < n_tokens; ++i) {
+            for (int j = 0; j < s->d; ++j) xt[j] = widen(x_rows[(size_t)i * s->d + j]);
+            route_token(s, xt, C, bias, lg, pr, tk, idx_out + (size_t)i * s->K,
+                        gate_out + (size_t)i * s->K, margin_out + i);
+            if (probs_out) memcpy(probs_out + (size_t)i * s->E, pr, sizeof(double) * (size_t)s->E);
+        }
+        free(xt); free(lg); free(pr); free(tk);
+    }
+    return used;
+}
+
+/* Full forward (steps 1-5) for n_tokens tokens whose rows are x_rows.
+ * w1[e], w3[e], w2[e]: per-expert pointers (E of them), ws*[s]: per shared
+ * expert (Ks of them).  forced_idx ([n_tokens, K] or NULL) replaces the
+ * selection of step 3; gates are then the softmax scores of the forced
+ * experts.  out, shared_part, routed_part: [n_tokens, d]. */
+int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
+                       const uint16_t* C, const float* bias,
+                       const uint16_t* const* w1, const uint16_t* const* w3,
+                       const uint16_t* const* w2,
+                       const uint16_t* const* ws1, const uint16_t* const* ws3,
+                       const uint16_t* const* ws2,
+                       const int32_t* forced_idx,
+                       double* out, double* shared_part, double* routed_part,
+                       int32_t* idx_out, double* gate_out, double* margin_out,
+                       int32_t nthreads) {
+    const int d = s->d, K = s->K;
+    const int hmax = s->I > s->Is ? s->I : s->Is;
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+#pragma omp parallel num_threads(nthreads)
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double* xt = malloc(sizeof(double) * (size_t)d);
+        double* y = malloc(sizeof(double) * (size_t)d);
+        double* h = malloc(sizeof(double) * (size_t)(hmax > 0 ? hmax : 1));
+        double* lg = malloc(sizeof(double) * (size_t)s->E);
+        double* pr = malloc(sizeof(double) * (size_t)s->E);
+        uint8_t* tk = malloc((size_t)s->E);
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t i = 0; i < n_tokens; ++i) {
+            int32_t* idx = idx_out + (size_t)i * K;
+            double* gate = gate_out + (size_t)i * K;
+            double* sh = shared_part + (size_t)i * d;
+            double* ro = routed_part + (size_t)i * d;
+            for (int j = 0; j < d; ++j) xt[j] = widen(x_rows[(size_t)i * d + j]);
+
+            route_token(s, xt, C, bias, lg, pr, tk, idx, gate, margin_out + i);
+            if (forced_idx) {
+                for (int k = 0; k < K; ++k) {
+                    idx[k] = forced_idx[(size_t)i * K + k];
+                    gate[k] = pr[idx[k]];
+                }
+            }
+
+            for (int j = 0; j < d; ++j) sh[j] = 0.0;
+            for (int si = 0; si < s->Ks; ++si) {
+                expert_ffn(d, s->Is, ws1[si], ws3[si], ws2[si], xt, h, y);
+                for (int j = 0; j < d; ++j) sh[j] += y[j];
+            }
+            for (int j = 0; j < d; ++j) ro[j] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const int e = idx[k];
+                expert_ffn(d, s->I, w1[e], w3[e], w2[e], xt, h, y);
+                for (int j = 0; j < d; ++j) ro[j] += gate[k] * y[j];
+            }
+            const double res = (s->flags & ORACLE_NO_RESIDUAL) ? 0.0 : 1.0;
+            for (int j = 0; j < d; ++j) out[(size_t)i * d + j] = res * xt[j] + sh[j] + ro[j];
+        }
+        free(xt); free(y); free(h); free(lg); free(pr); free(tk);
+    }
+    return used;
+}
