@@ -1,0 +1,66 @@
+// Combine: out[t] = x[t] + sum_s Y_shared_s[t] + sum_k gate[t,k] * Y[slot(t,k)]
+//
+// The DeepSeekMoE layer output ("DeepSeekMoE 深度解读报告", sections 2.3 and
+// 3.1): shared-expert outputs enter with weight one, routed outputs with their
+// softmax gate, plus the residual stream.  Accumulated in fp32 in a fixed
+// order (residual, shared experts in order, then k = 0..K-1) and rounded once
+// to bf16, nearest-even.  A pure HBM pass: 16-byte vectors, one workgroup per
+// token row.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 128;
+
+__device__ __forceinline__ void add8(float* acc, u32x4 v, float w) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += w * __uint_as_float(u[i] << 16);
+        acc[2 * i + 1] += w * __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Y, const float* __restrict__ gate,
+    const int32_t* __restrict__ slot_of, bf16_t* __restrict__ out, int T, int d, int K, int Ks,
+    int residual) {
+    const int t = blockIdx.x;
+    const int nv = d >> 3;
+    const size_t tk = (size_t)T * K;
+    __shared__ int s_slot[256];
+    __shared__ float s_gate[256];
+    for (int k = threadIdx.x; k < K; k += kThreads) {
+        s_slot[k] = slot_of[(size_t)t * K + k];
+        s_gate[k] = gate[(size_t)t * K + k];
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < nv; v += kThreads) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        if (residual) add8(acc, reinterpret_cast<const u32x4*>(x + (size_t)t * d)[v], 1.0f);
+        for (int s = 0; s < Ks; ++s)
+            add8(acc, reinterpret_cast<const u32x4*>(Y + (tk + (size_t)s * T + t) * d)[v], 1.0f);
+        for (int k = 0; k < K; ++k)
+            add8(acc, reinterpret_cast<const u32x4*>(Y + (size_t)s_slot[k] * d)[v], s_gate[k]);
+        u32x4 o;
+        o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+        o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+        o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+        reinterpret_cast<u32x4*>(out + (size_t)t * d)[v] = o;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st) {
+    const int residual = (p.flags & 1u) ? 0 : 1;
+    combine_kernel<<<p.T, kThreads, 0, st>>>(x, p.Y, p.gate, p.slot_of, out, p.T, p.d, p.K, p.Ks,
+                                             residual);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+// Shared definitions of the gfx950 MoE kernels: bf16 / MFMA vector types,
+// the per-call plan (shape-derived sizes and the workspace carve-up) and the
+// launchers each kernel file exports to the C-ABI dispatcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;                                   // bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes) for the raw buffer loads: the
+// base and size live in scalar registers and each lane supplies a 32-bit
+// byte offset.  0x00020000 is the gfx9-family dword-3 value for untyped
+// 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+// Tokens per routing chunk: one 64-bit lane mask per (chunk, expert).
+constexpr int kChunk = 64;
+// Router GEMM tile: 64 tokens x 64 experts, d consumed 64 at a time.
+constexpr int kRouterBT = 64;
+constexpr int kRouterBE = 64;
+
+// One entry of a grouped-GEMM work list.
+struct Tile {
+    int32_t group;   // 0..E-1 routed expert, E..E+Ks-1 shared expert
+    int32_t m0;      // first row of the group covered by the tile
+    int32_t n0;      // first output column
+    int32_t nrows;   // rows of the group in this tile (<= BM)
+};
+
+// Grouped-GEMM tile configuration chosen per call.
+struct GemmCfg {
+    int bm, bn;      // rows, B-rows (output cols; for SwiGLU half W1, half W3)
+};
+
+// Everything a call needs, derived on the host from the shape.  Device
+// pointers point into the caller's workspace.
+struct Plan {
+    int T, d, E, I, K, Ks, Is;
+    uint32_t flags;
+    int Epad;        // E rounded up to the router tile
+    int nchunk;      // ceil(T / kChunk)
+    int split;       // router split over d
+    int rows;        // T*K routed rows + T*Ks shared rows
+    GemmCfg g1, g2;
+    int max_tiles1, max_tiles2;
+
+    // workspace carve-up (byte offsets while planning, then pointers)
+    float* logits;       // [split, T, Epad]
+    int32_t* idx;        // [T, K]
+    float* gate;         // [T, K]
+    uint64_t* masks;     // [nchunk, Epad]
+    int32_t* chunk_base; // [nchunk, Epad]
+    int32_t* goff;       // [E + Ks + 1] row offset of each group
+    int32_t* tok_of;     // [rows] token of each permuted row
+    int32_t* slot_of;    // [T, K] permuted row of each (token, k)
+    Tile* tiles1;        // [max_tiles1]
+    Tile* tiles2;        // [max_tiles2]
+    int32_t* ntiles;     // [2]
+    bf16_t* H;           // routed [T*K, I] then shared [Ks*T, Is]
+    bf16_t* Y;           // [rows, d]
+};
+
+// Launchers (each enqueues on `st`; return the launch status).
+hipError_t launch_router(const Plan& p, const bf16_t* x, const bf16_t* C, const float* bias,
+                         hipStream_t st);
+hipError_t launch_permute(const Plan& p, hipStream_t st);
+hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
+                               const bf16_t* w3, const bf16_t* ws1, const bf16_t* ws3,
+                               hipStream_t st);
+hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, hipStream_t st);
+hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st);
+
+}  // namespace moe

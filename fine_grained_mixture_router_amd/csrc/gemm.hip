@@ -1,0 +1,295 @@
+// Grouped expert GEMMs on bf16 MFMA (gfx950), fp32 accumulation.
+//
+//   G1 (gate/up):  H[r,:] = silu(X[tok(r)] . W1_g^T) * (X[tok(r)] . W3_g^T)
+//   G2 (down):     Y[r,:] = H[r,:] . W2_g^T
+//
+// for every row r of group g (a routed expert or a shared expert) — the
+// Expert module w2(silu(w1 x) * w3 x) of the youleyou page, applied to the
+// rows the permutation grouped per expert.  W1 and W3 share one pass: a tile
+// holds matching rows of both, so each wave owns the w1 and w3 accumulators
+// of the same outputs and applies silu(a)*b in registers before the single
+// bf16 store (the gather-in-mainloop and activation-in-epilogue ideas the
+// SonicMoE note describes, re-done for CDNA4).
+//
+// One kernel template serves both: a work-list entry (group, m0, n0, nrows)
+// names the tile; A rows are gathered through tok_of (G1) or read in place
+// (G2).  Tiles are BM x BN with BK = 64, staged through LDS (double buffer,
+// XOR-swizzled 16-byte chunks) and consumed by v_mfma_f32_32x32x16_bf16.
+// The grid is the work-list bound; workgroups past the device-side count
+// exit at once.  Workgroup ids are remapped so that each XCD (ids are dealt
+// round-robin over the 8 XCDs) takes a contiguous slice of the list, whose
+// neighbouring tiles share weights or activations in that XCD's L2.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * kBK + ((chunk ^ (row & 7)) << 3);
+}
+
+struct GemmParams {
+    const Tile* tiles;
+    const int32_t* ntiles;
+    const int32_t* goff;
+    const int32_t* tok_of;   // G1 only
+    const bf16_t* A_r;       // routed A base (G1: x, G2: H routed)
+    const bf16_t* A_s;       // shared A base (G1: x, G2: H shared)
+    const bf16_t* Ba_r;      // routed weights (G1: W1, G2: W2)
+    const bf16_t* Bb_r;      // routed W3 (G1 only)
+    const bf16_t* Ba_s;      // shared weights
+    const bf16_t* Bb_s;
+    bf16_t* O_r;             // routed output base (G1: H routed, G2: Y)
+    bf16_t* O_s;             // shared output base (G1: H shared, G2: Y)
+    int kdim_r, kdim_s;      // reduction length
+    int n_r, n_s;            // output columns
+    int E, TK;               // routed experts, routed rows (T*K)
+    uint32_t abytes_r, abytes_s;  // sizes of the A regions in bytes
+};
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+// BM x BN tile, WM x WN waves.  SWIGLU: the BN B-rows are BN/2 rows of W1
+// followed by the same BN/2 rows of W3, and the output has BN/2 columns.
+template <int BM, int BN, int WM, int WN, bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int WROWS = BM / WM;                 // rows per wave
+    constexpr int WCOLS = BN / WN;                 // B-rows per wave
+    constexpr int MB = WROWS / 32;
+    constexpr int NB = WCOLS / 32;
+    static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile shape");
+    constexpr int AL = BM / 32;                    // A chunks per thread per stage
+    constexpr int BL = BN / 32;
+
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kBK];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * kBK];
+
+    const int nt = *P.ntiles;
+    const int wg = blockIdx.x;
+    const int nr = (nt + 7) & ~7;
+    if (wg >= nr) return;
+    const int lt = (wg & 7) * (nr >> 3) + (wg >> 3);
+    if (lt >= nt) return;
+    const Tile tl = P.tiles[lt];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    const bool shared = tl.group >= P.E;
+    const int s = tl.group - P.E;
+    const int kdim = shared ? P.kdim_s : P.kdim_r;
+    const int ncols = shared ? P.n_s : P.n_r;
+    const int grow = P.goff[tl.group] + tl.m0;      // first global row of the tile
+    const int rrow = shared ? grow - P.TK : grow;   // first row within its region
+
+    const bf16_t* wa = shared ? P.Ba_s + (size_t)s * ncols * kdim
+                              : P.Ba_r + (size_t)tl.group * ncols * kdim;
+    const bf16_t* wb = nullptr;
+    if (SWIGLU)
+        wb = shared ? P.Bb_s + (size_t)s * ncols * kdim : P.Bb_r + (size_t)tl.group * ncols * kdim;
+
+    // Raw buffer loads: resource (base, size) in scalar registers, a 32-bit
+    // byte offset per lane, the k position in the scalar offset.  Rows past
+    // the tile's end are clamped to its first row and weight rows past the
+    // output width to the last one, so every access stays inside its tensor
+    // (those rows are never stored).
+    const int ch = tid & 7;
+    const __amdgpu_buffer_rsrc_t ra_src =
+        make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * 2u;
+    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(wa, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(SWIGLU ? wb : wa, wbytes);
+    uint32_t aoff[AL];
+    uint32_t boff[BL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        const int rr = r < tl.nrows ? r : 0;
+        uint32_t arow;
+        if (SWIGLU) arow = (uint32_t)P.tok_of[grow + rr];
+        else arow = (uint32_t)(rrow + rr);
+        aoff[i] = (arow * (uint32_t)kdim + ch * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+        const int r = (tid >> 3) + 32 * i;        // i < BL/2 <=> r < BN/2
+        int n = tl.n0 + ((SWIGLU && r >= BN / 2) ? r - BN / 2 : r);
+        n = n < ncols ? n : ncols - 1;
+        boff[i] = ((uint32_t)n * (uint32_t)kdim + ch * 8) * 2u;
+    }
+
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+    // LDS addressing.  Every row index used below is (multiple of 8) + the
+    // lane's own (lane & 7) or (tid >> 3) & 7, so the swizzled chunk position
+    // of a lane is fixed per k16 step and the rest is a compile-time or
+    // wave-uniform row offset.
+    const int srow = tid >> 3;
+    const int sx = (ch ^ (srow & 7)) << 3;
+    bf16_t* const a_st = &sA[0][0] + srow * kBK + sx;
+    bf16_t* const b_st = &sB[0][0] + srow * kBK + sx;
+    const int lrow = lane & 31;
+    int cx[kBK / 16];
+#pragma unroll
+    for (int st = 0; st < kBK / 16; ++st) cx[st] = ((2 * st + (lane >> 5)) ^ (lane & 7)) << 3;
+    const bf16_t* const a_ld = &sA[0][0] + (wm * WROWS + lrow) * kBK;
+    const bf16_t* const b_ld = &sB[0][0] + lrow * kBK;
+
+    const int nk = kdim / kBK;
+    u32x4 ra[AL], rb[BL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], 0);
+#pragma unroll
+    for (int i = 0; i < BL; ++i) rb[i] = buf_load16((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], 0);
+#pragma unroll
+    for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(a_st + 32 * i * kBK) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(b_st + 32 * i * kBK) = rb[i];
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const uint32_t kb = (uint32_t)(kt + 1) * kBK * 2u;
+#pragma unroll
+            for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb);
+#pragma unroll
+            for (int i = 0; i < BL; ++i)
+                rb[i] = buf_load16((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], kb);
+        }
+        const bf16_t* a_b = a_ld + buf * (BM * kBK);
+        const bf16_t* b_b = b_ld + buf * (BN * kBK);
+#pragma unroll
+        for (int st = 0; st < kBK / 16; ++st) {
+            bf16x8 af[MB], bfr[NB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(a_b + i * 32 * kBK + cx[st]);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                int bro;
+                if (SWIGLU) {
+                    constexpr int half = NB / 2;
+                    bro = (j < half ? 0 : BN / 2) + wn * (WCOLS / 2) + (j < half ? j : j - half) * 32;
+                } else {
+                    bro = wn * WCOLS + j * 32;
+                }
+                bfr[j] = *reinterpret_cast<const bf16x8*>(b_b + bro * kBK + cx[st]);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            const int nb = buf ^ 1;
+#pragma unroll
+            for (int i = 0; i < AL; ++i)
+                *reinterpret_cast<u32x4*>(a_st + nb * (BM * kBK) + 32 * i * kBK) = ra[i];
+#pragma unroll
+            for (int i = 0; i < BL; ++i)
+                *reinterpret_cast<u32x4*>(b_st + nb * (BN * kBK) + 32 * i * kBK) = rb[i];
+        }
+        __syncthreads();
+    }
+
+    // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and
+    // rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
+    bf16_t* obase = shared ? P.O_s : P.O_r;
+    const int orow0 = SWIGLU ? rrow : grow;
+    const int ocols = SWIGLU ? ncols : ncols;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+        for (int j = 0; j < (SWIGLU ? NB / 2 : NB); ++j) {
+            const int col = tl.n0 + (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + j * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * WROWS + i * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+                float v;
+                if (SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + NB / 2][r];
+                else v = acc[i][j][r];
+                if (row < tl.nrows && col < ocols)
+                    obase[(size_t)(orow0 + row) * ocols + col] = f32_to_bf16(v);
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, bool SWIGLU>
+hipError_t launch_cfg(const GemmParams& gp, int max_tiles, hipStream_t st) {
+    const int grid = (max_tiles + 7) & ~7;
+    if (grid == 0) return hipSuccess;
+    grouped_gemm_kernel<BM, BN, WM, WN, SWIGLU><<<grid, kThreads, 0, st>>>(gp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
+                               const bf16_t* w3, const bf16_t* ws1, const bf16_t* ws3,
+                               hipStream_t st) {
+    GemmParams gp{};
+    gp.tiles = p.tiles1;
+    gp.ntiles = p.ntiles;
+    gp.goff = p.goff;
+    gp.tok_of = p.tok_of;
+    gp.A_r = x;
+    gp.A_s = x;
+    gp.Ba_r = w1;
+    gp.Bb_r = w3;
+    gp.Ba_s = ws1;
+    gp.Bb_s = ws3;
+    gp.O_r = p.H;
+    gp.O_s = p.H + (size_t)p.T * p.K * p.I;
+    gp.kdim_r = p.d;
+    gp.kdim_s = p.d;
+    gp.n_r = p.I;
+    gp.n_s = p.Is;
+    gp.E = p.E;
+    gp.TK = p.T * p.K;
+    gp.abytes_r = (uint32_t)((size_t)p.T * p.d * 2);
+    gp.abytes_s = gp.abytes_r;
+    if (p.g1.bm == 256) return launch_cfg<256, 256, 2, 2, true>(gp, p.max_tiles1, st);
+    return launch_cfg<32, 256, 1, 4, true>(gp, p.max_tiles1, st);
+}
+
+hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, hipStream_t st) {
+    GemmParams gp{};
+    gp.tiles = p.tiles2;
+    gp.ntiles = p.ntiles + 1;
+    gp.goff = p.goff;
+    gp.tok_of = nullptr;
+    gp.A_r = p.H;
+    gp.A_s = p.H + (size_t)p.T * p.K * p.I;
+    gp.Ba_r = w2;
+    gp.Bb_r = nullptr;
+    gp.Ba_s = ws2;
+    gp.Bb_s = nullptr;
+    gp.O_r = p.Y;
+    gp.O_s = p.Y;
+    gp.kdim_r = p.I;
+    gp.kdim_s = p.Is;
+    gp.n_r = p.d;
+    gp.n_s = p.d;
+    gp.E = p.E;
+    gp.TK = p.T * p.K;
+    gp.abytes_r = (uint32_t)((size_t)p.T * p.K * p.I * 2);
+    gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
+    if (p.g2.bm == 256) return launch_cfg<256, 256, 2, 2, false>(gp, p.max_tiles2, st);
+    return launch_cfg<32, 256, 1, 4, false>(gp, p.max_tiles2, st);
+}
+
+}  // namespace moe

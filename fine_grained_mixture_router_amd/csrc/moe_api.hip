@@ -1,0 +1,249 @@
+// C-ABI dispatcher: validation, per-call plan and workspace carve-up, and the
+// launch sequence router -> permutation -> G1 -> G2 -> combine, all enqueued
+// on the caller's stream with no host synchronisation and no allocation.
+#include <atomic>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool shape_ok(const moe_shape_t* s) {
+    if (!s) return false;
+    if (s->T < 1 || s->T > (1 << 24)) return false;
+    if (s->d < 64 || s->d > 65536 || s->d % 64) return false;
+    if (s->E < 1 || s->E > 256) return false;
+    if (s->K < 0 || s->K > s->E) return false;
+    if (s->I < 64 || s->I > 65536 || s->I % 64) return false;
+    if (s->Ks < 0 || s->Ks > 16) return false;
+    if (s->Ks > 0 && (s->Is < 64 || s->Is > 65536 || s->Is % 64)) return false;
+    if (s->flags & ~MOE_FLAG_NO_RESIDUAL) return false;
+    const long long rows = (long long)s->T * (s->K + s->Ks);
+    if (rows > (1LL << 30)) return false;
+    // The GEMM kernels address x, H and one expert's weights with 32-bit
+    // byte offsets: keep each of those below 2^31 bytes.
+    const long long lim = 1LL << 31;
+    const long long Is = s->Ks > 0 ? s->Is : 0;
+    if ((long long)s->T * s->d * 2 >= lim) return false;
+    if ((long long)s->T * s->K * s->I * 2 >= lim) return false;
+    if ((long long)s->T * s->Ks * Is * 2 >= lim) return false;
+    if ((long long)s->I * s->d * 2 >= lim || Is * s->d * 2 >= lim) return false;
+    return true;
+}
+
+// Fill the shape-derived part of the plan and the workspace offsets (as byte
+// offsets from 0); returns the total workspace size.
+size_t make_plan(const moe_shape_t* s, Plan* p) {
+    memset(p, 0, sizeof(*p));
+    p->T = s->T;
+    p->d = s->d;
+    p->E = s->E;
+    p->I = s->I;
+    p->K = s->K;
+    p->Ks = s->Ks;
+    p->Is = s->Ks > 0 ? s->Is : 64;
+    p->flags = s->flags;
+    p->Epad = (s->E + kRouterBE - 1) / kRouterBE * kRouterBE;
+    p->nchunk = (s->T + kChunk - 1) / kChunk;
+    const int nk = s->d / 64;
+    const int rtiles = ((s->T + kRouterBT - 1) / kRouterBT) * (p->Epad / kRouterBE);
+    int split = (256 + rtiles - 1) / rtiles;
+    split = split < 1 ? 1 : (split > nk ? nk : split);
+    const int kps = (nk + split - 1) / split;
+    p->split = (nk + kps - 1) / kps;
+    const long long TK = (long long)s->T * s->K;
+    p->rows = (int)(TK + (long long)s->T * s->Ks);
+
+    // Few rows per expert (decode-sized batches): thin tiles that stream each
+    // weight once; otherwise 256x256 MFMA tiles.
+    const bool thin = TK < 64LL * s->E;
+    p->g1.bm = thin ? 32 : 256;
+    p->g1.bn = 256;
+    p->g2.bm = thin ? 32 : 256;
+    p->g2.bn = 256;
+    const long long busy = TK < s->E ? TK : s->E;
+    const long long n1r = (s->I + p->g1.bn / 2 - 1) / (p->g1.bn / 2);
+    const long long n1s = (p->Is + p->g1.bn / 2 - 1) / (p->g1.bn / 2);
+    const long long n2 = (s->d + p->g2.bn - 1) / p->g2.bn;
+    const long long m1s = (s->T + p->g1.bm - 1) / p->g1.bm;
+    const long long m2s = (s->T + p->g2.bm - 1) / p->g2.bm;
+    const long long t1 = (TK / p->g1.bm + busy) * n1r + (long long)s->Ks * m1s * n1s;
+    const long long t2 = (TK / p->g2.bm + busy) * n2 + (long long)s->Ks * m2s * n2;
+    p->max_tiles1 = (int)t1;
+    p->max_tiles2 = (int)t2;
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    p->logits = (float*)take(s->K > 0 ? (size_t)p->split * s->T * p->Epad * 4 : 0);
+    p->idx = (int32_t*)take((size_t)TK * 4);
+    p->gate = (float*)take((size_t)TK * 4);
+    p->masks = (uint64_t*)take((size_t)p->nchunk * p->Epad * 8);
+    p->chunk_base = (int32_t*)take((size_t)p->nchunk * p->Epad * 4);
+    p->goff = (int32_t*)take((size_t)(s->E + s->Ks + 1) * 4);
+    p->tok_of = (int32_t*)take((size_t)p->rows * 4);
+    p->slot_of = (int32_t*)take((size_t)TK * 4);
+    p->tiles1 = (Tile*)take((size_t)p->max_tiles1 * sizeof(Tile));
+    p->tiles2 = (Tile*)take((size_t)p->max_tiles2 * sizeof(Tile));
+    p->ntiles = (int32_t*)take(16);
+    p->H = (bf16_t*)take(((size_t)TK * s->I + (size_t)s->T * s->Ks * p->Is) * 2);
+    p->Y = (bf16_t*)take((size_t)p->rows * s->d * 2);
+    return off;
+}
+
+template <class T>
+T* rebase(T* off, char* base) {
+    return reinterpret_cast<T*>(base + reinterpret_cast<size_t>(off));
+}
+
+void place(Plan* p, void* ws) {
+    char* b = static_cast<char*>(ws);
+    p->logits = rebase(p->logits, b);
+    p->idx = rebase(p->idx, b);
+    p->gate = rebase(p->gate, b);
+    p->masks = rebase(p->masks, b);
+    p->chunk_base = rebase(p->chunk_base, b);
+    p->goff = rebase(p->goff, b);
+    p->tok_of = rebase(p->tok_of, b);
+    p->slot_of = rebase(p->slot_of, b);
+    p->tiles1 = rebase(p->tiles1, b);
+    p->tiles2 = rebase(p->tiles2, b);
+    p->ntiles = rebase(p->ntiles, b);
+    p->H = rebase(p->H, b);
+    p->Y = rebase(p->Y, b);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// 0 unknown, 1 gfx950, 2 other architecture
+std::atomic<int> g_arch[64];
+
+moe_status_t device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return MOE_ERR_NO_DEVICE;
+    }
+    int known = dev < 64 ? g_arch[dev].load(std::memory_order_relaxed) : 0;
+    if (known == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return MOE_ERR_NO_DEVICE;
+        }
+        known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (dev < 64) g_arch[dev].store(known, std::memory_order_relaxed);
+    }
+    return known == 1 ? MOE_OK : MOE_ERR_DEVICE_ARCH;
+}
+
+moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* centroids,
+                          const float* bias, void* ws, size_t ws_bytes, Plan* plan) {
+    if (!shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (!x || !ws) return MOE_ERR_NULL;
+    if (shape->K > 0 && !centroids) return MOE_ERR_NULL;
+    if (!aligned(x, 16) || (centroids && !aligned(centroids, 16))) return MOE_ERR_ALIGN;
+    if (bias && !aligned(bias, 4)) return MOE_ERR_ALIGN;
+    if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
+    const size_t need = make_plan(shape, plan);
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) size_t moe_workspace_size(const moe_shape_t* shape) {
+    if (!shape_ok(shape)) return 0;
+    Plan p;
+    return make_plan(shape, &p);
+}
+
+__attribute__((visibility("default"))) const char* moe_status_string(moe_status_t st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: shape outside the supported limits or bad flags";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is misaligned";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_size()";
+        case MOE_ERR_NO_DEVICE: return "MOE_ERR_NO_DEVICE: no HIP device is available";
+        case MOE_ERR_DEVICE_ARCH: return "MOE_ERR_DEVICE_ARCH: the current device is not gfx950";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    }
+    return "unknown moe_status_t";
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_forward(
+    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
+    const void* w1, const void* w3, const void* w2, const void* ws1, const void* ws3,
+    const void* ws2, void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    Plan p;
+    moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes, &p);
+    if (st != MOE_OK) return st;
+    if (!out) return MOE_ERR_NULL;
+    if (shape->K > 0 && (!w1 || !w3 || !w2)) return MOE_ERR_NULL;
+    if (shape->Ks > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_NULL;
+    const void* bf[] = {out, shape->K > 0 ? w1 : nullptr, shape->K > 0 ? w3 : nullptr,
+                        shape->K > 0 ? w2 : nullptr, shape->Ks > 0 ? ws1 : nullptr,
+                        shape->Ks > 0 ? ws3 : nullptr, shape->Ks > 0 ? ws2 : nullptr};
+    for (const void* q : bf)
+        if (q && !aligned(q, 16)) return MOE_ERR_ALIGN;
+    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_gate && !aligned(topk_gate, 4)))
+        return MOE_ERR_ALIGN;
+    st = device_ok();
+    if (st != MOE_OK) return st;
+
+    place(&p, workspace);
+    if (topk_idx) p.idx = topk_idx;
+    if (topk_gate) p.gate = topk_gate;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    if (p.K > 0 &&
+        launch_router(p, xb, static_cast<const bf16_t*>(centroids), expert_bias, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_permute(p, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm_gate_up(p, xb, static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3),
+                            static_cast<const bf16_t*>(ws1), static_cast<const bf16_t*>(ws3),
+                            s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_gemm_down(p, static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(ws2), s) !=
+        hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_combine(p, xb, static_cast<bf16_t*>(out), s) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_route(
+    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
+    int32_t* topk_idx, float* topk_gate, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes, &p);
+    if (st != MOE_OK) return st;
+    if (shape->K < 1) return MOE_ERR_SHAPE;
+    if (!topk_idx || !topk_gate) return MOE_ERR_NULL;
+    if (!aligned(topk_idx, 4) || !aligned(topk_gate, 4)) return MOE_ERR_ALIGN;
+    st = device_ok();
+    if (st != MOE_OK) return st;
+    place(&p, workspace);
+    p.idx = topk_idx;
+    p.gate = topk_gate;
+    if (launch_router(p, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(centroids),
+                      expert_bias, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Router: token-to-centroid affinities, softmax and top-K selection.
+//
+// Definition: the generic top-K gate of "DeepSeekMoE 深度解读报告" section 3.1
+// (softmax over the inner products of the token with every expert centroid,
+// keep the K largest scores, zero the rest, no renormalisation), plus an
+// optional fixed per-expert logit bias.
+//
+// Two kernels:
+//   router_logits  bf16 MFMA GEMM x[T,d] . C[E,d]^T -> fp32 partial logits.
+//                  Tiles of 64 tokens x 64 experts; for small T the d range is
+//                  split so that the launch still covers the chip, and the
+//                  partials are summed in a fixed order by the next kernel.
+//   router_select  one wavefront per token: sum partials, add the bias, fp32
+//                  softmax, then K rounds of a wavefront arg-max over the E<=256
+//                  logits (4 per lane; ties go to the lower expert id).  Each
+//                  workgroup owns a 64-token chunk and also records, per expert,
+//                  the 64-bit mask of its tokens that chose that expert; the
+//                  permutation step turns those masks into a stable,
+//                  atomics-free grouping of tokens by expert.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+// 64 rows x 64 bf16 of a row-major tile, one 16-byte chunk per (row, c),
+// stored at chunk position c ^ (row & 7) so that the MFMA fragment reads of
+// eight consecutive rows hit distinct LDS banks.
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * 64 + ((chunk ^ (row & 7)) << 3);
+}
+
+__global__ __launch_bounds__(kThreads) void router_logits_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ C, float* __restrict__ logits,
+    int T, int d, int E, int Epad, int ksteps_per_split) {
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][kRouterBT * 64];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][kRouterBE * 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int t0 = blockIdx.x * kRouterBT;
+    const int e0 = blockIdx.y * kRouterBE;
+    const int split = blockIdx.z;
+    const int nk = d >> 6;
+    const int k_begin = split * ksteps_per_split;
+    const int k_end = min(nk, k_begin + ksteps_per_split);
+
+    // each thread moves 2 chunks of A and 2 of B per 64-wide k step
+    const int ch = tid & 7;
+    const bf16_t* pa[2];
+    const bf16_t* pb[2];
+    bool bvalid[2];
+    int rrow[2];
+    for (int i = 0; i < 2; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        rrow[i] = r;
+        const int t = min(t0 + r, T - 1);
+        pa[i] = x + (size_t)t * d + ch * 8;
+        const int e = e0 + r;
+        bvalid[i] = e < E;
+        pb[i] = C + (size_t)(bvalid[i] ? e : 0) * d + ch * 8;
+    }
+
+    f32x16 acc = {};
+    u32x4 ra[2], rb[2];
+    auto gload = [&](int kt) {
+        for (int i = 0; i < 2; ++i) {
+            ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + (size_t)kt * 64);
+            rb[i] = bvalid[i] ? *reinterpret_cast<const u32x4*>(pb[i] + (size_t)kt * 64)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto sstore = [&](int buf) {
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4*>(&sA[buf][swz(rrow[i], ch)]) = ra[i];
+            *reinterpret_cast<u32x4*>(&sB[buf][swz(rrow[i], ch)]) = rb[i];
+        }
+    };
+
+    if (k_begin < k_end) {
+        gload(k_begin);
+        sstore(0);
+        __syncthreads();
+        for (int kt = k_begin; kt < k_end; ++kt) {
+            const int buf = (kt - k_begin) & 1;
+            if (kt + 1 < k_end) gload(kt + 1);
+            const int arow = wm * 32 + (lane & 31);
+            const int brow = wn * 32 + (lane & 31);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int c = 2 * s + (lane >> 5);
+                bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(arow, c)]);
+                bf16x8 b = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(brow, c)]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+            }
+            if (kt + 1 < k_end) sstore(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // 32x32 accumulator: lane holds column (lane & 31), rows
+    // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
+    const int col = e0 + wn * 32 + (lane & 31);
+    float* outp = logits + (size_t)split * T * Epad;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = t0 + wm * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+        if (row < T) outp[(size_t)row * Epad + col] = acc[r];
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void router_select_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ idx,
+    float* __restrict__ gate, uint64_t* __restrict__ masks, int T, int E, int Epad, int K,
+    int split) {
+    __shared__ unsigned long long smask[256];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = blockIdx.x;
+    for (int e = tid; e < Epad; e += kThreads) smask[e] = 0ull;
+    __syncthreads();
+
+    const float NEG = -INFINITY;
+    for (int i = 0; i < kChunk / 4; ++i) {
+        const int tl = wave * (kChunk / 4) + i;       // token within the chunk
+        const int t = c * kChunk + tl;
+        if (t >= T) break;
+        float v[4];
+        int taken = 0;                                // bit j: expert lane + 64j is out
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E) {
+                float s = 0.f;
+                for (int z = 0; z < split; ++z) s += logits[((size_t)z * T + t) * Epad + e];
+                if (bias) s += bias[e];
+                v[j] = s;
+            } else {
+                v[j] = NEG;
+                taken |= 1 << j;
+            }
+        }
+        const float mx = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ps += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
+        const float sum = wave_sum(ps);
+
+        for (int k = 0; k < K; ++k) {
+            // local best: strictly greater wins, so the lower j (lower e) keeps ties
+            float bv = NEG;
+            int be = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!((taken >> j) & 1) && (be == 0x7fffffff || v[j] > bv)) {
+                    bv = v[j];
+                    be = lane + 64 * j;
+                }
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oe = __shfl_xor(be, o, 64);
+                if (ov > bv || (ov == bv && oe < be)) {
+                    bv = ov;
+                    be = oe;
+                }
+            }
+            if ((be & 63) == lane) taken |= 1 << (be >> 6);
+            if (lane == 0) {
+                idx[(size_t)t * K + k] = be;
+                gate[(size_t)t * K + k] = expf(bv - mx) / sum;
+                atomicOr(&smask[be], 1ull << tl);
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < Epad; e += kThreads) masks[(size_t)c * Epad + e] = smask[e];
+}
+
+}  // namespace
+
+hipError_t launch_router(const Plan& p, const bf16_t* x, const bf16_t* C, const float* bias,
+                         hipStream_t st) {
+    const int nk = p.d / 64;
+    const int kps = (nk + p.split - 1) / p.split;
+    dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.Epad / kRouterBE, p.split);
+    router_logits_kernel<<<grid, kThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    router_select_kernel<<<p.nchunk, kThreads, 0, st>>>(p.logits, bias, p.idx, p.gate, p.masks,
+                                                       p.T, p.E, p.Epad, p.K, p.split);
+    return hipGetLastError();
+}
+
+}  // namespace moe

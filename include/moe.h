@@ -1,0 +1,114 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ *
+ * The layer (definitions from "DeepSeekMoE 深度解读报告", sections 2.2, 2.3
+ * and 3.1, and the Expert module of the youleyou page "DeepSeek MoE模型优化
+ * 与未来演进及字节超稀疏内存技术"):
+ *
+ *   s[t,e]  = softmax_e( x[t]·C[e] + b[e] )               over E routed experts
+ *   top-K   = the K largest s[t,e] (ties: lower e first), gate = s, no renorm
+ *   FFN_W   = W2 · ( silu(W1·x) ⊙ (W3·x) ),  silu(z) = z / (1 + e^-z)
+ *   out[t]  = x[t] + Σ_{s<Ks} FFN_shared_s(x[t]) + Σ_k gate[t,k]·FFN_{idx[t,k]}(x[t])
+ *
+ * E = N·m fine-grained routed experts of inter-dim I (an FFN of inter I·m
+ * split m ways along its intermediate dimension, section 2.2); Ks shared
+ * experts of inter-dim Is that bypass the router (section 2.3).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates or frees device memory, never synchronises and
+ *     keeps no state between calls; work is enqueued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream) and faults surface
+ *     at the caller's next synchronisation.  Calls on different streams are
+ *     independent when each uses its own workspace.
+ *   - bf16 tensors are bfloat16 bit patterns, row-major and contiguous, in
+ *     the nn.Linear [out_features, in_features] layout; their pointers must
+ *     be 16-byte aligned.  float / int32 pointers must be 4-byte aligned; the
+ *     workspace 256-byte aligned.
+ *   - Every argument is validated before anything is enqueued.  On any error
+ *     nothing is launched and no output is written.  No C++ exception crosses
+ *     the ABI.
+ *   - Shape limits: 1 <= T <= 2^24; d a multiple of 64 in [64, 65536];
+ *     1 <= E <= 256; 0 <= K <= E; I a multiple of 64 in [64, 65536];
+ *     0 <= Ks <= 16; Is a multiple of 64 in [64, 65536] when Ks > 0 (ignored
+ *     when Ks == 0).  gfx950 devices only.
+ *   - NaN / Inf inputs are outside the contract.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer shape.  T tokens of width d; E routed experts of inter-dim I, K of
+ * them active per token; Ks shared experts of inter-dim Is. */
+typedef struct {
+    int32_t T, d, E, I, K, Ks, Is;
+    uint32_t flags;
+} moe_shape_t;
+
+/* flags: out excludes the residual x (out = shared + routed).  Used to
+ * check the expert contributions on their own.  All other bits must be 0. */
+#define MOE_FLAG_NO_RESIDUAL 1u
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                  */
+    MOE_ERR_SHAPE = 2,       /* shape outside the limits above, or bad flags */
+    MOE_ERR_ALIGN = 3,       /* a pointer is not aligned as required        */
+    MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size() */
+    MOE_ERR_NO_DEVICE = 5,   /* no HIP device is visible / current          */
+    MOE_ERR_DEVICE_ARCH = 6, /* the current device is not gfx950            */
+    MOE_ERR_HIP = 7          /* a HIP launch failed                         */
+} moe_status_t;
+
+/* Bytes of device workspace moe_forward / moe_route need for this shape
+ * (routing scratch, the token permutation, tile lists, and the bf16
+ * intermediates H [T·K·I + T·Ks·Is] and Y [T·(K+Ks), d]).  Pure host
+ * arithmetic, no HIP call.  Returns 0 when the shape is invalid. */
+size_t moe_workspace_size(const moe_shape_t* shape);
+
+/* Full layer forward (the definition at the top of this file).
+ *
+ *   x          bf16 [T, d]        tokens
+ *   centroids  bf16 [E, d]        expert centroids (may be NULL iff K == 0)
+ *   expert_bias fp32 [E] or NULL  fixed per-expert logit bias added before
+ *                                 the softmax (affects selection and gates)
+ *   w1, w3     bf16 [E, I, d]     routed gate / up projections (NULL iff K == 0)
+ *   w2         bf16 [E, d, I]     routed down projections      (NULL iff K == 0)
+ *   ws1, ws3   bf16 [Ks, Is, d]   shared experts               (NULL iff Ks == 0)
+ *   ws2        bf16 [Ks, d, Is]
+ *   out        bf16 [T, d]        result, rounded once from fp32 (nearest-even)
+ *   topk_idx   int32 [T, K] or NULL  selected experts, descending score
+ *   topk_gate  fp32  [T, K] or NULL  their softmax scores
+ *   workspace / workspace_bytes   device scratch of moe_workspace_size() bytes
+ *
+ * Arithmetic: affinities by bf16 MFMA with fp32 accumulation, softmax and
+ * top-K in fp32; expert GEMMs bf16 x bf16 -> fp32, SwiGLU in fp32, the
+ * intermediates H and Y stored as bf16; the combine accumulates in fp32.
+ * Results are bit-identical from run to run (no atomics decide any order). */
+moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* centroids,
+                         const float* expert_bias, const void* w1, const void* w3,
+                         const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                         void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Routing only: affinities, softmax, top-K ("DeepSeekMoE 深度解读报告",
+ * section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both
+ * required); same workspace as moe_forward.  K must be >= 1. */
+moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* centroids,
+                       const float* expert_bias, int32_t* topk_idx, float* topk_gate,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,119 @@
+"""Shared pieces of the GPU parity tests: upload of seeded inputs, the judged
+comparisons (routing under the 1e-5 score-margin rule, max |err| <= 2e-2 *
+RMS(out)) and the stricter component checks."""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+
+ROUTE_MARGIN = 1e-5
+OUT_TOL = 2e-2
+# Bars for the expert parts checked on their own (residual dropped).  Those
+# outputs are themselves bf16, so their final rounding alone reaches
+# 2^-9 * max|part| ~ 1.0-1.4 % of RMS(part) over a 64K-element tensor; the
+# bf16 intermediates H and Y add ~0.8 % and ~1.1-1.5 %.  Emulating the three
+# roundings on the CPU on the very token samples the tests draw gives a max
+# error of 2.1-3.1 % of RMS and an RMS error of 0.29 % of RMS at the tiny,
+# 2B, 16B and 16B-Zipf shapes.  So a part must meet max|err| <= 5e-2 * RMS
+# and RMS(err) <= 1e-2 * RMS — the second is far more sensitive to a wrong
+# expert, gate or row than any max bound.  The judged bar on the layer
+# output (whose RMS includes the residual) stays 2e-2.
+PART_TOL = 5e-2
+PART_RMS_TOL = 1e-2
+
+
+def to_dev(a, dtype=None):
+    import torch
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def upload(L: dict) -> dict:
+    return {k: to_dev(v) for k, v in L.items()}
+
+
+def gpu_forward(D: dict, K: int, no_residual=False, Ks=None, **kw):
+    import fine_grained_mixture_router_amd as moe
+    ws1, ws3, ws2 = D["ws1"], D["ws3"], D["ws2"]
+    if Ks == 0:
+        ws1 = ws3 = ws2 = None
+    return moe.forward(D["x"], D["C"] if K > 0 else D.get("C"), D["w1"], D["w3"], D["w2"],
+                       ws1, ws3, ws2, K=K, bias=D.get("bias"), no_residual=no_residual,
+                       return_routing=True, **kw)
+
+
+def bf16_bits(t) -> np.ndarray:
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def out_f64(t) -> np.ndarray:
+    return synth.bf16_to_f64(bf16_bits(t))
+
+
+def rms(a) -> float:
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def check_routing(idx_gpu, gate_gpu, ref_idx, ref_gate, ref_margin, K):
+    """Index sets equal wherever the oracle's K-th vs (K+1)-th score margin
+    exceeds 1e-5; positions equal where both neighbouring gaps exceed it;
+    gates to 1e-5 relative (+1e-7) at matching positions.  Returns the number
+    of tokens exempt from the set check."""
+    exempt = 0
+    n = ref_idx.shape[0]
+    for t in range(n):
+        if ref_margin[t] > ROUTE_MARGIN:
+            assert set(idx_gpu[t].tolist()) == set(ref_idx[t].tolist()), (
+                t, idx_gpu[t], ref_idx[t], ref_margin[t])
+        else:
+            exempt += 1
+        g = ref_gate[t]
+        for k in range(K):
+            left = k == 0 or g[k - 1] - g[k] > ROUTE_MARGIN
+            right = (ref_margin[t] > ROUTE_MARGIN) if k == K - 1 else (g[k] - g[k + 1] > ROUTE_MARGIN)
+            if left and right:
+                assert idx_gpu[t, k] == ref_idx[t, k], (t, k, idx_gpu[t], ref_idx[t])
+                assert abs(gate_gpu[t, k] - g[k]) <= 1e-5 * g[k] + 1e-7, (t, k, gate_gpu[t, k], g[k])
+    return exempt
+
+
+def check_close(got, ref, tol=OUT_TOL, what="out", rms_tol=None):
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    scale = rms(ref)
+    assert err <= tol * scale, f"{what}: max|err| {err:.3e} > {tol} * RMS {scale:.3e}"
+    if rms_tol is not None:
+        r = rms(got - ref)
+        assert r <= rms_tol * scale, f"{what}: RMS(err) {r:.3e} > {rms_tol} * RMS {scale:.3e}"
+    return err / scale if scale else 0.0
+
+
+def check_part(got, ref, what):
+    return check_close(got, ref, tol=PART_TOL, what=what, rms_tol=PART_RMS_TOL)
+
+
+def check_rounding(out_bits, ref, shared, routed, margin=None):
+    """Each bf16 output within one bf16 ulp of the exact value rounded once,
+    plus the bf16 error the expert outputs carry into it: H and Y are stored
+    as bf16, an error of about 2^-9 of the typical magnitude of the shared
+    and routed parts, budgeted here at 2^-6 of their RMS over the token's row
+    (an element can cancel to near zero while its error does not).  Catches
+    double rounding or a bf16 accumulation of the output, which cost a full
+    ulp on every large value."""
+    got = synth.bf16_to_f64(out_bits)
+    r32 = ref.astype(np.float32)
+    rne = synth.bf16_to_f64(synth.f32_to_bf16_rne(r32))
+    ulp = np.abs(synth.bf16_to_f64(synth.f32_to_bf16_rne(r32) + 1) - rne)
+    row_rms = np.sqrt(np.mean(shared ** 2, axis=1)) + np.sqrt(np.mean(routed ** 2, axis=1))
+    budget = ulp * 1.0000001 + 2.0 ** -6 * row_rms[:, None]
+    bad = np.abs(got - rne) > budget
+    if margin is not None:       # near-tie tokens may route differently: skip them
+        bad &= (np.asarray(margin) > ROUTE_MARGIN)[:, None]
+    assert not bad.any(), f"{bad.sum()} outputs more than 1 bf16 ulp (+ expert budget) from RNE(oracle)"

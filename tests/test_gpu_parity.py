@@ -1,0 +1,185 @@
+"""Parity of the HIP layer (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Judged bars: routing index sets equal wherever the oracle's K-th vs (K+1)-th
+softmax-score margin exceeds 1e-5; outputs within max|err| <= 2e-2 *
+RMS(out).  Because RMS(out) is dominated by the residual, the expert parts
+are also checked on their own: the delta with the residual dropped, the
+routed part alone under the GPU's own routing (forced in the oracle), the
+shared part alone, gates to 1e-5 relative, and every output within one bf16
+ulp of the oracle rounded once.  Runs twice must be bit-identical.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import workloads as wl
+
+from helpers import (bf16_bits, check_close, check_part, check_rounding, check_routing,
+                     gpu_forward, out_f64, rms, upload)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import fine_grained_mixture_router_amd as moe  # noqa: E402  (fails loudly if unbuilt)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _inputs(w):
+    L = wl.gen_all(w)
+    return L, upload(L)
+
+
+def _oracle(L, w, tokens, K=None, no_residual=False, forced=None, Ks=None):
+    K = w.K if K is None else K
+    x = L["x"][tokens]
+    ws = (L["ws1"], L["ws3"], L["ws2"]) if Ks != 0 else (L["ws1"][:0], L["ws3"][:0], L["ws2"][:0])
+    return oracle.forward(x, L["C"], L["bias"], L["w1"], L["w3"], L["w2"], *ws, K,
+                          no_residual=no_residual, forced_idx=forced)
+
+
+def _sample(T, n):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(T)
+    s = np.sort(rng.choice(T, n, replace=False))
+    s[0], s[-1] = 0, T - 1
+    return np.unique(s)
+
+
+SMALL = ["tiny", "2b", "16b", "16b_zipf"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_route_parity(name):
+    w = wl.WORKLOADS[name]
+    _log(f"[route] {name}")
+    L = {"x": wl.gen_x(w), "C": wl.gen_centroids(w), "bias": wl.gen_bias(w)}
+    D = upload(L)
+    idx, gate = moe.route(D["x"], D["C"], K=w.K, bias=D["bias"])
+    torch.cuda.synchronize()
+    ri, rg, rm = oracle.route(L["x"], L["C"], L["bias"], w.K)
+    exempt = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), ri, rg, rm, w.K)
+    assert exempt < 0.1 * w.T
+
+
+@pytest.mark.parametrize("name,nsample", [("tiny", 128), ("2b", 192), ("16b", 128),
+                                          ("16b_zipf", 128)])
+def test_forward_parity(name, nsample):
+    w = wl.WORKLOADS[name]
+    _log(f"[forward] {name}")
+    L, D = _inputs(w)
+    out, idx, gate = gpu_forward(D, w.K)
+    torch.cuda.synchronize()
+    tok = _sample(w.T, nsample)
+    ref = _oracle(L, w, tok)
+    gi, gg = idx.cpu().numpy()[tok], gate.cpu().numpy()[tok]
+    check_routing(gi, gg, ref["idx"], ref["gate"], ref["margin"], w.K)
+    ob = bf16_bits(out)[tok]
+    check_close(synth.bf16_to_f64(ob), ref["out"])
+    check_rounding(ob, ref["out"], ref["shared"], ref["routed"], ref["margin"])
+
+    # delta (residual dropped) under the GPU's routing
+    dout, didx, _ = gpu_forward(D, w.K, no_residual=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(didx.cpu().numpy(), idx.cpu().numpy())
+    dref = _oracle(L, w, tok, no_residual=True, forced=gi)
+    check_part(out_f64(dout)[tok], dref["out"], "delta")
+
+    # routed part alone (no shared experts), forced to the GPU's routing
+    rout, ridx, _ = gpu_forward(D, w.K, no_residual=True, Ks=0)
+    torch.cuda.synchronize()
+    rref = _oracle(L, w, tok, no_residual=True, forced=ridx.cpu().numpy()[tok], Ks=0)
+    check_part(out_f64(rout)[tok], rref["routed"], "routed")
+
+    # shared part alone (K = 0)
+    sout, _, _ = gpu_forward(D, 0, no_residual=True)
+    torch.cuda.synchronize()
+    sref = _oracle(L, w, tok, K=0, no_residual=True)
+    check_part(out_f64(sout)[tok], sref["shared"], "shared")
+
+    # determinism: a second run is bit-identical
+    out2, idx2, gate2 = gpu_forward(D, w.K)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
+
+
+def _rand_layer(seed, T, d, E, I, K, Ks, Is, sc=0.02, bias=False):
+    rng = np.random.default_rng(seed)
+
+    def r(shape, s):
+        return synth.f32_to_bf16_rne((rng.standard_normal(shape) * s).astype(np.float32))
+
+    L = dict(x=r((T, d), 1.0), C=r((E, d), 0.05), w1=r((E, I, d), sc), w3=r((E, I, d), sc),
+             w2=r((E, d, I), sc), ws1=r((Ks, Is, d), sc), ws3=r((Ks, Is, d), sc),
+             ws2=r((Ks, d, Is), sc),
+             bias=(rng.standard_normal(E) * 0.5).astype(np.float32) if bias else None)
+    return L
+
+
+EDGE = [
+    # T, d, E, I, K, Ks, Is, bias   — ragged token chunks, ragged N tiles in
+    # both GEMMs (I=192, d=576), E not a multiple of 64, K=E, Ks=0, I != Is
+    (1, 64, 1, 64, 1, 0, 64, False),
+    (1, 128, 8, 64, 2, 1, 128, True),
+    (67, 576, 13, 192, 3, 2, 320, True),
+    (300, 256, 64, 128, 64, 1, 64, False),
+    (129, 320, 256, 64, 8, 0, 64, True),
+    (1000, 512, 32, 256, 6, 1, 192, False),
+    (700, 1024, 5, 512, 1, 3, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}d{c[1]}E{c[2]}I{c[3]}K{c[4]}Ks{c[5]}Is{c[6]}"
+                                            for c in EDGE])
+def test_edge_shapes(case):
+    T, d, E, I, K, Ks, Is, has_bias = case
+    _log(f"[edge] {case}")
+    L = _rand_layer(hash(case) % 1000, T, d, E, I, K, Ks, Is, bias=has_bias)
+    D = upload(L)
+    out, idx, gate = gpu_forward(D, K, Ks=None if Ks else 0)
+    torch.cuda.synchronize()
+    tok = _sample(T, 96)
+    Lw = dict(L)
+    ref = oracle.forward(L["x"][tok], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"],
+                         L["ws3"], L["ws2"], K)
+    check_routing(idx.cpu().numpy()[tok], gate.cpu().numpy()[tok], ref["idx"], ref["gate"],
+                  ref["margin"], K)
+    ob = bf16_bits(out)[tok]
+    check_close(synth.bf16_to_f64(ob), ref["out"])
+    check_rounding(ob, ref["out"], ref["shared"], ref["routed"], ref["margin"])
+    dout, didx, _ = gpu_forward(D, K, no_residual=True, Ks=None if Ks else 0)
+    torch.cuda.synchronize()
+    dref = oracle.forward(Lw["x"][tok], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"],
+                          L["ws3"], L["ws2"], K, no_residual=True,
+                          forced_idx=didx.cpu().numpy()[tok])
+    if rms(dref["out"]) > 0:
+        check_part(out_f64(dout)[tok], dref["out"], "delta")
+
+
+def test_errors_leave_output_untouched():
+    """Validation errors launch nothing: out keeps its previous contents."""
+    w = wl.WORKLOADS["tiny"]
+    L, D = _inputs(w)
+    out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoEError) as e:
+        moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
+                    K=w.K, out=out, workspace=small)
+    assert e.value.code == 4
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+    with pytest.raises(moe.MoEError) as e:
+        moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
+                    K=w.E + 1, out=out)
+    assert e.value.code == 2
