@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer forward on one MI355X.
+
+One step = one full pass of the layer (router, permutation, gate/up GEMM
+with SwiGLU, down GEMM, combine) over one batch already resident in HBM.
+
+Headline workload: the DeepSeek-V3-shape prefill batch (T=16384 tokens,
+d=7168, 256 routed + 1 shared experts of inter 2048, top-8, Zipf(1.2) logit
+bias) — MFMA-bound.  The same layer on a 256-token decode batch (HBM-bound)
+is measured in the same run and reported under "decode".  Inputs are seeded
+synthetic data (bf16, N(0,1) activations, N(0,0.006) weights).
+
+Prints ONE JSON line:
+  value            tokens/s of the whole layer (T / ms_per_step)
+  roofline         the dominant kernel (gemm_gate_up): algorithmic FLOPs (or
+                   bytes, decode) per launch / its mean duration from HIP
+                   events recorded around it on its own stream during the
+                   timed steps, against the MI355X peak
+  cpu_baseline     the fp64 oracle on a bounded token sample of the same
+                   batch, on the host cores (a reported baseline, not a target)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s; % of MFMA (prefill) / HBM (decode) roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v3_prefill")
+    ap.add_argument("--decode", default="v3_decode",
+                    help="second workload on the same layer weights ('' to skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the oracle CPU baseline (0 to skip)")
+    return ap.parse_args()
+
+
+def hit_stats(idx, E):
+    """Expert load of one batch: touched experts, max/mean rows, and the
+    expert-hit entropy over ln(E) (the load diagnostic of the DeepSeek-V2
+    explainer page, section 6)."""
+    import numpy as np
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.float64)
+    p = counts[counts > 0] / counts.sum()
+    ent = float(-(p * np.log(p)).sum())
+    return dict(touched=int((counts > 0).sum()), max_rows=int(counts.max()),
+                mean_rows=float(counts.mean()), entropy_over_lnE=ent / math.log(E) if E > 1 else 1.0,
+                active_ratio=float((counts > 0).mean()))
+
+
+def algorithmic(w, counts):
+    """Algorithmic work of the layer and of its gate/up GEMM for one batch.
+
+    Per row of a routed (shared) expert the gate/up GEMM does 4*d*I (4*d*Is)
+    FLOPs; the down GEMM 2*d*I; the router 2*d*E per token.  Bytes: every
+    touched expert's weights once (bf16), the shared weights, the centroids,
+    x and out; the gate/up GEMM reads W1 and W3 of the touched experts and
+    the shared ones, x once and writes H."""
+    touched = int((counts > 0).sum())
+    rows_r, rows_s = w.T * w.K, w.T * w.Ks
+    g1_flops = 4.0 * w.d * (rows_r * w.I + rows_s * w.Is)
+    g2_flops = 2.0 * w.d * (rows_r * w.I + rows_s * w.Is)
+    layer_flops = 2.0 * w.T * w.d * w.E + g1_flops + g2_flops
+    wb_r = 2 * 3 * w.I * w.d           # one routed expert's W1, W3, W2 in bytes
+    wb_s = 2 * 3 * w.Is * w.d
+    layer_bytes = (touched * wb_r + w.Ks * wb_s + 2 * w.E * w.d + 2 * 2 * w.T * w.d)
+    g1_bytes = (touched * 2 * 2 * w.I * w.d + w.Ks * 2 * 2 * w.Is * w.d + 2 * w.T * w.d
+                + 2 * (rows_r * w.I + rows_s * w.Is))
+    return dict(touched=touched, g1_flops=g1_flops, layer_flops=layer_flops,
+                g1_bytes=float(g1_bytes), layer_bytes=float(layer_bytes))
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def time_workload(w, D, host_x, steps, warmup):
+    """Warm up, then time exactly `steps` forwards with HIP events around the
+    whole region and around every kernel.  Returns timings and routing."""
+    import torch
+
+    import fine_grained_mixture_router_amd as moe
+    x = dev(host_x)
+    bias = None if D.get("bias") is None else D["bias"]
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    gate = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+
+    def step():
+        moe.forward(x, D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"], K=w.K,
+                    bias=bias, out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.profile_begin(steps)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    kernels = moe.profile_end()
+    return dict(ms_per_step=total_ms / steps, kernels=kernels, out=out, idx=idx.cpu().numpy(),
+                gate=gate.cpu().numpy())
+
+
+def regime(w):
+    """Few rows per expert (under 64 on average) stream each weight once and
+    are HBM-bound; larger batches are MFMA-bound."""
+    return "hbm" if w.T * w.K < 64 * w.E else "mfma"
+
+
+def roofline(kind, work, kernels):
+    ms, n = kernels["gemm_gate_up"]
+    avg_s = ms / max(n, 1) / 1e3
+    if kind == "mfma":
+        ach = work["g1_flops"] / avg_s / 1e12
+        return dict(kernel="gemm_gate_up", bound="mfma", achieved=round(ach, 1),
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4),
+                    traffic=None, mean_launch_ms=round(ms / max(n, 1), 4), launches=n)
+    ach = work["g1_bytes"] / avg_s / 1e9
+    return dict(kernel="gemm_gate_up", bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS,
+                unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
+                mean_launch_ms=round(ms / max(n, 1), 4), launches=n)
+
+
+def cpu_baseline(w, L, res, seconds):
+    """The fp64 oracle, as it stands, on the first tokens of the same batch
+    for about `seconds` of wall clock; also a spot parity check of the GPU
+    output on those tokens."""
+    import numpy as np
+
+    import oracle
+    import synth
+    got_bits = res["out"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    done = 0
+    errs, mism = [], 0
+    t0 = time.time()
+    chunk = 16
+    threads = 0
+    ref_rows = []
+    while done < w.T and (time.time() - t0) < seconds:
+        tok = np.arange(done, min(done + chunk, w.T))
+        r = oracle.forward(L["x"][tok], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"],
+                           L["ws3"], L["ws2"], w.K)
+        threads = r["threads"]
+        ok = r["margin"] > 1e-5
+        for j, t in enumerate(tok):
+            if ok[j] and set(res["idx"][t].tolist()) != set(r["idx"][j].tolist()):
+                mism += 1
+        ref_rows.append((tok, r["out"]))
+        done += len(tok)
+    dt = time.time() - t0
+    toks = np.concatenate([t for t, _ in ref_rows])
+    ref = np.concatenate([o for _, o in ref_rows])
+    got = synth.bf16_to_f64(got_bits[toks])
+    rel = float(np.abs(got - ref).max() / np.sqrt(np.mean(ref ** 2)))
+    return (dict(value=round(done / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
+                 sample=f"first {done} tokens of the {w.name} batch, full layer in fp64 "
+                        f"(routing + {w.K} routed + {w.Ks} shared SwiGLU experts per token), "
+                        f"{dt:.1f} s"),
+            dict(tokens=int(done), max_err_over_rms=rel, routing_set_mismatches=int(mism)))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X and has "
+              "no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fine_grained_mixture_router_amd as moe  # noqa: F401  (fails loudly if unbuilt)
+    from synth import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    t_gen = time.time()
+    L = wl.gen_all(w)
+    D = {k: (None if v is None else dev(v)) for k, v in L.items() if k != "x"}
+    gen_s = time.time() - t_gen
+    print(f"[bench] inputs of {w.name} generated and uploaded in {gen_s:.1f} s", file=sys.stderr,
+          flush=True)
+
+    res = time_workload(w, D, L["x"], args.steps, args.warmup)
+    counts = np.bincount(res["idx"].ravel(), minlength=w.E)
+    work = algorithmic(w, counts)
+    ms = res["ms_per_step"]
+    line = {
+        "metric": METRIC,
+        "value": round(w.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; bf16 N(0,1) activations, N(0,0.006) weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "I": w.I, "K": w.K,
+                   "Ks": w.Ks, "Is": w.Is, "zipf_s": w.zipf_s, "parallelism": "single GPU"},
+        "roofline": roofline(regime(w), work, res["kernels"]),
+        "layer": {"tflops": round(work["layer_flops"] / (ms / 1e3) / 1e12, 1),
+                  "mfma_frac": round(work["layer_flops"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in res["kernels"].items()},
+                  "load": hit_stats(res["idx"], w.E)},
+    }
+    print(f"[bench] {w.name}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    if args.decode:
+        wd = wl.WORKLOADS[args.decode]
+        assert (wd.d, wd.E, wd.I, wd.Ks, wd.Is, wd.wseed) == (w.d, w.E, w.I, w.Ks, w.Is, w.wseed)
+        xd = wl.gen_x(wd)
+        Dd = dict(D, bias=None if wd.zipf_s == 0 else dev(wl.gen_bias(wd)))
+        rd = time_workload(wd, Dd, xd, args.steps, args.warmup)
+        cd = np.bincount(rd["idx"].ravel(), minlength=wd.E)
+        wk = algorithmic(wd, cd)
+        msd = rd["ms_per_step"]
+        line["decode"] = {
+            "workload": wd.name, "T": wd.T, "value": round(wd.T / (msd / 1e3), 1),
+            "unit": "tokens/s", "ms_per_step": round(msd, 4),
+            "roofline": roofline(regime(wd), wk, rd["kernels"]),
+            "layer_gbs": round(wk["layer_bytes"] / (msd / 1e3) / 1e9, 1),
+            "layer_hbm_frac": round(wk["layer_bytes"] / (msd / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rd["kernels"].items()},
+            "load": hit_stats(rd["idx"], wd.E),
+        }
+        print(f"[bench] {wd.name}: {msd:.3f} ms/step", file=sys.stderr, flush=True)
+
+    if args.cpu_seconds > 0:
+        base, spot = cpu_baseline(w, L, res, args.cpu_seconds)
+        line["cpu_baseline"] = base
+        line["spot_parity"] = spot
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

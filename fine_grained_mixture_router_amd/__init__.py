@@ -64,7 +64,16 @@ _lib.moe_route.restype = ctypes.c_int
 _lib.moe_route.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                            _vp]
 
-EXPORTS = ("moe_workspace_size", "moe_forward", "moe_route", "moe_status_string")
+_lib.moe_profile_begin.restype = ctypes.c_int
+_lib.moe_profile_begin.argtypes = [ctypes.c_int32]
+_lib.moe_profile_end.restype = ctypes.c_int
+_lib.moe_profile_end.argtypes = [_vp, _vp, ctypes.c_int32]
+_lib.moe_profile_slot_name.restype = ctypes.c_char_p
+_lib.moe_profile_slot_name.argtypes = [ctypes.c_int32]
+
+EXPORTS = ("moe_workspace_size", "moe_forward", "moe_route", "moe_status_string",
+           "moe_profile_begin", "moe_profile_end", "moe_profile_slot_name")
+N_SLOTS = 7
 
 
 def lib():
@@ -168,3 +177,17 @@ def route(x, centroids, *, K: int, bias=None, topk_idx=None, topk_gate=None, wor
                           workspace.numel() * workspace.element_size(), _stream(dev, stream))
     _check(code)
     return topk_idx, topk_gate
+
+
+def profile_begin(max_calls: int):
+    """Record HIP events around every kernel of the next max_calls forwards."""
+    _check(_lib.moe_profile_begin(int(max_calls)))
+
+
+def profile_end() -> dict:
+    """{kernel name: (summed ms, launches)} of the recorded forwards."""
+    ms = (ctypes.c_float * N_SLOTS)()
+    n = (ctypes.c_int32 * N_SLOTS)()
+    _check(_lib.moe_profile_end(ctypes.cast(ms, _vp), ctypes.cast(n, _vp), N_SLOTS))
+    return {_lib.moe_profile_slot_name(k).decode(): (float(ms[k]), int(n[k]))
+            for k in range(N_SLOTS)}

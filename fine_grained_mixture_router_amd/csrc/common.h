@@ -85,9 +85,10 @@ struct Plan {
 };
 
 // Launchers (each enqueues on `st`; return the launch status).
-hipError_t launch_router(const Plan& p, const bf16_t* x, const bf16_t* C, const float* bias,
-                         hipStream_t st);
-hipError_t launch_permute(const Plan& p, hipStream_t st);
+hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st);
+hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st);
+hipError_t launch_perm_scan(const Plan& p, hipStream_t st);
+hipError_t launch_perm_scatter(const Plan& p, hipStream_t st);
 hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
                                const bf16_t* w3, const bf16_t* ws1, const bf16_t* ws3,
                                hipStream_t st);

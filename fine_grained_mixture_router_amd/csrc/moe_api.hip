@@ -147,6 +147,34 @@ moe_status_t device_ok() {
     return known == 1 ? MOE_OK : MOE_ERR_DEVICE_ARCH;
 }
 
+// Benchmark instrumentation: HIP events recorded around every kernel of the
+// next moe_forward calls, on the call's stream.  One global recorder; not
+// thread-safe (documented in moe.h).
+constexpr int kSlots = 7;
+const char* const kSlotNames[kSlots] = {"router_logits", "router_select", "perm_scan",
+                                        "perm_scatter",  "gemm_gate_up",  "gemm_down",
+                                        "combine"};
+struct Recorder {
+    bool on = false;
+    int max_calls = 0;
+    int calls = 0;
+    hipEvent_t* ev = nullptr;   // [max_calls][kSlots][2]
+    bool used[kSlots] = {};
+} g_rec;
+
+void rec_mark(int slot, int end, hipStream_t s) {
+    if (!g_rec.on || g_rec.calls >= g_rec.max_calls) return;
+    (void)hipEventRecord(g_rec.ev[(g_rec.calls * kSlots + slot) * 2 + end], s);
+}
+
+void rec_free() {
+    if (g_rec.ev) {
+        for (int i = 0; i < g_rec.max_calls * kSlots * 2; ++i) (void)hipEventDestroy(g_rec.ev[i]);
+        delete[] g_rec.ev;
+    }
+    g_rec = Recorder{};
+}
+
 moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* centroids,
                           const float* bias, void* ws, size_t ws_bytes, Plan* plan) {
     if (!shape) return MOE_ERR_NULL;
@@ -211,18 +239,34 @@ __attribute__((visibility("default"))) moe_status_t moe_forward(
     if (topk_gate) p.gate = topk_gate;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bf16_t* xb = static_cast<const bf16_t*>(x);
-    if (p.K > 0 &&
-        launch_router(p, xb, static_cast<const bf16_t*>(centroids), expert_bias, s) != hipSuccess)
-        return MOE_ERR_HIP;
-    if (launch_permute(p, s) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_gemm_gate_up(p, xb, static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w3),
-                            static_cast<const bf16_t*>(ws1), static_cast<const bf16_t*>(ws3),
-                            s) != hipSuccess)
-        return MOE_ERR_HIP;
-    if (launch_gemm_down(p, static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(ws2), s) !=
-        hipSuccess)
-        return MOE_ERR_HIP;
-    if (launch_combine(p, xb, static_cast<bf16_t*>(out), s) != hipSuccess) return MOE_ERR_HIP;
+    const bf16_t* w1b = static_cast<const bf16_t*>(w1);
+    const bf16_t* w3b = static_cast<const bf16_t*>(w3);
+    const bf16_t* w2b = static_cast<const bf16_t*>(w2);
+    const bf16_t* ws1b = static_cast<const bf16_t*>(ws1);
+    const bf16_t* ws3b = static_cast<const bf16_t*>(ws3);
+    const bf16_t* ws2b = static_cast<const bf16_t*>(ws2);
+    hipError_t e = hipSuccess;
+    auto step = [&](int slot, auto&& launch) {
+        if (e != hipSuccess) return;
+        rec_mark(slot, 0, s);
+        e = launch();
+        rec_mark(slot, 1, s);
+    };
+    if (p.K > 0) {
+        step(0, [&] { return launch_router_logits(p, xb, static_cast<const bf16_t*>(centroids), s); });
+        step(1, [&] { return launch_router_select(p, expert_bias, s); });
+    }
+    step(2, [&] { return launch_perm_scan(p, s); });
+    step(3, [&] { return launch_perm_scatter(p, s); });
+    step(4, [&] { return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, s); });
+    step(5, [&] { return launch_gemm_down(p, w2b, ws2b, s); });
+    step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
+    if (g_rec.on && g_rec.calls < g_rec.max_calls) {
+        for (int k = 0; k < kSlots; ++k)
+            if (k >= 2 || p.K > 0) g_rec.used[k] = true;
+        ++g_rec.calls;
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
 
@@ -240,10 +284,65 @@ __attribute__((visibility("default"))) moe_status_t moe_route(
     place(&p, workspace);
     p.idx = topk_idx;
     p.gate = topk_gate;
-    if (launch_router(p, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(centroids),
-                      expert_bias, static_cast<hipStream_t>(stream)) != hipSuccess)
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_router_logits(p, static_cast<const bf16_t*>(x),
+                             static_cast<const bf16_t*>(centroids), s) != hipSuccess ||
+        launch_router_select(p, expert_bias, s) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_profile_begin(int32_t max_calls) {
+    if (max_calls < 1 || max_calls > 100000) return MOE_ERR_SHAPE;
+    moe_status_t st = device_ok();
+    if (st != MOE_OK) return st;
+    rec_free();
+    g_rec.ev = new hipEvent_t[(size_t)max_calls * kSlots * 2];
+    for (int i = 0; i < max_calls * kSlots * 2; ++i) {
+        if (hipEventCreate(&g_rec.ev[i]) != hipSuccess) {
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_rec.ev[j]);
+            delete[] g_rec.ev;
+            g_rec = Recorder{};
+            return MOE_ERR_HIP;
+        }
+    }
+    g_rec.max_calls = max_calls;
+    g_rec.on = true;
+    return MOE_OK;
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_profile_end(float* ms, int32_t* launches,
+                                                                    int32_t n_slots) {
+    if (!g_rec.on) return MOE_ERR_NULL;
+    moe_status_t st = MOE_OK;
+    for (int k = 0; k < n_slots && k < kSlots; ++k) {
+        float tot = 0.f;
+        int n = 0;
+        if (g_rec.used[k]) {
+            for (int c = 0; c < g_rec.calls; ++c) {
+                hipEvent_t b = g_rec.ev[(c * kSlots + k) * 2], en = g_rec.ev[(c * kSlots + k) * 2 + 1];
+                float t = 0.f;
+                if (hipEventSynchronize(en) != hipSuccess || hipEventElapsedTime(&t, b, en) != hipSuccess) {
+                    st = MOE_ERR_HIP;
+                    continue;
+                }
+                tot += t;
+                ++n;
+            }
+        }
+        if (ms) ms[k] = tot;
+        if (launches) launches[k] = n;
+    }
+    for (int k = kSlots; k < n_slots; ++k) {
+        if (ms) ms[k] = 0.f;
+        if (launches) launches[k] = 0;
+    }
+    rec_free();
+    return st;
+}
+
+__attribute__((visibility("default"))) const char* moe_profile_slot_name(int32_t slot) {
+    return (slot >= 0 && slot < kSlots) ? kSlotNames[slot] : "";
 }
 
 }  // extern "C"

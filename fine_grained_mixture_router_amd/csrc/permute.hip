@@ -16,8 +16,10 @@
 namespace moe {
 namespace {
 
-constexpr int kScanThreads = 512;   // >= E + Ks (E <= 256, Ks <= 16)
+constexpr int kScanThreads = 1024;
+constexpr int kQuarters = 4;        // threads per expert when counting chunk masks
 constexpr int kGroupM = 4;          // M-tiles per N sweep in the work-list order
+static_assert(kScanThreads >= 256 * kQuarters, "one thread per (expert, quarter)");
 
 __device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
     const int tid = threadIdx.x;
@@ -35,42 +37,68 @@ __device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
     return incl - v;
 }
 
-// Writes the tiles of one group in "kGroupM M-tiles x all N-tiles" blocks:
-// consecutive entries share either the A rows or the weight rows, which is
-// what keeps the L2 of one XCD warm (each XCD takes a contiguous slice of
-// the list, see the GEMM kernel).
-__device__ void emit_tiles(Tile* out, int base, int g, int nrows_g, int bm, int ncols, int bn_out,
-                           int tid, int nthr) {
-    const int mt = (nrows_g + bm - 1) / bm;
-    const int nt = (ncols + bn_out - 1) / bn_out;
-    const int total = mt * nt;
-    for (int i = tid; i < total; i += nthr) {
-        const int b = i / (kGroupM * nt);
-        const int j = i - b * kGroupM * nt;
-        const int gm = min(kGroupM, mt - b * kGroupM);
-        const int n = j / gm;
-        const int m = b * kGroupM + (j - n * gm);
-        Tile t;
-        t.group = g;
-        t.m0 = m * bm;
-        t.n0 = n * bn_out;
-        t.nrows = min(bm, nrows_g - m * bm);
-        out[base + i] = t;
+// Work-list entry i of a group with mt M-tiles and nt N-tiles, in
+// "kGroupM M-tiles x all N-tiles" blocks: consecutive entries share either
+// the A rows or the weight rows, which keeps the L2 of one XCD warm (each XCD
+// takes a contiguous slice of the list, see the GEMM kernel).
+__device__ Tile tile_at(int i, int g, int nrows_g, int bm, int bn_out, int mt, int nt) {
+    const int b = i / (kGroupM * nt);
+    const int j = i - b * kGroupM * nt;
+    const int gm = min(kGroupM, mt - b * kGroupM);
+    const int n = j / gm;
+    const int m = b * kGroupM + (j - n * gm);
+    Tile t;
+    t.group = g;
+    t.m0 = m * bm;
+    t.n0 = n * bn_out;
+    t.nrows = min(bm, nrows_g - m * bm);
+    return t;
+}
+
+// Fill a whole work list in parallel: entry i belongs to the last group whose
+// first entry is <= i (binary search over the exclusive tile offsets).
+__device__ void emit_list(Tile* out, int total, const int* s_off, const int* s_cnt, int G, int bm,
+                          int bn_out, int ncols_r, int ncols_s, int E) {
+    for (int i = threadIdx.x; i < total; i += kScanThreads) {
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        const int g = lo;
+        const int n = s_cnt[g];
+        const int mt = (n + bm - 1) / bm;
+        const int ncols = g < E ? ncols_r : ncols_s;
+        const int nt = (ncols + bn_out - 1) / bn_out;
+        out[i] = tile_at(i - s_off[g], g, n, bm, bn_out, mt, nt);
     }
 }
 
 __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int routed) {
     __shared__ int sbuf[kScanThreads];
+    __shared__ int s_part[kQuarters][256];
     __shared__ int s_cnt[kScanThreads];
     __shared__ int s_t1[kScanThreads];
     __shared__ int s_t2[kScanThreads];
     const int tid = threadIdx.x;
     const int G = p.E + p.Ks;
+    const int e = tid & 255;
+    const int q = tid >> 8;
+    const int cq = (p.nchunk + kQuarters - 1) / kQuarters;
+    const int c0 = min(p.nchunk, q * cq), c1 = min(p.nchunk, c0 + cq);
 
-    // rows per group
+    // rows of expert e in chunk quarter q
+    int part = 0;
+    if (routed && e < p.E && q < kQuarters)
+        for (int c = c0; c < c1; ++c) part += __popcll(p.masks[(size_t)c * p.Epad + e]);
+    if (q < kQuarters) s_part[q][e] = part;
+    __syncthreads();
+
+    // rows per group, then group offsets
     int cnt = 0;
     if (tid < p.E && routed) {
-        for (int c = 0; c < p.nchunk; ++c) cnt += __popcll(p.masks[(size_t)c * p.Epad + tid]);
+        for (int k = 0; k < kQuarters; ++k) cnt += s_part[k][tid];
     } else if (tid >= p.E && tid < G) {
         cnt = p.T;
     }
@@ -81,17 +109,19 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int rou
         s_cnt[tid] = cnt;
     }
     if (tid == 0) p.goff[G] = total;
+    __syncthreads();
 
     // per-(chunk, expert) first row
-    if (tid < p.E && routed) {
-        int run = off;
-        for (int c = 0; c < p.nchunk; ++c) {
-            p.chunk_base[(size_t)c * p.Epad + tid] = run;
-            run += __popcll(p.masks[(size_t)c * p.Epad + tid]);
+    if (routed && e < p.E && q < kQuarters) {
+        int run = p.goff[e];
+        for (int k = 0; k < q; ++k) run += s_part[k][e];
+        for (int c = c0; c < c1; ++c) {
+            p.chunk_base[(size_t)c * p.Epad + e] = run;
+            run += __popcll(p.masks[(size_t)c * p.Epad + e]);
         }
     }
 
-    // work-list sizes
+    // work lists
     const int bn1 = p.g1.bn / 2;   // SwiGLU tile: half W1 rows, half W3 rows
     int t1 = 0, t2 = 0;
     if (tid < G) {
@@ -111,13 +141,8 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int rou
         p.ntiles[1] = tot2;
     }
     __syncthreads();
-
-    for (int g = 0; g < G; ++g) {
-        const int n = s_cnt[g];
-        if (n == 0) continue;
-        emit_tiles(p.tiles1, s_t1[g], g, n, p.g1.bm, g < p.E ? p.I : p.Is, bn1, tid, kScanThreads);
-        emit_tiles(p.tiles2, s_t2[g], g, n, p.g2.bm, p.d, p.g2.bn, tid, kScanThreads);
-    }
+    emit_list(p.tiles1, tot1, s_t1, s_cnt, G, p.g1.bm, bn1, p.I, p.Is, p.E);
+    emit_list(p.tiles2, tot2, s_t2, s_cnt, G, p.g2.bm, p.g2.bn, p.d, p.d, p.E);
 }
 
 // One workgroup per 64-token chunk: slot of every (token, k) and the token of
@@ -148,12 +173,13 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(Plan p, int routed) {
 
 }  // namespace
 
-hipError_t launch_permute(const Plan& p, hipStream_t st) {
-    const int routed = p.K > 0 ? 1 : 0;
-    perm_scan_kernel<<<1, kScanThreads, 0, st>>>(p, routed);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    perm_scatter_kernel<<<p.nchunk, 256, 0, st>>>(p, routed);
+hipError_t launch_perm_scan(const Plan& p, hipStream_t st) {
+    perm_scan_kernel<<<1, kScanThreads, 0, st>>>(p, p.K > 0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_scatter(const Plan& p, hipStream_t st) {
+    perm_scatter_kernel<<<p.nchunk, 256, 0, st>>>(p, p.K > 0 ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -10,10 +10,11 @@
 //                  Tiles of 64 tokens x 64 experts; for small T the d range is
 //                  split so that the launch still covers the chip, and the
 //                  partials are summed in a fixed order by the next kernel.
-//   router_select  one wavefront per token: sum partials, add the bias, fp32
-//                  softmax, then K rounds of a wavefront arg-max over the E<=256
-//                  logits (4 per lane; ties go to the lower expert id).  Each
-//                  workgroup owns a 64-token chunk and also records, per expert,
+//   router_select  one wavefront per token (16 per workgroup, 4 tokens each):
+//                  sum partials, add the bias, fp32 softmax, then K rounds of a
+//                  wavefront arg-max over the E<=256 logits (4 per lane; ties go
+//                  to the lower expert id).  Each workgroup owns a 64-token
+//                  chunk and also records, per expert,
 //                  the 64-bit mask of its tokens that chose that expert; the
 //                  permutation step turns those masks into a stable,
 //                  atomics-free grouping of tokens by expert.
@@ -121,7 +122,10 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void router_select_kernel(
+// One workgroup per 64-token chunk, 16 waves, 4 tokens per wave.
+constexpr int kSelectThreads = 1024;
+
+__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ idx,
     float* __restrict__ gate, uint64_t* __restrict__ masks, int T, int E, int Epad, int K,
     int split) {
@@ -130,12 +134,18 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c = blockIdx.x;
-    for (int e = tid; e < Epad; e += kThreads) smask[e] = 0ull;
+    for (int e = tid; e < Epad; e += kSelectThreads) smask[e] = 0ull;
     __syncthreads();
 
     const float NEG = -INFINITY;
-    for (int i = 0; i < kChunk / 4; ++i) {
-        const int tl = wave * (kChunk / 4) + i;       // token within the chunk
+    float bj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        bj[j] = (bias && e < E) ? bias[e] : 0.f;
+    }
+    for (int i = 0; i < kChunk / 16; ++i) {
+        const int tl = wave + 16 * i;                 // token within the chunk
         const int t = c * kChunk + tl;
         if (t >= T) break;
         float v[4];
@@ -146,8 +156,7 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(
             if (e < E) {
                 float s = 0.f;
                 for (int z = 0; z < split; ++z) s += logits[((size_t)z * T + t) * Epad + e];
-                if (bias) s += bias[e];
-                v[j] = s;
+                v[j] = s + bj[j];
             } else {
                 v[j] = NEG;
                 taken |= 1 << j;
@@ -186,20 +195,21 @@ __global__ __launch_bounds__(kThreads) void router_select_kernel(
         }
     }
     __syncthreads();
-    for (int e = tid; e < Epad; e += kThreads) masks[(size_t)c * Epad + e] = smask[e];
+    for (int e = tid; e < Epad; e += kSelectThreads) masks[(size_t)c * Epad + e] = smask[e];
 }
 
 }  // namespace
 
-hipError_t launch_router(const Plan& p, const bf16_t* x, const bf16_t* C, const float* bias,
-                         hipStream_t st) {
+hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st) {
     const int nk = p.d / 64;
     const int kps = (nk + p.split - 1) / p.split;
     dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.Epad / kRouterBE, p.split);
     router_logits_kernel<<<grid, kThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    router_select_kernel<<<p.nchunk, kThreads, 0, st>>>(p.logits, bias, p.idx, p.gate, p.masks,
+    return hipGetLastError();
+}
+
+hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st) {
+    router_select_kernel<<<p.nchunk, kSelectThreads, 0, st>>>(p.logits, bias, p.idx, p.gate, p.masks,
                                                        p.T, p.E, p.Epad, p.K, p.split);
     return hipGetLastError();
 }

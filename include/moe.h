@@ -17,7 +17,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library never allocates or frees device memory, never synchronises and
- *     keeps no state between calls; work is enqueued on `stream` (a
+ *     keeps no state between calls (apart from the optional benchmark
+ *     recorder below); work is enqueued on `stream` (a
  *     hipStream_t passed as void*, NULL = the null stream) and faults surface
  *     at the caller's next synchronisation.  Calls on different streams are
  *     independent when each uses its own workspace.
@@ -31,7 +32,9 @@
  *   - Shape limits: 1 <= T <= 2^24; d a multiple of 64 in [64, 65536];
  *     1 <= E <= 256; 0 <= K <= E; I a multiple of 64 in [64, 65536];
  *     0 <= Ks <= 16; Is a multiple of 64 in [64, 65536] when Ks > 0 (ignored
- *     when Ks == 0).  gfx950 devices only.
+ *     when Ks == 0); T*(K+Ks) <= 2^30; and each of x, the routed and shared
+ *     parts of H, and one expert's weight matrix below 2^31 bytes (the GEMMs
+ *     address them with 32-bit offsets).  gfx950 devices only.
  *   - NaN / Inf inputs are outside the contract.
  */
 #ifndef MOE_H
@@ -106,6 +109,30 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* cent
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t status);
+
+/* Benchmark instrumentation (not part of the layer's computation).
+ *
+ * moe_profile_begin(max_calls): the next max_calls (1..100000) moe_forward
+ * calls record a HIP event before and after each kernel they launch, on the
+ * call's stream.  It creates 14*max_calls HIP events (host-side runtime
+ * objects; no device memory).  Errors: MOE_ERR_SHAPE for a bad count,
+ * MOE_ERR_NO_DEVICE / MOE_ERR_DEVICE_ARCH as for moe_forward, MOE_ERR_HIP if
+ * event creation fails.
+ *
+ * moe_profile_end(ms, launches, n_slots): waits for the recorded events and
+ * writes, for kernel slot k < n_slots, the summed duration in milliseconds
+ * (ms[k], host array) and the number of timed launches (launches[k], host
+ * array; either pointer may be NULL), then releases the events and stops
+ * recording.  MOE_ERR_NULL if no recording is active, MOE_ERR_HIP if an event
+ * could not be read.  Slots: 0 router_logits, 1 router_select, 2 perm_scan,
+ * 3 perm_scatter, 4 gemm_gate_up, 5 gemm_down, 6 combine
+ * (moe_profile_slot_name gives the name, "" past the end).
+ *
+ * One process-wide recorder: not thread-safe; do not record from several
+ * host threads at once. */
+moe_status_t moe_profile_begin(int32_t max_calls);
+moe_status_t moe_profile_end(float* ms, int32_t* launches, int32_t n_slots);
+const char* moe_profile_slot_name(int32_t slot);
 
 #ifdef __cplusplus
 }

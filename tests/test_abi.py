@@ -136,6 +136,14 @@ def test_route_validation():
              ctypes.c_size_t(n), None) == 2
 
 
+def test_profile_validation():
+    f = moe.lib()
+    assert f.moe_profile_begin(0) == 2
+    assert f.moe_profile_end(None, None, 7) == 1          # nothing recording
+    assert f.moe_profile_slot_name(4) == b"gemm_gate_up"
+    assert f.moe_profile_slot_name(7) == b""
+
+
 def test_segment_helper():
     # N=16 experts of inter 4096 split m=4 -> 64 experts of inter 1024
     g = moe.segment(16, 4, 4096, K=8, Ks=1)
