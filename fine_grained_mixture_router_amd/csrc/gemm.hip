@@ -228,6 +228,251 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tile for many rows per expert (MFMA-bound).  Four waves, each
+// 128 rows x 128 B-rows (4 x 4 blocks of 32x32x16 MFMAs, 256 accumulator
+// registers: the whole accumulator file, which is what bounds the tile).
+//
+// Global -> LDS with direct-to-LDS buffer loads: one wave instruction moves
+// 1 KB = (1024 / row bytes) rows of one BK slice into LDS, lane l filling
+// the 16-byte position l, so staging costs no VGPRs and no ds_write.  The
+// vector-memory path moves about 31 B/clk/CU when each row segment is 64
+// bytes, 43 with 128-byte segments and 72 for 1 KB contiguous (measured on
+// MI355X with L2-resident data), and this tile needs about 22 B/clk/CU at
+// 1.5 PFLOP/s — so the slice width BK sets the attainable rate as much as
+// the number of LDS stages (KSTAGES) that hide the load latency.
+//
+// LDS layout of one operand tile: rows of BK bf16; a row's logical 16-byte
+// chunk c sits at position c ^ f(row), f(row) = (row / R) mod (BK / 8) with
+// R = 256 / (2 * BK) rows per 256 bytes.  A fragment read of the 32x32x16
+// MFMA puts 16 consecutive lanes on 16 consecutive rows at one logical
+// chunk; those 16 reads then cover the 256 bytes of LDS banks exactly once
+// (row mod R picks the row's slot, f the chunk within it): no bank conflicts.
+//
+// Within a stage the fragments of k16 step s + 1 are read under the MFMAs
+// of step s; the barrier sits before the last step, so the first fragments
+// of the next stage are read under the stage's last MFMAs.  The order is
+// pinned with scheduling fences.
+// ---------------------------------------------------------------------------
+constexpr int kBig = 256;
+#ifndef MOE_BIG_BK
+#define MOE_BIG_BK 64
+#endif
+#ifndef MOE_BIG_STAGES
+#define MOE_BIG_STAGES 2
+#endif
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, 0, 0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// release semantics would wait for every outstanding load (vmcnt(0)) and
+// drain the multi-stage pipeline.  Ordering is kept explicitly: each wave
+// waits for its own stage loads first, and LDS fragment reads of a stage are
+// consumed by MFMAs before the barrier that precedes the refill of that
+// stage.  The "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// Wait until at most n (a multiple of `unit`, n <= 3 * unit) of this wave's
+// loads are in flight.
+template <int UNIT>
+__device__ __forceinline__ void wait_vm_runtime(int n) {
+    if (n >= 3 * UNIT) wait_vm<3 * UNIT>();
+    else if (n >= 2 * UNIT) wait_vm<2 * UNIT>();
+    else if (n >= UNIT) wait_vm<UNIT>();
+    else wait_vm<0>();
+}
+
+template <bool SWIGLU, int BK, int KSTAGES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_big_kernel(GemmParams P) {
+    constexpr int OPER = kBig * BK;                // elements of one operand tile
+    constexpr int STAGE = 2 * OPER;                // A then B
+    constexpr int CH = BK / 8;                     // 16-byte chunks per row
+    constexpr int RI = 1024 / (2 * BK);            // rows per load instruction
+    constexpr int R = 256 / (2 * BK);              // rows per 256 bytes of LDS
+    constexpr int NI = kBig / RI;                  // load instructions per operand per stage
+    constexpr int QI = NI / 4;                     // ... per wave
+    constexpr int LOADS = 2 * QI;                  // per wave per stage, both operands
+    constexpr int SPS = BK / 16;                   // k16 steps per stage
+    static_assert(BK == 32 || BK == 64, "slice width");
+    static_assert(KSTAGES >= 2 && LOADS * (KSTAGES - 1) <= 63, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[KSTAGES * STAGE];
+
+    const int nt = *P.ntiles;
+    const int wg = blockIdx.x;
+    const int nr = (nt + 7) & ~7;
+    if (wg >= nr) return;
+    const int lt = (wg & 7) * (nr >> 3) + (wg >> 3);
+    if (lt >= nt) return;
+    const Tile tl = P.tiles[lt];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const bool shared = tl.group >= P.E;
+    const int s = tl.group - P.E;
+    const int kdim = shared ? P.kdim_s : P.kdim_r;
+    const int ncols = shared ? P.n_s : P.n_r;
+    const int grow = P.goff[tl.group] + tl.m0;
+    const int rrow = shared ? grow - P.TK : grow;
+    const bf16_t* wa = shared ? P.Ba_s + (size_t)s * ncols * kdim
+                              : P.Ba_r + (size_t)tl.group * ncols * kdim;
+    const bf16_t* wb = wa;
+    if (SWIGLU)
+        wb = shared ? P.Bb_s + (size_t)s * ncols * kdim : P.Bb_r + (size_t)tl.group * ncols * kdim;
+    const __amdgpu_buffer_rsrc_t ra_src =
+        make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * 2u;
+    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(wa, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(wb, wbytes);
+
+    // Load assignment: wave w issues instructions j = w + 4q, q < QI, of each
+    // operand; instruction j fills rows RI*j .. RI*j + RI - 1.  Lane l fills
+    // position l % CH of row RI*j + l / CH, i.e. logical chunk
+    // (l % CH) ^ f(row).
+    uint32_t aoff[QI], boff[QI];
+#pragma unroll
+    for (int q = 0; q < QI; ++q) {
+        const int j = wave + 4 * q;
+        const int row = RI * j + lane / CH;
+        const uint32_t cbytes = (uint32_t)(((lane % CH) ^ ((row / R) % CH)) * 16);
+        const int rr = row < tl.nrows ? row : 0;
+        const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(rrow + rr);
+        aoff[q] = arow * (uint32_t)kdim * 2u + cbytes;
+        // SwiGLU: B rows 0..127 come from W1, 128..255 from W3
+        int n = tl.n0 + ((SWIGLU && q >= QI / 2) ? row - kBig / 2 : row);
+        n = n < ncols ? n : ncols - 1;
+        boff[q] = (uint32_t)n * (uint32_t)kdim * 2u + cbytes;
+    }
+    auto issue = [&](int kt) {
+        bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
+        bf16_t* sb = sa + OPER;
+        const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+            const int j = wave + 4 * q;
+            lds_load16(ra_src, sa + j * RI * BK, aoff[q] + kb);
+            lds_load16((SWIGLU && q >= QI / 2) ? rw3 : rw1, sb + j * RI * BK, boff[q] + kb);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    // Fragment addressing (elements): this lane's row base and the swizzled
+    // chunk of k16 step st (rows differ from lane & 31 by multiples of 32).
+    const int lrow = lane & 31;
+    const int a_row0 = (wm * 128 + lrow) * BK;
+    int b_row0[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int br = SWIGLU ? ((j < 2 ? 0 : kBig / 2) + wn * 64 + (j & 1) * 32)
+                              : (wn * 128 + j * 32);
+        b_row0[j] = (br + lrow) * BK;
+    }
+    int cx[SPS];
+#pragma unroll
+    for (int st = 0; st < SPS; ++st) cx[st] = ((2 * st + (lane >> 5)) ^ ((lrow / R) % CH)) << 3;
+
+    bf16x8 fa[2][4], fb[2][4];
+    auto read_frags = [&](int set, int kt, int st) {
+        const bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
+        const bf16_t* sb = sa + OPER;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + a_row0 + i * 32 * BK + cx[st]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fb[set][j] = *reinterpret_cast<const bf16x8*>(sb + b_row0[j] + cx[st]);
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j],
+                                                                   0, 0, 0);
+    };
+    // k16 steps 0 .. SPS-2 of stage kt (step 0's fragments already in set 0)
+    auto stage_body = [&](int kt) {
+#pragma unroll
+        for (int st = 0; st + 1 < SPS; ++st) {
+            read_frags((st + 1) & 1, kt, st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(st & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = kdim / BK;
+    // prologue: stages 0 .. KSTAGES-2 in flight, stage 0 resident
+    for (int k = 0; k < KSTAGES - 1 && k < nk; ++k) issue(k);
+    wait_vm_runtime<LOADS>(LOADS * (min(KSTAGES - 1, nk) - 1));
+    stage_barrier();
+    read_frags(0, 0, 0);
+    int kt = 0;
+    // Steady state: a refill every stage and KSTAGES - 1 stages in flight
+    // after it, so "stage kt + 1 landed" is a constant wait (no branches,
+    // which keeps the compiler's own wait counts exact).
+    for (; kt + KSTAGES - 1 < nk; ++kt) {
+        issue(kt + KSTAGES - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_body(kt);
+        wait_vm<LOADS * (KSTAGES - 2)>();
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(0, kt + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas((SPS - 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // tail: nothing left to issue
+    for (; kt < nk; ++kt) {
+        stage_body(kt);
+        const int ahead = nk - 1 - (kt + 1);       // stages that may still be in flight
+        wait_vm_runtime<LOADS>(LOADS * (ahead > 0 ? ahead : 0));
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(0, kt + 1, 0);                  // past the end: stale, unused
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas((SPS - 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue (32x32 accumulator layout: lane holds column lane & 31 and
+    // rows 8*(r/4) + 4*(lane/32) + (r%4)).
+    bf16_t* obase = shared ? P.O_s : P.O_r;
+    const int orow0 = SWIGLU ? rrow : grow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < (SWIGLU ? 2 : 4); ++j) {
+            const int col = tl.n0 + (SWIGLU ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 128 + i * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+                float v;
+                if (SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + 2][r];
+                else v = acc[i][j][r];
+                if (row < tl.nrows && col < ncols)
+                    obase[(size_t)(orow0 + row) * ncols + col] = f32_to_bf16(v);
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, bool SWIGLU>
 hipError_t launch_cfg(const GemmParams& gp, int max_tiles, hipStream_t st) {
     const int grid = (max_tiles + 7) & ~7;
@@ -262,7 +507,11 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.TK = p.T * p.K;
     gp.abytes_r = (uint32_t)((size_t)p.T * p.d * 2);
     gp.abytes_s = gp.abytes_r;
-    if (p.g1.bm == 256) return launch_cfg<256, 256, 2, 2, true>(gp, p.max_tiles1, st);
+    if (p.g1.bm == 256) {
+        const int grid = (p.max_tiles1 + 7) & ~7;
+        gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES><<<grid, kThreads, 0, st>>>(gp);
+        return hipGetLastError();
+    }
     return launch_cfg<32, 256, 1, 4, true>(gp, p.max_tiles1, st);
 }
 
@@ -288,7 +537,11 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, 
     gp.TK = p.T * p.K;
     gp.abytes_r = (uint32_t)((size_t)p.T * p.K * p.I * 2);
     gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
-    if (p.g2.bm == 256) return launch_cfg<256, 256, 2, 2, false>(gp, p.max_tiles2, st);
+    if (p.g2.bm == 256) {
+        const int grid = (p.max_tiles2 + 7) & ~7;
+        gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES><<<grid, kThreads, 0, st>>>(gp);
+        return hipGetLastError();
+    }
     return launch_cfg<32, 256, 1, 4, false>(gp, p.max_tiles2, st);
 }
 
