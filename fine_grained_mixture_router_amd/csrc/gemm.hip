@@ -251,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
 //
 // Within a stage the fragments of k16 step s + 1 are read under the MFMAs
 // of step s; the barrier sits before the last step, so the first fragments
-// of the next stage are read under the stage's last MFMAs.  The order is
-// pinned with scheduling fences.
+// of the next stage are read, and the stage's buffer is refilled, under the
+// stage's last MFMAs.  The order is pinned with scheduling fences.
 // ---------------------------------------------------------------------------
 constexpr int kBig = 256;
 #ifndef MOE_BIG_BK
@@ -260,6 +260,20 @@ constexpr int kBig = 256;
 #endif
 #ifndef MOE_BIG_STAGES
 #define MOE_BIG_STAGES 2
+#endif
+#ifndef MOE_INTERLEAVE
+#define MOE_INTERLEAVE 1
+#endif
+// Configuration of the many-rows tile (measured on MI355X, V3-shape prefill):
+// BK = 64 (128-byte row segments) with two LDS stages, 8 waves (two per
+// SIMD, so one issues MFMAs while its sibling waits on loads or LDS), and
+// the work list dispatched in its own order (the XCD-contiguous remap was
+// within +-3 % and slightly slower).
+#ifndef MOE_XCD_REMAP
+#define MOE_XCD_REMAP 0
+#endif
+#ifndef MOE_BIG_WAVES
+#define MOE_BIG_WAVES 8
 #endif
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -289,8 +303,8 @@ __device__ __forceinline__ void wait_vm_runtime(int n) {
     else wait_vm<0>();
 }
 
-template <bool SWIGLU, int BK, int KSTAGES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool SWIGLU, int BK, int KSTAGES, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_big_kernel(GemmParams P) {
     constexpr int OPER = kBig * BK;                // elements of one operand tile
     constexpr int STAGE = 2 * OPER;                // A then B
@@ -298,25 +312,37 @@ void gemm_big_kernel(GemmParams P) {
     constexpr int RI = 1024 / (2 * BK);            // rows per load instruction
     constexpr int R = 256 / (2 * BK);              // rows per 256 bytes of LDS
     constexpr int NI = kBig / RI;                  // load instructions per operand per stage
-    constexpr int QI = NI / 4;                     // ... per wave
+    constexpr int QI = NI / NW;                    // ... per wave
     constexpr int LOADS = 2 * QI;                  // per wave per stage, both operands
     constexpr int SPS = BK / 16;                   // k16 steps per stage
+    constexpr int WN = NW / 2;                     // waves along the B rows (2 along M)
+    constexpr int WCOLS = kBig / WN;               // B-rows per wave
+    constexpr int NB = WCOLS / 32;                 // 32-wide B blocks per wave
+    constexpr int HB = NB / 2;                     // SwiGLU: W1 blocks (then as many W3)
+    constexpr int NRD = 4 + NB;                    // fragment reads per k16 step
+    static_assert(NW == 4 || NW == 8, "waves per workgroup");
     static_assert(BK == 32 || BK == 64, "slice width");
     static_assert(KSTAGES >= 2 && LOADS * (KSTAGES - 1) <= 63, "vmcnt range");
+    static_assert(KSTAGES <= 4, "wait_vm_runtime covers up to three stages in flight");
+    static_assert(QI >= 2 && QI % 2 == 0, "W1 / W3 halves of the load list");
     __shared__ __attribute__((aligned(1024))) bf16_t smem[KSTAGES * STAGE];
 
     const int nt = *P.ntiles;
     const int wg = blockIdx.x;
     const int nr = (nt + 7) & ~7;
     if (wg >= nr) return;
+#if MOE_XCD_REMAP
     const int lt = (wg & 7) * (nr >> 3) + (wg >> 3);
+#else
+    const int lt = wg;
+#endif
     if (lt >= nt) return;
     const Tile tl = P.tiles[lt];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     const bool shared = tl.group >= P.E;
     const int s = tl.group - P.E;
@@ -335,58 +361,65 @@ void gemm_big_kernel(GemmParams P) {
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(wa, wbytes);
     const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(wb, wbytes);
 
-    // Load assignment: wave w issues instructions j = w + 4q, q < QI, of each
-    // operand; instruction j fills rows RI*j .. RI*j + RI - 1.  Lane l fills
-    // position l % CH of row RI*j + l / CH, i.e. logical chunk
-    // (l % CH) ^ f(row).
+    // Load assignment: wave w issues instructions j = w + NW q, q < QI, of
+    // each operand; instruction j fills rows RI*j .. RI*j + RI - 1.  Lane l
+    // fills position l % CH of row RI*j + l / CH, i.e. logical chunk
+    // (l % CH) ^ f(row).  SwiGLU: B rows 0..127 (q < QI/2) come from W1,
+    // 128..255 from W3.
     uint32_t aoff[QI], boff[QI];
 #pragma unroll
     for (int q = 0; q < QI; ++q) {
-        const int j = wave + 4 * q;
+        const int j = wave + NW * q;
         const int row = RI * j + lane / CH;
         const uint32_t cbytes = (uint32_t)(((lane % CH) ^ ((row / R) % CH)) * 16);
         const int rr = row < tl.nrows ? row : 0;
         const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(rrow + rr);
         aoff[q] = arow * (uint32_t)kdim * 2u + cbytes;
-        // SwiGLU: B rows 0..127 come from W1, 128..255 from W3
         int n = tl.n0 + ((SWIGLU && q >= QI / 2) ? row - kBig / 2 : row);
         n = n < ncols ? n : ncols - 1;
         boff[q] = (uint32_t)n * (uint32_t)kdim * 2u + cbytes;
     }
+    // LDS destinations are wave-uniform: computed from a scalar base so the
+    // M0 value of every load is a scalar add (no VGPR -> SGPR round trip).
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_ptr_t)smem + (uint32_t)(wave * RI * BK * 2));
     auto issue = [&](int kt) {
-        bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
-        bf16_t* sb = sa + OPER;
+        const uint32_t sa = lds_base + (uint32_t)((kt % KSTAGES) * STAGE * 2);
         const uint32_t kb = (uint32_t)kt * (BK * 2);
 #pragma unroll
         for (int q = 0; q < QI; ++q) {
-            const int j = wave + 4 * q;
-            lds_load16(ra_src, sa + j * RI * BK, aoff[q] + kb);
-            lds_load16((SWIGLU && q >= QI / 2) ? rw3 : rw1, sb + j * RI * BK, boff[q] + kb);
+            const uint32_t jo = (uint32_t)(NW * q * RI * BK * 2);   // instruction j = wave + NW q
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, (lds_ptr_t)(uintptr_t)(sa + jo), 16,
+                                                     (int)(aoff[q] + kb), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QI / 2) ? rw3 : rw1,
+                                                     (lds_ptr_t)(uintptr_t)(sa + OPER * 2 + jo), 16,
+                                                     (int)(boff[q] + kb), 0, 0, 0);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
     // Fragment addressing (elements): this lane's row base and the swizzled
     // chunk of k16 step st (rows differ from lane & 31 by multiples of 32).
+    // SwiGLU: blocks j < HB are W1 rows, j >= HB the same rows of W3.
     const int lrow = lane & 31;
     const int a_row0 = (wm * 128 + lrow) * BK;
-    int b_row0[4];
+    int b_row0[NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int br = SWIGLU ? ((j < 2 ? 0 : kBig / 2) + wn * 64 + (j & 1) * 32)
-                              : (wn * 128 + j * 32);
+    for (int j = 0; j < NB; ++j) {
+        const int br = SWIGLU ? ((j < HB ? 0 : kBig / 2) + wn * (WCOLS / 2) + (j % HB) * 32)
+                              : (wn * WCOLS + j * 32);
         b_row0[j] = (br + lrow) * BK;
     }
     int cx[SPS];
 #pragma unroll
     for (int st = 0; st < SPS; ++st) cx[st] = ((2 * st + (lane >> 5)) ^ ((lrow / R) % CH)) << 3;
 
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][4], fb[2][NB];
     auto read_frags = [&](int set, int kt, int st) {
         const bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
         const bf16_t* sb = sa + OPER;
@@ -394,58 +427,81 @@ void gemm_big_kernel(GemmParams P) {
         for (int i = 0; i < 4; ++i)
             fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + a_row0 + i * 32 * BK + cx[st]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
             fb[set][j] = *reinterpret_cast<const bf16x8*>(sb + b_row0[j] + cx[st]);
     };
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j],
                                                                    0, 0, 0);
+    };
+    // One MFMA, then one LDS read, NRD times, then the remaining MFMAs: the
+    // reads issue in the shadow of running MFMAs.
+    auto interleave_reads = [&]() {
+#if MOE_INTERLEAVE
+#pragma unroll
+        for (int k = 0; k < NRD; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - NRD, 0);
+#endif
     };
     // k16 steps 0 .. SPS-2 of stage kt (step 0's fragments already in set 0)
     auto stage_body = [&](int kt) {
 #pragma unroll
         for (int st = 0; st + 1 < SPS; ++st) {
             read_frags((st + 1) & 1, kt, st + 1);
-            __builtin_amdgcn_sched_barrier(0);
             mfmas(st & 1);
+            interleave_reads();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     const int nk = kdim / BK;
-    // prologue: stages 0 .. KSTAGES-2 in flight, stage 0 resident
-    for (int k = 0; k < KSTAGES - 1 && k < nk; ++k) issue(k);
-    wait_vm_runtime<LOADS>(LOADS * (min(KSTAGES - 1, nk) - 1));
+    // Prologue: every stage buffer starts empty, so stages 0 .. KSTAGES-1
+    // are all issued; wait for stage 0.
+    for (int k = 0; k < KSTAGES && k < nk; ++k) issue(k);
+    wait_vm_runtime<LOADS>(LOADS * (min(KSTAGES, nk) - 1));
     stage_barrier();
     read_frags(0, 0, 0);
+    // Iteration kt: k16 steps 0 .. SPS-2 of stage kt, then wait for stage
+    // kt+1 and pass the barrier — after it no wave reads stage kt's buffer
+    // (its last step's fragments are in registers), so the refill with
+    // stage kt+KSTAGES is issued right there, before the last step's MFMAs.
+    // A refill thus has KSTAGES - 1 stages of MFMA time to land.
     int kt = 0;
-    // Steady state: a refill every stage and KSTAGES - 1 stages in flight
-    // after it, so "stage kt + 1 landed" is a constant wait (no branches,
-    // which keeps the compiler's own wait counts exact).
-    for (; kt + KSTAGES - 1 < nk; ++kt) {
-        issue(kt + KSTAGES - 1);
-        __builtin_amdgcn_sched_barrier(0);
+    for (; kt + KSTAGES < nk; ++kt) {                // steady state: constant waits
         stage_body(kt);
-        wait_vm<LOADS * (KSTAGES - 2)>();
+        wait_vm<LOADS * (KSTAGES - 2)>();            // stage kt+1 landed
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        issue(kt + KSTAGES);
         read_frags(0, kt + 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
         mfmas((SPS - 1) & 1);
+#if MOE_INTERLEAVE
+        // the refill's loads and the next stage's first reads, spread
+        // between this step's MFMAs
+#pragma unroll
+        for (int k = 0; k < 2 * NB; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, LOADS / (2 * NB), 0);     // VMEM loads
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);
+#endif
         __builtin_amdgcn_sched_barrier(0);
     }
-    // tail: nothing left to issue
-    for (; kt < nk; ++kt) {
+    for (; kt < nk; ++kt) {                          // tail: nothing left to issue
         stage_body(kt);
-        const int ahead = nk - 1 - (kt + 1);       // stages that may still be in flight
+        const int ahead = nk - 1 - (kt + 1);         // stages that may still be in flight
         wait_vm_runtime<LOADS>(LOADS * (ahead > 0 ? ahead : 0));
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(0, kt + 1, 0);                  // past the end: stale, unused
+        read_frags(0, kt + 1, 0);                    // past the end: stale, unused
         __builtin_amdgcn_sched_barrier(0);
         mfmas((SPS - 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -458,13 +514,13 @@ void gemm_big_kernel(GemmParams P) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < (SWIGLU ? 2 : 4); ++j) {
-            const int col = tl.n0 + (SWIGLU ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+        for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
+            const int col = tl.n0 + (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + j * 32 + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = wm * 128 + i * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
                 float v;
-                if (SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + 2][r];
+                if (SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + HB][r];
                 else v = acc[i][j][r];
                 if (row < tl.nrows && col < ncols)
                     obase[(size_t)(orow0 + row) * ncols + col] = f32_to_bf16(v);
@@ -509,7 +565,8 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.abytes_s = gp.abytes_r;
     if (p.g1.bm == 256) {
         const int grid = (p.max_tiles1 + 7) & ~7;
-        gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES><<<grid, kThreads, 0, st>>>(gp);
+        gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
+            <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
     }
     return launch_cfg<32, 256, 1, 4, true>(gp, p.max_tiles1, st);
@@ -539,7 +596,8 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, 
     gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
     if (p.g2.bm == 256) {
         const int grid = (p.max_tiles2 + 7) & ~7;
-        gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES><<<grid, kThreads, 0, st>>>(gp);
+        gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
+            <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
     }
     return launch_cfg<32, 256, 1, 4, false>(gp, p.max_tiles2, st);

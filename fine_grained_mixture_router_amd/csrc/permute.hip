@@ -18,7 +18,10 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kQuarters = 4;        // threads per expert when counting chunk masks
-constexpr int kGroupM = 4;          // M-tiles per N sweep in the work-list order
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 4
+#endif
+constexpr int kGroupM = MOE_GROUP_M;  // M-tiles per N sweep in the work-list order
 static_assert(kScanThreads >= 256 * kQuarters, "one thread per (expert, quarter)");
 
 __device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
