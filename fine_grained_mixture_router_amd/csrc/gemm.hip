@@ -430,12 +430,17 @@ void gemm_big_kernel(GemmParams P) {
         for (int j = 0; j < NB; ++j)
             fb[set][j] = *reinterpret_cast<const bf16x8*>(sb + b_row0[j] + cx[st]);
     };
+    // The weight fragment is the MFMA's first operand, the activation
+    // fragment its second, so the accumulator is the transposed block: lane
+    // l holds activation row (l & 31) and output columns 8i + 4(l >> 5) + j
+    // (i, j = 0..3) — four runs of four consecutive columns, which the
+    // epilogue writes as 8-byte pieces.
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j],
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j],
                                                                    0, 0, 0);
     };
     // One MFMA, then one LDS read, NRD times, then the remaining MFMAs: the
@@ -507,23 +512,53 @@ void gemm_big_kernel(GemmParams P) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Epilogue (32x32 accumulator layout: lane holds column lane & 31 and
-    // rows 8*(r/4) + 4*(lane/32) + (r%4)).
-    bf16_t* obase = shared ? P.O_s : P.O_r;
-    const int orow0 = SWIGLU ? rrow : grow;
+    // Epilogue: the tile's outputs (bf16; SwiGLU applied in registers) go
+    // through LDS — now free — and leave as whole 16-byte row pieces, one
+    // row segment of OC * 2 bytes per CPR lanes.  In LDS, 16-byte chunk c of
+    // row r sits at position c ^ (r mod CPR), so the 32 rows one write
+    // instruction touches land in 32 different chunks.
+    constexpr int OC = SWIGLU ? kBig / 2 : kBig;     // output columns of the tile
+    constexpr int CPR = OC / 8;                      // 16-byte chunks per row
+    static_assert(kBig * OC <= KSTAGES * STAGE, "output tile fits the stage buffers");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();                                 // every wave is done with the stages
+    {
+        const int orow_l = wm * 128 + (lane & 31);   // + 32 i
+        const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (lane >> 5);   // + 32 j + 8 r4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
-            const int col = tl.n0 + (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + j * 32 + (lane & 31);
+            for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * 128 + i * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-                float v;
-                if (SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + HB][r];
-                else v = acc[i][j][r];
-                if (row < tl.nrows && col < ncols)
-                    obase[(size_t)(orow0 + row) * ncols + col] = f32_to_bf16(v);
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        v[e] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + HB][r] : acc[i][j][r];
+                    }
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    const int orow = orow_l + 32 * i;
+                    const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
+                    const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                    *reinterpret_cast<uint2*>(smem + off) = make_uint2(lo, hi);
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    {
+        bf16_t* obase = shared ? P.O_s : P.O_r;
+        const int orow0 = SWIGLU ? rrow : grow;
+        for (int c = tid; c < kBig * CPR; c += 64 * NW) {
+            const int row = c / CPR;
+            const int cc = c - row * CPR;
+            const int col = tl.n0 + cc * 8;
+            if (row < tl.nrows && col < ncols) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * OC + ((cc ^ (row % CPR)) << 3));
+                *reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col) = v;
             }
         }
     }
