@@ -22,9 +22,13 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,6 +38,17 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer fwd tokens/s; % of MFMA (prefill) / HBM (decode) roofline"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CSRC = os.path.join(ROOT, "fine_grained_mixture_router_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_v3_prefill_decode.md")
+CALIB_BYTES = 1 << 30         # the calibration copy: 1 GiB read + 1 GiB written
+# kernel-name prefix -> (workload, slot) in a default run (prefill on the
+# 256x256 tile, decode on the 32x256 tile)
+COUNTER_KERNELS = {
+    "gemm_big_kernel<true": ("v3_prefill", "gemm_gate_up"),
+    "gemm_big_kernel<false": ("v3_prefill", "gemm_down"),
+    "grouped_gemm_kernel<32, 256, 1, 4, true>": ("v3_decode", "gemm_gate_up"),
+    "grouped_gemm_kernel<32, 256, 1, 4, false>": ("v3_decode", "gemm_down"),
+}
 
 
 def parse():
@@ -46,7 +61,98 @@ def parse():
                     help="second workload on the same layer weights ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle CPU baseline (0 to skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with a 1 GiB device-to-device copy (the reference dispatch that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     return ap.parse_args()
+
+
+def source_digest():
+    """Digest of the HIP sources' code (comments and blank space removed):
+    recorded counters describe these kernels only."""
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(CSRC)):
+        if n.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, n)) as f:
+                code = f.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            h.update(n.encode())
+            h.update(" ".join(code.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(run_dir, counter):
+    """Mean value per dispatch of `counter`, per kernel name, from a rocprofv3
+    counter_collection.csv under run_dir."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    vals = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Traffic of the GEMM kernels from FETCH_SIZE and WRITE_SIZE runs (KiB
+    per dispatch), scaled by what the same counters read for the 1 GiB
+    calibration copy (the largest copy dispatch of each run)."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def copy_max(vals):
+        c = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        if not c:
+            raise SystemExit("no calibration copy dispatch found (run with --calibrate-copy)")
+        return max(c)
+
+    f_fetch = CALIB_BYTES / (copy_max(fetch) * 1024)
+    f_write = CALIB_BYTES / (copy_max(write) * 1024)
+    kern = {}
+    for name in set(fetch) | set(write):
+        short = re.sub(r"^void |\(.*$", "", name.replace("moe::(anonymous namespace)::", ""))
+        for pre, (wl_name, slot) in COUNTER_KERNELS.items():
+            if short.startswith(pre):
+                fk = sum(fetch.get(name, [0])) / max(len(fetch.get(name, [])), 1)
+                wk = sum(write.get(name, [0])) / max(len(write.get(name, [])), 1)
+                kern.setdefault(wl_name, {})[slot] = dict(
+                    kernel=short, dispatches=len(fetch.get(name, [])), fetch_kib=round(fk, 1),
+                    write_kib=round(wk, 1),
+                    bytes=round(fk * 1024 * f_fetch + wk * 1024 * f_write))
+    rec = dict(source_digest=source_digest(),
+               calibration=dict(copy_bytes=CALIB_BYTES, fetch_scale=round(f_fetch, 4),
+                                write_scale=round(f_write, 4)),
+               kernels=kern)
+    print("| workload | slot | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes |")
+    print("|---|---|---|---:|---:|---:|---:|")
+    for wl_name in sorted(kern):
+        for slot, k in sorted(kern[wl_name].items()):
+            print(f"| {wl_name} | {slot} | `{k['kernel']}` | {k['dispatches']} | {k['fetch_kib']:.0f} "
+                  f"| {k['write_kib']:.0f} | {k['bytes'] / 1e9:.3f} GB |")
+    print()
+    print("```json")
+    print(json.dumps(rec, indent=1))
+    print("```")
+
+
+def recorded_traffic(workload, slot):
+    """Bytes per launch of `slot` on `workload` from the committed counter
+    summary, or None when there is none or it was taken on other sources."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", txt, re.S).group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(workload, {}).get(slot)
+    return None if k is None else float(k["bytes"])
 
 
 def hit_stats(idx, E):
@@ -135,18 +241,23 @@ def regime(w):
     return "hbm" if w.T * w.K < 64 * w.E else "mfma"
 
 
-def roofline(kind, work, kernels):
+def roofline(kind, work, kernels, workload):
+    """The gate/up GEMM against its roofline.  `traffic` is the HBM bytes per
+    launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    calibrated), null when that summary is of other kernel sources."""
     ms, n = kernels["gemm_gate_up"]
     avg_s = ms / max(n, 1) / 1e3
+    traffic = recorded_traffic(workload, "gemm_gate_up")
+    common = dict(traffic=traffic, algorithmic_bytes=work["g1_bytes"],
+                  mean_launch_ms=round(ms / max(n, 1), 4), launches=n)
     if kind == "mfma":
         ach = work["g1_flops"] / avg_s / 1e12
         return dict(kernel="gemm_gate_up", bound="mfma", achieved=round(ach, 1),
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4),
-                    traffic=None, mean_launch_ms=round(ms / max(n, 1), 4), launches=n)
+                    **common)
     ach = work["g1_bytes"] / avg_s / 1e9
     return dict(kernel="gemm_gate_up", bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS,
-                unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
-                mean_launch_ms=round(ms / max(n, 1), 4), launches=n)
+                unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), **common)
 
 
 def cpu_baseline(w, L, res, seconds):
@@ -189,6 +300,9 @@ def cpu_baseline(w, L, res, seconds):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build runs the layer on a single MI355X and has "
@@ -228,7 +342,7 @@ def main():
         "data": "synthetic (seeded; bf16 N(0,1) activations, N(0,0.006) weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "I": w.I, "K": w.K,
                    "Ks": w.Ks, "Is": w.Is, "zipf_s": w.zipf_s, "parallelism": "single GPU"},
-        "roofline": roofline(regime(w), work, res["kernels"]),
+        "roofline": roofline(regime(w), work, res["kernels"], w.name),
         "layer": {"tflops": round(work["layer_flops"] / (ms / 1e3) / 1e12, 1),
                   "mfma_frac": round(work["layer_flops"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in res["kernels"].items()},
@@ -248,7 +362,7 @@ def main():
         line["decode"] = {
             "workload": wd.name, "T": wd.T, "value": round(wd.T / (msd / 1e3), 1),
             "unit": "tokens/s", "ms_per_step": round(msd, 4),
-            "roofline": roofline(regime(wd), wk, rd["kernels"]),
+            "roofline": roofline(regime(wd), wk, rd["kernels"], wd.name),
             "layer_gbs": round(wk["layer_bytes"] / (msd / 1e3) / 1e9, 1),
             "layer_hbm_frac": round(wk["layer_bytes"] / (msd / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rd["kernels"].items()},
@@ -262,6 +376,13 @@ def main():
         line["spot_parity"] = spot
     else:
         line["cpu_baseline"] = None
+    if args.calibrate_copy:
+        src = torch.ones(CALIB_BYTES // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(line), flush=True)
 
 

@@ -16,9 +16,9 @@
 // (G2).  Tiles are BM x BN with BK = 64, staged through LDS (double buffer,
 // XOR-swizzled 16-byte chunks) and consumed by v_mfma_f32_32x32x16_bf16.
 // The grid is the work-list bound; workgroups past the device-side count
-// exit at once.  Workgroup ids are remapped so that each XCD (ids are dealt
-// round-robin over the 8 XCDs) takes a contiguous slice of the list, whose
-// neighbouring tiles share weights or activations in that XCD's L2.
+// exit at once.  Workgroup ids are dealt round-robin over the 8 XCDs, so the
+// tiles one XCD runs together share A rows (same M-tile, alternate N-tiles)
+// in its L2; an XCD-contiguous remap is available (MOE_XCD_REMAP).
 #include "common.h"
 
 namespace moe {
