@@ -22,18 +22,29 @@ __device__ __forceinline__ void add8(float* acc, u32x4 v, float w) {
     }
 }
 
+constexpr int kMaxSrc = 16 + 256;   // Ks + K rows per token at most
+constexpr int kBatch = 8;            // source rows loaded ahead of their adds
+
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Y, const float* __restrict__ gate,
     const int32_t* __restrict__ slot_of, bf16_t* __restrict__ out, int T, int d, int K, int Ks,
     int residual) {
     const int t = blockIdx.x;
     const int nv = d >> 3;
+    const int ns = Ks + K;
     const size_t tk = (size_t)T * K;
-    __shared__ int s_slot[256];
-    __shared__ float s_gate[256];
-    for (int k = threadIdx.x; k < K; k += kThreads) {
-        s_slot[k] = slot_of[(size_t)t * K + k];
-        s_gate[k] = gate[(size_t)t * K + k];
+    // the token's source rows of Y in summation order (shared experts, then
+    // k = 0..K-1) and their weights
+    __shared__ int s_row[kMaxSrc];
+    __shared__ float s_w[kMaxSrc];
+    for (int i = threadIdx.x; i < ns; i += kThreads) {
+        if (i < Ks) {
+            s_row[i] = (int)(tk + (size_t)i * T + t);
+            s_w[i] = 1.0f;
+        } else {
+            s_row[i] = slot_of[(size_t)t * K + (i - Ks)];
+            s_w[i] = gate[(size_t)t * K + (i - Ks)];
+        }
     }
     __syncthreads();
     for (int v = threadIdx.x; v < nv; v += kThreads) {
@@ -41,10 +52,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
         if (residual) add8(acc, reinterpret_cast<const u32x4*>(x + (size_t)t * d)[v], 1.0f);
-        for (int s = 0; s < Ks; ++s)
-            add8(acc, reinterpret_cast<const u32x4*>(Y + (tk + (size_t)s * T + t) * d)[v], 1.0f);
-        for (int k = 0; k < K; ++k)
-            add8(acc, reinterpret_cast<const u32x4*>(Y + (size_t)s_slot[k] * d)[v], s_gate[k]);
+        for (int b0 = 0; b0 < ns; b0 += kBatch) {
+            u32x4 r[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (b0 + b < ns) r[b] = reinterpret_cast<const u32x4*>(Y + (size_t)s_row[b0 + b] * d)[v];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                if (b0 + b < ns) add8(acc, r[b], s_w[b0 + b]);
+        }
         u32x4 o;
         o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
         o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);

@@ -24,20 +24,33 @@ constexpr int kQuarters = 4;        // threads per expert when counting chunk ma
 constexpr int kGroupM = MOE_GROUP_M;  // M-tiles per N sweep in the work-list order
 static_assert(kScanThreads >= 256 * kQuarters, "one thread per (expert, quarter)");
 
-__device__ int block_exclusive_scan(int v, int* sbuf, int* total) {
-    const int tid = threadIdx.x;
-    sbuf[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < kScanThreads; o <<= 1) {
-        int add = tid >= o ? sbuf[tid - o] : 0;
-        __syncthreads();
-        sbuf[tid] += add;
-        __syncthreads();
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kMaskBatch = 8;       // chunk masks loaded ahead of their use
+
+// Exclusive prefix sum over the workgroup, in thread order: a shuffle scan
+// within each wavefront, then the wavefront totals.  Two barriers; `swave`
+// (kScanWaves ints of LDS) is free again on return.
+__device__ int block_exclusive_scan(int v, int* swave, int* total) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
     }
-    const int incl = sbuf[tid];
-    *total = sbuf[kScanThreads - 1];
+    if (lane == 63) swave[w] = x;
     __syncthreads();
-    return incl - v;
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kScanWaves; ++i) {
+        const int si = swave[i];
+        base += i < w ? si : 0;
+        tot += si;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + x - v;
 }
 
 // Work-list entry i of a group with mt M-tiles and nt N-tiles, in
@@ -79,7 +92,7 @@ __device__ void emit_list(Tile* out, int total, const int* s_off, const int* s_c
 }
 
 __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int routed) {
-    __shared__ int sbuf[kScanThreads];
+    __shared__ int sbuf[kScanWaves];
     __shared__ int s_part[kQuarters][256];
     __shared__ int s_cnt[kScanThreads];
     __shared__ int s_t1[kScanThreads];
@@ -94,7 +107,14 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int rou
     // rows of expert e in chunk quarter q
     int part = 0;
     if (routed && e < p.E && q < kQuarters)
-        for (int c = c0; c < c1; ++c) part += __popcll(p.masks[(size_t)c * p.Epad + e]);
+        for (int c = c0; c < c1; c += kMaskBatch) {
+            uint64_t m[kMaskBatch];
+#pragma unroll
+            for (int b = 0; b < kMaskBatch; ++b)
+                m[b] = c + b < c1 ? p.masks[(size_t)(c + b) * p.Epad + e] : 0ull;
+#pragma unroll
+            for (int b = 0; b < kMaskBatch; ++b) part += __popcll(m[b]);
+        }
     if (q < kQuarters) s_part[q][e] = part;
     __syncthreads();
 
@@ -118,9 +138,16 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int rou
     if (routed && e < p.E && q < kQuarters) {
         int run = p.goff[e];
         for (int k = 0; k < q; ++k) run += s_part[k][e];
-        for (int c = c0; c < c1; ++c) {
-            p.chunk_base[(size_t)c * p.Epad + e] = run;
-            run += __popcll(p.masks[(size_t)c * p.Epad + e]);
+        for (int c = c0; c < c1; c += kMaskBatch) {
+            uint64_t m[kMaskBatch];
+#pragma unroll
+            for (int b = 0; b < kMaskBatch; ++b)
+                m[b] = c + b < c1 ? p.masks[(size_t)(c + b) * p.Epad + e] : 0ull;
+#pragma unroll
+            for (int b = 0; b < kMaskBatch; ++b) {
+                if (c + b < c1) p.chunk_base[(size_t)(c + b) * p.Epad + e] = run;
+                run += __popcll(m[b]);
+            }
         }
     }
 

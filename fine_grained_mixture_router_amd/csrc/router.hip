@@ -10,14 +10,13 @@
 //                  Tiles of 64 tokens x 64 experts; for small T the d range is
 //                  split so that the launch still covers the chip, and the
 //                  partials are summed in a fixed order by the next kernel.
-//   router_select  one wavefront per token (16 per workgroup, 4 tokens each):
-//                  sum partials, add the bias, fp32 softmax, then K rounds of a
-//                  wavefront arg-max over the E<=256 logits (4 per lane; ties go
-//                  to the lower expert id).  Each workgroup owns a 64-token
-//                  chunk and also records, per expert,
-//                  the 64-bit mask of its tokens that chose that expert; the
-//                  permutation step turns those masks into a stable,
-//                  atomics-free grouping of tokens by expert.
+//   router_select  one wavefront per token (16 per workgroup): sum partials,
+//                  add the bias, fp32 softmax, then K rounds of a wavefront
+//                  arg-max over the E<=256 logits (4 per lane; ties go to the
+//                  lower expert id).  Per expert it also records the 64-bit
+//                  mask of the tokens of each 64-token chunk that chose that
+//                  expert; the permutation step turns those masks into a
+//                  stable, atomics-free grouping of tokens by expert.
 #include "common.h"
 
 namespace moe {
@@ -26,10 +25,12 @@ namespace {
 constexpr int kThreads = 256;
 
 // 64 rows x 64 bf16 of a row-major tile, one 16-byte chunk per (row, c),
-// stored at chunk position c ^ (row & 7) so that the MFMA fragment reads of
-// eight consecutive rows hit distinct LDS banks.
+// stored at chunk position c ^ ((row >> 1) & 7).  LDS serves 16 lanes x 16
+// bytes per cycle; an MFMA fragment read puts 16 lanes on 16 consecutive
+// rows at one logical chunk, and with 128-byte rows those 16 reads then
+// land in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * 64 + ((chunk ^ (row & 7)) << 3);
+    return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 __global__ __launch_bounds__(kThreads) void router_logits_kernel(
@@ -122,45 +123,63 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// One workgroup per 64-token chunk, 16 waves, 4 tokens per wave.
-constexpr int kSelectThreads = 1024;
+// One wavefront per token: a workgroup of 16 waves takes 16 consecutive
+// tokens, a quarter of a 64-token chunk, and writes that quarter's 16 bits
+// of every expert's chunk mask (a 16-bit store into the 64-bit word, so the
+// four workgroups of a chunk write disjoint bytes and no mask needs clearing
+// first; quarters past T write zeros).
+constexpr int kSelectWaves = 16;
+constexpr int kSelectThreads = 64 * kSelectWaves;
+constexpr int kSubChunks = kChunk / kSelectWaves;
+static_assert(kSubChunks == 4, "16-bit quarters of the 64-bit chunk mask");
+constexpr int kPartBatch = 8;       // partial logits loaded ahead of their adds
 
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ idx,
     float* __restrict__ gate, uint64_t* __restrict__ masks, int T, int E, int Epad, int K,
     int split) {
-    __shared__ unsigned long long smask[256];
+    __shared__ unsigned smask[256];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int c = blockIdx.x;
-    for (int e = tid; e < Epad; e += kSelectThreads) smask[e] = 0ull;
+    const int c = blockIdx.x / kSubChunks;
+    const int q = blockIdx.x % kSubChunks;
+    for (int e = tid; e < Epad; e += kSelectThreads) smask[e] = 0u;
     __syncthreads();
 
-    const float NEG = -INFINITY;
-    float bj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        bj[j] = (bias && e < E) ? bias[e] : 0.f;
-    }
-    for (int i = 0; i < kChunk / 16; ++i) {
-        const int tl = wave + 16 * i;                 // token within the chunk
-        const int t = c * kChunk + tl;
-        if (t >= T) break;
+    const int tl = q * kSelectWaves + wave;          // token within the chunk
+    const int t = c * kChunk + tl;
+    if (t < T) {
+        const float NEG = -INFINITY;
+        // logits of experts lane + 64 j: the split-K partials summed in
+        // order z = 0, 1, ..., loaded kPartBatch at a time
         float v[4];
-        int taken = 0;                                // bit j: expert lane + 64j is out
+        int taken = 0;                               // bit j: expert lane + 64j is out
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = 0.f;
+            if (lane + 64 * j >= E) taken |= 1 << j;
+        }
+        const float* lp = logits + (size_t)t * Epad + lane;
+        const size_t zstride = (size_t)T * Epad;
+        for (int z0 = 0; z0 < split; z0 += kPartBatch) {
+            float pv[kPartBatch][4];
+#pragma unroll
+            for (int b = 0; b < kPartBatch; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pv[b][j] = (z0 + b < split && !((taken >> j) & 1))
+                                   ? lp[(size_t)(z0 + b) * zstride + 64 * j] : 0.f;
+#pragma unroll
+            for (int b = 0; b < kPartBatch; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (z0 + b < split) v[j] += pv[b][j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
-            if (e < E) {
-                float s = 0.f;
-                for (int z = 0; z < split; ++z) s += logits[((size_t)z * T + t) * Epad + e];
-                v[j] = s + bj[j];
-            } else {
-                v[j] = NEG;
-                taken |= 1 << j;
-            }
+            v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : NEG;
         }
         const float mx = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
         float ps = 0.f;
@@ -190,12 +209,14 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
             if (lane == 0) {
                 idx[(size_t)t * K + k] = be;
                 gate[(size_t)t * K + k] = expf(bv - mx) / sum;
-                atomicOr(&smask[be], 1ull << tl);
+                atomicOr(&smask[be], 1u << wave);
             }
         }
     }
     __syncthreads();
-    for (int e = tid; e < Epad; e += kSelectThreads) masks[(size_t)c * Epad + e] = smask[e];
+    uint16_t* m16 = reinterpret_cast<uint16_t*>(masks);
+    for (int e = tid; e < Epad; e += kSelectThreads)
+        m16[((size_t)c * Epad + e) * kSubChunks + q] = (uint16_t)smask[e];
 }
 
 }  // namespace
@@ -209,8 +230,8 @@ hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C,
 }
 
 hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st) {
-    router_select_kernel<<<p.nchunk, kSelectThreads, 0, st>>>(p.logits, bias, p.idx, p.gate, p.masks,
-                                                       p.T, p.E, p.Epad, p.K, p.split);
+    router_select_kernel<<<p.nchunk * kSubChunks, kSelectThreads, 0, st>>>(
+        p.logits, bias, p.idx, p.gate, p.masks, p.T, p.E, p.Epad, p.K, p.split);
     return hipGetLastError();
 }
 
