@@ -18,6 +18,8 @@ Prints ONE JSON line:
                    timed steps, against the MI355X peak
   cpu_baseline     the fp64 oracle on a bounded token sample of the same
                    batch, on the host cores (a reported baseline, not a target)
+  hbm_read_ceiling the practical HBM read rate measured in the same run (a
+                   plain streaming-read kernel), beside the nominal 8 TB/s
 """
 from __future__ import annotations
 
@@ -69,18 +71,21 @@ def parse():
     return ap.parse_args()
 
 
+DIGEST_SOURCES = ("common.h", "gemm.hip", "permute.hip")   # the GEMMs and their tile order
+
+
 def source_digest():
-    """Digest of the HIP sources' code (comments and blank space removed):
-    recorded counters describe these kernels only."""
+    """Digest of the code (comments and blank space removed) of the sources
+    that decide the GEMMs' memory traffic: recorded counters describe these
+    kernels only."""
     h = hashlib.sha256()
-    for n in sorted(os.listdir(CSRC)):
-        if n.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, n)) as f:
-                code = f.read()
-            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
-            code = re.sub(r"//[^\n]*", " ", code)
-            h.update(n.encode())
-            h.update(" ".join(code.split()).encode())
+    for n in DIGEST_SOURCES:
+        with open(os.path.join(CSRC, n)) as f:
+            code = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(n.encode())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -235,6 +240,46 @@ def time_workload(w, D, host_x, steps, warmup):
                 gate=gate.cpu().numpy())
 
 
+def layer_roofline_ms(w, counts):
+    """Lower bound on the layer's time with every piece at the better of its
+    two ceilings (2.5 PFLOP/s, 8 TB/s): the router, each routed or shared
+    expert as max(FLOPs / peak, bytes / bandwidth) — an expert of n rows does
+    6·d·I·n FLOPs and moves its 3·d·I bf16 weights plus n rows of x, H
+    (written, then read) and Y — and the combine's (2 + K + Ks)·d bf16 per
+    token.  Few-row experts are bandwidth-bound even in a prefill batch."""
+    peak, bw = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
+    t = max(2.0 * w.T * w.d * w.E / peak, (2.0 * w.T * w.d + 2.0 * w.E * w.d) / bw)
+    groups = [(int(n), w.I) for n in counts if n > 0] + [(w.T, w.Is)] * w.Ks
+    for n, inter in groups:
+        f = 6.0 * w.d * inter * n
+        b = 6.0 * w.d * inter + n * (2.0 * w.d + 4.0 * inter + 2.0 * w.d)
+        t += max(f / peak, b / bw)
+    t += (2 + w.K + w.Ks) * w.T * w.d * 2.0 / bw
+    return t * 1e3
+
+
+def hbm_read_ceiling(nbytes=8 << 30, passes=5):
+    """The device's practical HBM read rate: one pass of 16-byte loads over
+    an nbytes buffer (the library's stream-read kernel), timed with events."""
+    import torch
+
+    import fine_grained_mixture_router_amd as moe
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    moe.stream_read(buf)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(passes):
+        moe.stream_read(buf)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / passes
+    del buf
+    return dict(gbs=round(nbytes / (ms / 1e3) / 1e9, 1), bytes=nbytes, passes=passes,
+                ms_per_pass=round(ms, 4))
+
+
 def regime(w):
     """Few rows per expert (under 64 on average) stream each weight once and
     are HBM-bound; larger batches are MFMA-bound."""
@@ -346,6 +391,8 @@ def main():
         "layer": {"tflops": round(work["layer_flops"] / (ms / 1e3) / 1e12, 1),
                   "mfma_frac": round(work["layer_flops"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                   "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in res["kernels"].items()},
+                  "roofline_ms": round(layer_roofline_ms(w, counts), 4),
+                  "frac_of_roofline": round(layer_roofline_ms(w, counts) / ms, 4),
                   "load": hit_stats(res["idx"], w.E)},
     }
     print(f"[bench] {w.name}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
@@ -366,9 +413,19 @@ def main():
             "layer_gbs": round(wk["layer_bytes"] / (msd / 1e3) / 1e9, 1),
             "layer_hbm_frac": round(wk["layer_bytes"] / (msd / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rd["kernels"].items()},
+            "roofline_ms": round(layer_roofline_ms(wd, cd), 4),
+            "frac_of_roofline": round(layer_roofline_ms(wd, cd) / msd, 4),
             "load": hit_stats(rd["idx"], wd.E),
         }
         print(f"[bench] {wd.name}: {msd:.3f} ms/step", file=sys.stderr, flush=True)
+
+    ceil = hbm_read_ceiling()
+    line["hbm_read_ceiling"] = ceil
+    if "decode" in line:
+        r = line["decode"]["roofline"]
+        r["frac_of_read_ceiling"] = round(r["achieved"] / ceil["gbs"], 4)
+        line["decode"]["layer_frac_of_read_ceiling"] = round(line["decode"]["layer_gbs"] / ceil["gbs"], 4)
+    print(f"[bench] HBM read ceiling {ceil['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     if args.cpu_seconds > 0:
         base, spot = cpu_baseline(w, L, res, args.cpu_seconds)

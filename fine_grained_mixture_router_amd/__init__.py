@@ -48,7 +48,7 @@ import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m fine_grained_mixture_router_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python fine_grained_mixture_router_amd/build.py` "
         "(there is no fallback implementation)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -70,9 +70,12 @@ _lib.moe_profile_end.restype = ctypes.c_int
 _lib.moe_profile_end.argtypes = [_vp, _vp, ctypes.c_int32]
 _lib.moe_profile_slot_name.restype = ctypes.c_char_p
 _lib.moe_profile_slot_name.argtypes = [ctypes.c_int32]
+_lib.moe_profile_stream_read.restype = ctypes.c_int
+_lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
 EXPORTS = ("moe_workspace_size", "moe_forward", "moe_route", "moe_status_string",
-           "moe_profile_begin", "moe_profile_end", "moe_profile_slot_name")
+           "moe_profile_begin", "moe_profile_end", "moe_profile_slot_name",
+           "moe_profile_stream_read")
 N_SLOTS = 7
 
 
@@ -191,3 +194,14 @@ def profile_end() -> dict:
     _check(_lib.moe_profile_end(ctypes.cast(ms, _vp), ctypes.cast(n, _vp), N_SLOTS))
     return {_lib.moe_profile_slot_name(k).decode(): (float(ms[k]), int(n[k]))
             for k in range(N_SLOTS)}
+
+
+def stream_read(buf, stream=None):
+    """Enqueue one pass of 16-byte loads over the device tensor `buf` (its
+    size a multiple of 16384 bytes): time it to get the practical HBM read
+    rate."""
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    _check(_lib.moe_profile_stream_read(ctypes.c_void_p(buf.data_ptr()),
+                                        buf.numel() * buf.element_size(),
+                                        ctypes.c_void_p(s.cuda_stream)))

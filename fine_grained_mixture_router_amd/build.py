@@ -1,6 +1,6 @@
 """Build libmoe.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
-    python -m fine_grained_mixture_router_amd.build
+    python fine_grained_mixture_router_amd/build.py
 """
 from __future__ import annotations
 

@@ -94,5 +94,6 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
                                hipStream_t st);
 hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, hipStream_t st);
 hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st);
+hipError_t launch_stream_read(const void* buf, size_t bytes, hipStream_t st);
 
 }  // namespace moe

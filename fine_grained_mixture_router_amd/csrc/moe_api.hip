@@ -345,4 +345,15 @@ __attribute__((visibility("default"))) const char* moe_profile_slot_name(int32_t
     return (slot >= 0 && slot < kSlots) ? kSlotNames[slot] : "";
 }
 
+__attribute__((visibility("default"))) moe_status_t moe_profile_stream_read(const void* buf,
+                                                                            size_t bytes,
+                                                                            void* stream) {
+    if (!buf) return MOE_ERR_NULL;
+    if (bytes == 0 || bytes % 16384) return MOE_ERR_SHAPE;
+    if ((uintptr_t)buf % 16) return MOE_ERR_ALIGN;
+    moe_status_t st = device_ok();
+    if (st != MOE_OK) return st;
+    return launch_stream_read(buf, bytes, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 }  // extern "C"

@@ -134,6 +134,15 @@ moe_status_t moe_profile_begin(int32_t max_calls);
 moe_status_t moe_profile_end(float* ms, int32_t* launches, int32_t n_slots);
 const char* moe_profile_slot_name(int32_t slot);
 
+/* moe_profile_stream_read(buf, bytes, stream): enqueue one pass of 16-byte
+ * loads over `bytes` of device memory at `buf` (caller-owned, 16-byte
+ * aligned, contents irrelevant, never written), on `stream`.  Timed by the
+ * caller, it gives the device's practical HBM read rate, the ceiling that the
+ * HBM-bound kernels are compared with beside the nominal peak.  Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE (bytes not a positive multiple of 16384),
+ * MOE_ERR_ALIGN, MOE_ERR_NO_DEVICE / MOE_ERR_DEVICE_ARCH, MOE_ERR_HIP. */
+moe_status_t moe_profile_stream_read(const void* buf, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

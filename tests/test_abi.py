@@ -150,3 +150,14 @@ def test_segment_helper():
     assert (g["E"], g["I"], g["K"], g["Ks"]) == (64, 1024, 8, 1)
     with pytest.raises(ValueError):
         moe.segment(4, 3, 1000, K=2)
+
+
+def test_stream_read_validation():
+    f = moe.lib().moe_profile_stream_read
+    assert f(None, ctypes.c_size_t(16384), None) == 1
+    assert f(ctypes.c_void_p(4096), ctypes.c_size_t(0), None) == 2
+    assert f(ctypes.c_void_p(4096), ctypes.c_size_t(16384 + 16), None) == 2
+    assert f(ctypes.c_void_p(4096 + 8), ctypes.c_size_t(16384), None) == 3
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() == 0:
+        assert f(ctypes.c_void_p(4096), ctypes.c_size_t(16384), None) == 5

@@ -183,3 +183,14 @@ def test_errors_leave_output_untouched():
         moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
                     K=w.E + 1, out=out)
     assert e.value.code == 2
+
+
+def test_stream_read_runs_and_writes_nothing():
+    """The bandwidth-ceiling kernel of the benchmark reads its buffer only."""
+    buf = torch.randint(0, 255, (64 << 20,), dtype=torch.uint8, device="cuda")
+    ref = buf.clone()
+    moe.stream_read(buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, ref)
+    with pytest.raises(moe.MoEError):
+        moe.stream_read(buf[: 16384 + 16])
