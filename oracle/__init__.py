@@ -23,6 +23,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 NO_RESIDUAL = 1
+RENORM = 2      # gates divided by their sum over the K selected experts
+SIGMOID = 4     # sigmoid affinities; the bias enters the selection only
 
 
 def build(force: bool = True) -> str:
@@ -83,18 +85,23 @@ def _ptr_table(stack, n, shape):
     return tbl, keep
 
 
-def route(x_rows, C, bias, K, nthreads=0, return_probs=False):
-    """Routing (affinity, softmax, top-K) of the given token rows.
+def _gating(renorm, sigmoid):
+    return (RENORM if renorm else 0) | (SIGMOID if sigmoid else 0)
+
+
+def route(x_rows, C, bias, K, nthreads=0, return_probs=False, renorm=False, sigmoid=False):
+    """Routing (affinity, score, top-K) of the given token rows.
 
     x_rows: uint16 bf16 bits [n, d]; C: [E, d]; bias: float32 [E] or None.
+    renorm / sigmoid select the gating variant (see oracle.c, steps 2-3).
     Returns idx int32 [n, K], gate float64 [n, K], margin float64 [n]
-    (and probs [n, E] when asked)."""
+    (and the scores [n, E] when asked)."""
     x_rows = np.ascontiguousarray(x_rows)
     n, d = x_rows.shape
     E = C.shape[0]
     C = _u16(C, (E, d))
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
-    sh = _Shape(n, d, E, 0, K, 0, 0, 0)
+    sh = _Shape(n, d, E, 0, K, 0, 0, _gating(renorm, sigmoid))
     idx = np.zeros((n, K), np.int32)
     gate = np.zeros((n, K), np.float64)
     margin = np.zeros(n, np.float64)
@@ -105,7 +112,7 @@ def route(x_rows, C, bias, K, nthreads=0, return_probs=False):
 
 
 def forward(x_rows, C, bias, w1, w3, w2, ws1, ws3, ws2, K, no_residual=False,
-            forced_idx=None, nthreads=0):
+            forced_idx=None, nthreads=0, renorm=False, sigmoid=False):
     """Layer forward of the given token rows, in fp64.
 
     x_rows: [n, d] bf16 bits.  w1/w3: per routed expert [I, d] (a [E, I, d]
@@ -143,7 +150,8 @@ def forward(x_rows, C, bias, w1, w3, w2, ws1, ws3, ws2, K, no_residual=False,
         assert fi.shape == (n, K)
         assert fi.size == 0 or (fi.min() >= 0 and fi.max() < E)
 
-    sh = _Shape(n, d, E, I, K, Ks, Is, NO_RESIDUAL if no_residual else 0)
+    sh = _Shape(n, d, E, I, K, Ks, Is,
+                (NO_RESIDUAL if no_residual else 0) | _gating(renorm, sigmoid))
     out = np.zeros((n, d), np.float64)
     shared = np.zeros((n, d), np.float64)
     routed = np.zeros((n, d), np.float64)

@@ -9,17 +9,26 @@
  * arithmetic in IEEE double, plain sequential loops, bf16 inputs widened
  * exactly):
  *
- *   1. affinity  l_e = sum_j x[t,j] * C[e,j] + b_e       (b_e = 0 without bias)
+ *   1. affinity  a_e = sum_j x[t,j] * C[e,j]
  *      The token-to-centroid inner product of the generic top-K MoE gate
  *      ("DeepSeekMoE 深度解读报告", section 3.1, Eq. 3-5 as described there).
- *   2. score     s_e = exp(l_e - max l) / sum_f exp(l_f - max l)
- *      softmax over the N*m routed experts only; shared experts never enter
- *      the gate (same page, sections 2.3 and 3.1).
- *   3. selection K rounds of argmax over the experts not yet taken, strict
- *      '>' so that the lower index wins a tie.  gate_k = s_{e_k}; the other
- *      experts get 0 and no renormalisation follows (section 3.1: keep the
- *      top scores, zero the rest).  margin = s_(K) - s_(K+1), +inf when
- *      K == E or K == 0.
+ *   2. score     softmax gate (default): l_e = a_e + b_e (b_e = 0 without
+ *      bias) and s_e = exp(l_e - max l) / sum_f exp(l_f - max l), over the
+ *      N*m routed experts only; shared experts never enter the gate (same
+ *      page, sections 2.3 and 3.1).  The selection key is s_e.
+ *      sigmoid gate (ORACLE_SIGMOID): s_e = 1 / (1 + exp(-a_e)) and the
+ *      selection key is s_e + b_e: the bias steers which experts are chosen
+ *      but not their weights (the auxiliary-loss-free routing remark of the
+ *      youleyou page, "DeepSeek MoE模型优化与未来演进及字节超稀疏内存技术",
+ *      and the sigmoid gate of the V3 line in the report's closing notes).
+ *   3. selection K rounds of argmax of the key over the experts not yet
+ *      taken, strict '>' so that the lower index wins a tie.  gate_k =
+ *      s_{e_k}; the other experts get 0 (section 3.1: keep the top scores,
+ *      zero the rest).  With ORACLE_RENORM the K gates are divided by their
+ *      sum, taken in selection order; for the softmax gate this equals a
+ *      softmax over the K selected logits, the routing code of the eliteato
+ *      DeepSeek-V2 explainer (section 3.1).  margin = key_(K) - key_(K+1),
+ *      +inf when K == E or K == 0.
  *   4. expert    FFN_W(x) = W2 (silu(W1 x) * (W3 x)), silu(z) = z/(1+e^-z),
  *      W1, W3 of shape [inter, d] and W2 of shape [d, inter], no bias
  *      (the Expert module printed on the youleyou page, "DeepSeek MoE模型优化
@@ -43,6 +52,8 @@
 #endif
 
 #define ORACLE_NO_RESIDUAL 1u
+#define ORACLE_RENORM 2u
+#define ORACLE_SIGMOID 4u
 
 typedef struct {
     int32_t T, d, E, I, K, Ks, Is;
@@ -58,44 +69,62 @@ static double widen(uint16_t h) {
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* Steps 1-3 for one token.  x_t: [d] widened.  probs: [E] scratch/out. */
+/* Steps 1-3 for one token.  x_t: [d] widened.  probs: [E] out (the scores
+ * s_e), key: [E] scratch (the selection keys). */
 static void route_token(const oracle_shape* s, const double* x_t,
                         const uint16_t* C, const float* bias,
-                        double* logits, double* probs, uint8_t* taken,
+                        double* key, double* probs, uint8_t* taken,
                         int32_t* idx, double* gate, double* margin) {
     const int d = s->d, E = s->E, K = s->K;
+    const int sigmoid = (s->flags & ORACLE_SIGMOID) != 0;
     for (int e = 0; e < E; ++e) {
         double acc = 0.0;
         const uint16_t* c = C + (size_t)e * d;
         for (int j = 0; j < d; ++j) acc += x_t[j] * widen(c[j]);
-        logits[e] = acc + (bias ? (double)bias[e] : 0.0);
+        const double b = bias ? (double)bias[e] : 0.0;
+        if (sigmoid) {
+            probs[e] = 1.0 / (1.0 + exp(-acc));
+            key[e] = probs[e] + b;
+        } else {
+            probs[e] = acc + b;              /* the logit, until the softmax below */
+        }
     }
-    double mx = logits[0];
-    for (int e = 1; e < E; ++e)
-        if (logits[e] > mx) mx = logits[e];
-    double z = 0.0;
-    for (int e = 0; e < E; ++e) {
-        probs[e] = exp(logits[e] - mx);
-        z += probs[e];
+    if (!sigmoid) {
+        double mx = probs[0];
+        for (int e = 1; e < E; ++e)
+            if (probs[e] > mx) mx = probs[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            probs[e] = exp(probs[e] - mx);
+            z += probs[e];
+        }
+        for (int e = 0; e < E; ++e) {
+            probs[e] /= z;
+            key[e] = probs[e];
+        }
     }
-    for (int e = 0; e < E; ++e) probs[e] /= z;
 
     memset(taken, 0, (size_t)E);
     for (int k = 0; k < K; ++k) {
         int best = -1;
         for (int e = 0; e < E; ++e)
-            if (!taken[e] && (best < 0 || probs[e] > probs[best])) best = e;
+            if (!taken[e] && (best < 0 || key[e] > key[best])) best = e;
         taken[best] = 1;
         idx[k] = best;
         gate[k] = probs[best];
+    }
+    if (s->flags & ORACLE_RENORM) {
+        double z = 0.0;
+        for (int k = 0; k < K; ++k) z += gate[k];
+        for (int k = 0; k < K; ++k) gate[k] /= z;
     }
     if (K == 0 || K == E) {
         *margin = INFINITY;
     } else {
         int next = -1;
         for (int e = 0; e < E; ++e)
-            if (!taken[e] && (next < 0 || probs[e] > probs[next])) next = e;
-        *margin = probs[idx[K - 1]] - probs[next];
+            if (!taken[e] && (next < 0 || key[e] > key[next])) next = e;
+        *margin = key[idx[K - 1]] - key[next];
     }
 }
 
@@ -121,7 +150,8 @@ static void expert_ffn(int d, int inter, const uint16_t* w1, const uint16_t* w3,
 }
 
 /* Routing only (steps 1-3) for n_tokens tokens; x_rows holds their rows
- * ([n_tokens, d], bf16).  probs_out may be NULL, else [n_tokens, E]. */
+ * ([n_tokens, d], bf16).  probs_out may be NULL, else [n_tokens, E]: the
+ * scores s_e of step 2. */
 int32_t oracle_route(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
                      const uint16_t* C, const float* bias,
                      int32_t* idx_out, double* gate_out, double* margin_out,
@@ -158,7 +188,8 @@ int32_t oracle_route(const oracle_shape* s, const uint16_t* x_rows, int32_t n_to
  * w1[e], w3[e], w2[e]: per-expert pointers (E of them), ws*[s]: per shared
  * expert (Ks of them).  forced_idx ([n_tokens, K] or NULL) replaces the
  * selection of step 3; gates are then the softmax scores of the forced
- * experts.  out, shared_part, routed_part: [n_tokens, d]. */
+ * experts (renormalised over them with ORACLE_RENORM).  out, shared_part,
+ * routed_part: [n_tokens, d]. */
 int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
                        const uint16_t* C, const float* bias,
                        const uint16_t* const* w1, const uint16_t* const* w3,
@@ -199,10 +230,14 @@ int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_
 
             route_token(s, xt, C, bias, lg, pr, tk, idx, gate, margin_out + i);
             if (forced_idx) {
+                double z = 0.0;
                 for (int k = 0; k < K; ++k) {
                     idx[k] = forced_idx[(size_t)i * K + k];
                     gate[k] = pr[idx[k]];
+                    z += gate[k];
                 }
+                if (s->flags & ORACLE_RENORM)
+                    for (int k = 0; k < K; ++k) gate[k] /= z;
             }
 
             for (int j = 0; j < d; ++j) sh[j] = 0.0;
