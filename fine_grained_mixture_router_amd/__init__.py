@@ -17,6 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 NO_RESIDUAL = 1
+RENORM = 2       # MOE_FLAG_RENORM
+SIGMOID = 4      # MOE_FLAG_SIGMOID
 
 STATUS = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
@@ -92,8 +94,11 @@ def _check(code: int):
         raise MoEError(code, status_string(code))
 
 
-def make_shape(T, d, E, I, K, Ks=0, Is=0, no_residual=False) -> Shape:
-    return Shape(T, d, E, I, K, Ks, Is if Ks else 0, NO_RESIDUAL if no_residual else 0)
+def make_shape(T, d, E, I, K, Ks=0, Is=0, no_residual=False, renorm=False,
+               sigmoid=False) -> Shape:
+    flags = ((NO_RESIDUAL if no_residual else 0) | (RENORM if renorm else 0)
+             | (SIGMOID if sigmoid else 0))
+    return Shape(T, d, E, I, K, Ks, Is if Ks else 0, flags)
 
 
 def segment(N: int, m: int, I_std: int, K: int, Ks: int = 0) -> dict:
@@ -122,24 +127,26 @@ def _stream(device, stream):
     return _vp(s.cuda_stream)
 
 
-def _shape_of(x, centroids, w1, ws1, K, no_residual):
+def _shape_of(x, centroids, w1, ws1, K, no_residual, renorm=False, sigmoid=False):
     T, d = x.shape
     E = centroids.shape[0] if centroids is not None else (w1.shape[0] if w1 is not None else 1)
     I = w1.shape[1] if w1 is not None else 64
     Ks = ws1.shape[0] if ws1 is not None else 0
     Is = ws1.shape[1] if ws1 is not None and Ks else 0
-    return make_shape(T, d, E, I, K, Ks, Is, no_residual)
+    return make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
 
 
 def forward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, bias=None,
-            no_residual: bool = False, out=None, topk_idx=None, topk_gate=None, workspace=None,
-            stream=None, return_routing: bool = False):
+            no_residual: bool = False, renorm: bool = False, sigmoid: bool = False, out=None,
+            topk_idx=None, topk_gate=None, workspace=None, stream=None,
+            return_routing: bool = False):
     """Layer forward on the GPU.  Tensors are CUDA (HIP) tensors: x [T,d],
     centroids [E,d], w1/w3 [E,I,d], w2 [E,d,I], ws1/ws3 [Ks,Is,d], ws2
-    [Ks,d,Is] in bfloat16; bias float32 [E] or None.  Returns out [T,d]
-    bfloat16 (and (idx, gate) when return_routing)."""
+    [Ks,d,Is] in bfloat16; bias float32 [E] or None.  renorm / sigmoid select
+    the gating variant (MOE_FLAG_RENORM / MOE_FLAG_SIGMOID).  Returns out
+    [T,d] bfloat16 (and (idx, gate) when return_routing)."""
     import torch
-    shape = _shape_of(x, centroids, w1, ws1, K, no_residual)
+    shape = _shape_of(x, centroids, w1, ws1, K, no_residual, renorm, sigmoid)
     dev = x.device
     if out is None:
         out = torch.empty((shape.T, shape.d), dtype=torch.bfloat16, device=dev)
@@ -161,12 +168,12 @@ def forward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, b
     return out
 
 
-def route(x, centroids, *, K: int, bias=None, topk_idx=None, topk_gate=None, workspace=None,
-          I: int = 64, stream=None):
+def route(x, centroids, *, K: int, bias=None, renorm: bool = False, sigmoid: bool = False,
+          topk_idx=None, topk_gate=None, workspace=None, I: int = 64, stream=None):
     """Routing only: returns (idx int32 [T,K], gate float32 [T,K])."""
     import torch
     T, d = x.shape
-    shape = make_shape(T, d, centroids.shape[0], I, K)
+    shape = make_shape(T, d, centroids.shape[0], I, K, renorm=renorm, sigmoid=sigmoid)
     dev = x.device
     if topk_idx is None:
         topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)

@@ -39,6 +39,8 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 
 // Tokens per routing chunk: one 64-bit lane mask per (chunk, expert).
 constexpr int kChunk = 64;
+constexpr uint32_t kGateRenorm = 2u;    // shape flag bits of the gating variants
+constexpr uint32_t kGateSigmoid = 4u;
 // Router GEMM tile: 64 tokens x 64 experts, d consumed 64 at a time.
 constexpr int kRouterBT = 64;
 constexpr int kRouterBE = 64;

@@ -9,6 +9,9 @@
 
 using namespace moe;
 
+static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID,
+              "gating flag bits");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -24,7 +27,7 @@ bool shape_ok(const moe_shape_t* s) {
     if (s->I < 64 || s->I > 65536 || s->I % 64) return false;
     if (s->Ks < 0 || s->Ks > 16) return false;
     if (s->Ks > 0 && (s->Is < 64 || s->Is > 65536 || s->Is % 64)) return false;
-    if (s->flags & ~MOE_FLAG_NO_RESIDUAL) return false;
+    if (s->flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_RENORM | MOE_FLAG_SIGMOID)) return false;
     const long long rows = (long long)s->T * (s->K + s->Ks);
     if (rows > (1LL << 30)) return false;
     // The GEMM kernels address x, H and one expert's weights with 32-bit

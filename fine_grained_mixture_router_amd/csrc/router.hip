@@ -3,7 +3,11 @@
 // Definition: the generic top-K gate of "DeepSeekMoE 深度解读报告" section 3.1
 // (softmax over the inner products of the token with every expert centroid,
 // keep the K largest scores, zero the rest, no renormalisation), plus an
-// optional fixed per-expert logit bias.
+// optional fixed per-expert logit bias.  Variants: gates renormalised over
+// the K selected (the eliteato DeepSeek-V2 explainer's routing code, section
+// 3.1: softmax over the top-K logits), and sigmoid affinities whose bias only
+// steers the selection (the youleyou page's auxiliary-loss-free remark; the
+// V3 line in the report's closing notes).
 //
 // Two kernels:
 //   router_logits  bf16 MFMA GEMM x[T,d] . C[E,d]^T -> fp32 partial logits.
@@ -11,9 +15,12 @@
 //                  split so that the launch still covers the chip, and the
 //                  partials are summed in a fixed order by the next kernel.
 //   router_select  one wavefront per token (16 per workgroup): sum partials,
-//                  add the bias, fp32 softmax, then K rounds of a wavefront
-//                  arg-max over the E<=256 logits (4 per lane; ties go to the
-//                  lower expert id).  Per expert it also records the 64-bit
+//                  then the gate — softmax of logit + bias (default), or
+//                  sigmoid of the affinity with the bias added to the
+//                  selection key only — and K rounds of a wavefront arg-max
+//                  over the E<=256 keys (4 per lane; ties go to the lower
+//                  expert id); optionally the K gates are renormalised to sum
+//                  to one.  Per expert it also records the 64-bit
 //                  mask of the tokens of each 64-token chunk that chose that
 //                  expert; the permutation step turns those masks into a
 //                  stable, atomics-free grouping of tokens by expert.
@@ -134,16 +141,22 @@ constexpr int kSubChunks = kChunk / kSelectWaves;
 static_assert(kSubChunks == 4, "16-bit quarters of the 64-bit chunk mask");
 constexpr int kPartBatch = 8;       // partial logits loaded ahead of their adds
 
+__device__ __forceinline__ float pick4(const float (&a)[4], int j) {
+    return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+}
+
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ idx,
     float* __restrict__ gate, uint64_t* __restrict__ masks, int T, int E, int Epad, int K,
-    int split) {
+    int split, uint32_t flags) {
     __shared__ unsigned smask[256];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c = blockIdx.x / kSubChunks;
     const int q = blockIdx.x % kSubChunks;
+    const bool sig = (flags & kGateSigmoid) != 0;
+    const bool ren = (flags & kGateRenorm) != 0;
     for (int e = tid; e < Epad; e += kSelectThreads) smask[e] = 0u;
     __syncthreads();
 
@@ -151,7 +164,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const int t = c * kChunk + tl;
     if (t < T) {
         const float NEG = -INFINITY;
-        // logits of experts lane + 64 j: the split-K partials summed in
+        // affinities of experts lane + 64 j: the split-K partials summed in
         // order z = 0, 1, ..., loaded kPartBatch at a time
         float v[4];
         int taken = 0;                               // bit j: expert lane + 64j is out
@@ -176,17 +189,28 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
                 for (int j = 0; j < 4; ++j)
                     if (z0 + b < split) v[j] += pv[b][j];
         }
+        // selection keys: softmax gate -> logit + bias (the softmax is
+        // monotone in it); sigmoid gate -> sigmoid(affinity) + bias, the bias
+        // steering the choice only
+        float sc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane + 64 * j;
-            v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : NEG;
+            const float b = (bias && e < E) ? bias[e] : 0.f;
+            sc[j] = sig ? 1.0f / (1.0f + expf(-v[j])) : 0.f;
+            v[j] = e < E ? (sig ? sc[j] + b : v[j] + b) : NEG;
         }
-        const float mx = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-        float ps = 0.f;
+        float mx = 0.f, sum = 1.f;
+        if (!sig) {
+            mx = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+            float ps = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ps += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
-        const float sum = wave_sum(ps);
+            for (int j = 0; j < 4; ++j) ps += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
+            sum = wave_sum(ps);
+        }
 
+        float gk[4] = {0.f, 0.f, 0.f, 0.f};          // renormalised: gate k kept by lane k % 64
+        float zsum = 0.f;
         for (int k = 0; k < K; ++k) {
             // local best: strictly greater wins, so the lower j (lower e) keeps ties
             float bv = NEG;
@@ -206,10 +230,24 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
                 }
             }
             if ((be & 63) == lane) taken |= 1 << (be >> 6);
+            const float g = sig ? __shfl(pick4(sc, be >> 6), be & 63, 64) : expf(bv - mx) / sum;
+            if (ren) {
+                zsum += g;                           // every lane, in selection order
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if ((k & 63) == lane && (k >> 6) == j) gk[j] = g;
+            }
             if (lane == 0) {
                 idx[(size_t)t * K + k] = be;
-                gate[(size_t)t * K + k] = expf(bv - mx) / sum;
+                if (!ren) gate[(size_t)t * K + k] = g;
                 atomicOr(&smask[be], 1u << wave);
+            }
+        }
+        if (ren) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = 64 * j + lane;
+                if (k < K) gate[(size_t)t * K + k] = gk[j] / zsum;
             }
         }
     }
@@ -231,7 +269,7 @@ hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C,
 
 hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st) {
     router_select_kernel<<<p.nchunk * kSubChunks, kSelectThreads, 0, st>>>(
-        p.logits, bias, p.idx, p.gate, p.masks, p.T, p.E, p.Epad, p.K, p.split);
+        p.logits, bias, p.idx, p.gate, p.masks, p.T, p.E, p.Epad, p.K, p.split, p.flags);
     return hipGetLastError();
 }
 

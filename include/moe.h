@@ -7,6 +7,7 @@
  *
  *   s[t,e]  = softmax_e( x[t]·C[e] + b[e] )               over E routed experts
  *   top-K   = the K largest s[t,e] (ties: lower e first), gate = s, no renorm
+ *             (two other gates are selectable: see the flags below)
  *   FFN_W   = W2 · ( silu(W1·x) ⊙ (W3·x) ),  silu(z) = z / (1 + e^-z)
  *   out[t]  = x[t] + Σ_{s<Ks} FFN_shared_s(x[t]) + Σ_k gate[t,k]·FFN_{idx[t,k]}(x[t])
  *
@@ -54,9 +55,26 @@ typedef struct {
     uint32_t flags;
 } moe_shape_t;
 
-/* flags: out excludes the residual x (out = shared + routed).  Used to
- * check the expert contributions on their own.  All other bits must be 0. */
+/* flags (all other bits must be 0):
+ *
+ * MOE_FLAG_NO_RESIDUAL: out excludes the residual x (out = shared + routed).
+ * Used to check the expert contributions on their own.
+ *
+ * MOE_FLAG_RENORM: the K gates of a token are divided by their sum (taken in
+ * selection order), so they sum to one.  With the softmax gate this equals a
+ * softmax over the K selected logits, the routing code of the eliteato
+ * DeepSeek-V2 explainer (section 3.1).
+ *
+ * MOE_FLAG_SIGMOID: affinity a_e = x.C[e]; score s_e = 1 / (1 + e^-a_e); the
+ * K experts with the largest s_e + expert_bias[e] are selected (ties: lower
+ * e first) and gate = s_e: the bias steers the selection only (the
+ * auxiliary-loss-free routing remark of the youleyou page, and the sigmoid
+ * gate of the V3 line in "DeepSeekMoE 深度解读报告", closing notes).  Usually
+ * combined with MOE_FLAG_RENORM.  Without this flag the bias is added to the
+ * logits before the softmax and so enters both selection and gates. */
 #define MOE_FLAG_NO_RESIDUAL 1u
+#define MOE_FLAG_RENORM 2u
+#define MOE_FLAG_SIGMOID 4u
 
 typedef enum {
     MOE_OK = 0,
@@ -90,8 +108,8 @@ size_t moe_workspace_size(const moe_shape_t* shape);
  *   topk_gate  fp32  [T, K] or NULL  their softmax scores
  *   workspace / workspace_bytes   device scratch of moe_workspace_size() bytes
  *
- * Arithmetic: affinities by bf16 MFMA with fp32 accumulation, softmax and
- * top-K in fp32; expert GEMMs bf16 x bf16 -> fp32, SwiGLU in fp32, the
+ * Arithmetic: affinities by bf16 MFMA with fp32 accumulation, softmax (or
+ * sigmoid), top-K and renormalisation in fp32; expert GEMMs bf16 x bf16 -> fp32, SwiGLU in fp32, the
  * intermediates H and Y stored as bf16; the combine accumulates in fp32.
  * Results are bit-identical from run to run (no atomics decide any order). */
 moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* centroids,
@@ -100,8 +118,8 @@ moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* ce
                          void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Routing only: affinities, softmax, top-K ("DeepSeekMoE 深度解读报告",
- * section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both
+/* Routing only: affinities, softmax (or the flags' gate), top-K
+ * ("DeepSeekMoE 深度解读报告", section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both
  * required); same workspace as moe_forward.  K must be >= 1. */
 moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* centroids,
                        const float* expert_bias, int32_t* topk_idx, float* topk_gate,

@@ -62,11 +62,13 @@ def rms(a) -> float:
     return float(np.sqrt(np.mean(np.square(a))))
 
 
-def check_routing(idx_gpu, gate_gpu, ref_idx, ref_gate, ref_margin, K):
-    """Index sets equal wherever the oracle's K-th vs (K+1)-th score margin
-    exceeds 1e-5; positions equal where both neighbouring gaps exceed it;
-    gates to 1e-5 relative (+1e-7) at matching positions.  Returns the number
-    of tokens exempt from the set check."""
+def check_routing(idx_gpu, gate_gpu, ref_idx, ref_gate, ref_margin, K, ref_keys=None):
+    """Index sets equal wherever the oracle's K-th vs (K+1)-th selection-key
+    margin exceeds 1e-5; positions equal where both neighbouring key gaps
+    exceed it; gates to 1e-5 relative (+1e-7) at matching positions.
+    ref_keys [n, K]: the oracle's selection keys of its chosen experts, in
+    order (default: the gates, which are the keys of the plain softmax gate).
+    Returns the number of tokens exempt from the set check."""
     exempt = 0
     n = ref_idx.shape[0]
     for t in range(n):
@@ -75,13 +77,14 @@ def check_routing(idx_gpu, gate_gpu, ref_idx, ref_gate, ref_margin, K):
                 t, idx_gpu[t], ref_idx[t], ref_margin[t])
         else:
             exempt += 1
-        g = ref_gate[t]
+        g = ref_gate[t] if ref_keys is None else ref_keys[t]
         for k in range(K):
             left = k == 0 or g[k - 1] - g[k] > ROUTE_MARGIN
             right = (ref_margin[t] > ROUTE_MARGIN) if k == K - 1 else (g[k] - g[k + 1] > ROUTE_MARGIN)
             if left and right:
                 assert idx_gpu[t, k] == ref_idx[t, k], (t, k, idx_gpu[t], ref_idx[t])
-                assert abs(gate_gpu[t, k] - g[k]) <= 1e-5 * g[k] + 1e-7, (t, k, gate_gpu[t, k], g[k])
+                rg = ref_gate[t, k]
+                assert abs(gate_gpu[t, k] - rg) <= 1e-5 * rg + 1e-7, (t, k, gate_gpu[t, k], rg)
     return exempt
 
 

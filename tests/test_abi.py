@@ -71,8 +71,12 @@ def test_bad_shapes(kw):
 
 def test_bad_flags():
     s = S()
-    s.flags = 2
-    assert moe.lib().moe_workspace_size(ctypes.byref(s)) == 0
+    for f in (8, 16, 1 << 31):
+        s.flags = f
+        assert moe.lib().moe_workspace_size(ctypes.byref(s)) == 0
+    for f in (0, 1, 2, 4, 7):                    # NO_RESIDUAL, RENORM, SIGMOID and combinations
+        s.flags = f
+        assert moe.lib().moe_workspace_size(ctypes.byref(s)) > 0
 
 
 def _fwd(shape, ws_bytes=1 << 40, **over):
