@@ -59,6 +59,12 @@ def lib():
         L.oracle_forward.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_forward_fp8.restype = i32
+        L.oracle_forward_fp8.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_e4m3.restype = ctypes.c_double
+        L.oracle_e4m3.argtypes = [ctypes.c_uint8]
         _lib = L
     return _lib
 
@@ -74,15 +80,22 @@ def _u16(a, shape):
     return a
 
 
-def _ptr_table(stack, n, shape):
+def _ptr_table(stack, n, shape, dtype=np.uint16):
     """Per-expert pointer table from a [n, ...] stack or a list of n arrays."""
     keep = []
     tbl = (ctypes.c_void_p * max(n, 1))()
     for i in range(n):
-        a = _u16(stack[i], shape)
+        a = np.ascontiguousarray(stack[i])
+        assert a.dtype == dtype, a.dtype
+        assert a.shape == tuple(shape), (a.shape, shape)
         keep.append(a)
         tbl[i] = a.ctypes.data
     return tbl, keep
+
+
+def e4m3(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code (NaN for 0x7F / 0xFF)."""
+    return float(lib().oracle_e4m3(int(code)))
 
 
 def _gating(renorm, sigmoid):
@@ -162,5 +175,54 @@ def forward(x_rows, C, bias, w1, w3, w2, ws1, ws3, ws2, K, no_residual=False,
                                 tw[0], tw[1], tw[2], ts[0], ts[1], ts[2], _ptr(fi),
                                 _ptr(out), _ptr(shared), _ptr(routed), _ptr(idx), _ptr(gate),
                                 _ptr(margin), int(nthreads))
+    return dict(out=out, shared=shared, routed=routed, idx=idx, gate=gate, margin=margin,
+                threads=int(used))
+
+
+def forward_fp8(x_rows, C, bias, q1, s1, q3, s3, q2, s2, ws1, ws3, ws2, K, no_residual=False,
+                forced_idx=None, nthreads=0, renorm=False, sigmoid=False):
+    """Layer forward with 8-bit routed weights, in fp64: q1/q3 uint8 [E, I, d]
+    and q2 [E, d, I] E4M3 codes, s1/s3 float32 [E, I] and s2 [E, d] per-row
+    scales (weight = e4m3(q) * scale); shared experts ws* in bf16 as for
+    forward().  Returns the same dict as forward()."""
+    x_rows = np.ascontiguousarray(x_rows)
+    n, d = x_rows.shape
+    E = C.shape[0]
+    C = _u16(C, (E, d))
+    I = q1.shape[1]
+    Ks = 0 if ws1 is None else len(ws1)
+    Is = ws1[0].shape[0] if Ks else 0
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    keep = []
+    tq, ts_ = [], []
+    for q, sc, shp in ((q1, s1, (I, d)), (q3, s3, (I, d)), (q2, s2, (d, I))):
+        t, k = _ptr_table(q, E, shp, np.uint8)
+        tq.append(t)
+        keep.append(k)
+        t, k = _ptr_table(np.ascontiguousarray(sc, dtype=np.float32), E, (shp[0],), np.float32)
+        ts_.append(t)
+        keep.append(k)
+    tsh = []
+    for stack, shp in ((ws1, (Is, d)), (ws3, (Is, d)), (ws2, (d, Is))):
+        t, k = _ptr_table(stack if Ks else [], Ks, shp)
+        tsh.append(t)
+        keep.append(k)
+    fi = None
+    if forced_idx is not None:
+        fi = np.ascontiguousarray(forced_idx, dtype=np.int32)
+        assert fi.shape == (n, K)
+    sh = _Shape(n, d, E, I, K, Ks, Is,
+                (NO_RESIDUAL if no_residual else 0) | _gating(renorm, sigmoid))
+    out = np.zeros((n, d), np.float64)
+    shared = np.zeros((n, d), np.float64)
+    routed = np.zeros((n, d), np.float64)
+    idx = np.zeros((n, K), np.int32)
+    gate = np.zeros((n, K), np.float64)
+    margin = np.zeros(n, np.float64)
+    used = lib().oracle_forward_fp8(ctypes.byref(sh), _ptr(x_rows), n, _ptr(C), _ptr(b),
+                                    tq[0], ts_[0], tq[1], ts_[1], tq[2], ts_[2],
+                                    tsh[0], tsh[1], tsh[2], _ptr(fi),
+                                    _ptr(out), _ptr(shared), _ptr(routed), _ptr(idx),
+                                    _ptr(gate), _ptr(margin), int(nthreads))
     return dict(out=out, shared=shared, routed=routed, idx=idx, gate=gate, margin=margin,
                 threads=int(used))

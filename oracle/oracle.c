@@ -40,6 +40,16 @@
  * Fine-grained segmentation (section 2.2) enters only through the shape:
  * E = N*m routed experts, each of inter-dim I = I_std/m.
  *
+ * 8-bit routed weights (oracle_forward_fp8): each routed weight matrix is
+ * given as OCP FP8 E4M3 codes q with one float scale per output row, the
+ * weight being e4m3(q) * scale[row]; the shared experts stay bf16.  This is
+ * the per-channel quantisation of routed experts, shared experts kept at
+ * 16 bits, that the eliteato DeepSeek-V2 explainer recommends (section 5.5).
+ * e4m3() follows the OCP 8-bit floating point definition: sign bit 7,
+ * exponent field bits 6-3 with bias 7, mantissa field bits 2-0; exponent
+ * field 0 holds the subnormals m/8 * 2^-6, and 0x7F / 0xFF are NaN.  Every
+ * finite value and every product with a float scale is exact in double.
+ *
  * Tokens are independent; OpenMP runs them on separate threads without
  * changing any token's order of operations.
  */
@@ -128,23 +138,43 @@ static void route_token(const oracle_shape* s, const double* x_t,
     }
 }
 
+/* OCP FP8 E4M3 code -> value (see the header). */
+double oracle_e4m3(uint8_t q) {
+    const int sign = q >> 7, e = (q >> 3) & 15, m = q & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* One weight matrix of `cols` columns: bf16 bit patterns, or 8-bit codes
+ * with one float scale per row. */
+typedef struct {
+    const uint16_t* bf16;
+    const uint8_t* q;
+    const float* scale;
+} wmat;
+
+static double wat(const wmat* w, int row, int cols, int col) {
+    const size_t i = (size_t)row * cols + col;
+    return w->bf16 ? widen(w->bf16[i]) : oracle_e4m3(w->q[i]) * (double)w->scale[row];
+}
+
 /* Step 4: y = W2 (silu(W1 x) * W3 x) for one token. h: [inter] scratch. */
-static void expert_ffn(int d, int inter, const uint16_t* w1, const uint16_t* w3,
-                       const uint16_t* w2, const double* x_t, double* h, double* y) {
+static void expert_ffn(int d, int inter, const wmat* w1, const wmat* w3, const wmat* w2,
+                       const double* x_t, double* h, double* y) {
     for (int i = 0; i < inter; ++i) {
         double a = 0.0, b = 0.0;
-        const uint16_t* r1 = w1 + (size_t)i * d;
-        const uint16_t* r3 = w3 + (size_t)i * d;
         for (int j = 0; j < d; ++j) {
-            a += widen(r1[j]) * x_t[j];
-            b += widen(r3[j]) * x_t[j];
+            a += wat(w1, i, d, j) * x_t[j];
+            b += wat(w3, i, d, j) * x_t[j];
         }
         h[i] = silu(a) * b;
     }
     for (int o = 0; o < d; ++o) {
         double acc = 0.0;
-        const uint16_t* r2 = w2 + (size_t)o * inter;
-        for (int i = 0; i < inter; ++i) acc += widen(r2[i]) * h[i];
+        for (int i = 0; i < inter; ++i) acc += wat(w2, o, inter, i) * h[i];
         y[o] = acc;
     }
 }
@@ -185,21 +215,18 @@ int32_t oracle_route(const oracle_shape* s, const uint16_t* x_rows, int32_t n_to
 }
 
 /* Full forward (steps 1-5) for n_tokens tokens whose rows are x_rows.
- * w1[e], w3[e], w2[e]: per-expert pointers (E of them), ws*[s]: per shared
- * expert (Ks of them).  forced_idx ([n_tokens, K] or NULL) replaces the
- * selection of step 3; gates are then the softmax scores of the forced
- * experts (renormalised over them with ORACLE_RENORM).  out, shared_part,
- * routed_part: [n_tokens, d]. */
-int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
-                       const uint16_t* C, const float* bias,
-                       const uint16_t* const* w1, const uint16_t* const* w3,
-                       const uint16_t* const* w2,
-                       const uint16_t* const* ws1, const uint16_t* const* ws3,
-                       const uint16_t* const* ws2,
-                       const int32_t* forced_idx,
-                       double* out, double* shared_part, double* routed_part,
-                       int32_t* idx_out, double* gate_out, double* margin_out,
-                       int32_t nthreads) {
+ * rw1/rw3/rw2: the E routed experts' matrices, sw1/sw3/sw2: the Ks shared
+ * experts'.  forced_idx ([n_tokens, K] or NULL) replaces the selection of
+ * step 3; gates are then the scores of the forced experts (renormalised over
+ * them with ORACLE_RENORM).  out, shared_part, routed_part: [n_tokens, d]. */
+static int32_t forward_impl(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
+                            const uint16_t* C, const float* bias,
+                            const wmat* rw1, const wmat* rw3, const wmat* rw2,
+                            const wmat* sw1, const wmat* sw3, const wmat* sw2,
+                            const int32_t* forced_idx,
+                            double* out, double* shared_part, double* routed_part,
+                            int32_t* idx_out, double* gate_out, double* margin_out,
+                            int32_t nthreads) {
     const int d = s->d, K = s->K;
     const int hmax = s->I > s->Is ? s->I : s->Is;
     int used = 1;
@@ -242,13 +269,13 @@ int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_
 
             for (int j = 0; j < d; ++j) sh[j] = 0.0;
             for (int si = 0; si < s->Ks; ++si) {
-                expert_ffn(d, s->Is, ws1[si], ws3[si], ws2[si], xt, h, y);
+                expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xt, h, y);
                 for (int j = 0; j < d; ++j) sh[j] += y[j];
             }
             for (int j = 0; j < d; ++j) ro[j] = 0.0;
             for (int k = 0; k < K; ++k) {
                 const int e = idx[k];
-                expert_ffn(d, s->I, w1[e], w3[e], w2[e], xt, h, y);
+                expert_ffn(d, s->I, &rw1[e], &rw3[e], &rw2[e], xt, h, y);
                 for (int j = 0; j < d; ++j) ro[j] += gate[k] * y[j];
             }
             const double res = (s->flags & ORACLE_NO_RESIDUAL) ? 0.0 : 1.0;
@@ -256,5 +283,64 @@ int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_
         }
         free(xt); free(y); free(h); free(lg); free(pr); free(tk);
     }
+    return used;
+}
+
+static wmat* bf16_mats(const uint16_t* const* w, int n) {
+    wmat* m = calloc((size_t)(n > 0 ? n : 1), sizeof(wmat));
+    for (int i = 0; i < n; ++i) m[i].bf16 = w ? w[i] : NULL;
+    return m;
+}
+
+static wmat* fp8_mats(const uint8_t* const* q, const float* const* scale, int n) {
+    wmat* m = calloc((size_t)(n > 0 ? n : 1), sizeof(wmat));
+    for (int i = 0; i < n; ++i) {
+        m[i].q = q[i];
+        m[i].scale = scale[i];
+    }
+    return m;
+}
+
+/* Full forward with bf16 weights.  w1[e], w3[e], w2[e]: per routed expert
+ * (E of them), ws*[s]: per shared expert (Ks of them); see forward_impl. */
+int32_t oracle_forward(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
+                       const uint16_t* C, const float* bias,
+                       const uint16_t* const* w1, const uint16_t* const* w3,
+                       const uint16_t* const* w2,
+                       const uint16_t* const* ws1, const uint16_t* const* ws3,
+                       const uint16_t* const* ws2,
+                       const int32_t* forced_idx,
+                       double* out, double* shared_part, double* routed_part,
+                       int32_t* idx_out, double* gate_out, double* margin_out,
+                       int32_t nthreads) {
+    wmat *r1 = bf16_mats(w1, s->E), *r3 = bf16_mats(w3, s->E), *r2 = bf16_mats(w2, s->E);
+    wmat *h1 = bf16_mats(ws1, s->Ks), *h3 = bf16_mats(ws3, s->Ks), *h2 = bf16_mats(ws2, s->Ks);
+    const int32_t used = forward_impl(s, x_rows, n_tokens, C, bias, r1, r3, r2, h1, h3, h2,
+                                      forced_idx, out, shared_part, routed_part, idx_out,
+                                      gate_out, margin_out, nthreads);
+    free(r1); free(r3); free(r2); free(h1); free(h3); free(h2);
+    return used;
+}
+
+/* Full forward with 8-bit routed weights: q1[e], q3[e] [I, d] and q2[e]
+ * [d, I] codes with per-row scales s1[e], s3[e] [I] and s2[e] [d]; the
+ * shared experts ws*[s] stay bf16. */
+int32_t oracle_forward_fp8(const oracle_shape* s, const uint16_t* x_rows, int32_t n_tokens,
+                           const uint16_t* C, const float* bias,
+                           const uint8_t* const* q1, const float* const* s1,
+                           const uint8_t* const* q3, const float* const* s3,
+                           const uint8_t* const* q2, const float* const* s2,
+                           const uint16_t* const* ws1, const uint16_t* const* ws3,
+                           const uint16_t* const* ws2,
+                           const int32_t* forced_idx,
+                           double* out, double* shared_part, double* routed_part,
+                           int32_t* idx_out, double* gate_out, double* margin_out,
+                           int32_t nthreads) {
+    wmat *r1 = fp8_mats(q1, s1, s->E), *r3 = fp8_mats(q3, s3, s->E), *r2 = fp8_mats(q2, s2, s->E);
+    wmat *h1 = bf16_mats(ws1, s->Ks), *h3 = bf16_mats(ws3, s->Ks), *h2 = bf16_mats(ws2, s->Ks);
+    const int32_t used = forward_impl(s, x_rows, n_tokens, C, bias, r1, r3, r2, h1, h3, h2,
+                                      forced_idx, out, shared_part, routed_part, idx_out,
+                                      gate_out, margin_out, nthreads);
+    free(r1); free(r3); free(r2); free(h1); free(h3); free(h2);
     return used;
 }

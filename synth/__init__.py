@@ -23,6 +23,8 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 STREAM_X, STREAM_C, STREAM_BIAS, STREAM_W1, STREAM_W3, STREAM_W2 = 0, 1, 2, 3, 4, 5
 STREAM_WS1, STREAM_WS3, STREAM_WS2 = 6, 7, 8
+STREAM_Q1, STREAM_Q3, STREAM_Q2 = 9, 10, 11            # 8-bit routed weight codes
+STREAM_S1, STREAM_S3, STREAM_S2 = 12, 13, 14           # their per-row scales
 
 
 def build(force: bool = True) -> str:
@@ -56,6 +58,10 @@ def lib():
         L.synth_normal_f64.argtypes = [u64, u64, u64, u64, vp]
         L.synth_permutation.restype = None
         L.synth_permutation.argtypes = [u64, u64, i32, vp]
+        L.synth_fp8_codes.restype = None
+        L.synth_fp8_codes.argtypes = [u64, u64, u64, u64, vp]
+        L.synth_uniform_f32.restype = None
+        L.synth_uniform_f32.argtypes = [u64, u64, u64, u64, ctypes.c_float, ctypes.c_float, vp]
         _lib = L
     return _lib
 
@@ -78,6 +84,26 @@ def normal_f64(seed: int, stream: int, n: int, offset: int = 0) -> np.ndarray:
     out = np.empty(n, dtype=np.float64)
     if n:
         lib().synth_normal_f64(seed, stream, offset, n, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def fp8_codes(seed: int, stream: int, shape, offset: int = 0,
+              out: np.ndarray | None = None) -> np.ndarray:
+    """uint8 codes number offset .. offset+prod(shape)-1 of an 8-bit weight
+    stream (E4M3 bit layout; see gen.c for the draw)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    if out is None:
+        out = np.empty(shape, dtype=np.uint8)
+    assert out.dtype == np.uint8 and out.flags.c_contiguous and out.size == n
+    if n:
+        lib().synth_fp8_codes(seed, stream, offset, n, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def uniform_f32(seed: int, stream: int, n: int, lo: float, hi: float, offset: int = 0) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    if n:
+        lib().synth_uniform_f32(seed, stream, offset, n, lo, hi, out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 

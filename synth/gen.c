@@ -16,6 +16,10 @@
  *     makes the two-step rounding exact).
  *   - A seeded permutation (Fisher-Yates driven by the same counter hash)
  *     for the per-expert Zipf ranks.
+ *   - Synthetic 8-bit weight codes in the OCP FP8 E4M3 layout (sign, 4-bit
+ *     exponent field, 3-bit mantissa field) drawn directly as bit fields, and
+ *     uniform floats for their per-row scales.  Nothing is rounded or
+ *     encoded: the codes are drawn, not produced from real values.
  *
  * Built with gcc; OpenMP splits the element range across host threads.  The
  * result does not depend on the thread count.
@@ -118,5 +122,36 @@ void synth_permutation(uint64_t seed, uint64_t stream, int32_t n, int32_t* perm)
         int32_t t = perm[i];
         perm[i] = perm[j];
         perm[j] = t;
+    }
+}
+
+/* Code n of an 8-bit weight stream, from word n: sign = bit 0; exponent field
+ * 14 - g, g = the number of leading zeros of the 14-bit field (bits 8..21)
+ * (so field 14 has probability 1/2, 13 probability 1/4, ... like values
+ * scaled so that the largest sit near the top of the range); mantissa field
+ * = bits 1..3.  The largest exponent field (15) is never drawn, so no code is
+ * NaN. */
+void synth_fp8_codes(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t n, uint8_t* out) {
+    const uint64_t key = stream_key(seed, stream);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < (int64_t)n; ++i) {
+        const uint64_t w = word_at(key, offset + (uint64_t)i);
+        const uint32_t field = (uint32_t)((w >> 8) & 0x3FFFu);        /* 14 bits */
+        int g = 0;
+        while (g < 14 && !(field & (0x2000u >> g))) ++g;
+        const uint32_t e = 14u - (uint32_t)g;
+        const uint32_t m = (uint32_t)((w >> 1) & 7u);
+        out[i] = (uint8_t)(((w & 1u) << 7) | (e << 3) | m);
+    }
+}
+
+/* Uniform floats in [lo, hi): the top 24 bits of word n as a fraction u,
+ * then lo + (hi - lo) * u in float. */
+void synth_uniform_f32(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t n, float lo,
+                       float hi, float* out) {
+    const uint64_t key = stream_key(seed, stream);
+    for (uint64_t i = 0; i < n; ++i) {
+        const float u = (float)(word_at(key, offset + i) >> 40) * (1.0f / 16777216.0f);
+        out[i] = lo + (hi - lo) * u;
     }
 }

@@ -19,11 +19,16 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (STREAM_C, STREAM_W1, STREAM_W2, STREAM_W3, STREAM_WS1, STREAM_WS2,
-               STREAM_WS3, STREAM_X, normal_bf16, zipf_bias)
+from . import (STREAM_C, STREAM_Q1, STREAM_Q2, STREAM_Q3, STREAM_S1, STREAM_S2, STREAM_S3,
+               STREAM_W1, STREAM_W2, STREAM_W3, STREAM_WS1, STREAM_WS2, STREAM_WS3, STREAM_X,
+               fp8_codes, normal_bf16, uniform_f32, zipf_bias)
 
 SIGMA_W = 0.006
 SIGMA_X = 1.0
+# 8-bit routed weights: the drawn E4M3 codes have an RMS value of about 134,
+# so per-row scales of FP8_SCALE * U(0.5, 1.5) give weights of about the same
+# size as the bf16 ones.
+FP8_SCALE = SIGMA_W / 134.0
 
 
 @dataclass(frozen=True)
@@ -117,6 +122,19 @@ def gen_shared(w: Workload):
     ws3 = normal_bf16(w.wseed, STREAM_WS3, n, SIGMA_W)
     ws2 = normal_bf16(w.wseed, STREAM_WS2, (w.Ks, w.d, w.Is), SIGMA_W)
     return ws1, ws3, ws2
+
+
+def gen_routed_fp8(w: Workload):
+    """Routed weights as 8-bit E4M3 codes with one float32 scale per output
+    row: (q1, s1, q3, s3, q2, s2), q1/q3 uint8 [E, I, d], s1/s3 [E, I], q2
+    [E, d, I], s2 [E, d].  The weight is decode(q) * scale of its row."""
+    q1 = fp8_codes(w.wseed, STREAM_Q1, (w.E, w.I, w.d))
+    q3 = fp8_codes(w.wseed, STREAM_Q3, (w.E, w.I, w.d))
+    q2 = fp8_codes(w.wseed, STREAM_Q2, (w.E, w.d, w.I))
+    s1 = (uniform_f32(w.wseed, STREAM_S1, w.E * w.I, 0.5, 1.5) * np.float32(FP8_SCALE)).reshape(w.E, w.I)
+    s3 = (uniform_f32(w.wseed, STREAM_S3, w.E * w.I, 0.5, 1.5) * np.float32(FP8_SCALE)).reshape(w.E, w.I)
+    s2 = (uniform_f32(w.wseed, STREAM_S2, w.E * w.d, 0.5, 1.5) * np.float32(FP8_SCALE)).reshape(w.E, w.d)
+    return q1, s1, q3, s3, q2, s2
 
 
 def gen_all(w: Workload) -> dict:

@@ -10,7 +10,7 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ["tests/test_oracle_pins.py", "tests/test_oracle_gating.py"]
+PIN_FILES = ["tests/test_oracle_pins.py", "tests/test_oracle_gating.py", "tests/test_oracle_fp8.py"]
 
 MUTATIONS = [
     ("sigmoid gate includes the bias", "        gate[k] = probs[best];\n", "        gate[k] = key[best];\n"),
@@ -28,10 +28,15 @@ MUTATIONS = [
      "*margin = probs[idx[K - 1]] - probs[next];"),
     ("silu sign flipped", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     ("residual dropped", "res * xt[j] + sh[j] + ro[j]", "sh[j] + ro[j]"),
-    ("up projection reads W1", "b += widen(r3[j]) * x_t[j];", "b += widen(r1[j]) * x_t[j];"),
+    ("up projection reads W1", "b += wat(w3, i, d, j) * x_t[j];", "b += wat(w1, i, d, j) * x_t[j];"),
     ("softmax denominator skips the last expert", "            z += probs[e];\n", "            z += e + 1 < E ? probs[e] : 0.0;\n"),
     ("shared experts skipped", "for (int si = 0; si < s->Ks; ++si) {", "for (int si = 0; si < 0; ++si) {"),
     ("gate taken from the next expert", "        gate[k] = probs[best];\n", "        gate[k] = probs[(best + 1) % E];\n"),
+    ("e4m3 exponent bias 8", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3 subnormals one binade low", "v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
+    ("e4m3 mantissa reversed", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)(7 - m) / 8.0, e - 7);"),
+    ("8-bit row scale from the neighbouring row", "oracle_e4m3(w->q[i]) * (double)w->scale[row]",
+     "oracle_e4m3(w->q[i]) * (double)w->scale[row ^ 1]"),
 ]
 
 
