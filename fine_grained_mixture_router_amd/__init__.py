@@ -72,10 +72,12 @@ _lib.moe_profile_end.restype = ctypes.c_int
 _lib.moe_profile_end.argtypes = [_vp, _vp, ctypes.c_int32]
 _lib.moe_profile_slot_name.restype = ctypes.c_char_p
 _lib.moe_profile_slot_name.argtypes = [ctypes.c_int32]
+_lib.moe_forward_fp8.restype = ctypes.c_int
+_lib.moe_forward_fp8.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [ctypes.c_size_t, _vp]
 _lib.moe_profile_stream_read.restype = ctypes.c_int
 _lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
-EXPORTS = ("moe_workspace_size", "moe_forward", "moe_route", "moe_status_string",
+EXPORTS = ("moe_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
            "moe_profile_begin", "moe_profile_end", "moe_profile_slot_name",
            "moe_profile_stream_read")
 N_SLOTS = 7
@@ -162,6 +164,42 @@ def forward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, b
                             _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out),
                             _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _check(code)
+    if return_routing:
+        return out, topk_idx, topk_gate
+    return out
+
+
+def forward_fp8(x, centroids, w1q, w1s, w3q, w3s, w2q, w2s, ws1=None, ws3=None, ws2=None, *,
+                K: int, bias=None, no_residual: bool = False, renorm: bool = False,
+                sigmoid: bool = False, out=None, topk_idx=None, topk_gate=None, workspace=None,
+                stream=None, return_routing: bool = False):
+    """Layer forward with 8-bit routed weights: w1q/w3q uint8 [E,I,d], w2q
+    [E,d,I] (OCP E4M3 codes) with float32 per-row scales w1s/w3s [E,I], w2s
+    [E,d]; shared experts ws* in bfloat16; the rest as forward()."""
+    import torch
+    T, d = x.shape
+    E = centroids.shape[0] if centroids is not None else (w1q.shape[0] if w1q is not None else 1)
+    I = w1q.shape[1] if w1q is not None else 64
+    Ks = ws1.shape[0] if ws1 is not None else 0
+    Is = ws1.shape[1] if ws1 is not None and Ks else 0
+    shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    if return_routing and K > 0:
+        if topk_idx is None:
+            topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        if topk_gate is None:
+            topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+    nbytes = workspace_size(shape)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    code = _lib.moe_forward_fp8(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(bias),
+                                _ptr(w1q), _ptr(w1s), _ptr(w3q), _ptr(w3s), _ptr(w2q), _ptr(w2s),
+                                _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out), _ptr(topk_idx),
+                                _ptr(topk_gate), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev, stream))
     _check(code)
     if return_routing:
         return out, topk_idx, topk_gate

@@ -86,15 +86,24 @@ struct Plan {
     bf16_t* Y;           // [rows, d]
 };
 
-// Launchers (each enqueues on `st`; return the launch status).
+// 8-bit routed weights: E4M3 codes with one float scale per output row
+// (q1, q3 [E, I, d] with s1, s3 [E, I]; q2 [E, d, I] with s2 [E, d]).
+struct RoutedQ8 {
+    const uint8_t *q1, *q3, *q2;
+    const float *s1, *s3, *s2;
+};
+
+// Launchers (each enqueues on `st`; return the launch status).  q8 != null:
+// the routed weights are 8-bit (the plan then uses the thin tiles).
 hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st);
 hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st);
 hipError_t launch_perm_scan(const Plan& p, hipStream_t st);
 hipError_t launch_perm_scatter(const Plan& p, hipStream_t st);
 hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
                                const bf16_t* w3, const bf16_t* ws1, const bf16_t* ws3,
-                               hipStream_t st);
-hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, hipStream_t st);
+                               const RoutedQ8* q8, hipStream_t st);
+hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
+                            const RoutedQ8* q8, hipStream_t st);
 hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, hipStream_t st);
 

@@ -42,6 +42,10 @@ struct GemmParams {
     const bf16_t* Bb_r;      // routed W3 (G1 only)
     const bf16_t* Ba_s;      // shared weights
     const bf16_t* Bb_s;
+    const uint8_t* Qa_r;     // 8-bit routed weights (G1: W1, G2: W2), or null
+    const uint8_t* Qb_r;     // 8-bit routed W3 (G1 only)
+    const float* Sa_r;       // their per-row scales [E, n_r]
+    const float* Sb_r;
     bf16_t* O_r;             // routed output base (G1: H routed, G2: Y)
     bf16_t* O_s;             // shared output base (G1: H shared, G2: Y)
     int kdim_r, kdim_s;      // reduction length
@@ -52,10 +56,28 @@ struct GemmParams {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
+// Two packed bf16 from the two 8-bit E4M3 codes in the low (HI = false) or
+// high (HI = true) half of `w`, the lower byte in the lower half.  Every
+// E4M3 value is exact in bf16; the scale operand 1.0 leaves it unscaled.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // BM x BN tile, WM x WN waves.  SWIGLU: the BN B-rows are BN/2 rows of W1
 // followed by the same BN/2 rows of W3, and the output has BN/2 columns.
-template <int BM, int BN, int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
+// Q8: the tile's weights are 8-bit E4M3 codes with one float scale per
+// weight row (a routed expert's matrices in moe_forward_fp8): each thread
+// loads 64-byte row pieces (64 codes = one BK slice), widens them to bf16
+// exactly on the way into LDS — so the LDS layout and the MFMA fragments are
+// those of the bf16 path — and the scale multiplies the fp32 accumulator of
+// its output column in the epilogue (the scale is per output channel, so it
+// factors out of the reduction).
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool Q8>
+__device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, bf16_t* sA,
+                                          bf16_t* sB) {
     static_assert(WM * WN == 4, "four waves");
     constexpr int WROWS = BM / WM;                 // rows per wave
     constexpr int WCOLS = BN / WN;                 // B-rows per wave
@@ -63,18 +85,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
     constexpr int NB = WCOLS / 32;
     static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile shape");
     constexpr int AL = BM / 32;                    // A chunks per thread per stage
-    constexpr int BL = BN / 32;
-
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kBK];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * kBK];
-
-    const int nt = *P.ntiles;
-    const int wg = blockIdx.x;
-    const int nr = (nt + 7) & ~7;
-    if (wg >= nr) return;
-    const int lt = (wg & 7) * (nr >> 3) + (wg >> 3);
-    if (lt >= nt) return;
-    const Tile tl = P.tiles[lt];
+    constexpr int BL = Q8 ? BN / 64 : BN / 32;     // B chunks per thread per stage
+    static_assert(!Q8 || BN == 256, "the 8-bit row mapping assumes 256 B-rows");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -88,12 +100,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
     const int grow = P.goff[tl.group] + tl.m0;      // first global row of the tile
     const int rrow = shared ? grow - P.TK : grow;   // first row within its region
 
-    const bf16_t* wa = shared ? P.Ba_s + (size_t)s * ncols * kdim
-                              : P.Ba_r + (size_t)tl.group * ncols * kdim;
-    const bf16_t* wb = nullptr;
-    if (SWIGLU)
-        wb = shared ? P.Bb_s + (size_t)s * ncols * kdim : P.Bb_r + (size_t)tl.group * ncols * kdim;
-
     // Raw buffer loads: resource (base, size) in scalar registers, a 32-bit
     // byte offset per lane, the k position in the scalar offset.  Rows past
     // the tile's end are clamped to its first row and weight rows past the
@@ -102,9 +108,20 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
     const int ch = tid & 7;
     const __amdgpu_buffer_rsrc_t ra_src =
         make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
-    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * 2u;
+    constexpr uint32_t WB = Q8 ? 1u : 2u;          // bytes per weight
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * WB;
+    const size_t wofs = (size_t)(shared ? s : tl.group) * ncols * kdim;
+    const void* wa;
+    const void* wb;
+    if (Q8) {
+        wa = P.Qa_r + wofs;
+        wb = SWIGLU ? P.Qb_r + wofs : wa;
+    } else {
+        wa = (shared ? P.Ba_s : P.Ba_r) + wofs;
+        wb = SWIGLU ? (shared ? P.Bb_s : P.Bb_r) + wofs : wa;
+    }
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(wa, wbytes);
-    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(SWIGLU ? wb : wa, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(wb, wbytes);
     uint32_t aoff[AL];
     uint32_t boff[BL];
 #pragma unroll
@@ -116,12 +133,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
         else arow = (uint32_t)(rrow + rr);
         aoff[i] = (arow * (uint32_t)kdim + ch * 8) * 2u;
     }
+    // bf16: thread moves 16-byte chunk ch of rows (tid >> 3) + 32 i;
+    // 8-bit: 16-byte piece c8 = tid & 3 (codes 16 c8 .. 16 c8 + 15) of rows
+    // (tid >> 2) + 64 i.  Either way i < BL/2 <=> the row is in the W1 half.
+    const int c8 = tid & 3;
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        const int r = (tid >> 3) + 32 * i;        // i < BL/2 <=> r < BN/2
+        const int r = Q8 ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
         int n = tl.n0 + ((SWIGLU && r >= BN / 2) ? r - BN / 2 : r);
         n = n < ncols ? n : ncols - 1;
-        boff[i] = ((uint32_t)n * (uint32_t)kdim + ch * 8) * 2u;
+        boff[i] = Q8 ? (uint32_t)n * (uint32_t)kdim + c8 * 16u
+                     : ((uint32_t)n * (uint32_t)kdim + ch * 8) * 2u;
     }
 
     f32x16 acc[MB][NB];
@@ -131,43 +153,61 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
     // LDS addressing.  Every row index used below is (multiple of 8) + the
-    // lane's own (lane & 7) or (tid >> 3) & 7, so the swizzled chunk position
-    // of a lane is fixed per k16 step and the rest is a compile-time or
-    // wave-uniform row offset.
+    // lane's own (lane & 7), (tid >> 3) & 7 or (tid >> 2) & 7, so the
+    // swizzled chunk position of a lane is fixed per k16 step and the rest is
+    // a compile-time or wave-uniform row offset.
     const int srow = tid >> 3;
     const int sx = (ch ^ (srow & 7)) << 3;
-    bf16_t* const a_st = &sA[0][0] + srow * kBK + sx;
-    bf16_t* const b_st = &sB[0][0] + srow * kBK + sx;
+    bf16_t* const a_st = sA + srow * kBK + sx;
+    bf16_t* const b_st = sB + srow * kBK + sx;
+    const int qrow = tid >> 2;                     // 8-bit path: rows qrow + 64 i
+    bf16_t* const q_st0 = sB + qrow * kBK + (((2 * c8) ^ (qrow & 7)) << 3);
+    bf16_t* const q_st1 = sB + qrow * kBK + (((2 * c8 + 1) ^ (qrow & 7)) << 3);
     const int lrow = lane & 31;
     int cx[kBK / 16];
 #pragma unroll
     for (int st = 0; st < kBK / 16; ++st) cx[st] = ((2 * st + (lane >> 5)) ^ (lane & 7)) << 3;
-    const bf16_t* const a_ld = &sA[0][0] + (wm * WROWS + lrow) * kBK;
-    const bf16_t* const b_ld = &sB[0][0] + lrow * kBK;
+    const bf16_t* const a_ld = sA + (wm * WROWS + lrow) * kBK;
+    const bf16_t* const b_ld = sB + lrow * kBK;
 
     const int nk = kdim / kBK;
     u32x4 ra[AL], rb[BL];
+    auto gload = [&](uint32_t kb_bf16) {             // kb: byte offset of the slice in bf16 rows
 #pragma unroll
-    for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], 0);
+        for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb_bf16);
 #pragma unroll
-    for (int i = 0; i < BL; ++i) rb[i] = buf_load16((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], 0);
+        for (int i = 0; i < BL; ++i)
+            rb[i] = buf_load16((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], Q8 ? kb_bf16 / 2 : kb_bf16);
+    };
+    auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(a_st + 32 * i * kBK) = ra[i];
+        for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(a_st + buf * (BM * kBK) + 32 * i * kBK) = ra[i];
+        if (Q8) {
 #pragma unroll
-    for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(b_st + 32 * i * kBK) = rb[i];
+            for (int i = 0; i < BL; ++i) {
+                const u32x4 q = rb[i];
+                const u32x4 lo = {e4m3x2_to_bf16x2<false>(q.x), e4m3x2_to_bf16x2<true>(q.x),
+                                  e4m3x2_to_bf16x2<false>(q.y), e4m3x2_to_bf16x2<true>(q.y)};
+                const u32x4 hi = {e4m3x2_to_bf16x2<false>(q.z), e4m3x2_to_bf16x2<true>(q.z),
+                                  e4m3x2_to_bf16x2<false>(q.w), e4m3x2_to_bf16x2<true>(q.w)};
+                *reinterpret_cast<u32x4*>(q_st0 + buf * (BN * kBK) + 64 * i * kBK) = lo;
+                *reinterpret_cast<u32x4*>(q_st1 + buf * (BN * kBK) + 64 * i * kBK) = hi;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < BL; ++i)
+                *reinterpret_cast<u32x4*>(b_st + buf * (BN * kBK) + 32 * i * kBK) = rb[i];
+        }
+    };
+
+    gload(0);
+    sstore(0);
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         const bool more = kt + 1 < nk;
-        if (more) {
-            const uint32_t kb = (uint32_t)(kt + 1) * kBK * 2u;
-#pragma unroll
-            for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb);
-#pragma unroll
-            for (int i = 0; i < BL; ++i)
-                rb[i] = buf_load16((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], kb);
-        }
+        if (more) gload((uint32_t)(kt + 1) * kBK * 2u);
         const bf16_t* a_b = a_ld + buf * (BM * kBK);
         const bf16_t* b_b = b_ld + buf * (BN * kBK);
 #pragma unroll
@@ -193,15 +233,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
                 for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (more) {
-            const int nb = buf ^ 1;
-#pragma unroll
-            for (int i = 0; i < AL; ++i)
-                *reinterpret_cast<u32x4*>(a_st + nb * (BM * kBK) + 32 * i * kBK) = ra[i];
-#pragma unroll
-            for (int i = 0; i < BL; ++i)
-                *reinterpret_cast<u32x4*>(b_st + nb * (BN * kBK) + 32 * i * kBK) = rb[i];
-        }
+        if (more) sstore(buf ^ 1);
         __syncthreads();
     }
 
@@ -209,23 +241,48 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
     // rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
     bf16_t* obase = shared ? P.O_s : P.O_r;
     const int orow0 = SWIGLU ? rrow : grow;
-    const int ocols = SWIGLU ? ncols : ncols;
+    const float* sca = Q8 ? P.Sa_r + (size_t)tl.group * ncols : nullptr;
+    const float* scb = Q8 && SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : nullptr;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
         for (int j = 0; j < (SWIGLU ? NB / 2 : NB); ++j) {
             const int col = tl.n0 + (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + j * 32 + (lane & 31);
+            float fa = 1.f, fb = 1.f;
+            if (Q8 && col < ncols) {
+                fa = sca[col];
+                if (SWIGLU) fb = scb[col];
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = wm * WROWS + i * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
                 float v;
-                if (SWIGLU) v = silu(acc[i][j][r]) * acc[i][j + NB / 2][r];
-                else v = acc[i][j][r];
-                if (row < tl.nrows && col < ocols)
-                    obase[(size_t)(orow0 + row) * ocols + col] = f32_to_bf16(v);
+                if (SWIGLU) v = silu(Q8 ? acc[i][j][r] * fa : acc[i][j][r]) *
+                                (Q8 ? acc[i][j + NB / 2][r] * fb : acc[i][j + NB / 2][r]);
+                else v = Q8 ? acc[i][j][r] * fa : acc[i][j][r];
+                if (row < tl.nrows && col < ncols)
+                    obase[(size_t)(orow0 + row) * ncols + col] = f32_to_bf16(v);
             }
         }
     }
+}
+
+// Few-rows-per-expert tiles.  Q8: routed experts' weights are 8-bit codes
+// with per-row scales; shared experts' tiles always take the bf16 path.
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool Q8>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2 * BM * kBK];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2 * BN * kBK];
+
+    const int nt = *P.ntiles;
+    const int wg = blockIdx.x;
+    const int nr = (nt + 7) & ~7;
+    if (wg >= nr) return;
+    const int lt = (wg & 7) * (nr >> 3) + (wg >> 3);
+    if (lt >= nt) return;
+    const Tile tl = P.tiles[lt];
+    if (Q8 && tl.group < P.E) thin_tile<BM, BN, WM, WN, SWIGLU, true>(P, tl, sA, sB);
+    else thin_tile<BM, BN, WM, WN, SWIGLU, false>(P, tl, sA, sB);
 }
 
 // ---------------------------------------------------------------------------
@@ -568,7 +625,8 @@ template <int BM, int BN, int WM, int WN, bool SWIGLU>
 hipError_t launch_cfg(const GemmParams& gp, int max_tiles, hipStream_t st) {
     const int grid = (max_tiles + 7) & ~7;
     if (grid == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, SWIGLU><<<grid, kThreads, 0, st>>>(gp);
+    if (gp.Qa_r) grouped_gemm_kernel<BM, BN, WM, WN, SWIGLU, true><<<grid, kThreads, 0, st>>>(gp);
+    else grouped_gemm_kernel<BM, BN, WM, WN, SWIGLU, false><<<grid, kThreads, 0, st>>>(gp);
     return hipGetLastError();
 }
 
@@ -576,8 +634,14 @@ hipError_t launch_cfg(const GemmParams& gp, int max_tiles, hipStream_t st) {
 
 hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
                                const bf16_t* w3, const bf16_t* ws1, const bf16_t* ws3,
-                               hipStream_t st) {
+                               const RoutedQ8* q8, hipStream_t st) {
     GemmParams gp{};
+    if (q8) {
+        gp.Qa_r = q8->q1;
+        gp.Qb_r = q8->q3;
+        gp.Sa_r = q8->s1;
+        gp.Sb_r = q8->s3;
+    }
     gp.tiles = p.tiles1;
     gp.ntiles = p.ntiles;
     gp.goff = p.goff;
@@ -599,6 +663,7 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.abytes_r = (uint32_t)((size_t)p.T * p.d * 2);
     gp.abytes_s = gp.abytes_r;
     if (p.g1.bm == 256) {
+        if (q8) return hipErrorInvalidValue;       // 8-bit plans use the thin tiles
         const int grid = (p.max_tiles1 + 7) & ~7;
         gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
             <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
@@ -607,8 +672,13 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     return launch_cfg<32, 256, 1, 4, true>(gp, p.max_tiles1, st);
 }
 
-hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, hipStream_t st) {
+hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
+                            const RoutedQ8* q8, hipStream_t st) {
     GemmParams gp{};
+    if (q8) {
+        gp.Qa_r = q8->q2;
+        gp.Sa_r = q8->s2;
+    }
     gp.tiles = p.tiles2;
     gp.ntiles = p.ntiles + 1;
     gp.goff = p.goff;
@@ -630,6 +700,7 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2, 
     gp.abytes_r = (uint32_t)((size_t)p.T * p.K * p.I * 2);
     gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
     if (p.g2.bm == 256) {
+        if (q8) return hipErrorInvalidValue;
         const int grid = (p.max_tiles2 + 7) & ~7;
         gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
             <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);

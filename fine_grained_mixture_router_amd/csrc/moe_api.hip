@@ -42,8 +42,9 @@ bool shape_ok(const moe_shape_t* s) {
 }
 
 // Fill the shape-derived part of the plan and the workspace offsets (as byte
-// offsets from 0); returns the total workspace size.
-size_t make_plan(const moe_shape_t* s, Plan* p) {
+// offsets from 0); returns the total workspace size.  q8: the routed weights
+// are 8-bit, which the thin tiles serve at every batch size.
+size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
     memset(p, 0, sizeof(*p));
     p->T = s->T;
     p->d = s->d;
@@ -66,7 +67,7 @@ size_t make_plan(const moe_shape_t* s, Plan* p) {
 
     // Few rows per expert (decode-sized batches): thin tiles that stream each
     // weight once; otherwise 256x256 MFMA tiles.
-    const bool thin = TK < 64LL * s->E;
+    const bool thin = q8 || TK < 64LL * s->E;
     p->g1.bm = thin ? 32 : 256;
     p->g1.bn = 256;
     p->g2.bm = thin ? 32 : 256;
@@ -179,7 +180,8 @@ void rec_free() {
 }
 
 moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* centroids,
-                          const float* bias, void* ws, size_t ws_bytes, Plan* plan) {
+                          const float* bias, void* ws, size_t ws_bytes, Plan* plan,
+                          bool q8 = false) {
     if (!shape) return MOE_ERR_NULL;
     if (!shape_ok(shape)) return MOE_ERR_SHAPE;
     if (!x || !ws) return MOE_ERR_NULL;
@@ -187,7 +189,7 @@ moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* c
     if (!aligned(x, 16) || (centroids && !aligned(centroids, 16))) return MOE_ERR_ALIGN;
     if (bias && !aligned(bias, 4)) return MOE_ERR_ALIGN;
     if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
-    const size_t need = make_plan(shape, plan);
+    const size_t need = make_plan(shape, plan, q8);
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     return MOE_OK;
 }
@@ -199,7 +201,9 @@ extern "C" {
 __attribute__((visibility("default"))) size_t moe_workspace_size(const moe_shape_t* shape) {
     if (!shape_ok(shape)) return 0;
     Plan p;
-    return make_plan(shape, &p);
+    const size_t a = make_plan(shape, &p, false);
+    const size_t b = make_plan(shape, &p, true);   // moe_forward_fp8's plan
+    return a > b ? a : b;
 }
 
 __attribute__((visibility("default"))) const char* moe_status_string(moe_status_t st) {
@@ -216,24 +220,39 @@ __attribute__((visibility("default"))) const char* moe_status_string(moe_status_
     return "unknown moe_status_t";
 }
 
-__attribute__((visibility("default"))) moe_status_t moe_forward(
-    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
-    const void* w1, const void* w3, const void* w2, const void* ws1, const void* ws3,
-    const void* ws2, void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
-    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of both entry points: w1/w3/w2 are bf16 (q8 == null) or
+// ignored in favour of the 8-bit routed weights q8.
+moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* centroids,
+                         const float* expert_bias, const void* w1, const void* w3,
+                         const void* w2, const RoutedQ8* q8, const void* ws1, const void* ws3,
+                         const void* ws2, void* out, int32_t* topk_idx, float* topk_gate,
+                         void* workspace, size_t workspace_bytes, void* stream) {
     Plan p;
-    moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes, &p);
+    moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes,
+                                   &p, q8 != nullptr);
     if (st != MOE_OK) return st;
     if (!out) return MOE_ERR_NULL;
-    if (shape->K > 0 && (!w1 || !w3 || !w2)) return MOE_ERR_NULL;
+    if (shape->K > 0) {
+        if (q8 ? (!q8->q1 || !q8->q3 || !q8->q2 || !q8->s1 || !q8->s3 || !q8->s2)
+               : (!w1 || !w3 || !w2))
+            return MOE_ERR_NULL;
+    }
     if (shape->Ks > 0 && (!ws1 || !ws3 || !ws2)) return MOE_ERR_NULL;
-    const void* bf[] = {out, shape->K > 0 ? w1 : nullptr, shape->K > 0 ? w3 : nullptr,
-                        shape->K > 0 ? w2 : nullptr, shape->Ks > 0 ? ws1 : nullptr,
-                        shape->Ks > 0 ? ws3 : nullptr, shape->Ks > 0 ? ws2 : nullptr};
-    for (const void* q : bf)
-        if (q && !aligned(q, 16)) return MOE_ERR_ALIGN;
-    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_gate && !aligned(topk_gate, 4)))
-        return MOE_ERR_ALIGN;
+    const bool rk = shape->K > 0, sk = shape->Ks > 0;
+    const void* a16[] = {out, rk && !q8 ? w1 : nullptr, rk && !q8 ? w3 : nullptr,
+                         rk && !q8 ? w2 : nullptr, sk ? ws1 : nullptr, sk ? ws3 : nullptr,
+                         sk ? ws2 : nullptr, rk && q8 ? q8->q1 : nullptr,
+                         rk && q8 ? q8->q3 : nullptr, rk && q8 ? q8->q2 : nullptr};
+    for (const void* a : a16)
+        if (a && !aligned(a, 16)) return MOE_ERR_ALIGN;
+    const void* a4[] = {topk_idx, topk_gate, rk && q8 ? q8->s1 : nullptr,
+                        rk && q8 ? q8->s3 : nullptr, rk && q8 ? q8->s2 : nullptr};
+    for (const void* a : a4)
+        if (a && !aligned(a, 4)) return MOE_ERR_ALIGN;
     st = device_ok();
     if (st != MOE_OK) return st;
 
@@ -248,6 +267,7 @@ __attribute__((visibility("default"))) moe_status_t moe_forward(
     const bf16_t* ws1b = static_cast<const bf16_t*>(ws1);
     const bf16_t* ws3b = static_cast<const bf16_t*>(ws3);
     const bf16_t* ws2b = static_cast<const bf16_t*>(ws2);
+    const RoutedQ8* q = rk ? q8 : nullptr;
     hipError_t e = hipSuccess;
     auto step = [&](int slot, auto&& launch) {
         if (e != hipSuccess) return;
@@ -261,8 +281,8 @@ __attribute__((visibility("default"))) moe_status_t moe_forward(
     }
     step(2, [&] { return launch_perm_scan(p, s); });
     step(3, [&] { return launch_perm_scatter(p, s); });
-    step(4, [&] { return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, s); });
-    step(5, [&] { return launch_gemm_down(p, w2b, ws2b, s); });
+    step(4, [&] { return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s); });
+    step(5, [&] { return launch_gemm_down(p, w2b, ws2b, q, s); });
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
         for (int k = 0; k < kSlots; ++k)
@@ -271,6 +291,31 @@ __attribute__((visibility("default"))) moe_status_t moe_forward(
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) moe_status_t moe_forward(
+    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
+    const void* w1, const void* w3, const void* w2, const void* ws1, const void* ws3,
+    const void* ws2, void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
+    size_t workspace_bytes, void* stream) {
+    return run_forward(shape, x, centroids, expert_bias, w1, w3, w2, nullptr, ws1, ws3, ws2, out,
+                       topk_idx, topk_gate, workspace, workspace_bytes, stream);
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_forward_fp8(
+    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
+    const void* w1q, const float* w1_scale, const void* w3q, const float* w3_scale,
+    const void* w2q, const float* w2_scale, const void* ws1, const void* ws3, const void* ws2,
+    void* out, int32_t* topk_idx, float* topk_gate, void* workspace, size_t workspace_bytes,
+    void* stream) {
+    const RoutedQ8 q8{static_cast<const uint8_t*>(w1q), static_cast<const uint8_t*>(w3q),
+                      static_cast<const uint8_t*>(w2q), w1_scale, w3_scale, w2_scale};
+    return run_forward(shape, x, centroids, expert_bias, nullptr, nullptr, nullptr, &q8, ws1, ws3,
+                       ws2, out, topk_idx, topk_gate, workspace, workspace_bytes, stream);
 }
 
 __attribute__((visibility("default"))) moe_status_t moe_route(

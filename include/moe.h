@@ -87,7 +87,8 @@ typedef enum {
     MOE_ERR_HIP = 7          /* a HIP launch failed                         */
 } moe_status_t;
 
-/* Bytes of device workspace moe_forward / moe_route need for this shape
+/* Bytes of device workspace moe_forward / moe_forward_fp8 / moe_route need
+ * for this shape
  * (routing scratch, the token permutation, tile lists, and the bf16
  * intermediates H [T·K·I + T·Ks·Is] and Y [T·(K+Ks), d]).  Pure host
  * arithmetic, no HIP call.  Returns 0 when the shape is invalid. */
@@ -117,6 +118,38 @@ moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* ce
                          const void* w2, const void* ws1, const void* ws3, const void* ws2,
                          void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Full layer forward with 8-bit routed-expert weights (the survey's next
+ * step for decode: it halves the bytes every routed weight costs).
+ *
+ * Routed experts are stored as OCP FP8 E4M3 codes (sign bit 7, exponent
+ * bits 6-3 with bias 7, mantissa bits 2-0; codes 0x7F / 0xFF are NaN and
+ * outside the contract) with one fp32 scale per output row — per-channel
+ * quantisation of the routed experts, shared experts kept at 16 bits, as the
+ * eliteato DeepSeek-V2 explainer advises (section 5.5):
+ *
+ *   W1[e][i][j] = e4m3(w1q[e][i][j]) * w1_scale[e][i]     w1q, w3q uint8 [E, I, d]
+ *   W3[e][i][j] = e4m3(w3q[e][i][j]) * w3_scale[e][i]     w1_scale, w3_scale fp32 [E, I]
+ *   W2[e][o][i] = e4m3(w2q[e][o][i]) * w2_scale[e][o]     w2q uint8 [E, d, I], w2_scale fp32 [E, d]
+ *
+ * Everything else — shape, flags, x, centroids, bias, the bf16 shared
+ * experts ws1/ws3/ws2, out, routing outputs, workspace (the same
+ * moe_workspace_size()), stream, validation and errors — is as for
+ * moe_forward.  w1q/w3q/w2q must be 16-byte aligned, the scales 4-byte
+ * aligned; all six may be NULL iff K == 0.
+ *
+ * Arithmetic: each code is widened exactly to bf16, the expert GEMMs run in
+ * bf16 with fp32 accumulation, and the row scale multiplies the fp32
+ * accumulator of its output column before SwiGLU (gate/up) or before the
+ * bf16 rounding of Y (down).  Every batch size runs on the few-rows tile
+ * (32 rows by 256 weight rows), which streams each weight once per 32 rows:
+ * the configuration for decode-sized batches. */
+moe_status_t moe_forward_fp8(const moe_shape_t* shape, const void* x, const void* centroids,
+                             const float* expert_bias, const void* w1q, const float* w1_scale,
+                             const void* w3q, const float* w3_scale, const void* w2q,
+                             const float* w2_scale, const void* ws1, const void* ws3,
+                             const void* ws2, void* out, int32_t* topk_idx, float* topk_gate,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Routing only: affinities, softmax (or the flags' gate), top-K
  * ("DeepSeekMoE 深度解读报告", section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both

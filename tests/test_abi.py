@@ -16,7 +16,7 @@ moe = pytest.importorskip("fine_grained_mixture_router_amd")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -165,3 +165,37 @@ def test_stream_read_validation():
     torch = pytest.importorskip("torch")
     if torch.cuda.device_count() == 0:
         assert f(ctypes.c_void_p(4096), ctypes.c_size_t(16384), None) == 5
+
+
+def _fwd8(shape, ws_bytes=1 << 40, **over):
+    ptrs = dict(x=4096, C=4096, bias=None, q1=4096, s1=4096, q3=4096, s3=4096, q2=4096, s2=4096,
+                ws1=4096, ws3=4096, ws2=4096, out=4096, idx=None, gate=None, ws=4096)
+    ptrs.update(over)
+    keys = ("x", "C", "bias", "q1", "s1", "q3", "s3", "q2", "s2", "ws1", "ws3", "ws2", "out",
+            "idx", "gate", "ws")
+    return moe.lib().moe_forward_fp8(ctypes.byref(shape),
+                                     *[None if ptrs[k] is None else ctypes.c_void_p(ptrs[k])
+                                       for k in keys],
+                                     ctypes.c_size_t(ws_bytes), None)
+
+
+def test_fp8_entry_validation():
+    s = S()
+    assert moe.lib().moe_forward_fp8(None, *([None] * 16), ctypes.c_size_t(0), None) == 1
+    for k in ("q1", "s1", "q3", "s3", "q2", "s2", "out", "ws1"):
+        assert _fwd8(s, **{k: None}) == 1, k
+    assert _fwd8(s, q2=4096 + 8) == 3
+    assert _fwd8(s, s3=4096 + 2) == 3
+    assert _fwd8(s, ws_bytes=moe.workspace_size(s) - 1) == 4
+    # K = 0: no routed weights or centroids needed
+    s0 = S(K=0)
+    assert _fwd8(s0, C=None, q1=None, s1=None, q3=None, s3=None, q2=None, s2=None, ws_bytes=1) == 4
+    bad = S(d=100)
+    assert _fwd8(bad) == 2
+
+
+def test_workspace_covers_both_weight_forms():
+    # a prefill-sized batch: the 8-bit form plans thin tiles, whose work list
+    # is longer; the one workspace size serves both entry points
+    s = moe.make_shape(16384, 7168, 256, 2048, 8, 1, 2048)
+    assert moe.workspace_size(s) >= 2.5e9
