@@ -7,8 +7,10 @@ with SwiGLU, down GEMM, combine) over one batch already resident in HBM.
 Headline workload: the DeepSeek-V3-shape prefill batch (T=16384 tokens,
 d=7168, 256 routed + 1 shared experts of inter 2048, top-8, Zipf(1.2) logit
 bias) — MFMA-bound.  The same layer on a 256-token decode batch (HBM-bound)
-is measured in the same run and reported under "decode".  Inputs are seeded
-synthetic data (bf16, N(0,1) activations, N(0,0.006) weights).
+is measured in the same run and reported under "decode", and again with
+8-bit (E4M3, per-row scaled) routed weights under "decode_fp8".  Inputs are
+seeded synthetic data (bf16, N(0,1) activations, N(0,0.006) weights; the
+8-bit codes are drawn as bit fields with per-row scales of a similar size).
 
 Prints ONE JSON line:
   value            tokens/s of the whole layer (T / ms_per_step)
@@ -44,12 +46,15 @@ CSRC = os.path.join(ROOT, "fine_grained_mixture_router_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_v3_prefill_decode.md")
 CALIB_BYTES = 1 << 30         # the calibration copy: 1 GiB read + 1 GiB written
 # kernel-name prefix -> (workload, slot) in a default run (prefill on the
-# 256x256 tile, decode on the 32x256 tile)
+# 256x256 tile, decode on the 32x256 tile, the 8-bit decode on its 8-bit
+# instance)
 COUNTER_KERNELS = {
     "gemm_big_kernel<true": ("v3_prefill", "gemm_gate_up"),
     "gemm_big_kernel<false": ("v3_prefill", "gemm_down"),
-    "grouped_gemm_kernel<32, 256, 1, 4, true>": ("v3_decode", "gemm_gate_up"),
-    "grouped_gemm_kernel<32, 256, 1, 4, false>": ("v3_decode", "gemm_down"),
+    "grouped_gemm_kernel<32, 256, 1, 4, true, false>": ("v3_decode", "gemm_gate_up"),
+    "grouped_gemm_kernel<32, 256, 1, 4, false, false>": ("v3_decode", "gemm_down"),
+    "grouped_gemm_kernel<32, 256, 1, 4, true, true>": ("v3_decode_fp8", "gemm_gate_up"),
+    "grouped_gemm_kernel<32, 256, 1, 4, false, true>": ("v3_decode_fp8", "gemm_down"),
 }
 
 
@@ -61,6 +66,8 @@ def parse():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode",
                     help="second workload on the same layer weights ('' to skip)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the decode batch with 8-bit routed weights")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle CPU baseline (0 to skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -173,6 +180,23 @@ def hit_stats(idx, E):
                 active_ratio=float((counts > 0).mean()))
 
 
+def algorithmic_fp8(w, counts):
+    """As algorithmic(), with the routed weights at one byte each plus one
+    fp32 scale per weight row; shared experts stay bf16."""
+    touched = int((counts > 0).sum())
+    rows_r, rows_s = w.T * w.K, w.T * w.Ks
+    g1_flops = 4.0 * w.d * (rows_r * w.I + rows_s * w.Is)
+    g2_flops = 2.0 * w.d * (rows_r * w.I + rows_s * w.Is)
+    layer_flops = 2.0 * w.T * w.d * w.E + g1_flops + g2_flops
+    wb_r = 3 * w.I * w.d + 4 * (2 * w.I + w.d)
+    wb_s = 2 * 3 * w.Is * w.d
+    layer_bytes = (touched * wb_r + w.Ks * wb_s + 2 * w.E * w.d + 2 * 2 * w.T * w.d)
+    g1_bytes = (touched * (2 * w.I * w.d + 4 * 2 * w.I) + w.Ks * 2 * 2 * w.Is * w.d
+                + 2 * w.T * w.d + 2 * (rows_r * w.I + rows_s * w.Is))
+    return dict(touched=touched, g1_flops=g1_flops, layer_flops=layer_flops,
+                g1_bytes=float(g1_bytes), layer_bytes=float(layer_bytes))
+
+
 def algorithmic(w, counts):
     """Algorithmic work of the layer and of its gate/up GEMM for one batch.
 
@@ -219,8 +243,13 @@ def time_workload(w, D, host_x, steps, warmup):
     gate = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
 
     def step():
-        moe.forward(x, D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"], K=w.K,
-                    bias=bias, out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
+        if "q1" in D:
+            moe.forward_fp8(x, D["C"], D["q1"], D["s1"], D["q3"], D["s3"], D["q2"], D["s2"],
+                            D["ws1"], D["ws3"], D["ws2"], K=w.K, bias=bias, out=out,
+                            topk_idx=idx, topk_gate=gate, workspace=ws)
+        else:
+            moe.forward(x, D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
+                        K=w.K, bias=bias, out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -419,12 +448,37 @@ def main():
         }
         print(f"[bench] {wd.name}: {msd:.3f} ms/step", file=sys.stderr, flush=True)
 
+        if not args.no_fp8:
+            # the same decode batch with 8-bit routed weights (shared experts bf16)
+            q1, s1, q3, s3, q2, s2 = wl.gen_routed_fp8(wd)
+            D8 = {k: v for k, v in Dd.items() if k not in ("w1", "w3", "w2")}
+            for k, v in (("q1", q1), ("s1", s1), ("q3", q3), ("s3", s3), ("q2", q2), ("s2", s2)):
+                D8[k] = dev(v)
+            del q1, q3, q2
+            r8 = time_workload(wd, D8, xd, args.steps, args.warmup)
+            c8 = np.bincount(r8["idx"].ravel(), minlength=wd.E)
+            k8 = algorithmic_fp8(wd, c8)
+            ms8 = r8["ms_per_step"]
+            line["decode_fp8"] = {
+                "workload": wd.name + " (8-bit E4M3 routed weights, per-row fp32 scales; shared bf16)",
+                "T": wd.T, "value": round(wd.T / (ms8 / 1e3), 1), "unit": "tokens/s",
+                "ms_per_step": round(ms8, 4), "speedup_vs_bf16": round(msd / ms8, 3),
+                "roofline": roofline(regime(wd), k8, r8["kernels"], wd.name + "_fp8"),
+                "layer_gbs": round(k8["layer_bytes"] / (ms8 / 1e3) / 1e9, 1),
+                "layer_hbm_frac": round(k8["layer_bytes"] / (ms8 / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in r8["kernels"].items()},
+            }
+            del D8
+            torch.cuda.empty_cache()
+            print(f"[bench] {wd.name} fp8: {ms8:.3f} ms/step", file=sys.stderr, flush=True)
+
     ceil = hbm_read_ceiling()
     line["hbm_read_ceiling"] = ceil
-    if "decode" in line:
-        r = line["decode"]["roofline"]
-        r["frac_of_read_ceiling"] = round(r["achieved"] / ceil["gbs"], 4)
-        line["decode"]["layer_frac_of_read_ceiling"] = round(line["decode"]["layer_gbs"] / ceil["gbs"], 4)
+    for key in ("decode", "decode_fp8"):
+        if key in line:
+            r = line[key]["roofline"]
+            r["frac_of_read_ceiling"] = round(r["achieved"] / ceil["gbs"], 4)
+            line[key]["layer_frac_of_read_ceiling"] = round(line[key]["layer_gbs"] / ceil["gbs"], 4)
     print(f"[bench] HBM read ceiling {ceil['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     if args.cpu_seconds > 0:

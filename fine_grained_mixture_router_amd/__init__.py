@@ -243,7 +243,7 @@ def profile_end() -> dict:
 
 def stream_read(buf, stream=None):
     """Enqueue one pass of 16-byte loads over the device tensor `buf` (its
-    size a multiple of 16384 bytes): time it to get the practical HBM read
+    size a multiple of 32768 bytes): time it to get the practical HBM read
     rate."""
     import torch
     s = torch.cuda.current_stream() if stream is None else stream

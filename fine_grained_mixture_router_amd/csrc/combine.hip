@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
             u32x4 r[kBatch];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
-                if (b0 + b < ns) r[b] = reinterpret_cast<const u32x4*>(Y + (size_t)s_row[b0 + b] * d)[v];
+                if (b0 + b < ns)                    // rows of Y are read once: nontemporal
+                    r[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Y + (size_t)s_row[b0 + b] * d) + v);
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
                 if (b0 + b < ns) add8(acc, r[b], s_w[b0 + b]);

@@ -171,15 +171,25 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
     const bf16_t* const b_ld = sB + lrow * kBK;
 
     const int nk = kdim / kBK;
-    u32x4 ra[AL], rb[BL];
-    auto gload = [&](uint32_t kb_bf16) {             // kb: byte offset of the slice in bf16 rows
+    // Two register stages: the loads of slice kt + 2 are issued while slice kt
+    // is multiplied out of LDS, and slice kt + 1 (loaded one iteration
+    // earlier) goes to LDS at the end of the iteration — two iterations of
+    // MFMA work hide each load's latency.
+    u32x4 ra0[AL], rb0[BL], ra1[AL], rb1[BL];
+    auto gload = [&](int kt, u32x4 (&ra)[AL], u32x4 (&rb)[BL]) {
+        const uint32_t kb = (uint32_t)kt * kBK * 2u;  // byte offset of the slice in bf16 rows
 #pragma unroll
-        for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb_bf16);
+        for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb);
+        // bf16 weights are streamed with the nontemporal policy (read once
+        // per tile); an 8-bit slice is half a 128-byte line whose other half
+        // the next slice reads, so those keep the default policy and hit L2.
 #pragma unroll
-        for (int i = 0; i < BL; ++i)
-            rb[i] = buf_load16((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], Q8 ? kb_bf16 / 2 : kb_bf16);
+        for (int i = 0; i < BL; ++i) {
+            const __amdgpu_buffer_rsrc_t r = (SWIGLU && i >= BL / 2) ? rw3 : rw1;
+            rb[i] = Q8 ? buf_load16(r, boff[i], kb / 2) : buf_load16_nt(r, boff[i], kb);
+        }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, const u32x4 (&ra)[AL], const u32x4 (&rb)[BL]) {
 #pragma unroll
         for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(a_st + buf * (BM * kBK) + 32 * i * kBK) = ra[i];
         if (Q8) {
@@ -199,15 +209,7 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
                 *reinterpret_cast<u32x4*>(b_st + buf * (BN * kBK) + 32 * i * kBK) = rb[i];
         }
     };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) gload((uint32_t)(kt + 1) * kBK * 2u);
+    auto compute = [&](int buf) {
         const bf16_t* a_b = a_ld + buf * (BM * kBK);
         const bf16_t* b_b = b_ld + buf * (BN * kBK);
 #pragma unroll
@@ -233,8 +235,40 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
                 for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (more) sstore(buf ^ 1);
-        __syncthreads();
+    };
+    // iteration kt: (ca, cb) are free (their slice went to LDS last
+    // iteration) and take slice kt + 2; (na, nb) hold slice kt + 1
+    // Barrier after this wave's LDS stores, without __syncthreads()'s wait
+    // for every outstanding global load (which would drain the prefetch).
+    auto bar = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    auto iter = [&](int kt, bool load, bool store, u32x4 (&ca)[AL], u32x4 (&cb)[BL],
+                    u32x4 (&na)[AL], u32x4 (&nb)[BL]) {
+        if (load) gload(kt + 2, ca, cb);
+        __builtin_amdgcn_sched_barrier(0);           // the prefetch leaves before the MFMAs
+        compute(kt & 1);
+        if (store) sstore((kt + 1) & 1, na, nb);
+        bar();
+    };
+
+    gload(0, ra0, rb0);
+    if (nk > 1) gload(1, ra1, rb1);
+    sstore(0, ra0, rb0);
+    bar();
+    // Steady state, two iterations at a time (the register sets swap roles):
+    // every iteration loads and stores, so the loop body has no branch and
+    // each wait covers just the older slice.  The last one to three
+    // iterations run in the tail.
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 2) {
+        iter(kt, true, true, ra0, rb0, ra1, rb1);
+        iter(kt + 1, true, true, ra1, rb1, ra0, rb0);
+    }
+    if (kt < nk) {
+        iter(kt, kt + 2 < nk, kt + 1 < nk, ra0, rb0, ra1, rb1);
+        if (kt + 1 < nk) {
+            iter(kt + 1, kt + 3 < nk, kt + 2 < nk, ra1, rb1, ra0, rb0);
+            if (kt + 2 < nk) iter(kt + 2, false, false, ra0, rb0, ra1, rb1);
+        }
     }
 
     // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and

@@ -397,7 +397,7 @@ __attribute__((visibility("default"))) moe_status_t moe_profile_stream_read(cons
                                                                             size_t bytes,
                                                                             void* stream) {
     if (!buf) return MOE_ERR_NULL;
-    if (bytes == 0 || bytes % 16384) return MOE_ERR_SHAPE;
+    if (bytes == 0 || bytes % 32768) return MOE_ERR_SHAPE;
     if ((uintptr_t)buf % 16) return MOE_ERR_ALIGN;
     moe_status_t st = device_ok();
     if (st != MOE_OK) return st;

@@ -190,7 +190,7 @@ const char* moe_profile_slot_name(int32_t slot);
  * aligned, contents irrelevant, never written), on `stream`.  Timed by the
  * caller, it gives the device's practical HBM read rate, the ceiling that the
  * HBM-bound kernels are compared with beside the nominal peak.  Errors:
- * MOE_ERR_NULL, MOE_ERR_SHAPE (bytes not a positive multiple of 16384),
+ * MOE_ERR_NULL, MOE_ERR_SHAPE (bytes not a positive multiple of 32768),
  * MOE_ERR_ALIGN, MOE_ERR_NO_DEVICE / MOE_ERR_DEVICE_ARCH, MOE_ERR_HIP. */
 moe_status_t moe_profile_stream_read(const void* buf, size_t bytes, void* stream);
 

@@ -158,13 +158,13 @@ def test_segment_helper():
 
 def test_stream_read_validation():
     f = moe.lib().moe_profile_stream_read
-    assert f(None, ctypes.c_size_t(16384), None) == 1
+    assert f(None, ctypes.c_size_t(32768), None) == 1
     assert f(ctypes.c_void_p(4096), ctypes.c_size_t(0), None) == 2
-    assert f(ctypes.c_void_p(4096), ctypes.c_size_t(16384 + 16), None) == 2
-    assert f(ctypes.c_void_p(4096 + 8), ctypes.c_size_t(16384), None) == 3
+    assert f(ctypes.c_void_p(4096), ctypes.c_size_t(32768 + 16), None) == 2
+    assert f(ctypes.c_void_p(4096 + 8), ctypes.c_size_t(32768), None) == 3
     torch = pytest.importorskip("torch")
     if torch.cuda.device_count() == 0:
-        assert f(ctypes.c_void_p(4096), ctypes.c_size_t(16384), None) == 5
+        assert f(ctypes.c_void_p(4096), ctypes.c_size_t(32768), None) == 5
 
 
 def _fwd8(shape, ws_bytes=1 << 40, **over):

@@ -193,4 +193,4 @@ def test_stream_read_runs_and_writes_nothing():
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
     with pytest.raises(moe.MoEError):
-        moe.stream_read(buf[: 16384 + 16])
+        moe.stream_read(buf[: 32768 + 16])
