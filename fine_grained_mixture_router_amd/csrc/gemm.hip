@@ -16,9 +16,9 @@
 // (G2).  Tiles are BM x BN with BK = 64, staged through LDS (double buffer,
 // XOR-swizzled 16-byte chunks) and consumed by v_mfma_f32_32x32x16_bf16.
 // The grid is the work-list bound; workgroups past the device-side count
-// exit at once.  Workgroup ids are dealt round-robin over the 8 XCDs, so the
-// tiles one XCD runs together share A rows (same M-tile, alternate N-tiles)
-// in its L2; an XCD-contiguous remap is available (MOE_XCD_REMAP).
+// exit at once.  Workgroup ids are remapped so that each XCD (ids are dealt
+// round-robin over the 8 XCDs) takes runs of consecutive work-list tiles,
+// whose A rows and weight rows its L2 then shares.
 #include "common.h"
 
 namespace moe {
@@ -358,11 +358,10 @@ constexpr int kBig = 256;
 // Configuration of the many-rows tile (measured on MI355X, V3-shape prefill):
 // BK = 64 (128-byte row segments) with two LDS stages, 8 waves (two per
 // SIMD, so one issues MFMAs while its sibling waits on loads or LDS), and
-// the work list dispatched in its own order (the XCD-contiguous remap was
-// within +-3 % and slightly slower).
-#ifndef MOE_XCD_REMAP
-#define MOE_XCD_REMAP 0
-#endif
+// runs of 16 consecutive tiles per XCD (3 % faster than the list dealt
+// tile by tile, which shares fewer panels in each L2, and than one
+// contiguous slice per XCD, which leaves the XCDs unevenly loaded at the end).
+constexpr int kXcdChunk = 16;
 #ifndef MOE_BIG_WAVES
 #define MOE_BIG_WAVES 8
 #endif
@@ -420,13 +419,16 @@ void gemm_big_kernel(GemmParams P) {
 
     const int nt = *P.ntiles;
     const int wg = blockIdx.x;
-    const int nr = (nt + 7) & ~7;
+    // XCD-aware order: workgroup ids are dealt round-robin over the 8 XCDs,
+    // so the j-th workgroup of XCD x is id 8 j + x; it takes tile
+    // (j / kXcdChunk) * 8 kXcdChunk + x * kXcdChunk + j % kXcdChunk.  Each
+    // XCD thus works through runs of kXcdChunk consecutive work-list tiles
+    // (sharing A and weight panels in its own L2), and the runs are dealt out
+    // in turn, so every XCD keeps drawing from the whole list.
+    const int nr = (nt + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
     if (wg >= nr) return;
-#if MOE_XCD_REMAP
-    const int lt = (wg & 7) * (nr >> 3) + (wg >> 3);
-#else
-    const int lt = wg;
-#endif
+    const int jx = wg >> 3;
+    const int lt = (jx / kXcdChunk) * (8 * kXcdChunk) + (wg & 7) * kXcdChunk + jx % kXcdChunk;
     if (lt >= nt) return;
     const Tile tl = P.tiles[lt];
 
@@ -698,7 +700,7 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.abytes_s = gp.abytes_r;
     if (p.g1.bm == 256) {
         if (q8) return hipErrorInvalidValue;       // 8-bit plans use the thin tiles
-        const int grid = (p.max_tiles1 + 7) & ~7;
+        const int grid = (p.max_tiles1 + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
         gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
             <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
@@ -735,7 +737,7 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
     gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
     if (p.g2.bm == 256) {
         if (q8) return hipErrorInvalidValue;
-        const int grid = (p.max_tiles2 + 7) & ~7;
+        const int grid = (p.max_tiles2 + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
         gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
             <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();

@@ -56,7 +56,7 @@ __device__ int block_exclusive_scan(int v, int* swave, int* total) {
 // Work-list entry i of a group with mt M-tiles and nt N-tiles, in
 // "kGroupM M-tiles x all N-tiles" blocks: consecutive entries share either
 // the A rows or the weight rows, which keeps the L2 of one XCD warm (each XCD
-// takes a contiguous slice of the list, see the GEMM kernel).
+// takes runs of consecutive entries, see the GEMM kernels).
 __device__ Tile tile_at(int i, int g, int nrows_g, int bm, int bn_out, int mt, int nt) {
     const int b = i / (kGroupM * nt);
     const int j = i - b * kGroupM * nt;
