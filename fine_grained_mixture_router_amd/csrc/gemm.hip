@@ -68,13 +68,19 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 
 // BM x BN tile, WM x WN waves.  SWIGLU: the BN B-rows are BN/2 rows of W1
 // followed by the same BN/2 rows of W3, and the output has BN/2 columns.
+//
+// bf16 weights: each BK slice is loaded into registers two iterations ahead
+// (two register sets), stored to the LDS double buffer, and multiplied.
+//
 // Q8: the tile's weights are 8-bit E4M3 codes with one float scale per
-// weight row (a routed expert's matrices in moe_forward_fp8): each thread
-// loads 64-byte row pieces (64 codes = one BK slice), widens them to bf16
-// exactly on the way into LDS — so the LDS layout and the MFMA fragments are
-// those of the bf16 path — and the scale multiplies the fp32 accumulator of
-// its output column in the epilogue (the scale is per output channel, so it
-// factors out of the reduction).
+// weight row (a routed expert's matrices in moe_forward_fp8).  Codes are
+// loaded a slice pair at a time — 128 codes, one whole 128-byte line, per
+// row — so that they can stream with the nontemporal policy; each half is
+// widened exactly to bf16 on its way into LDS when its slice's turn comes,
+// so the LDS layout and the MFMA fragments are those of the bf16 path.  The
+// scale multiplies the fp32 accumulator of its output column in the
+// epilogue (the scale is per output channel, so it factors out of the
+// reduction).
 template <int BM, int BN, int WM, int WN, bool SWIGLU, bool Q8>
 __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, bf16_t* sA,
                                           bf16_t* sB) {
@@ -84,9 +90,9 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
     constexpr int MB = WROWS / 32;
     constexpr int NB = WCOLS / 32;
     static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile shape");
-    constexpr int AL = BM / 32;                    // A chunks per thread per stage
-    constexpr int BL = Q8 ? BN / 64 : BN / 32;     // B chunks per thread per stage
-    static_assert(!Q8 || BN == 256, "the 8-bit row mapping assumes 256 B-rows");
+    constexpr int AL = BM / 32;                    // A chunks per thread per slice
+    constexpr int BL = BN / 32;                    // B chunks per thread per slice (bf16) or pair (8-bit)
+    static_assert(!Q8 || AL == 1, "the 8-bit path loads one A chunk per thread per slice");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -104,7 +110,7 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
     // byte offset per lane, the k position in the scalar offset.  Rows past
     // the tile's end are clamped to its first row and weight rows past the
     // output width to the last one, so every access stays inside its tensor
-    // (those rows are never stored).
+    // (those rows are never stored); loads past a resource's end return 0.
     const int ch = tid & 7;
     const __amdgpu_buffer_rsrc_t ra_src =
         make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
@@ -133,17 +139,16 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
         else arow = (uint32_t)(rrow + rr);
         aoff[i] = (arow * (uint32_t)kdim + ch * 8) * 2u;
     }
-    // bf16: thread moves 16-byte chunk ch of rows (tid >> 3) + 32 i;
-    // 8-bit: 16-byte piece c8 = tid & 3 (codes 16 c8 .. 16 c8 + 15) of rows
-    // (tid >> 2) + 64 i.  Either way i < BL/2 <=> the row is in the W1 half.
-    const int c8 = tid & 3;
+    // B: thread moves 16-byte piece ch of rows (tid >> 3) + 32 i — for bf16
+    // the 8 weights 8 ch .. 8 ch + 7 of a slice, for 8-bit the 16 codes
+    // 16 ch .. 16 ch + 15 of a slice pair (slice 2p when ch < 4, else 2p+1).
+    // i < BL/2 <=> the row is in the W1 half.
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-        const int r = Q8 ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
+        const int r = (tid >> 3) + 32 * i;
         int n = tl.n0 + ((SWIGLU && r >= BN / 2) ? r - BN / 2 : r);
         n = n < ncols ? n : ncols - 1;
-        boff[i] = Q8 ? (uint32_t)n * (uint32_t)kdim + c8 * 16u
-                     : ((uint32_t)n * (uint32_t)kdim + ch * 8) * 2u;
+        boff[i] = Q8 ? (uint32_t)n * (uint32_t)kdim + ch * 16u : ((uint32_t)n * (uint32_t)kdim + ch * 8) * 2u;
     }
 
     f32x16 acc[MB][NB];
@@ -153,16 +158,17 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
     // LDS addressing.  Every row index used below is (multiple of 8) + the
-    // lane's own (lane & 7), (tid >> 3) & 7 or (tid >> 2) & 7, so the
-    // swizzled chunk position of a lane is fixed per k16 step and the rest is
-    // a compile-time or wave-uniform row offset.
+    // lane's own (lane & 7) or (tid >> 3) & 7, so the swizzled chunk
+    // position of a lane is fixed per k16 step and the rest is a
+    // compile-time or wave-uniform row offset.
     const int srow = tid >> 3;
     const int sx = (ch ^ (srow & 7)) << 3;
     bf16_t* const a_st = sA + srow * kBK + sx;
     bf16_t* const b_st = sB + srow * kBK + sx;
-    const int qrow = tid >> 2;                     // 8-bit path: rows qrow + 64 i
-    bf16_t* const q_st0 = sB + qrow * kBK + (((2 * c8) ^ (qrow & 7)) << 3);
-    bf16_t* const q_st1 = sB + qrow * kBK + (((2 * c8 + 1) ^ (qrow & 7)) << 3);
+    // 8-bit: the 16 codes of piece ch are k16 step (ch & 3) of their slice,
+    // i.e. bf16 chunks 2 (ch & 3) and 2 (ch & 3) + 1 of the row
+    bf16_t* const q_st0 = sB + srow * kBK + (((2 * (ch & 3)) ^ (srow & 7)) << 3);
+    bf16_t* const q_st1 = sB + srow * kBK + (((2 * (ch & 3) + 1) ^ (srow & 7)) << 3);
     const int lrow = lane & 31;
     int cx[kBK / 16];
 #pragma unroll
@@ -170,45 +176,6 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
     const bf16_t* const a_ld = sA + (wm * WROWS + lrow) * kBK;
     const bf16_t* const b_ld = sB + lrow * kBK;
 
-    const int nk = kdim / kBK;
-    // Two register stages: the loads of slice kt + 2 are issued while slice kt
-    // is multiplied out of LDS, and slice kt + 1 (loaded one iteration
-    // earlier) goes to LDS at the end of the iteration — two iterations of
-    // MFMA work hide each load's latency.
-    u32x4 ra0[AL], rb0[BL], ra1[AL], rb1[BL];
-    auto gload = [&](int kt, u32x4 (&ra)[AL], u32x4 (&rb)[BL]) {
-        const uint32_t kb = (uint32_t)kt * kBK * 2u;  // byte offset of the slice in bf16 rows
-#pragma unroll
-        for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb);
-        // bf16 weights are streamed with the nontemporal policy (read once
-        // per tile); an 8-bit slice is half a 128-byte line whose other half
-        // the next slice reads, so those keep the default policy and hit L2.
-#pragma unroll
-        for (int i = 0; i < BL; ++i) {
-            const __amdgpu_buffer_rsrc_t r = (SWIGLU && i >= BL / 2) ? rw3 : rw1;
-            rb[i] = Q8 ? buf_load16(r, boff[i], kb / 2) : buf_load16_nt(r, boff[i], kb);
-        }
-    };
-    auto sstore = [&](int buf, const u32x4 (&ra)[AL], const u32x4 (&rb)[BL]) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(a_st + buf * (BM * kBK) + 32 * i * kBK) = ra[i];
-        if (Q8) {
-#pragma unroll
-            for (int i = 0; i < BL; ++i) {
-                const u32x4 q = rb[i];
-                const u32x4 lo = {e4m3x2_to_bf16x2<false>(q.x), e4m3x2_to_bf16x2<true>(q.x),
-                                  e4m3x2_to_bf16x2<false>(q.y), e4m3x2_to_bf16x2<true>(q.y)};
-                const u32x4 hi = {e4m3x2_to_bf16x2<false>(q.z), e4m3x2_to_bf16x2<true>(q.z),
-                                  e4m3x2_to_bf16x2<false>(q.w), e4m3x2_to_bf16x2<true>(q.w)};
-                *reinterpret_cast<u32x4*>(q_st0 + buf * (BN * kBK) + 64 * i * kBK) = lo;
-                *reinterpret_cast<u32x4*>(q_st1 + buf * (BN * kBK) + 64 * i * kBK) = hi;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < BL; ++i)
-                *reinterpret_cast<u32x4*>(b_st + buf * (BN * kBK) + 32 * i * kBK) = rb[i];
-        }
-    };
     auto compute = [&](int buf) {
         const bf16_t* a_b = a_ld + buf * (BM * kBK);
         const bf16_t* b_b = b_ld + buf * (BN * kBK);
@@ -236,38 +203,136 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     };
-    // iteration kt: (ca, cb) are free (their slice went to LDS last
-    // iteration) and take slice kt + 2; (na, nb) hold slice kt + 1
     // Barrier after this wave's LDS stores, without __syncthreads()'s wait
     // for every outstanding global load (which would drain the prefetch).
     auto bar = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    auto iter = [&](int kt, bool load, bool store, u32x4 (&ca)[AL], u32x4 (&cb)[BL],
-                    u32x4 (&na)[AL], u32x4 (&nb)[BL]) {
-        if (load) gload(kt + 2, ca, cb);
-        __builtin_amdgcn_sched_barrier(0);           // the prefetch leaves before the MFMAs
-        compute(kt & 1);
-        if (store) sstore((kt + 1) & 1, na, nb);
-        bar();
+    auto store_a = [&](int buf, const u32x4 (&ra)[AL]) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(a_st + buf * (BM * kBK) + 32 * i * kBK) = ra[i];
     };
+    const int nk = kdim / kBK;
 
-    gload(0, ra0, rb0);
-    if (nk > 1) gload(1, ra1, rb1);
-    sstore(0, ra0, rb0);
-    bar();
-    // Steady state, two iterations at a time (the register sets swap roles):
-    // every iteration loads and stores, so the loop body has no branch and
-    // each wait covers just the older slice.  The last one to three
-    // iterations run in the tail.
-    int kt = 0;
-    for (; kt + 3 < nk; kt += 2) {
-        iter(kt, true, true, ra0, rb0, ra1, rb1);
-        iter(kt + 1, true, true, ra1, rb1, ra0, rb0);
-    }
-    if (kt < nk) {
-        iter(kt, kt + 2 < nk, kt + 1 < nk, ra0, rb0, ra1, rb1);
-        if (kt + 1 < nk) {
-            iter(kt + 1, kt + 3 < nk, kt + 2 < nk, ra1, rb1, ra0, rb0);
-            if (kt + 2 < nk) iter(kt + 2, false, false, ra0, rb0, ra1, rb1);
+    if constexpr (!Q8) {
+        // Two register sets: iteration kt loads slice kt + 2 into the free
+        // set, multiplies slice kt out of LDS and stores slice kt + 1 (loaded
+        // one iteration earlier) to the other LDS buffer — two iterations of
+        // MFMA work hide each load's latency.
+        u32x4 ra0[AL], rb0[BL], ra1[AL], rb1[BL];
+        auto gload = [&](int kt, u32x4 (&ra)[AL], u32x4 (&rb)[BL]) {
+            const uint32_t kb = (uint32_t)kt * kBK * 2u;
+#pragma unroll
+            for (int i = 0; i < AL; ++i) ra[i] = buf_load16(ra_src, aoff[i], kb);
+#pragma unroll
+            for (int i = 0; i < BL; ++i)            // weights: read once, streamed
+                rb[i] = buf_load16_nt((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], kb);
+        };
+        auto sstore = [&](int buf, const u32x4 (&ra)[AL], const u32x4 (&rb)[BL]) {
+            store_a(buf, ra);
+#pragma unroll
+            for (int i = 0; i < BL; ++i)
+                *reinterpret_cast<u32x4*>(b_st + buf * (BN * kBK) + 32 * i * kBK) = rb[i];
+        };
+        auto iter = [&](int kt, bool load, bool store, u32x4 (&ca)[AL], u32x4 (&cb)[BL],
+                        u32x4 (&na)[AL], u32x4 (&nb)[BL]) {
+            if (load) gload(kt + 2, ca, cb);
+            __builtin_amdgcn_sched_barrier(0);       // the prefetch leaves before the MFMAs
+            compute(kt & 1);
+            if (store) sstore((kt + 1) & 1, na, nb);
+            bar();
+        };
+        gload(0, ra0, rb0);
+        if (nk > 1) gload(1, ra1, rb1);
+        sstore(0, ra0, rb0);
+        bar();
+        // Steady state, two iterations at a time (the register sets swap
+        // roles): every iteration loads and stores, so the loop body has no
+        // branch and each wait covers just the older slice.  The last one to
+        // three iterations run in the tail.
+        int kt = 0;
+        for (; kt + 3 < nk; kt += 2) {
+            iter(kt, true, true, ra0, rb0, ra1, rb1);
+            iter(kt + 1, true, true, ra1, rb1, ra0, rb0);
+        }
+        if (kt < nk) {
+            iter(kt, kt + 2 < nk, kt + 1 < nk, ra0, rb0, ra1, rb1);
+            if (kt + 1 < nk) {
+                iter(kt + 1, kt + 3 < nk, kt + 2 < nk, ra1, rb1, ra0, rb0);
+                if (kt + 2 < nk) iter(kt + 2, false, false, ra0, rb0, ra1, rb1);
+            }
+        }
+    } else {
+        // Slice pairs.  Register set p & 1 holds pair p: its codes and the A
+        // chunks of its two slices.  Iteration kt multiplies slice kt and
+        // stores slice kt + 1; after an even iteration (slice 2p + 1, the
+        // pair's last half, just stored) the set is free and takes pair
+        // p + 2, three iterations before its first half is stored.
+        const int np = (nk + 1) / 2;                // an odd nk leaves the last pair half-used
+        u32x4 qa0[2], qb0[BL], qa1[2], qb1[BL];
+        auto gload = [&](int p, u32x4 (&qa)[2], u32x4 (&qb)[BL]) {
+            const uint32_t kb = (uint32_t)p * (2 * kBK * 2u);   // A: bytes of two bf16 slices
+            qa[0] = buf_load16(ra_src, aoff[0], kb);
+            qa[1] = buf_load16(ra_src, aoff[0], kb + kBK * 2u);
+#pragma unroll
+            for (int i = 0; i < BL; ++i)            // codes: whole 128-byte lines, streamed
+                qb[i] = buf_load16_nt((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], kb / 2);
+        };
+        // slice with parity `half` of the pair in (qa, qb) to LDS buffer buf
+        auto sstore = [&](int buf, int half, const u32x4 (&qa)[2], const u32x4 (&qb)[BL]) {
+            const u32x4 ra[1] = {qa[half]};
+            store_a(buf, ra);
+            if ((ch >> 2) == half) {
+#pragma unroll
+                for (int i = 0; i < BL; ++i) {
+                    const u32x4 q = qb[i];
+                    const u32x4 lo = {e4m3x2_to_bf16x2<false>(q.x), e4m3x2_to_bf16x2<true>(q.x),
+                                      e4m3x2_to_bf16x2<false>(q.y), e4m3x2_to_bf16x2<true>(q.y)};
+                    const u32x4 hi = {e4m3x2_to_bf16x2<false>(q.z), e4m3x2_to_bf16x2<true>(q.z),
+                                      e4m3x2_to_bf16x2<false>(q.w), e4m3x2_to_bf16x2<true>(q.w)};
+                    *reinterpret_cast<u32x4*>(q_st0 + buf * (BN * kBK) + 32 * i * kBK) = lo;
+                    *reinterpret_cast<u32x4*>(q_st1 + buf * (BN * kBK) + 32 * i * kBK) = hi;
+                }
+            }
+        };
+        // even iteration 2p: store slice 2p + 1 (set p) to buffer 1, reload
+        // set p with pair p + 2, multiply slice 2p (buffer 0); odd iteration
+        // 2p + 1: store slice 2p + 2 (first half of pair p + 1) to buffer 0,
+        // multiply slice 2p + 1.  The buffer stored to was last read before
+        // the previous barrier, so stores and loads go out ahead of the MFMAs.
+        auto even = [&](int p, bool store, bool load, u32x4 (&ca)[2], u32x4 (&cb)[BL]) {
+            if (store) sstore(1, 1, ca, cb);
+            if (load) gload(p + 2, ca, cb);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            bar();
+        };
+        auto odd = [&](bool store, u32x4 (&na)[2], u32x4 (&nb)[BL]) {
+            if (store) sstore(0, 0, na, nb);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            bar();
+        };
+        gload(0, qa0, qb0);
+        if (np > 1) gload(1, qa1, qb1);
+        sstore(0, 0, qa0, qb0);
+        bar();
+        // Steady state: two pairs (four slices) per trip with every store and
+        // load present; the tail takes what is left with runtime checks.
+        int p = 0;
+        for (; 2 * p + 7 < 2 * np && 2 * p + 4 < nk; p += 2) {
+            even(p, true, true, qa0, qb0);
+            odd(true, qa1, qb1);
+            even(p + 1, true, true, qa1, qb1);
+            odd(true, qa0, qb0);
+        }
+        for (int kt = 2 * p; kt < nk; ++kt) {
+            const int pp = kt >> 1;
+            if ((kt & 1) == 0) {
+                if (pp & 1) even(pp, kt + 1 < nk, pp + 2 < np, qa1, qb1);
+                else even(pp, kt + 1 < nk, pp + 2 < np, qa0, qb0);
+            } else {
+                if (pp & 1) odd(kt + 1 < nk, qa0, qb0);
+                else odd(kt + 1 < nk, qa1, qb1);
+            }
         }
     }
 
