@@ -9,6 +9,13 @@
 
 using namespace moe;
 
+#ifndef MOE_ROUTER_WGS
+#define MOE_ROUTER_WGS 512
+#endif
+#ifndef MOE_ROUTER_MINK
+#define MOE_ROUTER_MINK 4
+#endif
+
 static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID,
               "gating flag bits");
 
@@ -57,9 +64,14 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
     p->Epad = (s->E + kRouterBE - 1) / kRouterBE * kRouterBE;
     p->nchunk = (s->T + kChunk - 1) / kChunk;
     const int nk = s->d / 64;
-    const int rtiles = ((s->T + kRouterBT - 1) / kRouterBT) * (p->Epad / kRouterBE);
-    int split = (256 + rtiles - 1) / rtiles;
-    split = split < 1 ? 1 : (split > nk ? nk : split);
+    // Router: a tile covers 64 tokens and every expert; the d range is split
+    // so that the launch has about kRouterWGs workgroups (two per CU, which
+    // its 80 KB of LDS allows), each split keeping at least kRouterMinK
+    // slices of 64.
+    const int rtiles = (s->T + kRouterBT - 1) / kRouterBT;
+    const int kmax = nk / MOE_ROUTER_MINK > 0 ? nk / MOE_ROUTER_MINK : 1;
+    int split = (MOE_ROUTER_WGS + rtiles - 1) / rtiles;
+    split = split < 1 ? 1 : (split > kmax ? kmax : split);
     const int kps = (nk + split - 1) / split;
     p->split = (nk + kps - 1) / kps;
     const long long TK = (long long)s->T * s->K;

@@ -11,8 +11,8 @@
 //
 // Two kernels:
 //   router_logits  bf16 MFMA GEMM x[T,d] . C[E,d]^T -> fp32 partial logits.
-//                  Tiles of 64 tokens x 64 experts; for small T the d range is
-//                  split so that the launch still covers the chip, and the
+//                  Tiles of 64 tokens x all experts; for small T the d range
+//                  is split so that the launch still covers the chip, and the
 //                  partials are summed in a fixed order by the next kernel.
 //   router_select  one wavefront per token (16 per workgroup): sum partials,
 //                  then the gate — softmax of logit + bias (default), or
@@ -31,94 +31,126 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// 64 rows x 64 bf16 of a row-major tile, one 16-byte chunk per (row, c),
-// stored at chunk position c ^ ((row >> 1) & 7).  LDS serves 16 lanes x 16
-// bytes per cycle; an MFMA fragment read puts 16 lanes on 16 consecutive
+// Rows of 64 bf16 (one BK = 64 slice), one 16-byte chunk per (row, c),
+// chunk c stored at position c ^ ((row >> 1) & 7).  LDS serves 16 lanes x
+// 16 bytes per cycle; an MFMA fragment read puts 16 lanes on 16 consecutive
 // rows at one logical chunk, and with 128-byte rows those 16 reads then
 // land in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
     return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
-__global__ __launch_bounds__(kThreads) void router_logits_kernel(
+// Affinities x . C^T for a tile of kRouterBT = 64 tokens and all Epad (<= 256)
+// experts, over the d range of split blockIdx.y, written as fp32 partials
+// [split, T, Epad].  A tile reads its token rows once and the centroids from
+// L2 (at most 3.7 MB, shared by every tile).  Four waves; wave w computes
+// experts 64 w .. 64 w + 63 for all 64 tokens (2 x 2 MFMA 32x32x16 blocks).
+// Slices of BK = 64 are staged through registers into a double buffer.
+constexpr int kRouterThreads = 256;
+constexpr int kRouterMaxE = 256;
+
+__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ C, float* __restrict__ logits,
     int T, int d, int E, int Epad, int ksteps_per_split) {
     __shared__ __attribute__((aligned(16))) bf16_t sA[2][kRouterBT * 64];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][kRouterBE * 64];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][kRouterMaxE * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
     const int t0 = blockIdx.x * kRouterBT;
-    const int e0 = blockIdx.y * kRouterBE;
-    const int split = blockIdx.z;
+    const int split = blockIdx.y;
     const int nk = d >> 6;
     const int k_begin = split * ksteps_per_split;
     const int k_end = min(nk, k_begin + ksteps_per_split);
+    const int nbl = Epad / 32;                     // B chunks per thread per slice (<= 8)
+    const bool active = 64 * wave < Epad;          // this wave's experts exist
 
-    // each thread moves 2 chunks of A and 2 of B per 64-wide k step
+    // loads: thread moves chunk ch of token rows srow + 32 i and of centroid
+    // rows srow + 32 i; rows past T or E are clamped to the last one (their
+    // results are never read)
     const int ch = tid & 7;
-    const bf16_t* pa[2];
-    const bf16_t* pb[2];
-    bool bvalid[2];
-    int rrow[2];
-    for (int i = 0; i < 2; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        rrow[i] = r;
-        const int t = min(t0 + r, T - 1);
-        pa[i] = x + (size_t)t * d + ch * 8;
-        const int e = e0 + r;
-        bvalid[i] = e < E;
-        pb[i] = C + (size_t)(bvalid[i] ? e : 0) * d + ch * 8;
-    }
+    const int srow = tid >> 3;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * (uint32_t)d * 2u);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (uint32_t)E * (uint32_t)d * 2u);
+    uint32_t aoff[2], boff[8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        aoff[i] = ((uint32_t)min(t0 + srow + 32 * i, T - 1) * (uint32_t)d + ch * 8) * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        boff[i] = ((uint32_t)min(srow + 32 * i, E - 1) * (uint32_t)d + ch * 8) * 2u;
+    const int sx = swz(srow, ch);                  // rows srow + 32 i share the swizzle
 
-    f32x16 acc = {};
-    u32x4 ra[2], rb[2];
+    u32x4 ra[2], rb[8];
     auto gload = [&](int kt) {
-        for (int i = 0; i < 2; ++i) {
-            ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + (size_t)kt * 64);
-            rb[i] = bvalid[i] ? *reinterpret_cast<const u32x4*>(pb[i] + (size_t)kt * 64)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
+        const uint32_t kb = (uint32_t)kt * 128u;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ra[i] = buf_load16(rx, aoff[i], kb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nbl) rb[i] = buf_load16(rc, boff[i], kb);
     };
     auto sstore = [&](int buf) {
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4*>(&sA[buf][swz(rrow[i], ch)]) = ra[i];
-            *reinterpret_cast<u32x4*>(&sB[buf][swz(rrow[i], ch)]) = rb[i];
-        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&sA[buf][sx + 32 * i * 64]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nbl) *reinterpret_cast<u32x4*>(&sB[buf][sx + 32 * i * 64]) = rb[i];
     };
 
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    const int lrow = lane & 31;
     if (k_begin < k_end) {
         gload(k_begin);
         sstore(0);
         __syncthreads();
         for (int kt = k_begin; kt < k_end; ++kt) {
             const int buf = (kt - k_begin) & 1;
-            if (kt + 1 < k_end) gload(kt + 1);
-            const int arow = wm * 32 + (lane & 31);
-            const int brow = wn * 32 + (lane & 31);
+            const bool more = kt + 1 < k_end;
+            if (more) gload(kt + 1);
+            if (active) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = 2 * s + (lane >> 5);
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(arow, c)]);
-                bf16x8 b = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(brow, c)]);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+                for (int st = 0; st < 4; ++st) {
+                    const int c = 2 * st + (lane >> 5);
+                    bf16x8 a[2], b[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(32 * i + lrow, c)]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        b[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(64 * wave + 32 * j + lrow, c)]);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                }
             }
-            if (kt + 1 < k_end) sstore(buf ^ 1);
+            if (more) sstore(buf ^ 1);
             __syncthreads();
         }
     }
 
-    // 32x32 accumulator: lane holds column (lane & 31), rows
+    // 32x32 accumulator: lane holds column (lane & 31) = expert, rows (tokens)
     // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
-    const int col = e0 + wn * 32 + (lane & 31);
+    if (!active) return;
     float* outp = logits + (size_t)split * T * Epad;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = t0 + wm * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-        if (row < T) outp[(size_t)row * Epad + col] = acc[r];
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = 64 * wave + 32 * j + lrow;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = t0 + 32 * i + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+                if (row < T) outp[(size_t)row * Epad + col] = acc[i][j][r];
+            }
+        }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -262,8 +294,8 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
 hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st) {
     const int nk = p.d / 64;
     const int kps = (nk + p.split - 1) / p.split;
-    dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.Epad / kRouterBE, p.split);
-    router_logits_kernel<<<grid, kThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
+    dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.split);
+    router_logits_kernel<<<grid, kRouterThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
     return hipGetLastError();
 }
 
