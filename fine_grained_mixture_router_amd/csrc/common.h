@@ -83,6 +83,7 @@ struct Plan {
     uint64_t* masks;     // [nchunk, Epad]
     int32_t* chunk_base; // [nchunk, Epad]
     int32_t* goff;       // [E + Ks + 1] row offset of each group
+    int32_t* toff;       // [2 (E + Ks + 1)] first work-list entry of each group, G1 then G2
     int32_t* tok_of;     // [rows] token of each permuted row
     int32_t* slot_of;    // [T, K] permuted row of each (token, k)
     Tile* tiles1;        // [max_tiles1]

@@ -107,6 +107,7 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
     p->masks = (uint64_t*)take((size_t)p->nchunk * p->Epad * 8);
     p->chunk_base = (int32_t*)take((size_t)p->nchunk * p->Epad * 4);
     p->goff = (int32_t*)take((size_t)(s->E + s->Ks + 1) * 4);
+    p->toff = (int32_t*)take((size_t)2 * (s->E + s->Ks + 1) * 4);
     p->tok_of = (int32_t*)take((size_t)p->rows * 4);
     p->slot_of = (int32_t*)take((size_t)TK * 4);
     p->tiles1 = (Tile*)take((size_t)p->max_tiles1 * sizeof(Tile));
@@ -130,6 +131,7 @@ void place(Plan* p, void* ws) {
     p->masks = rebase(p->masks, b);
     p->chunk_base = rebase(p->chunk_base, b);
     p->goff = rebase(p->goff, b);
+    p->toff = rebase(p->toff, b);
     p->tok_of = rebase(p->tok_of, b);
     p->slot_of = rebase(p->slot_of, b);
     p->tiles1 = rebase(p->tiles1, b);

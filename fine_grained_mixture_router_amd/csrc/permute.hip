@@ -71,11 +71,13 @@ __device__ Tile tile_at(int i, int g, int nrows_g, int bm, int bn_out, int mt, i
     return t;
 }
 
-// Fill a whole work list in parallel: entry i belongs to the last group whose
-// first entry is <= i (binary search over the exclusive tile offsets).
-__device__ void emit_list(Tile* out, int total, const int* s_off, const int* s_cnt, int G, int bm,
-                          int bn_out, int ncols_r, int ncols_s, int E) {
-    for (int i = threadIdx.x; i < total; i += kScanThreads) {
+// Fill entries first, first + stride, ... of a work list: entry i belongs to
+// the last group whose first entry is <= i (binary search over the exclusive
+// tile offsets s_off[0..G)).
+__device__ void emit_list(Tile* out, int total, int first, int stride, const int* s_off,
+                          const int* s_cnt, int G, int bm, int bn_out, int ncols_r, int ncols_s,
+                          int E) {
+    for (int i = first; i < total; i += stride) {
         int lo = 0, hi = G - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -95,8 +97,6 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int rou
     __shared__ int sbuf[kScanWaves];
     __shared__ int s_part[kQuarters][256];
     __shared__ int s_cnt[kScanThreads];
-    __shared__ int s_t1[kScanThreads];
-    __shared__ int s_t2[kScanThreads];
     const int tid = threadIdx.x;
     const int G = p.E + p.Ks;
     const int e = tid & 255;
@@ -163,26 +163,47 @@ __global__ __launch_bounds__(kScanThreads) void perm_scan_kernel(Plan p, int rou
     const int o1 = block_exclusive_scan(t1, sbuf, &tot1);
     const int o2 = block_exclusive_scan(t2, sbuf, &tot2);
     if (tid < G) {
-        s_t1[tid] = o1;
-        s_t2[tid] = o2;
+        p.toff[tid] = o1;                           // the lists themselves are filled by
+        p.toff[G + 1 + tid] = o2;                   // every workgroup of perm_scatter
     }
     if (tid == 0) {
+        p.toff[G] = tot1;
+        p.toff[2 * G + 1] = tot2;
         p.ntiles[0] = tot1;
         p.ntiles[1] = tot2;
     }
-    __syncthreads();
-    emit_list(p.tiles1, tot1, s_t1, s_cnt, G, p.g1.bm, bn1, p.I, p.Is, p.E);
-    emit_list(p.tiles2, tot2, s_t2, s_cnt, G, p.g2.bm, p.g2.bn, p.d, p.d, p.E);
 }
 
 // One workgroup per 64-token chunk: slot of every (token, k) and the token of
-// every permuted row (routed rows by expert, then the shared rows).
-__global__ __launch_bounds__(256) void perm_scatter_kernel(Plan p, int routed) {
+// every permuted row (routed rows by expert, then the shared rows).  Every
+// workgroup (at least kEmitGroups of them) also fills a strided share of the
+// two GEMM work lists from the group offsets and tile offsets perm_scan left.
+constexpr int kEmitGroups = 64;
+constexpr int kScatterThreads = 256;
+
+__global__ __launch_bounds__(kScatterThreads) void perm_scatter_kernel(Plan p, int routed) {
+    __shared__ int s_cnt[256 + 16];
+    __shared__ int s_t1[256 + 16];
+    __shared__ int s_t2[256 + 16];
+    const int G = p.E + p.Ks;
+    for (int g = threadIdx.x; g < G; g += kScatterThreads) {
+        s_cnt[g] = p.goff[g + 1] - p.goff[g];
+        s_t1[g] = p.toff[g];
+        s_t2[g] = p.toff[G + 1 + g];
+    }
+    const int tot1 = p.toff[G], tot2 = p.toff[2 * G + 1];
+    __syncthreads();
+    const int first = blockIdx.x * kScatterThreads + threadIdx.x;
+    const int stride = gridDim.x * kScatterThreads;
+    emit_list(p.tiles1, tot1, first, stride, s_t1, s_cnt, G, p.g1.bm, p.g1.bn / 2, p.I, p.Is, p.E);
+    emit_list(p.tiles2, tot2, first, stride, s_t2, s_cnt, G, p.g2.bm, p.g2.bn, p.d, p.d, p.E);
+
     const int c = blockIdx.x;
+    if (c >= p.nchunk) return;
     const int t0 = c * kChunk;
     const int nt = min(kChunk, p.T - t0);
     if (routed) {
-        for (int i = threadIdx.x; i < nt * p.K; i += blockDim.x) {
+        for (int i = threadIdx.x; i < nt * p.K; i += kScatterThreads) {
             const int tl = i / p.K;
             const int t = t0 + tl;
             const int e = p.idx[(size_t)t * p.K + (i - tl * p.K)];
@@ -194,7 +215,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(Plan p, int routed) {
         }
     }
     const int tk = p.T * p.K;
-    for (int i = threadIdx.x; i < nt * p.Ks; i += blockDim.x) {
+    for (int i = threadIdx.x; i < nt * p.Ks; i += kScatterThreads) {
         const int s = i / nt;
         const int t = t0 + (i - s * nt);
         p.tok_of[(size_t)tk + (size_t)s * p.T + t] = t;
@@ -209,7 +230,8 @@ hipError_t launch_perm_scan(const Plan& p, hipStream_t st) {
 }
 
 hipError_t launch_perm_scatter(const Plan& p, hipStream_t st) {
-    perm_scatter_kernel<<<p.nchunk, 256, 0, st>>>(p, p.K > 0 ? 1 : 0);
+    const int grid = p.nchunk > kEmitGroups ? p.nchunk : kEmitGroups;
+    perm_scatter_kernel<<<grid, kScatterThreads, 0, st>>>(p, p.K > 0 ? 1 : 0);
     return hipGetLastError();
 }
 
