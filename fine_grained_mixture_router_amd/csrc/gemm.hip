@@ -439,9 +439,9 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, bf16_t* lds
 // Workgroup barrier without the memory fence of __syncthreads(), whose
 // release semantics would wait for every outstanding load (vmcnt(0)) and
 // drain the multi-stage pipeline.  Ordering is kept explicitly: each wave
-// waits for its own stage loads first, and LDS fragment reads of a stage are
-// consumed by MFMAs before the barrier that precedes the refill of that
-// stage.  The "memory" clobber keeps the compiler from moving memory
+// waits for its own stage loads first (vmcnt), and for its own LDS fragment
+// reads of a stage (lgkmcnt(0)) before the barrier that precedes the refill
+// of that stage.  The "memory" clobber keeps the compiler from moving memory
 // accesses across it.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -640,6 +640,9 @@ void gemm_big_kernel(GemmParams P) {
     for (; kt + KSTAGES < nk; ++kt) {                // steady state: constant waits
         stage_body(kt);
         wait_vm<LOADS * (KSTAGES - 2)>();            // stage kt+1 landed
+        // this wave's reads of stage kt (the last step's fragments) have
+        // returned before the barrier after which stage kt's buffer is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(kt + KSTAGES);
