@@ -431,6 +431,7 @@ constexpr int kXcdChunk = 16;
 #define MOE_BIG_WAVES 8
 #endif
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;   // bf16 in LDS
 
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, 0, 0, 0);
@@ -458,9 +459,28 @@ __device__ __forceinline__ void wait_vm_runtime(int n) {
     else wait_vm<0>();
 }
 
+// Work-list tile of workgroup blockIdx.x for the many-rows kernels; false
+// when the workgroup has none.  XCD-aware order: workgroup ids are dealt
+// round-robin over the 8 XCDs, so the j-th workgroup of XCD x is id 8 j + x;
+// it takes tile (j / kXcdChunk) * 8 kXcdChunk + x * kXcdChunk + j % kXcdChunk.
+// Each XCD thus works through runs of kXcdChunk consecutive work-list tiles
+// (sharing A and weight panels in its own L2), and the runs are dealt out in
+// turn, so every XCD keeps drawing from the whole list.
+__device__ __forceinline__ bool fetch_tile(const GemmParams& P, Tile& tl) {
+    const int nt = *P.ntiles;
+    const int wg = blockIdx.x;
+    const int nr = (nt + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
+    if (wg >= nr) return false;
+    const int jx = wg >> 3;
+    const int lt = (jx / kXcdChunk) * (8 * kXcdChunk) + (wg & 7) * kXcdChunk + jx % kXcdChunk;
+    if (lt >= nt) return false;
+    tl = P.tiles[lt];
+    return true;
+}
+
+// One 256 x 256 tile with bf16 weights, staged through smem (KSTAGES stages).
 template <bool SWIGLU, int BK, int KSTAGES, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-void gemm_big_kernel(GemmParams P) {
+__device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, lds_bf16_t* smem) {
     constexpr int OPER = kBig * BK;                // elements of one operand tile
     constexpr int STAGE = 2 * OPER;                // A then B
     constexpr int CH = BK / 8;                     // 16-byte chunks per row
@@ -480,22 +500,7 @@ void gemm_big_kernel(GemmParams P) {
     static_assert(KSTAGES >= 2 && LOADS * (KSTAGES - 1) <= 63, "vmcnt range");
     static_assert(KSTAGES <= 4, "wait_vm_runtime covers up to three stages in flight");
     static_assert(QI >= 2 && QI % 2 == 0, "W1 / W3 halves of the load list");
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[KSTAGES * STAGE];
 
-    const int nt = *P.ntiles;
-    const int wg = blockIdx.x;
-    // XCD-aware order: workgroup ids are dealt round-robin over the 8 XCDs,
-    // so the j-th workgroup of XCD x is id 8 j + x; it takes tile
-    // (j / kXcdChunk) * 8 kXcdChunk + x * kXcdChunk + j % kXcdChunk.  Each
-    // XCD thus works through runs of kXcdChunk consecutive work-list tiles
-    // (sharing A and weight panels in its own L2), and the runs are dealt out
-    // in turn, so every XCD keeps drawing from the whole list.
-    const int nr = (nt + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
-    if (wg >= nr) return;
-    const int jx = wg >> 3;
-    const int lt = (jx / kXcdChunk) * (8 * kXcdChunk) + (wg & 7) * kXcdChunk + jx % kXcdChunk;
-    if (lt >= nt) return;
-    const Tile tl = P.tiles[lt];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -540,7 +545,7 @@ void gemm_big_kernel(GemmParams P) {
     // LDS destinations are wave-uniform: computed from a scalar base so the
     // M0 value of every load is a scalar add (no VGPR -> SGPR round trip).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_ptr_t)smem + (uint32_t)(wave * RI * BK * 2));
+        (uint32_t)(uintptr_t)smem + (uint32_t)(wave * RI * BK * 2));
     auto issue = [&](int kt) {
         const uint32_t sa = lds_base + (uint32_t)((kt % KSTAGES) * STAGE * 2);
         const uint32_t kb = (uint32_t)kt * (BK * 2);
@@ -579,14 +584,14 @@ void gemm_big_kernel(GemmParams P) {
 
     bf16x8 fa[2][4], fb[2][NB];
     auto read_frags = [&](int set, int kt, int st) {
-        const bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
-        const bf16_t* sb = sa + OPER;
+        const lds_bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
+        const lds_bf16_t* sb = sa + OPER;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            fa[set][i] = *reinterpret_cast<const bf16x8*>(sa + a_row0 + i * 32 * BK + cx[st]);
+            fa[set][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + i * 32 * BK + cx[st]);
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-            fb[set][j] = *reinterpret_cast<const bf16x8*>(sb + b_row0[j] + cx[st]);
+            fb[set][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[j] + cx[st]);
     };
     // The weight fragment is the MFMA's first operand, the activation
     // fragment its second, so the accumulator is the transposed block: lane
@@ -703,7 +708,7 @@ void gemm_big_kernel(GemmParams P) {
                     const int orow = orow_l + 32 * i;
                     const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
                     const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
-                    *reinterpret_cast<uint2*>(smem + off) = make_uint2(lo, hi);
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{lo, hi};
                 }
             }
         }
@@ -718,12 +723,283 @@ void gemm_big_kernel(GemmParams P) {
             const int cc = c - row * CPR;
             const int col = tl.n0 + cc * 8;
             if (row < tl.nrows && col < ncols) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * OC + ((cc ^ (row % CPR)) << 3));
+                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(smem + row * OC + ((cc ^ (row % CPR)) << 3));
                 *reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col) = v;
             }
         }
     }
 }
+
+// ---------------------------------------------------------------------------
+// 256 x 256 tile with 8-bit routed weights (moe_forward_fp8 on many rows per
+// expert).  Eight waves as in big_tile; the B slice of a stage is 64 E4M3
+// codes per weight row (16 KB) next to the 32 KB bf16 A slice, so three
+// 48 KB stages fit the 160 KB of LDS.  Both operands come in by
+// direct-to-LDS buffer loads: A as 8 rows x 128 B, B as 16 rows x 64 B per
+// wave instruction, each 16-byte chunk c of row r at position c ^ f(r),
+// f = (r >> 1) & 7 for A and (r >> 2) & 3 for B — conflict-free for 16
+// lanes on 16 consecutive rows.
+//
+// The order of k inside a slice is permuted the same way for both operands:
+// k16 step st = 2u + s, lane half h and element e stand for
+// k = 32 u + 16 h + 8 s + e.  A lane's 16 codes for steps 2u and 2u + 1 are
+// then one 16-byte chunk (codes 32 u + 16 h .. + 15), read once and widened
+// exactly to two bf16 fragments; its A fragment of step st is the 8-element
+// chunk 4 u + 2 h + s.  The row scales multiply the fp32 accumulators of their
+// output columns in the epilogue.
+// ---------------------------------------------------------------------------
+template <bool SWIGLU>
+__device__ __forceinline__ void big_tile_q8(const GemmParams& P, const Tile& tl,
+                                            __attribute__((address_space(3))) uint8_t* smem) {
+    constexpr int NW = 8, KS = 3, BK = 64;
+    constexpr int A_BYTES = kBig * BK * 2;          // 32 KB
+    constexpr int STAGE = A_BYTES + kBig * BK;      // + 16 KB of codes
+    constexpr int QA = 4, QB = 2;                   // load instructions per wave per stage
+    constexpr int LOADS = QA + QB;
+    constexpr int WN = NW / 2, WCOLS = kBig / WN, NB = WCOLS / 32, HB = NB / 2;
+    static_assert(KS * STAGE <= 160 * 1024, "LDS");
+    static_assert(NB == 2, "two B blocks per wave");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int kdim = P.kdim_r, ncols = P.n_r;      // routed tiles only
+    const int grow = P.goff[tl.group] + tl.m0;
+    const size_t wofs = (size_t)tl.group * ncols * kdim;
+    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(P.A_r, P.abytes_r);
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim;
+    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(P.Qa_r + wofs, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc((SWIGLU ? P.Qb_r : P.Qa_r) + wofs, wbytes);
+
+    // A: instruction j = wave + 8 q fills rows 8 j .. 8 j + 7; lane l row
+    // 8 j + l / 8, position l % 8.  B: instruction j = wave + 8 q fills rows
+    // 16 j .. 16 j + 15; lane l row 16 j + l / 4, position l % 4; SwiGLU: q = 0
+    // loads W1 rows, q = 1 the same rows of W3.
+    uint32_t aoff[QA], boff[QB];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int row = 8 * (wave + 8 * q) + lane / 8;
+        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        const int rr = row < tl.nrows ? row : 0;
+        const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(grow + rr);
+        aoff[q] = arow * (uint32_t)kdim * 2u + cb;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int row = 16 * (wave + 8 * q) + lane / 4;
+        const uint32_t cb = (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 16);
+        int n = tl.n0 + ((SWIGLU && q == 1) ? row - kBig / 2 : row);
+        n = n < ncols ? n : ncols - 1;
+        boff[q] = (uint32_t)n * (uint32_t)kdim + cb;
+    }
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)(wave * 1024));
+    auto issue = [&](int kt) {
+        const uint32_t sa = lds_base + (uint32_t)((kt % KS) * STAGE);
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, (lds_ptr_t)(uintptr_t)(sa + q * 8 * 1024), 16,
+                                                     (int)(aoff[q] + (uint32_t)kt * 128u), 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(q ? rw3 : rw1,
+                                                     (lds_ptr_t)(uintptr_t)(sa + A_BYTES + q * 8 * 1024), 16,
+                                                     (int)(boff[q] + (uint32_t)kt * 64u), 0, 0, 0);
+    };
+
+    f32x16 acc[4][NB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+    const int lrow = lane & 31;
+    const int h = lane >> 5;
+    const uint32_t a_row = (uint32_t)((wm * 128 + lrow) * 128);   // + 32 i rows
+    uint32_t ca[4];                                               // A chunk of step st
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        ca[st] = (uint32_t)(((4 * (st >> 1) + 2 * h + (st & 1)) ^ ((lrow >> 1) & 7)) << 4);
+    uint32_t b_row[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int br = SWIGLU ? ((j < HB ? 0 : kBig / 2) + wn * (WCOLS / 2)) : (wn * WCOLS + j * 32);
+        b_row[j] = (uint32_t)(A_BYTES + (br + lrow) * 64);
+    }
+    uint32_t cq[2];                                               // B chunk of step pair u
+#pragma unroll
+    for (int u = 0; u < 2; ++u) cq[u] = (uint32_t)(((2 * u + h) ^ ((lrow >> 2) & 3)) << 4);
+
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    bf16x8 fa[2][4];                                // A fragments, double-buffered by step
+    u32x4 codes[NB];                                // B codes of the next step pair
+    bf16x8 fb[2][NB];                               // widened B of steps 2u, 2u + 1
+    auto read_a = [&](int set, int kt, int st) {
+        const uint32_t base = (uint32_t)((kt % KS) * STAGE) + a_row + ca[st];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[set][i] = *reinterpret_cast<lds_bf16x8*>(smem + base + i * 32 * 128);
+    };
+    auto read_b = [&](int kt, int u) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            codes[j] = *reinterpret_cast<lds_u32x4*>(smem + (uint32_t)((kt % KS) * STAGE) + b_row[j] + cq[u]);
+    };
+    auto widen = [&]() {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const u32x4 w = codes[j];
+            const u32x4 lo = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x),
+                              e4m3x2_to_bf16x2<false>(w.y), e4m3x2_to_bf16x2<true>(w.y)};
+            const u32x4 hi = {e4m3x2_to_bf16x2<false>(w.z), e4m3x2_to_bf16x2<true>(w.z),
+                              e4m3x2_to_bf16x2<false>(w.w), e4m3x2_to_bf16x2<true>(w.w)};
+            fb[0][j] = __builtin_bit_cast(bf16x8, lo);
+            fb[1][j] = __builtin_bit_cast(bf16x8, hi);
+        }
+    };
+    auto mfmas = [&](int set, int s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[set][i], acc[i][j], 0, 0, 0);
+    };
+    // steps 0 .. 2 of stage kt (step 0's A fragments and pair 0's codes
+    // already in registers)
+    auto steps012 = [&](int kt) {
+        widen();                                     // pair 0
+        read_b(kt, 1);
+        read_a(1, kt, 1);
+        mfmas(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(0, kt, 2);
+        mfmas(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        widen();                                     // pair 1
+        read_a(1, kt, 3);
+        mfmas(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int nk = kdim / BK;
+    for (int k = 0; k < KS && k < nk; ++k) issue(k);
+    wait_vm_runtime<LOADS>(LOADS * (min(KS, nk) - 1));
+    stage_barrier();
+    read_a(0, 0, 0);
+    read_b(0, 0);
+    // Iteration kt: steps 0 .. 2, then wait for stage kt + 1 and for this
+    // wave's reads of stage kt, pass the barrier — after it stage kt's buffer
+    // is free — and issue its refill (stage kt + KS) before step 3's MFMAs,
+    // with the next stage's first reads.
+    int kt = 0;
+    for (; kt + KS < nk; ++kt) {
+        steps012(kt);
+        wait_vm<LOADS * (KS - 2)>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + KS);
+        read_a(0, kt + 1, 0);
+        read_b(kt + 1, 0);
+        mfmas(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; kt < nk; ++kt) {                          // tail: nothing left to issue
+        steps012(kt);
+        const int ahead = nk - 1 - (kt + 1);
+        wait_vm_runtime<LOADS>(LOADS * (ahead > 0 ? ahead : 0));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(0, kt + 1, 0);                        // past the end: stale, unused
+        read_b(kt + 1, 0);
+        mfmas(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue as in big_tile, each output column's accumulators first
+    // multiplied by its weight rows' scales.
+    constexpr int OC = SWIGLU ? kBig / 2 : kBig;
+    constexpr int CPR = OC / 8;
+    static_assert(kBig * OC * 2 <= KS * STAGE, "output tile fits the stage buffers");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    lds_bf16_t* sout = reinterpret_cast<lds_bf16_t*>(smem);
+    const float* sca = P.Sa_r + (size_t)tl.group * ncols;
+    const float* scb = SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : nullptr;
+    {
+        const int orow_l = wm * 128 + (lane & 31);
+        const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int ocol = ocol_l + 32 * j + 8 * r4;
+                float fa4[4], fb4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = tl.n0 + ocol + e;
+                    fa4[e] = n < ncols ? sca[n] : 0.f;
+                    fb4[e] = SWIGLU && n < ncols ? scb[n] : 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        v[e] = SWIGLU ? silu(acc[i][j][r] * fa4[e]) * (acc[i][j + HB][r] * fb4[e])
+                                      : acc[i][j][r] * fa4[e];
+                    }
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    const int orow = orow_l + 32 * i;
+                    const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(sout + off) = u32x2{lo, hi};
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    {
+        bf16_t* obase = P.O_r;
+        for (int c = tid; c < kBig * CPR; c += 64 * NW) {
+            const int row = c / CPR;
+            const int cc = c - row * CPR;
+            const int col = tl.n0 + cc * 8;
+            if (row < tl.nrows && col < ncols) {
+                const u32x4 v = *reinterpret_cast<lds_u32x4*>(sout + row * OC + ((cc ^ (row % CPR)) << 3));
+                *reinterpret_cast<u32x4*>(obase + (size_t)(grow + row) * ncols + col) = v;
+            }
+        }
+    }
+}
+
+// Many rows per expert with 8-bit routed weights: routed tiles take the
+// 8-bit tile, shared-expert tiles (bf16 weights) the bf16 one.
+template <bool SWIGLU>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_big_q8_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * (kBig * 64 * 3)];
+    Tile tl;
+    if (!fetch_tile(P, tl)) return;
+    if (tl.group < P.E)
+        big_tile_q8<SWIGLU>(P, tl, (__attribute__((address_space(3))) uint8_t*)smem);
+    else
+        big_tile<SWIGLU, 64, 2, 8>(P, tl, (lds_bf16_t*)smem);
+}
+
+template <bool SWIGLU, int BK, int KSTAGES, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void gemm_big_kernel(GemmParams P) {
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[KSTAGES * 2 * kBig * BK];
+    Tile tl;
+    if (!fetch_tile(P, tl)) return;
+    big_tile<SWIGLU, BK, KSTAGES, NW>(P, tl, (lds_bf16_t*)smem);
+}
+
 
 template <int BM, int BN, int WM, int WN, bool SWIGLU>
 hipError_t launch_cfg(const GemmParams& gp, int max_tiles, hipStream_t st) {
@@ -767,10 +1043,10 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.abytes_r = (uint32_t)((size_t)p.T * p.d * 2);
     gp.abytes_s = gp.abytes_r;
     if (p.g1.bm == 256) {
-        if (q8) return hipErrorInvalidValue;       // 8-bit plans use the thin tiles
         const int grid = (p.max_tiles1 + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
-        gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
-            <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
+        if (q8) gemm_big_q8_kernel<true><<<grid, 512, 0, st>>>(gp);
+        else gemm_big_kernel<true, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
+                 <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
     }
     return launch_cfg<32, 256, 1, 4, true>(gp, p.max_tiles1, st);
@@ -804,10 +1080,10 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
     gp.abytes_r = (uint32_t)((size_t)p.T * p.K * p.I * 2);
     gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
     if (p.g2.bm == 256) {
-        if (q8) return hipErrorInvalidValue;
         const int grid = (p.max_tiles2 + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
-        gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
-            <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
+        if (q8) gemm_big_q8_kernel<false><<<grid, 512, 0, st>>>(gp);
+        else gemm_big_kernel<false, MOE_BIG_BK, MOE_BIG_STAGES, MOE_BIG_WAVES>
+                 <<<grid, 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
     }
     return launch_cfg<32, 256, 1, 4, false>(gp, p.max_tiles2, st);

@@ -50,8 +50,9 @@ bool shape_ok(const moe_shape_t* s) {
 
 // Fill the shape-derived part of the plan and the workspace offsets (as byte
 // offsets from 0); returns the total workspace size.  q8: the routed weights
-// are 8-bit, which the thin tiles serve at every batch size.
+// are 8-bit (the same tile sizes; each has an 8-bit kernel).
 size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
+    (void)q8;
     memset(p, 0, sizeof(*p));
     p->T = s->T;
     p->d = s->d;
@@ -79,7 +80,7 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
 
     // Few rows per expert (decode-sized batches): thin tiles that stream each
     // weight once; otherwise 256x256 MFMA tiles.
-    const bool thin = q8 || TK < 64LL * s->E;
+    const bool thin = TK < 64LL * s->E;
     p->g1.bm = thin ? 32 : 256;
     p->g1.bn = 256;
     p->g2.bm = thin ? 32 : 256;

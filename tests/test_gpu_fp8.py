@@ -213,3 +213,34 @@ def test_fp8_v3_decode_shape():
     check_part(out_f64(dout)[tok], dref["out"], "delta")
     del D
     torch.cuda.empty_cache()
+
+
+def test_fp8_v3_prefill_shape():
+    """The V3-shape prefill batch (16384 tokens, Zipf(1.2) bias) with 8-bit
+    routed weights: the 256 x 256 tiles of the 8-bit kernel, shared-expert
+    tiles in bf16 within the same launch; routing of every token, the output
+    and its delta on a token sample."""
+    w = wl.WORKLOADS["v3_prefill"]
+    _log("[fp8] v3_prefill: generating inputs")
+    L = _fp8_layer(w)
+    D = _upload(L)
+    _log("[fp8] v3_prefill: uploaded")
+    out, idx, gate = _gpu(D, w.K)
+    torch.cuda.synchronize()
+    ri, rg, rm = oracle.route(L["x"], L["C"], L["bias"], w.K)
+    exempt = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), ri, rg, rm, w.K)
+    assert exempt < 0.1 * w.T
+    tok = np.unique(np.r_[0, np.random.default_rng(9).choice(w.T, 32, replace=False), w.T - 1])
+    ref = _ref(L, w.K, tok)
+    ob = bf16_bits(out)[tok]
+    check_close(synth.bf16_to_f64(ob), ref["out"])
+    check_rounding(ob, ref["out"], ref["shared"], ref["routed"], ref["margin"])
+    dout, _, _ = _gpu(D, w.K, no_residual=True)
+    torch.cuda.synchronize()
+    dref = _ref(L, w.K, tok, no_residual=True, forced_idx=idx.cpu().numpy()[tok])
+    check_part(out_f64(dout)[tok], dref["out"], "delta")
+    out2, _, _ = _gpu(D, w.K)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    del D
+    torch.cuda.empty_cache()
