@@ -7,8 +7,9 @@ with SwiGLU, down GEMM, combine) over one batch already resident in HBM.
 Headline workload: the DeepSeek-V3-shape prefill batch (T=16384 tokens,
 d=7168, 256 routed + 1 shared experts of inter 2048, top-8, Zipf(1.2) logit
 bias) — MFMA-bound.  The same layer on a 256-token decode batch (HBM-bound)
-is measured in the same run and reported under "decode", and again with
-8-bit (E4M3, per-row scaled) routed weights under "decode_fp8".  Inputs are
+is measured in the same run and reported under "decode", and both batches
+again with 8-bit (E4M3, per-row scaled) routed weights under "prefill_fp8"
+and "decode_fp8".  Inputs are
 seeded synthetic data (bf16, N(0,1) activations, N(0,0.006) weights; the
 8-bit codes are drawn as bit fields with per-row scales of a similar size).
 
@@ -46,8 +47,8 @@ CSRC = os.path.join(ROOT, "fine_grained_mixture_router_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_v3_prefill_decode.md")
 CALIB_BYTES = 1 << 30         # the calibration copy: 1 GiB read + 1 GiB written
 # kernel-name prefix -> (workload, slot) in a default run (prefill on the
-# 256x256 tile, decode on the 32x256 tile, the 8-bit decode on its 8-bit
-# instance)
+# 256x256 tile, decode on the 32x256 tile, the 8-bit batches on the 8-bit
+# instances of each)
 COUNTER_KERNELS = {
     "gemm_big_kernel<true": ("v3_prefill", "gemm_gate_up"),
     "gemm_big_kernel<false": ("v3_prefill", "gemm_down"),
@@ -55,6 +56,8 @@ COUNTER_KERNELS = {
     "grouped_gemm_kernel<32, 256, 1, 4, false, false>": ("v3_decode", "gemm_down"),
     "grouped_gemm_kernel<32, 256, 1, 4, true, true>": ("v3_decode_fp8", "gemm_gate_up"),
     "grouped_gemm_kernel<32, 256, 1, 4, false, true>": ("v3_decode_fp8", "gemm_down"),
+    "gemm_big_q8_kernel<true": ("v3_prefill_fp8", "gemm_gate_up"),
+    "gemm_big_q8_kernel<false": ("v3_prefill_fp8", "gemm_down"),
 }
 
 
@@ -67,7 +70,7 @@ def parse():
     ap.add_argument("--decode", default="v3_decode",
                     help="second workload on the same layer weights ('' to skip)")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the decode batch with 8-bit routed weights")
+                    help="skip the batches with 8-bit routed weights")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle CPU baseline (0 to skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -426,6 +429,28 @@ def main():
     }
     print(f"[bench] {w.name}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    Q8 = None
+    if not args.no_fp8:
+        # the same prefill batch with 8-bit routed weights (shared experts bf16)
+        Q8 = dict(zip(("q1", "s1", "q3", "s3", "q2", "s2"),
+                      (dev(a) for a in wl.gen_routed_fp8(w))))
+        P8 = {k: v for k, v in D.items() if k not in ("w1", "w3", "w2")}
+        P8.update(Q8)
+        rp = time_workload(w, P8, L["x"], args.steps, args.warmup)
+        cp = np.bincount(rp["idx"].ravel(), minlength=w.E)
+        kp = algorithmic_fp8(w, cp)
+        msp = rp["ms_per_step"]
+        line["prefill_fp8"] = {
+            "workload": w.name + " (8-bit E4M3 routed weights, per-row fp32 scales; shared bf16)",
+            "T": w.T, "value": round(w.T / (msp / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(msp, 4), "speedup_vs_bf16": round(ms / msp, 3),
+            "mfma_dtype": "bf16 (codes widened exactly before the products)",
+            "roofline": roofline("mfma", kp, rp["kernels"], w.name + "_fp8"),
+            "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rp["kernels"].items()},
+        }
+        del P8
+        print(f"[bench] {w.name} fp8: {msp:.3f} ms/step", file=sys.stderr, flush=True)
+
     if args.decode:
         wd = wl.WORKLOADS[args.decode]
         assert (wd.d, wd.E, wd.I, wd.Ks, wd.Is, wd.wseed) == (w.d, w.E, w.I, w.Ks, w.Is, w.wseed)
@@ -450,11 +475,11 @@ def main():
 
         if not args.no_fp8:
             # the same decode batch with 8-bit routed weights (shared experts bf16)
-            q1, s1, q3, s3, q2, s2 = wl.gen_routed_fp8(wd)
+            if Q8 is None:   # the decode batch shares the prefill batch's weights
+                Q8 = dict(zip(("q1", "s1", "q3", "s3", "q2", "s2"),
+                              (dev(a) for a in wl.gen_routed_fp8(wd))))
             D8 = {k: v for k, v in Dd.items() if k not in ("w1", "w3", "w2")}
-            for k, v in (("q1", q1), ("s1", s1), ("q3", q3), ("s3", s3), ("q2", q2), ("s2", s2)):
-                D8[k] = dev(v)
-            del q1, q3, q2
+            D8.update(Q8)
             r8 = time_workload(wd, D8, xd, args.steps, args.warmup)
             c8 = np.bincount(r8["idx"].ravel(), minlength=wd.E)
             k8 = algorithmic_fp8(wd, c8)

@@ -141,9 +141,11 @@ moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* ce
  * Arithmetic: each code is widened exactly to bf16, the expert GEMMs run in
  * bf16 with fp32 accumulation, and the row scale multiplies the fp32
  * accumulator of its output column before SwiGLU (gate/up) or before the
- * bf16 rounding of Y (down).  Every batch size runs on the few-rows tile
- * (32 rows by 256 weight rows), which streams each weight once per 32 rows:
- * the configuration for decode-sized batches. */
+ * bf16 rounding of Y (down).  The tile follows the batch as for
+ * moe_forward: few rows per expert take the 32-row tile, which streams each
+ * weight once per 32 rows; many rows take the 256 x 256 tile, which widens
+ * the codes from LDS, so the 8-bit layer costs what the bf16 one does there.
+ * Shared experts always take the bf16 tiles. */
 moe_status_t moe_forward_fp8(const moe_shape_t* shape, const void* x, const void* centroids,
                              const float* expert_bias, const void* w1q, const float* w1_scale,
                              const void* w3q, const float* w3_scale, const void* w2q,
