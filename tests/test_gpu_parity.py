@@ -167,6 +167,47 @@ def test_edge_shapes(case):
         check_part(out_f64(dout)[tok], dref["out"], "delta")
 
 
+# The many-rows tile (T*K >= 64 E) with expert row counts skewed by a strong
+# logit bias, so that groups end in ragged tiles of many sizes: remainders
+# mod 256 from 4 to 240 rows, i.e. partial and empty 32-row blocks in both
+# halves of a tile (the kernel skips the products of empty blocks).  Every
+# token is checked, not a sample.
+BIG_RAGGED = [
+    # T, d, E, I, K, Ks, Is, seed, bias scale
+    (1024, 512, 8, 256, 3, 1, 256, 0, 1.5),
+    (1536, 256, 12, 128, 4, 1, 128, 1, 1.5),
+    (2048, 256, 6, 128, 2, 2, 192, 2, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", BIG_RAGGED, ids=[f"T{c[0]}E{c[2]}K{c[4]}" for c in BIG_RAGGED])
+def test_big_tile_ragged_groups(case):
+    T, d, E, I, K, Ks, Is, seed, bscale = case
+    _log(f"[big-ragged] {case}")
+    assert T * K >= 64 * E                      # the many-rows tile serves this batch
+    L = _rand_layer(500 + seed, T, d, E, I, K, Ks, Is)
+    L["bias"] = (np.random.default_rng(900 + seed).standard_normal(E) * bscale).astype(np.float32)
+    D = upload(L)
+    out, idx, gate = gpu_forward(D, K)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    rem = np.bincount(gi.ravel(), minlength=E) % 256
+    assert (rem[(rem > 0) & (rem <= 128)]).size and (rem[rem > 128]).size
+    tok = np.arange(T)
+    ref = oracle.forward(L["x"], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"], L["ws3"],
+                         L["ws2"], K)
+    check_routing(gi, gate.cpu().numpy(), ref["idx"], ref["gate"], ref["margin"], K)
+    ob = bf16_bits(out)
+    check_close(synth.bf16_to_f64(ob), ref["out"])
+    check_rounding(ob, ref["out"], ref["shared"], ref["routed"], ref["margin"])
+    rout, ridx, _ = gpu_forward(D, K, no_residual=True, Ks=0)
+    torch.cuda.synchronize()
+    rref = oracle.forward(L["x"], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"][:0],
+                          L["ws3"][:0], L["ws2"][:0], K, no_residual=True,
+                          forced_idx=ridx.cpu().numpy()[tok])
+    check_part(out_f64(rout), rref["routed"], "routed")
+
+
 def test_errors_leave_output_untouched():
     """Validation errors launch nothing: out keeps its previous contents."""
     w = wl.WORKLOADS["tiny"]
