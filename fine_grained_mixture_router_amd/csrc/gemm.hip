@@ -582,18 +582,25 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
     // M0 value of every load is a scalar add (no VGPR -> SGPR round trip).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)smem + (uint32_t)(wave * RI * BK * 2));
-    auto issue = [&](const Ctx& c, int kt) {
+    // Load t of a stage (t < 2 QI): the A piece of instruction q = t / 2
+    // for even t, its B piece for odd t.  The slice's k offset goes in the
+    // scalar offset, so the lane offsets stay fixed over the main loop.
+    auto issue_one = [&](const Ctx& c, int kt, int t) {
         const uint32_t sa = lds_base + (uint32_t)((kt % KSTAGES) * STAGE * 2);
-        const uint32_t kb = (uint32_t)kt * (BK * 2);
-#pragma unroll
-        for (int q = 0; q < QI; ++q) {
-            const uint32_t jo = (uint32_t)(NW * q * RI * BK * 2);   // instruction j = wave + NW q
+        const int kb = kt * (BK * 2);
+        const int q = t >> 1;
+        const uint32_t jo = (uint32_t)(NW * q * RI * BK * 2);   // instruction j = wave + NW q
+        if ((t & 1) == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_ptr_t)(uintptr_t)(sa + jo), 16,
-                                                     (int)(c.aoff[q] + kb), 0, 0, 0);
+                                                     (int)c.aoff[q], kb, 0, 0);
+        else
             __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QI / 2) ? c.rw3 : c.rw1,
                                                      (lds_ptr_t)(uintptr_t)(sa + OPER * 2 + jo), 16,
-                                                     (int)(c.boff[q] + kb), 0, 0, 0);
-        }
+                                                     (int)c.boff[q], kb, 0, 0);
+    };
+    auto issue = [&](const Ctx& c, int kt) {
+#pragma unroll
+        for (int t = 0; t < 2 * QI; ++t) issue_one(c, kt, t);
     };
     // Wait until stage 0 of the tile has landed: the loads issued after it
     // are stage 1 (when the tile has two slices or more) and the next tile's
@@ -651,11 +658,25 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
                 fb[set][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[j] + cx[st]);
         }
     };
+    // Fragment read r of a step: fa[r] for r < NA, then fb[r - NA].
+    auto read_one = [&](auto na_c, int set, int kt, int st, int r) {
+        constexpr int NA = decltype(na_c)::value;
+        const lds_bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
+        const lds_bf16_t* sb = sa + OPER;
+        if (r < NA)
+            fa[set][r] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + r * 32 * BK + cx[st]);
+        else
+            fb[set][r - NA] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[r - NA] + cx[st]);
+    };
     // The weight fragment is the MFMA's first operand, the activation
     // fragment its second, so the accumulator is the transposed block: lane
     // l holds activation row (l & 31) and output columns 8i + 4(l >> 5) + j
     // (i, j = 0..3) — four runs of four consecutive columns, which the
     // epilogue writes as 8-byte pieces.
+    auto mfma_one = [&](int set, int m) {
+        const int i = m / NB, j = m % NB;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+    };
     auto mfmas = [&](auto na_c, int set) {
         constexpr int NA = decltype(na_c)::value;
 #pragma unroll
@@ -713,22 +734,21 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             stage_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            issue(c, kt + KSTAGES);
-            read_frags(na_c, 0, kt + 1, 0);
-            mfmas(na_c, (SPS - 1) & 1);
-#if MOE_INTERLEAVE
-            // the refill's loads and the next stage's first reads, spread
-            // between this step's MFMAs
-            constexpr int G = MF < 2 * NB ? MF : 2 * NB;
+            // The last step: its MFMAs, the refill's loads and the next
+            // stage's first fragment reads, in groups of one MFMA, its share
+            // of the loads and one read, each group fenced so that the order
+            // holds (left to the scheduler, the loads issue in one burst and
+            // the MFMAs wait behind them).
+            constexpr int RD = NA > 0 ? NA + NB : 0;
+            constexpr int G = MF > RD ? MF : (RD > 0 ? RD : 1);
 #pragma unroll
-            for (int k = 0; k < G; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, LOADS / (2 * NB), 0);     // VMEM loads
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // DS read
+            for (int g = 0; g < G; ++g) {
+                if (g < MF) mfma_one((SPS - 1) & 1, g);
+#pragma unroll
+                for (int t = g * LOADS / G; t < (g + 1) * LOADS / G; ++t) issue_one(c, kt + KSTAGES, t);
+                if (g < RD) read_one(na_c, 0, kt + 1, 0, g);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (MF > G) __builtin_amdgcn_sched_group_barrier(0x008, MF - G, 0);
-#endif
-            __builtin_amdgcn_sched_barrier(0);
         }
         for (; kt < nk; ++kt) {                      // tail: nothing left to issue
             stage_body(na_c, kt);
@@ -776,25 +796,32 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
         asm volatile("" : "+v"(etid));
         const int elane = etid & 63, elrow = etid & 31;
         const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (elane >> 5);   // + 32 j + 8 r4
-        // All outputs to packed bf16 first (SwiGLU in fp32), which frees
-        // half of the accumulator registers before the first pass.
+        // Four outputs (SwiGLU in fp32) as packed bf16.  With two waves per
+        // SIMD the accumulators share the register file with everything
+        // else, so all outputs are packed first, which frees half of their
+        // registers before the first pass; with one wave per SIMD they sit in
+        // the accumulator registers and are packed as they are written.
         constexpr int OB = SWIGLU ? HB : NB;         // 32-column output blocks per wave
-        u32x2 pk[4][OB][4];
+        constexpr bool PACK_FIRST = NW == 8;
+        auto pack = [&](int i, int j, int r4) {
+            float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * r4 + e;
+                v[e] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + HB][r] : acc[i][j][r];
+            }
+            return u32x2{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                         (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+        };
+        u32x2 pk[PACK_FIRST ? 4 : 1][OB][4];
+        if (PACK_FIRST) {
 #pragma unroll
-            for (int j = 0; j < OB; ++j)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    float v[4];
+                for (int j = 0; j < OB; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * r4 + e;
-                        v[e] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + HB][r] : acc[i][j][r];
-                    }
-                    pk[i][j][r4] = u32x2{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                                         (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
-                }
+                    for (int r4 = 0; r4 < 4; ++r4) pk[PACK_FIRST ? i : 0][j][r4] = pack(i, j, r4);
+        }
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             if (p > 0) {
@@ -811,7 +838,8 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
                         const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
-                        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(eb + off) = pk[i][j][r4];
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(eb + off) =
+                            PACK_FIRST ? pk[PACK_FIRST ? i : 0][j][r4] : pack(i, j, r4);
                     }
                 }
             }
@@ -936,17 +964,21 @@ __device__ __forceinline__ void big_tile_q8(const GemmParams& P, const Tile& tl,
         boff[q] = (uint32_t)n * (uint32_t)kdim + cb;
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)(wave * 1024));
-    auto issue = [&](int kt) {
+    // Load t of a stage (t < QA + QB): A pieces first, then codes; the
+    // slice's k offset goes in the scalar offset.
+    auto issue_one = [&](int kt, int t) {
         const uint32_t sa = lds_base + (uint32_t)((kt % KS) * STAGE);
+        if (t < QA)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, (lds_ptr_t)(uintptr_t)(sa + t * 8 * 1024), 16,
+                                                     (int)aoff[t], kt * 128, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(t > QA ? rw3 : rw1,
+                                                     (lds_ptr_t)(uintptr_t)(sa + A_BYTES + (t - QA) * 8 * 1024),
+                                                     16, (int)boff[t - QA], kt * 64, 0, 0);
+    };
+    auto issue = [&](int kt) {
 #pragma unroll
-        for (int q = 0; q < QA; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, (lds_ptr_t)(uintptr_t)(sa + q * 8 * 1024), 16,
-                                                     (int)(aoff[q] + (uint32_t)kt * 128u), 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < QB; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(q ? rw3 : rw1,
-                                                     (lds_ptr_t)(uintptr_t)(sa + A_BYTES + q * 8 * 1024), 16,
-                                                     (int)(boff[q] + (uint32_t)kt * 64u), 0, 0, 0);
+        for (int t = 0; t < QA + QB; ++t) issue_one(kt, t);
     };
 
     f32x16 acc[4][NB];
@@ -1000,12 +1032,21 @@ __device__ __forceinline__ void big_tile_q8(const GemmParams& P, const Tile& tl,
             fb[1][j] = __builtin_bit_cast(bf16x8, hi);
         }
     };
+    auto mfma_one = [&](int set, int s, int m) {
+        const int i = m / NB, j = m % NB;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[set][i], acc[i][j], 0, 0, 0);
+    };
     auto mfmas = [&](int set, int s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[set][i], acc[i][j], 0, 0, 0);
+        for (int m = 0; m < 4 * NB; ++m) mfma_one(set, s, m);
+    };
+    // Fragment read r of the next stage's first step: A blocks 0..3, then
+    // the codes of B blocks 0 .. NB-1.
+    auto read_one0 = [&](int kt, int r) {
+        if (r < 4)
+            fa[0][r] = *reinterpret_cast<lds_bf16x8*>(smem + (uint32_t)((kt % KS) * STAGE) + a_row + ca[0] + r * 32 * 128);
+        else
+            codes[r - 4] = *reinterpret_cast<lds_u32x4*>(smem + (uint32_t)((kt % KS) * STAGE) + b_row[r - 4] + cq[0]);
     };
     // steps 0 .. 2 of stage kt (step 0's A fragments and pair 0's codes
     // already in registers)
@@ -1041,11 +1082,15 @@ __device__ __forceinline__ void big_tile_q8(const GemmParams& P, const Tile& tl,
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(kt + KS);
-        read_a(0, kt + 1, 0);
-        read_b(kt + 1, 0);
-        mfmas(1, 1);
-        __builtin_amdgcn_sched_barrier(0);
+        // step 3's MFMAs with the refill's loads and the next stage's first
+        // reads between them, one of each per MFMA, the order fenced
+#pragma unroll
+        for (int g = 0; g < 4 * NB; ++g) {
+            mfma_one(1, 1, g);
+            if (g < QA + QB) issue_one(kt + KS, g);
+            if (g < 4 + NB) read_one0(kt + 1, g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     for (; kt < nk; ++kt) {                          // tail: nothing left to issue
         steps012(kt);
