@@ -78,10 +78,9 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 // Q8: the tile's weights are 8-bit E4M3 codes with one float scale per
 // weight row (a routed expert's matrices in moe_forward_fp8).  Codes are
 // loaded a slice pair at a time — 128 codes, one whole 128-byte line, per
-// row — so that they can stream with the nontemporal policy; each half is
-// widened exactly to bf16 on its way into LDS when its slice's turn comes,
-// so the LDS layout and the MFMA fragments are those of the bf16 path.  The
-// scale multiplies the fp32 accumulator of its output column in the
+// row — so that they can stream with the nontemporal policy; they stay
+// 8-bit in LDS and are widened exactly to bf16 after each fragment read.
+// The scale multiplies the fp32 accumulator of its output column in the
 // epilogue (the scale is per output channel, so it factors out of the
 // reduction).
 template <int BM, int BN, int WM, int WN, bool SWIGLU, bool Q8>
@@ -168,10 +167,6 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
     const int sx = (ch ^ (srow & 7)) << 3;
     bf16_t* const a_st = sA + srow * kBK + sx;
     bf16_t* const b_st = sB + srow * kBK + sx;
-    // 8-bit: the 16 codes of piece ch are k16 step (ch & 3) of their slice,
-    // i.e. bf16 chunks 2 (ch & 3) and 2 (ch & 3) + 1 of the row
-    bf16_t* const q_st0 = sB + srow * kBK + (((2 * (ch & 3)) ^ (srow & 7)) << 3);
-    bf16_t* const q_st1 = sB + srow * kBK + (((2 * (ch & 3) + 1) ^ (srow & 7)) << 3);
     const int lrow = lane & 31;
     int cx[kBK / 16];
 #pragma unroll
@@ -264,12 +259,29 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
             }
         }
     } else {
-        // Slice pairs.  Register set p & 1 holds pair p: its codes and the A
-        // chunks of its two slices.  Iteration kt multiplies slice kt and
-        // stores slice kt + 1; after an even iteration (slice 2p + 1, the
-        // pair's last half, just stored) the set is free and takes pair
-        // p + 2, three iterations before its first half is stored.
-        const int np = (nk + 1) / 2;                // an odd nk leaves the last pair half-used
+        // Slice pairs: an iteration covers 128 k.  Register set p & 1 holds
+        // pair p — its codes (one whole 128-byte line per weight row,
+        // streamed) and the two 128-byte A pieces of each row — and goes to
+        // the LDS buffer p & 1 as is: codes stay 8-bit in LDS and are widened
+        // after the fragment read, so a pair costs one barrier, half the LDS
+        // traffic of widened weights, and widening work for every lane.
+        //
+        // k order of a pair: in k16 step t (0..7) lanes 0-31 take the pair's
+        // k 8t .. 8t+7 and lanes 32-63 take k 64 + 8t .. 64 + 8t + 7, for the
+        // activations and the codes alike (the products pair up as in any
+        // order).  One 16-byte code read then serves steps 2u and 2u + 1,
+        // and an activation read is one 16-byte chunk of the row.
+        //
+        // LDS: A rows of 256 bytes (the pair's 128 bf16), chunk c at c ^
+        // (row & 15); code rows of 128 bytes, chunk c at c ^ ((row >> 1) & 7).
+        // Either way the 16 lanes of one LDS service group read 16 rows at
+        // one logical chunk and hit 16 distinct bank groups.
+        static_assert(MB == 1, "one 32-row activation block per wave");
+        constexpr int QAB = BM * 256;                // bytes of one A buffer
+        constexpr int QBB = BN * 128;                // bytes of one code buffer
+        uint8_t* const qa_lds = reinterpret_cast<uint8_t*>(sA);
+        uint8_t* const qb_lds = reinterpret_cast<uint8_t*>(sB);
+        const int np = (nk + 1) / 2;                 // an odd nk leaves the last pair half-used
         u32x4 qa0[2], qb0[BL], qa1[2], qb1[BL];
         auto gload = [&](int p, u32x4 (&qa)[2], u32x4 (&qb)[BL]) {
             const uint32_t kb = (uint32_t)p * (2 * kBK * 2u);   // A: bytes of two bf16 slices
@@ -279,62 +291,90 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
             for (int i = 0; i < BL; ++i)            // codes: whole 128-byte lines, streamed
                 qb[i] = buf_load16_nt((SWIGLU && i >= BL / 2) ? rw3 : rw1, boff[i], kb / 2);
         };
-        // slice with parity `half` of the pair in (qa, qb) to LDS buffer buf
-        auto sstore = [&](int buf, int half, const u32x4 (&qa)[2], const u32x4 (&qb)[BL]) {
-            const u32x4 ra[1] = {qa[half]};
-            store_a(buf, ra);
-            if ((ch >> 2) == half) {
+        // thread (row srow + 32 i, piece ch): A chunks ch and 8 + ch, code chunk ch
+        const int qa_st0 = srow * 256 + ((ch ^ (srow & 15)) << 4);
+        const int qa_st1 = srow * 256 + (((8 + ch) ^ (srow & 15)) << 4);
+        auto sstore = [&](int buf, const u32x4 (&qa)[2], const u32x4 (&qb)[BL]) {
+            *reinterpret_cast<u32x4*>(qa_lds + buf * QAB + qa_st0) = qa[0];
+            *reinterpret_cast<u32x4*>(qa_lds + buf * QAB + qa_st1) = qa[1];
 #pragma unroll
-                for (int i = 0; i < BL; ++i) {
-                    const u32x4 q = qb[i];
-                    const u32x4 lo = {e4m3x2_to_bf16x2<false>(q.x), e4m3x2_to_bf16x2<true>(q.x),
-                                      e4m3x2_to_bf16x2<false>(q.y), e4m3x2_to_bf16x2<true>(q.y)};
-                    const u32x4 hi = {e4m3x2_to_bf16x2<false>(q.z), e4m3x2_to_bf16x2<true>(q.z),
-                                      e4m3x2_to_bf16x2<false>(q.w), e4m3x2_to_bf16x2<true>(q.w)};
-                    *reinterpret_cast<u32x4*>(q_st0 + buf * (BN * kBK) + 32 * i * kBK) = lo;
-                    *reinterpret_cast<u32x4*>(q_st1 + buf * (BN * kBK) + 32 * i * kBK) = hi;
-                }
+            for (int i = 0; i < BL; ++i) {
+                const int r = srow + 32 * i;
+                *reinterpret_cast<u32x4*>(qb_lds + buf * QBB + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4)) = qb[i];
             }
         };
-        // even iteration 2p: store slice 2p + 1 (set p) to buffer 1, reload
-        // set p with pair p + 2, multiply slice 2p (buffer 0); odd iteration
-        // 2p + 1: store slice 2p + 2 (first half of pair p + 1) to buffer 0,
-        // multiply slice 2p + 1.  The buffer stored to was last read before
-        // the previous barrier, so stores and loads go out ahead of the MFMAs.
-        auto even = [&](int p, bool store, bool load, u32x4 (&ca)[2], u32x4 (&cb)[BL]) {
-            if (store) sstore(1, 1, ca, cb);
-            if (load) gload(p + 2, ca, cb);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0);
-            bar();
+        // fragment addressing: lane (row lrow, half h)
+        const int h = lane >> 5;
+        int qbrow[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            int bro;
+            if (SWIGLU) {
+                constexpr int half = NB / 2;
+                bro = (j < half ? 0 : BN / 2) + wn * (WCOLS / 2) + (j < half ? j : j - half) * 32;
+            } else {
+                bro = wn * WCOLS + j * 32;
+            }
+            qbrow[j] = (bro + lrow) * 128;
+        }
+        const int qaro = lrow * 256;
+        auto compute_q = [&](int buf, bool half_pair) {
+            const uint8_t* ab = qa_lds + buf * QAB + qaro;
+            const uint8_t* bb = qb_lds + buf * QBB;
+            // the second 64 k of a half-used pair lie past the row: lanes
+            // 32-63 multiply zeros there
+            const bool zero_hi = half_pair && h;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c0 = 8 * h + 2 * u;        // A chunks of steps 2u, 2u + 1
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ab + ((c0 ^ (lrow & 15)) << 4));
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ab + (((c0 + 1) ^ (lrow & 15)) << 4));
+                bf16x8 b0[NB], b1[NB];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int r = (qbrow[j] >> 7);
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(bb + qbrow[j] + (((4 * h + u) ^ ((r >> 1) & 7)) << 4));
+                    u32x4 lo = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x),
+                                e4m3x2_to_bf16x2<false>(w.y), e4m3x2_to_bf16x2<true>(w.y)};
+                    u32x4 hi = {e4m3x2_to_bf16x2<false>(w.z), e4m3x2_to_bf16x2<true>(w.z),
+                                e4m3x2_to_bf16x2<false>(w.w), e4m3x2_to_bf16x2<true>(w.w)};
+                    if (zero_hi) lo = hi = u32x4{0u, 0u, 0u, 0u};
+                    b0[j] = __builtin_bit_cast(bf16x8, lo);
+                    b1[j] = __builtin_bit_cast(bf16x8, hi);
+                }
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0[j], acc[0][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1[j], acc[0][j], 0, 0, 0);
+            }
         };
-        auto odd = [&](bool store, u32x4 (&na)[2], u32x4 (&nb)[BL]) {
-            if (store) sstore(0, 0, na, nb);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1);
+        // Iteration p: load pair p + 2 into the free register set, multiply
+        // pair p out of LDS, store pair p + 1 (loaded an iteration earlier)
+        // to the other buffer — as the bf16 path does with slices.
+        auto iter = [&](int p, bool load, bool store, u32x4 (&ca)[2], u32x4 (&cb)[BL],
+                        u32x4 (&na)[2], u32x4 (&nb)[BL]) {
+            if (load) gload(p + 2, ca, cb);
+            __builtin_amdgcn_sched_barrier(0);       // the prefetch leaves before the MFMAs
+            compute_q(p & 1, 2 * p + 1 == nk);
+            if (store) sstore((p + 1) & 1, na, nb);
             bar();
         };
         gload(0, qa0, qb0);
         if (np > 1) gload(1, qa1, qb1);
-        sstore(0, 0, qa0, qb0);
+        sstore(0, qa0, qb0);
         bar();
-        // Steady state: two pairs (four slices) per trip with every store and
-        // load present; the tail takes what is left with runtime checks.
         int p = 0;
-        for (; 2 * p + 7 < 2 * np && 2 * p + 4 < nk; p += 2) {
-            even(p, true, true, qa0, qb0);
-            odd(true, qa1, qb1);
-            even(p + 1, true, true, qa1, qb1);
-            odd(true, qa0, qb0);
+        for (; p + 3 < np; p += 2) {                 // steady state: no branch, constant waits
+            iter(p, true, true, qa0, qb0, qa1, qb1);
+            iter(p + 1, true, true, qa1, qb1, qa0, qb0);
         }
-        for (int kt = 2 * p; kt < nk; ++kt) {
-            const int pp = kt >> 1;
-            if ((kt & 1) == 0) {
-                if (pp & 1) even(pp, kt + 1 < nk, pp + 2 < np, qa1, qb1);
-                else even(pp, kt + 1 < nk, pp + 2 < np, qa0, qb0);
-            } else {
-                if (pp & 1) odd(kt + 1 < nk, qa0, qb0);
-                else odd(kt + 1 < nk, qa1, qb1);
+        if (p < np) {
+            iter(p, p + 2 < np, p + 1 < np, qa0, qb0, qa1, qb1);
+            if (p + 1 < np) {
+                iter(p + 1, p + 3 < np, p + 2 < np, qa1, qb1, qa0, qb0);
+                if (p + 2 < np) iter(p + 2, false, false, qa0, qb0, qa1, qb1);
             }
         }
     }
@@ -373,7 +413,8 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
 // with per-row scales; shared experts' tiles always take the bf16 path.
 template <int BM, int BN, int WM, int WN, bool SWIGLU, bool Q8>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2 * BM * kBK];
+    // the 8-bit path's A buffers hold slice pairs (twice the bf16 slice)
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2 * BM * kBK * (Q8 ? 2 : 1)];
     __shared__ __attribute__((aligned(16))) bf16_t sB[2 * BN * kBK];
 
     const int nt = *P.ntiles;
