@@ -76,7 +76,6 @@ struct Plan {
     int rows;        // T*K routed rows + T*Ks shared rows
     GemmCfg g1, g2;
     int max_tiles1, max_tiles2;
-    int num_cu;      // compute units of the device (persistent grids)
 
     // workspace carve-up (byte offsets while planning, then pointers)
     float* logits;       // [split, T, Epad]

@@ -15,11 +15,11 @@
 // names the tile; A rows are gathered through tok_of (G1) or read in place
 // (G2).  Tiles are BM x BN with BK = 64, staged through LDS (double buffer,
 // XOR-swizzled 16-byte chunks) and consumed by v_mfma_f32_32x32x16_bf16.
-// The few-rows kernel's grid is the work-list bound (workgroups past the
-// device-side count exit at once); the many-rows kernel is persistent, one
-// workgroup per CU.  Either way each XCD (workgroup ids are dealt
-// round-robin over the 8 XCDs) takes runs of consecutive work-list tiles,
-// whose A rows and weight rows its L2 then shares.
+// The grid is the work-list bound; workgroups past the device-side count
+// exit at once.  Workgroup ids are dealt round-robin over the 8 XCDs; the
+// many-rows kernels (and the 8-bit few-rows one) remap them so that each
+// XCD takes runs of consecutive work-list tiles, whose A rows and weight
+// rows its L2 then shares.
 #include "common.h"
 
 #include <type_traits>
@@ -31,6 +31,7 @@ constexpr int kThreads = 256;
 constexpr int kBK = 64;
 // Runs of consecutive work-list tiles per XCD (see fetch_tile).
 constexpr int kXcdChunk = 16;
+
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return row * kBK + ((chunk ^ (row & 7)) << 3);
@@ -452,9 +453,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
 // 256 x 256 tile for many rows per expert (MFMA-bound).  Eight waves, two
 // per SIMD, each 128 rows x 64 B-rows (4 x 2 blocks of 32x32x16 MFMAs, 128
 // fp32 accumulators per lane: with two waves per SIMD that is the register
-// budget, which is what bounds the tile).  The kernel is persistent: one
-// workgroup per CU runs tile after tile, loading the next tile's first slice
-// while the finished one is written out.
+// budget, which is what bounds the tile).
 //
 // Global -> LDS with direct-to-LDS buffer loads: one wave instruction moves
 // 1 KB = (1024 / row bytes) rows of one BK slice into LDS, lane l filling
@@ -462,8 +461,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
 // vector-memory path moves about 31 B/clk/CU when each row segment is 64
 // bytes, 43 with 128-byte segments and 72 for 1 KB contiguous (measured on
 // MI355X with L2-resident data), and this tile needs about 22 B/clk/CU at
-// 1.5 PFLOP/s — so the slice width BK sets the attainable rate as much as
-// the number of LDS stages (KSTAGES) that hide the load latency.
+// 1.5 PFLOP/s — so the slice width BK = 64 (128-byte segments) is kept and
+// the load latency is hidden by a ring of operand slots (big_tile).
 //
 // LDS layout of one operand tile: rows of BK bf16; a row's logical 16-byte
 // chunk c sits at position c ^ f(row), f(row) = (row / R) mod (BK / 8) with
@@ -472,21 +471,19 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
 // chunk; those 16 reads then cover the 256 bytes of LDS banks exactly once
 // (row mod R picks the row's slot, f the chunk within it): no bank conflicts.
 //
-// Within a stage the fragments of k16 step s + 1 are read under the MFMAs
+// Within a slice the fragments of k16 step s + 1 are read under the MFMAs
 // of step s; the barrier sits before the last step, so the first fragments
-// of the next stage are read, and the stage's buffer is refilled, under the
-// stage's last MFMAs.  The order is pinned with scheduling fences.
+// of the next slice are read, and the slice's slots are refilled, under the
+// slice's last MFMAs.  The order is pinned with scheduling fences.
 // ---------------------------------------------------------------------------
 constexpr int kBig = 256;
-#ifndef MOE_BIG_BK
-#define MOE_BIG_BK 64
-#endif
 #ifndef MOE_INTERLEAVE
 #define MOE_INTERLEAVE 1
 #endif
 // Configuration of the many-rows tile (measured on MI355X, V3-shape prefill):
-// BK = 64 (128-byte row segments) with two LDS stages, 8 waves (two per
-// SIMD, so one issues MFMAs while its sibling waits on loads or LDS), and
+// BK = 64 (128-byte row segments) in a ring of five 32 KB operand slots,
+// 8 waves (two per SIMD, so one issues MFMAs while its sibling waits on
+// loads or LDS), and
 // runs of 16 consecutive tiles per XCD (kXcdChunk: 3 % faster than the list
 // dealt tile by tile, which shares fewer panels in each L2, and than one
 // contiguous slice per XCD, which leaves the XCDs unevenly loaded at the end).
@@ -541,33 +538,39 @@ __device__ __forceinline__ bool fetch_tile(const GemmParams& P, Tile& tl) {
     return true;
 }
 
-// Runs 256 x 256 tiles with bf16 weights, one after another, through the
-// KSTAGES (= 2) LDS stages in smem: first `tl`, then each tile `next(t)`
-// yields until it returns false.  Between two tiles the next tile's first
-// stage is loaded into stage buffer 0 while the finished tile's outputs go
-// out through stage buffer 1, and the next tile's A-row indices (gathered
-// through tok_of) were loaded during the finished tile's main loop, so a
-// tile starts without the load latency of its first slice.
-template <bool SWIGLU, int BK, int KSTAGES, int NW, class Next>
-__device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t* smem, Next next) {
-    constexpr int OPER = kBig * BK;                // elements of one operand tile
-    constexpr int STAGE = 2 * OPER;                // A then B
+// One 256 x 256 tile with bf16 weights.
+//
+// LDS is a ring of five 32 KB slots, each holding one operand half — the
+// A or the B part of one BK = 64 slice; half h (A of slice s: h = 2s, B:
+// h = 2s + 1) lives in slot h mod 5.  Four slots hold the slice being read
+// and the next one; the fifth lets the A half of the slice after that load
+// a whole slice earlier: iteration kt issues A of slice kt + 2 from its
+// start, spread over steps 0-2 (its slot held B of slice kt - 1, free since
+// the previous barrier), and B of slice kt + 2 after the barrier that ends
+// the reads of slice kt, over step 3 (into A of slice kt's slot).  Fewer
+// loads then leave at once, and half of them have nearly two slices of MFMA
+// time to land.  (Measured on the V3-shape prefill: gate/up 6.82 -> 6.47 ms
+// and down 3.63 -> 3.57 ms against two 64 KB stages; running several tiles
+// per workgroup, with the next tile's first slice loading under the
+// epilogue, measured slower than one tile per workgroup with this ring.)
+template <bool SWIGLU, int NW>
+__device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, lds_bf16_t* smem) {
+    constexpr int BK = 64;
+    constexpr int OPER = kBig * BK;                // elements of one operand half (32 KB)
+    constexpr int NSLOT = 5;
     constexpr int CH = BK / 8;                     // 16-byte chunks per row
     constexpr int RI = 1024 / (2 * BK);            // rows per load instruction
     constexpr int R = 256 / (2 * BK);              // rows per 256 bytes of LDS
-    constexpr int NI = kBig / RI;                  // load instructions per operand per stage
+    constexpr int NI = kBig / RI;                  // load instructions per half
     constexpr int QI = NI / NW;                    // ... per wave
-    constexpr int LOADS = 2 * QI;                  // per wave per stage, both operands
-    constexpr int SPS = BK / 16;                   // k16 steps per stage
+    constexpr int SPS = BK / 16;                   // k16 steps per slice
     constexpr int WN = NW / 2;                     // waves along the B rows (2 along M)
     constexpr int WCOLS = kBig / WN;               // B-rows per wave
     constexpr int NB = WCOLS / 32;                 // 32-wide B blocks per wave
     constexpr int HB = NB / 2;                     // SwiGLU: W1 blocks (then as many W3)
-    constexpr int NRD = 4 + NB;                    // fragment reads per k16 step
     static_assert(NW == 4 || NW == 8, "waves per workgroup");
-    static_assert(BK == 32 || BK == 64, "slice width");
-    static_assert(KSTAGES == 2, "one stage buffer loads the next tile, the other drains this one");
-    static_assert(LOADS + QI <= 63, "vmcnt range");
+    static_assert(SPS == 4, "four k16 steps per slice");
+    static_assert(2 * QI <= 63, "vmcnt range");
     static_assert(QI >= 2 && QI % 2 == 0, "W1 / W3 halves of the load list");
 
     const int tid = threadIdx.x;
@@ -576,104 +579,58 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
     const int wm = wave / WN, wn = wave % WN;
 
     // Load assignment: wave w issues instructions j = w + NW q, q < QI, of
-    // each operand; instruction j fills rows RI*j .. RI*j + RI - 1.  Lane l
+    // each half; instruction j fills rows RI*j .. RI*j + RI - 1.  Lane l
     // fills position l % CH of row RI*j + l / CH, i.e. logical chunk
     // (l % CH) ^ f(row).  SwiGLU: B rows 0..127 (q < QI/2) come from W1,
     // 128..255 from W3.
-    //
-    // Per-tile state: sizes, buffer descriptors and load offsets.  setup()
-    // takes the scalars and starts the tok_of loads (G1: `aoff` holds the
-    // A row of each load instruction); finalize() computes the offsets when
-    // the tile's first loads are due, so the tok_of loads stay in flight and
-    // no per-lane state of the next tile is held through a main loop.
-    struct Ctx {
-        int kdim, ncols, nrows, n0, orow0, arow0;
-        bf16_t* obase;
-        __amdgpu_buffer_rsrc_t ra, rw1, rw3;
-        uint32_t aoff[QI], boff[QI];
-    };
-    auto setup = [&](const Tile& t, Ctx& c) {
-        const bool shared = t.group >= P.E;
-        const int s = t.group - P.E;
-        c.kdim = shared ? P.kdim_s : P.kdim_r;
-        c.ncols = shared ? P.n_s : P.n_r;
-        c.nrows = t.nrows;
-        c.n0 = t.n0;
-        const int grow = P.goff[t.group] + t.m0;
-        const int rrow = shared ? grow - P.TK : grow;
-        c.obase = shared ? P.O_s : P.O_r;
-        c.orow0 = SWIGLU ? rrow : grow;
-        c.arow0 = rrow;
-        const bf16_t* wa = shared ? P.Ba_s + (size_t)s * c.ncols * c.kdim
-                                  : P.Ba_r + (size_t)t.group * c.ncols * c.kdim;
-        const bf16_t* wb = wa;
-        if (SWIGLU)
-            wb = shared ? P.Bb_s + (size_t)s * c.ncols * c.kdim
-                        : P.Bb_r + (size_t)t.group * c.ncols * c.kdim;
-        c.ra = make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
-        const uint32_t wbytes = (uint32_t)c.ncols * (uint32_t)c.kdim * 2u;
-        c.rw1 = make_rsrc(wa, wbytes);
-        c.rw3 = make_rsrc(wb, wbytes);
-        if (SWIGLU) {
+    const bool shared = tl.group >= P.E;
+    const int s = tl.group - P.E;
+    const int kdim = shared ? P.kdim_s : P.kdim_r;
+    const int ncols = shared ? P.n_s : P.n_r;
+    const int grow = P.goff[tl.group] + tl.m0;
+    const int rrow = shared ? grow - P.TK : grow;
+    const bf16_t* wa = shared ? P.Ba_s + (size_t)s * ncols * kdim
+                              : P.Ba_r + (size_t)tl.group * ncols * kdim;
+    const bf16_t* wb = wa;
+    if (SWIGLU)
+        wb = shared ? P.Bb_s + (size_t)s * ncols * kdim : P.Bb_r + (size_t)tl.group * ncols * kdim;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * 2u;
+    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(wa, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(wb, wbytes);
+    uint32_t aoff[QI], boff[QI];
 #pragma unroll
-            for (int q = 0; q < QI; ++q) {
-                const int row = RI * (wave + NW * q) + lane / CH;
-                const int rr = row < t.nrows ? row : 0;
-                c.aoff[q] = (uint32_t)P.tok_of[grow + rr];
-            }
-        }
-    };
-    auto finalize = [&](Ctx& c) {
-        int flane = lane;
-        asm volatile("" : "+v"(flane));              // computed per tile, not hoisted
-#pragma unroll
-        for (int q = 0; q < QI; ++q) {
-            const int row = RI * (wave + NW * q) + flane / CH;
-            const uint32_t cbytes = (uint32_t)(((flane % CH) ^ ((row / R) % CH)) * 16);
-            const uint32_t arow = SWIGLU ? c.aoff[q] : (uint32_t)(c.arow0 + (row < c.nrows ? row : 0));
-            c.aoff[q] = arow * (uint32_t)c.kdim * 2u + cbytes;
-            int n = c.n0 + ((SWIGLU && q >= QI / 2) ? row - kBig / 2 : row);
-            n = n < c.ncols ? n : c.ncols - 1;
-            c.boff[q] = (uint32_t)n * (uint32_t)c.kdim * 2u + cbytes;
-        }
-    };
+    for (int q = 0; q < QI; ++q) {
+        const int row = RI * (wave + NW * q) + lane / CH;
+        const uint32_t cbytes = (uint32_t)(((lane % CH) ^ ((row / R) % CH)) * 16);
+        const int rr = row < tl.nrows ? row : 0;
+        const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(rrow + rr);
+        aoff[q] = arow * (uint32_t)kdim * 2u + cbytes;
+        int n = tl.n0 + ((SWIGLU && q >= QI / 2) ? row - kBig / 2 : row);
+        n = n < ncols ? n : ncols - 1;
+        boff[q] = (uint32_t)n * (uint32_t)kdim * 2u + cbytes;
+    }
 
     // LDS destinations are wave-uniform: computed from a scalar base so the
     // M0 value of every load is a scalar add (no VGPR -> SGPR round trip).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)smem + (uint32_t)(wave * RI * BK * 2));
-    // Load t of a stage (t < 2 QI): the A piece of instruction q = t / 2
-    // for even t, its B piece for odd t.  The slice's k offset goes in the
-    // scalar offset, so the lane offsets stay fixed over the main loop.
-    auto issue_one = [&](const Ctx& c, int kt, int t) {
-        const uint32_t sa = lds_base + (uint32_t)((kt % KSTAGES) * STAGE * 2);
-        const int kb = kt * (BK * 2);
-        const int q = t >> 1;
-        const uint32_t jo = (uint32_t)(NW * q * RI * BK * 2);   // instruction j = wave + NW q
-        if ((t & 1) == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_ptr_t)(uintptr_t)(sa + jo), 16,
-                                                     (int)c.aoff[q], kb, 0, 0);
+    auto slot = [](int h) { return h % NSLOT; };
+    // Load q of half h: the A rows of slice h / 2 for even h, else its B
+    // rows.  The slice's k offset goes in the scalar offset, so the lane
+    // offsets stay fixed over the main loop.
+    auto load_one = [&](int h, int q) {
+        const uint32_t sa = lds_base + (uint32_t)(slot(h) * OPER * 2) + (uint32_t)(NW * q * RI * BK * 2);
+        const int kb = (h >> 1) * (BK * 2);
+        if ((h & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)sa, 16, (int)aoff[q], kb, 0, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QI / 2) ? c.rw3 : c.rw1,
-                                                     (lds_ptr_t)(uintptr_t)(sa + OPER * 2 + jo), 16,
-                                                     (int)c.boff[q], kb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QI / 2) ? rw3 : rw1,
+                                                     (lds_ptr_t)(uintptr_t)sa, 16, (int)boff[q], kb, 0, 0);
     };
-    auto issue = [&](const Ctx& c, int kt) {
+    auto load_half = [&](int h) {
 #pragma unroll
-        for (int t = 0; t < 2 * QI; ++t) issue_one(c, kt, t);
-    };
-    // Wait until stage 0 of the tile has landed: the loads issued after it
-    // are stage 1 (when the tile has two slices or more) and the next tile's
-    // QI tok_of loads (when there is one and A is gathered); the epilogue's
-    // stores in between are waited for as well.
-    auto wait_stage0 = [&](bool two, bool tok) {
-        if (two) {
-            if (tok) wait_vm<LOADS + QI>();
-            else wait_vm<LOADS>();
-        } else {
-            if (tok) wait_vm<QI>();
-            else wait_vm<0>();
-        }
+        for (int q = 0; q < QI; ++q) load_one(h, q);
     };
 
     f32x16 acc[4][NB];
@@ -698,35 +655,23 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
 #pragma unroll
     for (int st = 0; st < SPS; ++st) cx[st] = ((2 * st + (lane >> 5)) ^ ((lrow / R) % CH)) << 3;
 
+    // The fragment reads and MFMAs take the number of this wave's 32-row
+    // activation blocks that hold rows of the tile (NA, a compile-time
+    // constant per main-loop instance): a ragged last tile of a group skips
+    // the products (and fragment reads) of its padding blocks.  The waves of
+    // one SIMD are one from each half of the tile's rows, so the skipped
+    // work shortens every SIMD's share alike.
     bf16x8 fa[2][4], fb[2][NB];
-    // The fragment reads and MFMAs below take the number of this wave's
-    // 32-row activation blocks that hold rows of the tile (NA, a compile-
-    // time constant per main-loop instance): a ragged last tile of a group
-    // skips the products (and fragment reads) of its padding blocks.  The
-    // waves of one SIMD are one from each half of the tile's rows, so the
-    // skipped work shortens every SIMD's share alike.
-    auto read_frags = [&](auto na_c, int set, int kt, int st) {
-        constexpr int NA = decltype(na_c)::value;
-        const lds_bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
-        const lds_bf16_t* sb = sa + OPER;
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-            fa[set][i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + i * 32 * BK + cx[st]);
-        if (NA > 0) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                fb[set][j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[j] + cx[st]);
-        }
-    };
-    // Fragment read r of a step: fa[r] for r < NA, then fb[r - NA].
+    // fragment read r of step st of slice kt: fa[r] for r < NA, then fb[r - NA]
     auto read_one = [&](auto na_c, int set, int kt, int st, int r) {
         constexpr int NA = decltype(na_c)::value;
-        const lds_bf16_t* sa = smem + (kt % KSTAGES) * STAGE;
-        const lds_bf16_t* sb = sa + OPER;
-        if (r < NA)
+        if (r < NA) {
+            const lds_bf16_t* sa = smem + slot(2 * kt) * OPER;
             fa[set][r] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + r * 32 * BK + cx[st]);
-        else
+        } else {
+            const lds_bf16_t* sb = smem + slot(2 * kt + 1) * OPER;
             fb[set][r - NA] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[r - NA] + cx[st]);
+        }
     };
     // The weight fragment is the MFMA's first operand, the activation
     // fragment its second, so the accumulator is the transposed block: lane
@@ -737,226 +682,143 @@ __device__ __forceinline__ void big_run(const GemmParams& P, Tile tl, lds_bf16_t
         const int i = m / NB, j = m % NB;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
     };
-    auto mfmas = [&](auto na_c, int set) {
-        constexpr int NA = decltype(na_c)::value;
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j],
-                                                                   0, 0, 0);
-    };
-    // One MFMA, then one LDS read, as many times as both last, then the
-    // remaining MFMAs: the reads issue in the shadow of running MFMAs.
-    auto interleave_reads = [&](auto na_c) {
-#if MOE_INTERLEAVE
-        constexpr int NA = decltype(na_c)::value;
-        constexpr int MF = NA * NB, RD = NA > 0 ? NA + NB : 0;
-        constexpr int K1 = MF < RD ? MF : RD;
-#pragma unroll
-        for (int k = 0; k < K1; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        }
-        if (MF > K1) __builtin_amdgcn_sched_group_barrier(0x008, MF - K1, 0);
-#else
-        (void)na_c;
-#endif
-    };
-    // k16 steps 0 .. SPS-2 of stage kt (step 0's fragments already in set 0)
-    auto stage_body = [&](auto na_c, int kt) {
-#pragma unroll
-        for (int st = 0; st + 1 < SPS; ++st) {
-            read_frags(na_c, (st + 1) & 1, kt, st + 1);
-            mfmas(na_c, st & 1);
-            interleave_reads(na_c);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
 
-    // Main loop of tile c (nk slices), stages 0 and 1 issued and stage 0
-    // landed.  Iteration kt: k16 steps 0 .. SPS-2 of stage kt, then wait
-    // for stage kt+1 and pass the barrier — after it no wave reads stage
-    // kt's buffer (its last step's fragments are in registers), so the
-    // refill with stage kt+KSTAGES is issued right there, before the last
-    // step's MFMAs.  A refill thus has KSTAGES - 1 stages of MFMA time to
-    // land.
-    auto main_loop = [&](auto na_c, const Ctx& c, int nk) {
+    // Main loop (nk slices), slices 0 and 1 issued and slice 0 landed.  Each k16 step is a sequence of fenced groups — one MFMA of
+    // the step, one fragment read of the next step and the group's share of
+    // the loads — so that the reads and loads issue under running MFMAs
+    // (left to the scheduler, loads leave in one burst and the MFMAs wait
+    // behind them).  Before step 3 of slice kt: wait for slice kt + 1 and
+    // for this wave's reads of slice kt, then the barrier after which slice
+    // kt's slots are free.
+    auto main_loop = [&](auto na_c, int nk) {
         constexpr int NA = decltype(na_c)::value;
         constexpr int MF = NA * NB;
-        read_frags(na_c, 0, 0, 0);
+        constexpr int RD = NA > 0 ? NA + NB : 0;
+        constexpr int G = MF > RD ? MF : (RD > 0 ? RD : 1);
+#pragma unroll
+        for (int r = 0; r < RD; ++r) read_one(na_c, 0, 0, 0, r);
         int kt = 0;
-        for (; kt + KSTAGES < nk; ++kt) {            // steady state: constant waits
-            stage_body(na_c, kt);
-            wait_vm<LOADS * (KSTAGES - 2)>();        // stage kt+1 landed
-            // this wave's reads of stage kt (the last step's fragments) have
-            // returned before the barrier after which stage kt's buffer is refilled
+        for (; kt + 2 < nk; ++kt) {                  // steady state: slice kt + 2 to issue
+#pragma unroll
+            for (int st = 0; st + 1 < SPS; ++st) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    if (g < MF) mfma_one(st & 1, g);
+                    if (g < RD) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
+                    const int t = st * G + g;        // A of slice kt + 2 over steps 0-2
+#pragma unroll
+                    for (int q = t * QI / (3 * G); q < (t + 1) * QI / (3 * G); ++q)
+                        load_one(2 * (kt + 2), q);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            wait_vm<QI>();                           // slice kt + 1 landed (A of kt + 2 may not)
+            // this wave's reads of slice kt (the last step's fragments) have
+            // returned before the barrier after which its slots are refilled
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             stage_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            // The last step: its MFMAs, the refill's loads and the next
-            // stage's first fragment reads, in groups of one MFMA, its share
-            // of the loads and one read, each group fenced so that the order
-            // holds (left to the scheduler, the loads issue in one burst and
-            // the MFMAs wait behind them).
-            constexpr int RD = NA > 0 ? NA + NB : 0;
-            constexpr int G = MF > RD ? MF : (RD > 0 ? RD : 1);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int g = 0; g < G; ++g) {            // step 3, B of slice kt + 2, slice kt + 1's first reads
                 if (g < MF) mfma_one((SPS - 1) & 1, g);
 #pragma unroll
-                for (int t = g * LOADS / G; t < (g + 1) * LOADS / G; ++t) issue_one(c, kt + KSTAGES, t);
+                for (int q = g * QI / G; q < (g + 1) * QI / G; ++q) load_one(2 * (kt + 2) + 1, q);
                 if (g < RD) read_one(na_c, 0, kt + 1, 0, g);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         for (; kt < nk; ++kt) {                      // tail: nothing left to issue
-            stage_body(na_c, kt);
-            const int ahead = nk - 1 - (kt + 1);     // stages that may still be in flight
-            wait_vm_runtime<LOADS>(LOADS * (ahead > 0 ? ahead : 0));
-            stage_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags(na_c, 0, kt + 1, 0);          // past the end: stale, unused
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(na_c, (SPS - 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // The instance for this wave's share of the tile's rows (wave-uniform).
-    auto run_tile = [&](const Ctx& c, int nk) {
-        const int na = (c.nrows - wm * 128 + 31) >> 5;
-        if (na >= 4) main_loop(std::integral_constant<int, 4>{}, c, nk);
-        else if (na == 3) main_loop(std::integral_constant<int, 3>{}, c, nk);
-        else if (na == 2) main_loop(std::integral_constant<int, 2>{}, c, nk);
-        else if (na == 1) main_loop(std::integral_constant<int, 1>{}, c, nk);
-        else main_loop(std::integral_constant<int, 0>{}, c, nk);
-    };
-
-    // Epilogue of tile c through the last stage buffer (the other one may
-    // be loading the next tile): bf16 outputs (SwiGLU applied in registers)
-    // are written to LDS PROWS rows at a time and leave as whole 16-byte row
-    // pieces, one row segment of OC * 2 bytes per CPR lanes.  In LDS, 16-byte
-    // chunk c of row r sits at position c ^ (r mod CPR), so the 32 rows one
-    // write instruction touches land in 32 different chunks.  Called after
-    // every wave is done reading the stages; returns once every wave is done
-    // reading the buffer.
-    constexpr int OC = SWIGLU ? kBig / 2 : kBig;     // output columns of the tile
-    constexpr int CPR = OC / 8;                      // 16-byte chunks per row
-    constexpr int PROWS = STAGE / OC;                // rows per pass through one stage buffer
-    constexpr int NPASS = kBig / PROWS;
-    static_assert(PROWS % 32 == 0 && kBig % PROWS == 0, "whole 32-row blocks per pass");
-    constexpr int SU = NPASS > 1 ? 2 : PROWS * CPR / (64 * NW);   // store-loop unroll
-    auto epilogue = [&](const Ctx& c) {
-        lds_bf16_t* eb = smem + (KSTAGES - 1) * STAGE;
-        // The thread's indices pass through an empty asm statement, so the
-        // addresses derived from them are computed here, per tile, rather
-        // than hoisted out of the tile loop and held (spilled) through the
-        // main loop.
-        int etid = tid;
-        asm volatile("" : "+v"(etid));
-        const int elane = etid & 63, elrow = etid & 31;
-        const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (elane >> 5);   // + 32 j + 8 r4
-        // Four outputs (SwiGLU in fp32) as packed bf16.  With two waves per
-        // SIMD the accumulators share the register file with everything
-        // else, so all outputs are packed first, which frees half of their
-        // registers before the first pass; with one wave per SIMD they sit in
-        // the accumulator registers and are packed as they are written.
-        constexpr int OB = SWIGLU ? HB : NB;         // 32-column output blocks per wave
-        constexpr bool PACK_FIRST = NW == 8;
-        auto pack = [&](int i, int j, int r4) {
-            float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * r4 + e;
-                v[e] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + HB][r] : acc[i][j][r];
-            }
-            return u32x2{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                         (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
-        };
-        u32x2 pk[PACK_FIRST ? 4 : 1][OB][4];
-        if (PACK_FIRST) {
+            for (int st = 0; st + 1 < SPS; ++st) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < OB; ++j)
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) pk[PACK_FIRST ? i : 0][j][r4] = pack(i, j, r4);
-        }
-#pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            if (p > 0) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                stage_barrier();                     // the previous pass's reads are done
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int orow = wm * 128 + 32 * i + elrow - p * PROWS;  // row within the pass
-                if ((wm * 128 + 32 * i) / PROWS != p) continue;           // wave-uniform
-#pragma unroll
-                for (int j = 0; j < OB; ++j) {
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
-                        const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
-                        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(eb + off) =
-                            PACK_FIRST ? pk[PACK_FIRST ? i : 0][j][r4] : pack(i, j, r4);
-                    }
+                for (int g = 0; g < G; ++g) {
+                    if (g < MF) mfma_one(st & 1, g);
+                    if (g < RD) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
+            wait_vm<0>();
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             stage_barrier();
-            // with passes left, the outputs of the later passes are still
-            // live: fewer stores in flight keep the registers in budget
-#pragma unroll SU
-            for (int e = etid; e < PROWS * CPR; e += 64 * NW) {
-                const int row = e / CPR;
-                const int cc = e - row * CPR;
-                const int trow = p * PROWS + row;
-                const int col = c.n0 + cc * 8;
-                if (trow < c.nrows && col < c.ncols) {
-                    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(eb + row * OC + ((cc ^ (row % CPR)) << 3));
-                    *reinterpret_cast<u32x4*>(c.obase + (size_t)(c.orow0 + trow) * c.ncols + col) = v;
+            __builtin_amdgcn_sched_barrier(0);
+            const bool more_k = kt + 1 < nk;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (g < MF) mfma_one((SPS - 1) & 1, g);
+                if (g < RD && more_k) read_one(na_c, 0, kt + 1, 0, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    const int nk = kdim / BK;
+    load_half(0);
+    load_half(1);
+    if (nk > 1) {
+        load_half(2);
+        load_half(3);
+        wait_vm<2 * QI>();                           // slice 0 landed
+    } else {
+        wait_vm<0>();
+    }
+    stage_barrier();
+    // the instance for this wave's share of the tile's rows (wave-uniform)
+    {
+        const int na = (tl.nrows - wm * 128 + 31) >> 5;
+        if (na >= 4) main_loop(std::integral_constant<int, 4>{}, nk);
+        else if (na == 3) main_loop(std::integral_constant<int, 3>{}, nk);
+        else if (na == 2) main_loop(std::integral_constant<int, 2>{}, nk);
+        else if (na == 1) main_loop(std::integral_constant<int, 1>{}, nk);
+        else main_loop(std::integral_constant<int, 0>{}, nk);
+    }
+
+    // Epilogue: the tile's outputs (bf16; SwiGLU applied in registers) go
+    // through LDS — now free — and leave as whole 16-byte row pieces, one
+    // row segment of OC * 2 bytes per CPR lanes.  In LDS, 16-byte chunk c of
+    // row r sits at position c ^ (r mod CPR), so the 32 rows one write
+    // instruction touches land in 32 different chunks.
+    constexpr int OC = SWIGLU ? kBig / 2 : kBig;     // output columns of the tile
+    constexpr int CPR = OC / 8;                      // 16-byte chunks per row
+    static_assert(kBig * OC <= NSLOT * OPER, "output tile fits the slots");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();                                 // every wave is done with the slots
+    {
+        const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (lane >> 5);   // + 32 j + 8 r4
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        v[e] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + HB][r] : acc[i][j][r];
+                    }
+                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    const int orow = wm * 128 + 32 * i + lrow;
+                    const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
+                    const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{lo, hi};
                 }
             }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        stage_barrier();
-    };
-
-    Ctx c, cn;
-    setup(tl, c);
-    finalize(c);
-    int nk = c.kdim / BK;
-    issue(c, 0);
-    if (nk > 1) issue(c, 1);
-    Tile tn;
-    bool more = next(tn);
-    if (more) setup(tn, cn);
-    wait_stage0(nk > 1, more && SWIGLU);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_barrier();
-    for (;;) {
-        run_tile(c, nk);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        stage_barrier();                             // every wave is done with the stages
-        int nk2 = 0;
-        if (more) {
-            finalize(cn);
-            nk2 = cn.kdim / BK;
-            issue(cn, 0);                            // stage buffer 0
+    {
+        bf16_t* obase = shared ? P.O_s : P.O_r;
+        const int orow0 = SWIGLU ? rrow : grow;
+        for (int c = tid; c < kBig * CPR; c += 64 * NW) {
+            const int row = c / CPR;
+            const int cc = c - row * CPR;
+            const int col = tl.n0 + cc * 8;
+            if (row < tl.nrows && col < ncols) {
+                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(smem + row * OC + ((cc ^ (row % CPR)) << 3));
+                *reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col) = v;
+            }
         }
-        epilogue(c);                                 // stage buffer 1
-        if (!more) break;
-        if (nk2 > 1) issue(cn, 1);
-        c = cn;
-        nk = nk2;
-        more = next(tn);
-        if (more) setup(tn, cn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
-        wait_stage0(nk > 1, more && SWIGLU);
-        stage_barrier();
     }
 }
 
@@ -1229,39 +1091,27 @@ __device__ __forceinline__ void big_tile_q8(const GemmParams& P, const Tile& tl,
 template <bool SWIGLU>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_big_q8_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * (kBig * 64 * 3)];
+    // three 48 KB 8-bit stages, or the bf16 tile's five 32 KB slots
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * kBig * 64 * 2];
+    static_assert(3 * (kBig * 64 * 3) <= 5 * kBig * 64 * 2, "the 8-bit stages fit");
     Tile tl;
     if (!fetch_tile(P, tl)) return;
     if (tl.group < P.E)
         big_tile_q8<SWIGLU>(P, tl, (__attribute__((address_space(3))) uint8_t*)smem);
     else
-        big_run<SWIGLU, 64, 2, 8>(P, tl, (lds_bf16_t*)smem, [](Tile&) { return false; });
+        big_tile<SWIGLU, 8>(P, tl, (lds_bf16_t*)smem);
 }
 
-template <bool SWIGLU, int BK, int KSTAGES, int NW>
+// LDS of the many-rows bf16 tile: five 32 KB operand slots (160 KB).
+constexpr int kBigLdsBytes = 5 * kBig * 64 * 2;
+
+template <bool SWIGLU, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_big_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[KSTAGES * 2 * kBig * BK];
-    // Persistent: the grid is a multiple of 8 workgroups, at most one per
-    // CU.  Workgroup u of XCD x (id 8 u + x) takes local tiles jx = u,
-    // u + G, u + 2G, ... (G workgroups per XCD), local tile jx of XCD x being
-    // work-list tile (jx / kXcdChunk) * 8 kXcdChunk + x * kXcdChunk +
-    // jx % kXcdChunk: as in fetch_tile, each XCD works through runs of
-    // consecutive tiles, the runs dealt out to the XCDs in turn.  The tile
-    // index grows with jx, so the first one past the list ends the loop.
-    const int nt = *P.ntiles;
-    const int per = gridDim.x >> 3, xcd = blockIdx.x & 7, u = blockIdx.x >> 3;
-    int it = 0;
-    auto next = [&](Tile& t) -> bool {
-        const int jx = it++ * per + u;
-        const int lt = (jx / kXcdChunk) * (8 * kXcdChunk) + xcd * kXcdChunk + jx % kXcdChunk;
-        if (lt >= nt) return false;
-        t = P.tiles[lt];
-        return true;
-    };
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kBigLdsBytes / 2];
     Tile tl;
-    if (!next(tl)) return;
-    big_run<SWIGLU, BK, KSTAGES, NW>(P, tl, (lds_bf16_t*)smem, next);
+    if (!fetch_tile(P, tl)) return;
+    big_tile<SWIGLU, NW>(P, tl, (lds_bf16_t*)smem);
 }
 
 
@@ -1269,15 +1119,6 @@ void gemm_big_kernel(GemmParams P) {
 // rounds of 8 kXcdChunk).
 int tile_grid(int max_tiles) {
     return (max_tiles + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * (8 * kXcdChunk);
-}
-
-// The persistent many-rows kernel: one workgroup per CU (a multiple of 8,
-// one share per XCD), fewer when the work list is shorter.
-int persistent_grid(const Plan& p, int max_tiles) {
-    int g = p.num_cu & ~7;
-    if (g < 8) g = 8;
-    const int t = (max_tiles + 7) & ~7;
-    return t < g ? t : g;
 }
 
 template <int BM, int BN, int WM, int WN, bool SWIGLU>
@@ -1326,8 +1167,8 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
         if (q8)
             gemm_big_q8_kernel<true><<<tile_grid(p.max_tiles1), 512, 0, st>>>(gp);
         else
-            gemm_big_kernel<true, MOE_BIG_BK, 2, MOE_BIG_WAVES>
-                <<<persistent_grid(p, p.max_tiles1), 64 * MOE_BIG_WAVES, 0, st>>>(gp);
+            gemm_big_kernel<true, MOE_BIG_WAVES>
+                <<<tile_grid(p.max_tiles1), 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
     }
     return launch_cfg<32, 256, 1, 4, true>(gp, p.max_tiles1, st);
@@ -1364,8 +1205,8 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
         if (q8)
             gemm_big_q8_kernel<false><<<tile_grid(p.max_tiles2), 512, 0, st>>>(gp);
         else
-            gemm_big_kernel<false, MOE_BIG_BK, 2, MOE_BIG_WAVES>
-                <<<persistent_grid(p, p.max_tiles2), 64 * MOE_BIG_WAVES, 0, st>>>(gp);
+            gemm_big_kernel<false, MOE_BIG_WAVES>
+                <<<tile_grid(p.max_tiles2), 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         return hipGetLastError();
     }
     return launch_cfg<32, 256, 1, 4, false>(gp, p.max_tiles2, st);

@@ -144,18 +144,16 @@ void place(Plan* p, void* ws) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// 0 unknown, 1 gfx950, 2 other architecture; and the CU count
+// 0 unknown, 1 gfx950, 2 other architecture
 std::atomic<int> g_arch[64];
-std::atomic<int> g_cus[64];
 
-moe_status_t device_ok(int* num_cu = nullptr) {
+moe_status_t device_ok() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
         (void)hipGetLastError();
         return MOE_ERR_NO_DEVICE;
     }
-    int known = dev < 64 ? g_arch[dev].load(std::memory_order_acquire) : 0;
-    int cus = dev < 64 ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+    int known = dev < 64 ? g_arch[dev].load(std::memory_order_relaxed) : 0;
     if (known == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -163,13 +161,8 @@ moe_status_t device_ok(int* num_cu = nullptr) {
             return MOE_ERR_NO_DEVICE;
         }
         known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 8;
-        if (dev < 64) {
-            g_cus[dev].store(cus, std::memory_order_relaxed);
-            g_arch[dev].store(known, std::memory_order_release);
-        }
+        if (dev < 64) g_arch[dev].store(known, std::memory_order_relaxed);
     }
-    if (num_cu) *num_cu = cus;
     return known == 1 ? MOE_OK : MOE_ERR_DEVICE_ARCH;
 }
 
@@ -275,7 +268,7 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
                         rk && q8 ? q8->s3 : nullptr, rk && q8 ? q8->s2 : nullptr};
     for (const void* a : a4)
         if (a && !aligned(a, 4)) return MOE_ERR_ALIGN;
-    st = device_ok(&p.num_cu);
+    st = device_ok();
     if (st != MOE_OK) return st;
 
     place(&p, workspace);
