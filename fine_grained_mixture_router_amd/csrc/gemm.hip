@@ -553,7 +553,7 @@ __device__ __forceinline__ bool fetch_tile(const GemmParams& P, Tile& tl) {
 // and down 3.63 -> 3.57 ms against two 64 KB stages; running several tiles
 // per workgroup, with the next tile's first slice loading under the
 // epilogue, measured slower than one tile per workgroup with this ring.)
-template <bool SWIGLU, int NW>
+template <bool SWIGLU, int NW, bool Q8 = false>
 __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, lds_bf16_t* smem) {
     constexpr int BK = 64;
     constexpr int OPER = kBig * BK;                // elements of one operand half (32 KB)
@@ -563,6 +563,9 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     constexpr int R = 256 / (2 * BK);              // rows per 256 bytes of LDS
     constexpr int NI = kBig / RI;                  // load instructions per half
     constexpr int QI = NI / NW;                    // ... per wave
+    // 8-bit B: a half is 64 codes per weight row (16 KB of its slot), one
+    // instruction moving 16 rows x 64 B
+    constexpr int QB = Q8 ? (kBig / 16) / NW : QI; // B load instructions per wave per half
     constexpr int SPS = BK / 16;                   // k16 steps per slice
     constexpr int WN = NW / 2;                     // waves along the B rows (2 along M)
     constexpr int WCOLS = kBig / WN;               // B-rows per wave
@@ -571,7 +574,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     static_assert(NW == 4 || NW == 8, "waves per workgroup");
     static_assert(SPS == 4, "four k16 steps per slice");
     static_assert(2 * QI <= 63, "vmcnt range");
-    static_assert(QI >= 2 && QI % 2 == 0, "W1 / W3 halves of the load list");
+    static_assert(QI >= 2 && QI % 2 == 0 && QB >= 2 && QB % 2 == 0, "W1 / W3 halves of the load list");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -589,16 +592,22 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     const int ncols = shared ? P.n_s : P.n_r;
     const int grow = P.goff[tl.group] + tl.m0;
     const int rrow = shared ? grow - P.TK : grow;
-    const bf16_t* wa = shared ? P.Ba_s + (size_t)s * ncols * kdim
-                              : P.Ba_r + (size_t)tl.group * ncols * kdim;
-    const bf16_t* wb = wa;
-    if (SWIGLU)
-        wb = shared ? P.Bb_s + (size_t)s * ncols * kdim : P.Bb_r + (size_t)tl.group * ncols * kdim;
+    const void* wa;
+    const void* wb;
+    if (Q8) {                                      // routed tiles only
+        wa = P.Qa_r + (size_t)tl.group * ncols * kdim;
+        wb = SWIGLU ? P.Qb_r + (size_t)tl.group * ncols * kdim : wa;
+    } else {
+        wa = shared ? P.Ba_s + (size_t)s * ncols * kdim : P.Ba_r + (size_t)tl.group * ncols * kdim;
+        wb = wa;
+        if (SWIGLU)
+            wb = shared ? P.Bb_s + (size_t)s * ncols * kdim : P.Bb_r + (size_t)tl.group * ncols * kdim;
+    }
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(shared ? P.A_s : P.A_r, shared ? P.abytes_s : P.abytes_r);
-    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * 2u;
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim * (Q8 ? 1u : 2u);
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(wa, wbytes);
     const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(wb, wbytes);
-    uint32_t aoff[QI], boff[QI];
+    uint32_t aoff[QI], boff[QB];
 #pragma unroll
     for (int q = 0; q < QI; ++q) {
         const int row = RI * (wave + NW * q) + lane / CH;
@@ -606,9 +615,17 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
         const int rr = row < tl.nrows ? row : 0;
         const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(rrow + rr);
         aoff[q] = arow * (uint32_t)kdim * 2u + cbytes;
-        int n = tl.n0 + ((SWIGLU && q >= QI / 2) ? row - kBig / 2 : row);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        // bf16: as A; 8-bit: lane l fills chunk l % 4 of row 16 j + l / 4,
+        // at position (l % 4) ^ ((row >> 2) & 3)
+        const int row = Q8 ? 16 * (wave + NW * q) + lane / 4 : RI * (wave + NW * q) + lane / CH;
+        const uint32_t cbytes = Q8 ? (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 16)
+                                   : (uint32_t)(((lane % CH) ^ ((row / R) % CH)) * 16);
+        int n = tl.n0 + ((SWIGLU && q >= QB / 2) ? row - kBig / 2 : row);
         n = n < ncols ? n : ncols - 1;
-        boff[q] = (uint32_t)n * (uint32_t)kdim * 2u + cbytes;
+        boff[q] = (uint32_t)n * (uint32_t)kdim * (Q8 ? 1u : 2u) + cbytes;
     }
 
     // LDS destinations are wave-uniform: computed from a scalar base so the
@@ -620,17 +637,18 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     // rows.  The slice's k offset goes in the scalar offset, so the lane
     // offsets stay fixed over the main loop.
     auto load_one = [&](int h, int q) {
-        const uint32_t sa = lds_base + (uint32_t)(slot(h) * OPER * 2) + (uint32_t)(NW * q * RI * BK * 2);
-        const int kb = (h >> 1) * (BK * 2);
+        const uint32_t sa = lds_base + (uint32_t)(slot(h) * OPER * 2) + (uint32_t)(NW * q * 1024);
         if ((h & 1) == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)sa, 16, (int)aoff[q], kb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)sa, 16, (int)aoff[q],
+                                                     (h >> 1) * (BK * 2), 0, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QI / 2) ? rw3 : rw1,
-                                                     (lds_ptr_t)(uintptr_t)sa, 16, (int)boff[q], kb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QB / 2) ? rw3 : rw1,
+                                                     (lds_ptr_t)(uintptr_t)sa, 16, (int)boff[q],
+                                                     (h >> 1) * (BK * (Q8 ? 1 : 2)), 0, 0);
     };
     auto load_half = [&](int h) {
 #pragma unroll
-        for (int q = 0; q < QI; ++q) load_one(h, q);
+        for (int q = 0; q < ((h & 1) ? QB : QI); ++q) load_one(h, q);
     };
 
     f32x16 acc[4][NB];
@@ -651,9 +669,25 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
                               : (wn * WCOLS + j * 32);
         b_row0[j] = (br + lrow) * BK;
     }
+    // 8-bit: the order of k inside a slice is permuted alike for both
+    // operands — step st = 2u + s, lane half h and element e stand for k =
+    // 32 u + 16 h + 8 s + e — so a lane's 16 codes for steps 2u and 2u + 1
+    // are one 16-byte chunk (codes 32 u + 16 h .. + 15), read once and
+    // widened exactly to two bf16 fragments, and its A fragment of step st
+    // is the 8-element chunk 4 u + 2 h + s.
+    const int h = lane >> 5;
     int cx[SPS];
 #pragma unroll
-    for (int st = 0; st < SPS; ++st) cx[st] = ((2 * st + (lane >> 5)) ^ ((lrow / R) % CH)) << 3;
+    for (int st = 0; st < SPS; ++st) {
+        const int chunk = Q8 ? 4 * (st >> 1) + 2 * h + (st & 1) : 2 * st + h;
+        cx[st] = (chunk ^ ((lrow / R) % CH)) << 3;
+    }
+    int qb_row[NB];                                 // 8-bit: byte offset of the lane's code row
+    uint32_t cq[2];                                 // 8-bit: code chunk of step pair u
+#pragma unroll
+    for (int j = 0; j < NB; ++j) qb_row[j] = (b_row0[j] / BK) * 64;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) cq[u] = (uint32_t)(((2 * u + h) ^ ((lrow >> 2) & 3)) << 4);
 
     // The fragment reads and MFMAs take the number of this wave's 32-row
     // activation blocks that hold rows of the tile (NA, a compile-time
@@ -662,15 +696,40 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     // one SIMD are one from each half of the tile's rows, so the skipped
     // work shortens every SIMD's share alike.
     bf16x8 fa[2][4], fb[2][NB];
-    // fragment read r of step st of slice kt: fa[r] for r < NA, then fb[r - NA]
+    u32x4 codes[NB];                                // 8-bit: codes of the next step pair
+    // Fragment read r of step st of slice kt: fa[r] for r < NA, then fb[r -
+    // NA] (bf16) or, 8-bit and st even, the codes of blocks r - NA for
+    // steps st and st + 1.
     auto read_one = [&](auto na_c, int set, int kt, int st, int r) {
         constexpr int NA = decltype(na_c)::value;
         if (r < NA) {
             const lds_bf16_t* sa = smem + slot(2 * kt) * OPER;
             fa[set][r] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + r * 32 * BK + cx[st]);
-        } else {
+        } else if (!Q8) {
             const lds_bf16_t* sb = smem + slot(2 * kt + 1) * OPER;
             fb[set][r - NA] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[r - NA] + cx[st]);
+        } else {
+            const __attribute__((address_space(3))) uint8_t* sb =
+                reinterpret_cast<const __attribute__((address_space(3))) uint8_t*>(smem + slot(2 * kt + 1) * OPER);
+            codes[r - NA] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(sb + qb_row[r - NA] + cq[st >> 1]);
+        }
+    };
+    // reads of step st: the A fragments, and the B fragments (bf16) or the
+    // codes of the step pair starting at st (8-bit)
+    auto reads_of = [](int na, int st) {
+        return na > 0 ? na + ((!Q8 || (st & 1) == 0) ? NB : 0) : 0;
+    };
+    // 8-bit: the codes of a step pair to the B fragments of its two steps
+    auto widen = [&]() {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const u32x4 w = codes[j];
+            const u32x4 lo = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x),
+                              e4m3x2_to_bf16x2<false>(w.y), e4m3x2_to_bf16x2<true>(w.y)};
+            const u32x4 hi = {e4m3x2_to_bf16x2<false>(w.z), e4m3x2_to_bf16x2<true>(w.z),
+                              e4m3x2_to_bf16x2<false>(w.w), e4m3x2_to_bf16x2<true>(w.w)};
+            fb[0][j] = __builtin_bit_cast(bf16x8, lo);
+            fb[1][j] = __builtin_bit_cast(bf16x8, hi);
         }
     };
     // The weight fragment is the MFMA's first operand, the activation
@@ -693,7 +752,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     auto main_loop = [&](auto na_c, int nk) {
         constexpr int NA = decltype(na_c)::value;
         constexpr int MF = NA * NB;
-        constexpr int RD = NA > 0 ? NA + NB : 0;
+        constexpr int RD = NA > 0 ? NA + NB : 0;     // most reads of one step
         constexpr int G = MF > RD ? MF : (RD > 0 ? RD : 1);
 #pragma unroll
         for (int r = 0; r < RD; ++r) read_one(na_c, 0, 0, 0, r);
@@ -701,10 +760,11 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
         for (; kt + 2 < nk; ++kt) {                  // steady state: slice kt + 2 to issue
 #pragma unroll
             for (int st = 0; st + 1 < SPS; ++st) {
+                if (Q8 && NA > 0 && (st & 1) == 0) widen();
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     if (g < MF) mfma_one(st & 1, g);
-                    if (g < RD) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
+                    if (g < reads_of(NA, st + 1)) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
                     const int t = st * G + g;        // A of slice kt + 2 over steps 0-2
 #pragma unroll
                     for (int q = t * QI / (3 * G); q < (t + 1) * QI / (3 * G); ++q)
@@ -722,7 +782,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
             for (int g = 0; g < G; ++g) {            // step 3, B of slice kt + 2, slice kt + 1's first reads
                 if (g < MF) mfma_one((SPS - 1) & 1, g);
 #pragma unroll
-                for (int q = g * QI / G; q < (g + 1) * QI / G; ++q) load_one(2 * (kt + 2) + 1, q);
+                for (int q = g * QB / G; q < (g + 1) * QB / G; ++q) load_one(2 * (kt + 2) + 1, q);
                 if (g < RD) read_one(na_c, 0, kt + 1, 0, g);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -730,10 +790,11 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
         for (; kt < nk; ++kt) {                      // tail: nothing left to issue
 #pragma unroll
             for (int st = 0; st + 1 < SPS; ++st) {
+                if (Q8 && NA > 0 && (st & 1) == 0) widen();
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     if (g < MF) mfma_one(st & 1, g);
-                    if (g < RD) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
+                    if (g < reads_of(NA, st + 1)) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -756,7 +817,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     if (nk > 1) {
         load_half(2);
         load_half(3);
-        wait_vm<2 * QI>();                           // slice 0 landed
+        wait_vm<QI + QB>();                          // slice 0 landed
     } else {
         wait_vm<0>();
     }
@@ -783,17 +844,30 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     stage_barrier();                                 // every wave is done with the slots
     {
         const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (lane >> 5);   // + 32 j + 8 r4
+        // 8-bit: each output column's accumulators times its weight rows' scales
+        const float* sca = Q8 ? P.Sa_r + (size_t)tl.group * ncols : nullptr;
+        const float* scb = Q8 && SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : nullptr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
 #pragma unroll
-            for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float fa4[4] = {1.f, 1.f, 1.f, 1.f}, fb4[4] = {1.f, 1.f, 1.f, 1.f};
+                if (Q8) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
+                    for (int e = 0; e < 4; ++e) {
+                        const int n = tl.n0 + ocol_l + 32 * j + 8 * r4 + e;
+                        fa4[e] = n < ncols ? sca[n] : 0.f;
+                        if (SWIGLU) fb4[e] = n < ncols ? scb[n] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * r4 + e;
-                        v[e] = SWIGLU ? silu(acc[i][j][r]) * acc[i][j + HB][r] : acc[i][j][r];
+                        const float a = Q8 ? acc[i][j][r] * fa4[e] : acc[i][j][r];
+                        v[e] = SWIGLU ? silu(a) * (Q8 ? acc[i][j + HB][r] * fb4[e] : acc[i][j + HB][r]) : a;
                     }
                     const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
                     const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
@@ -822,288 +896,20 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     }
 }
 
-// ---------------------------------------------------------------------------
-// 256 x 256 tile with 8-bit routed weights (moe_forward_fp8 on many rows per
-// expert).  Eight waves as in big_tile; the B slice of a stage is 64 E4M3
-// codes per weight row (16 KB) next to the 32 KB bf16 A slice, so three
-// 48 KB stages fit the 160 KB of LDS.  Both operands come in by
-// direct-to-LDS buffer loads: A as 8 rows x 128 B, B as 16 rows x 64 B per
-// wave instruction, each 16-byte chunk c of row r at position c ^ f(r),
-// f = (r >> 1) & 7 for A and (r >> 2) & 3 for B — conflict-free for 16
-// lanes on 16 consecutive rows.
-//
-// The order of k inside a slice is permuted the same way for both operands:
-// k16 step st = 2u + s, lane half h and element e stand for
-// k = 32 u + 16 h + 8 s + e.  A lane's 16 codes for steps 2u and 2u + 1 are
-// then one 16-byte chunk (codes 32 u + 16 h .. + 15), read once and widened
-// exactly to two bf16 fragments; its A fragment of step st is the 8-element
-// chunk 4 u + 2 h + s.  The row scales multiply the fp32 accumulators of their
-// output columns in the epilogue.
-// ---------------------------------------------------------------------------
-template <bool SWIGLU>
-__device__ __forceinline__ void big_tile_q8(const GemmParams& P, const Tile& tl,
-                                            __attribute__((address_space(3))) uint8_t* smem) {
-    constexpr int NW = 8, KS = 3, BK = 64;
-    constexpr int A_BYTES = kBig * BK * 2;          // 32 KB
-    constexpr int STAGE = A_BYTES + kBig * BK;      // + 16 KB of codes
-    constexpr int QA = 4, QB = 2;                   // load instructions per wave per stage
-    constexpr int LOADS = QA + QB;
-    constexpr int WN = NW / 2, WCOLS = kBig / WN, NB = WCOLS / 32, HB = NB / 2;
-    static_assert(KS * STAGE <= 160 * 1024, "LDS");
-    static_assert(NB == 2, "two B blocks per wave");
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int kdim = P.kdim_r, ncols = P.n_r;      // routed tiles only
-    const int grow = P.goff[tl.group] + tl.m0;
-    const size_t wofs = (size_t)tl.group * ncols * kdim;
-    const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(P.A_r, P.abytes_r);
-    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim;
-    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(P.Qa_r + wofs, wbytes);
-    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc((SWIGLU ? P.Qb_r : P.Qa_r) + wofs, wbytes);
-
-    // A: instruction j = wave + 8 q fills rows 8 j .. 8 j + 7; lane l row
-    // 8 j + l / 8, position l % 8.  B: instruction j = wave + 8 q fills rows
-    // 16 j .. 16 j + 15; lane l row 16 j + l / 4, position l % 4; SwiGLU: q = 0
-    // loads W1 rows, q = 1 the same rows of W3.
-    uint32_t aoff[QA], boff[QB];
-#pragma unroll
-    for (int q = 0; q < QA; ++q) {
-        const int row = 8 * (wave + 8 * q) + lane / 8;
-        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((row >> 1) & 7)) * 16);
-        const int rr = row < tl.nrows ? row : 0;
-        const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(grow + rr);
-        aoff[q] = arow * (uint32_t)kdim * 2u + cb;
-    }
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-        const int row = 16 * (wave + 8 * q) + lane / 4;
-        const uint32_t cb = (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) * 16);
-        int n = tl.n0 + ((SWIGLU && q == 1) ? row - kBig / 2 : row);
-        n = n < ncols ? n : ncols - 1;
-        boff[q] = (uint32_t)n * (uint32_t)kdim + cb;
-    }
-    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)(wave * 1024));
-    // Load t of a stage (t < QA + QB): A pieces first, then codes; the
-    // slice's k offset goes in the scalar offset.
-    auto issue_one = [&](int kt, int t) {
-        const uint32_t sa = lds_base + (uint32_t)((kt % KS) * STAGE);
-        if (t < QA)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, (lds_ptr_t)(uintptr_t)(sa + t * 8 * 1024), 16,
-                                                     (int)aoff[t], kt * 128, 0, 0);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(t > QA ? rw3 : rw1,
-                                                     (lds_ptr_t)(uintptr_t)(sa + A_BYTES + (t - QA) * 8 * 1024),
-                                                     16, (int)boff[t - QA], kt * 64, 0, 0);
-    };
-    auto issue = [&](int kt) {
-#pragma unroll
-        for (int t = 0; t < QA + QB; ++t) issue_one(kt, t);
-    };
-
-    f32x16 acc[4][NB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
-
-    const int lrow = lane & 31;
-    const int h = lane >> 5;
-    const uint32_t a_row = (uint32_t)((wm * 128 + lrow) * 128);   // + 32 i rows
-    uint32_t ca[4];                                               // A chunk of step st
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-        ca[st] = (uint32_t)(((4 * (st >> 1) + 2 * h + (st & 1)) ^ ((lrow >> 1) & 7)) << 4);
-    uint32_t b_row[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const int br = SWIGLU ? ((j < HB ? 0 : kBig / 2) + wn * (WCOLS / 2)) : (wn * WCOLS + j * 32);
-        b_row[j] = (uint32_t)(A_BYTES + (br + lrow) * 64);
-    }
-    uint32_t cq[2];                                               // B chunk of step pair u
-#pragma unroll
-    for (int u = 0; u < 2; ++u) cq[u] = (uint32_t)(((2 * u + h) ^ ((lrow >> 2) & 3)) << 4);
-
-    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-    bf16x8 fa[2][4];                                // A fragments, double-buffered by step
-    u32x4 codes[NB];                                // B codes of the next step pair
-    bf16x8 fb[2][NB];                               // widened B of steps 2u, 2u + 1
-    auto read_a = [&](int set, int kt, int st) {
-        const uint32_t base = (uint32_t)((kt % KS) * STAGE) + a_row + ca[st];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[set][i] = *reinterpret_cast<lds_bf16x8*>(smem + base + i * 32 * 128);
-    };
-    auto read_b = [&](int kt, int u) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-            codes[j] = *reinterpret_cast<lds_u32x4*>(smem + (uint32_t)((kt % KS) * STAGE) + b_row[j] + cq[u]);
-    };
-    auto widen = [&]() {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const u32x4 w = codes[j];
-            const u32x4 lo = {e4m3x2_to_bf16x2<false>(w.x), e4m3x2_to_bf16x2<true>(w.x),
-                              e4m3x2_to_bf16x2<false>(w.y), e4m3x2_to_bf16x2<true>(w.y)};
-            const u32x4 hi = {e4m3x2_to_bf16x2<false>(w.z), e4m3x2_to_bf16x2<true>(w.z),
-                              e4m3x2_to_bf16x2<false>(w.w), e4m3x2_to_bf16x2<true>(w.w)};
-            fb[0][j] = __builtin_bit_cast(bf16x8, lo);
-            fb[1][j] = __builtin_bit_cast(bf16x8, hi);
-        }
-    };
-    auto mfma_one = [&](int set, int s, int m) {
-        const int i = m / NB, j = m % NB;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[set][i], acc[i][j], 0, 0, 0);
-    };
-    auto mfmas = [&](int set, int s) {
-#pragma unroll
-        for (int m = 0; m < 4 * NB; ++m) mfma_one(set, s, m);
-    };
-    // Fragment read r of the next stage's first step: A blocks 0..3, then
-    // the codes of B blocks 0 .. NB-1.
-    auto read_one0 = [&](int kt, int r) {
-        if (r < 4)
-            fa[0][r] = *reinterpret_cast<lds_bf16x8*>(smem + (uint32_t)((kt % KS) * STAGE) + a_row + ca[0] + r * 32 * 128);
-        else
-            codes[r - 4] = *reinterpret_cast<lds_u32x4*>(smem + (uint32_t)((kt % KS) * STAGE) + b_row[r - 4] + cq[0]);
-    };
-    // steps 0 .. 2 of stage kt (step 0's A fragments and pair 0's codes
-    // already in registers)
-    auto steps012 = [&](int kt) {
-        widen();                                     // pair 0
-        read_b(kt, 1);
-        read_a(1, kt, 1);
-        mfmas(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(0, kt, 2);
-        mfmas(1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        widen();                                     // pair 1
-        read_a(1, kt, 3);
-        mfmas(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    const int nk = kdim / BK;
-    for (int k = 0; k < KS && k < nk; ++k) issue(k);
-    wait_vm_runtime<LOADS>(LOADS * (min(KS, nk) - 1));
-    stage_barrier();
-    read_a(0, 0, 0);
-    read_b(0, 0);
-    // Iteration kt: steps 0 .. 2, then wait for stage kt + 1 and for this
-    // wave's reads of stage kt, pass the barrier — after it stage kt's buffer
-    // is free — and issue its refill (stage kt + KS) before step 3's MFMAs,
-    // with the next stage's first reads.
-    int kt = 0;
-    for (; kt + KS < nk; ++kt) {
-        steps012(kt);
-        wait_vm<LOADS * (KS - 2)>();
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        stage_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        // step 3's MFMAs with the refill's loads and the next stage's first
-        // reads between them, one of each per MFMA, the order fenced
-#pragma unroll
-        for (int g = 0; g < 4 * NB; ++g) {
-            mfma_one(1, 1, g);
-            if (g < QA + QB) issue_one(kt + KS, g);
-            if (g < 4 + NB) read_one0(kt + 1, g);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    for (; kt < nk; ++kt) {                          // tail: nothing left to issue
-        steps012(kt);
-        const int ahead = nk - 1 - (kt + 1);
-        wait_vm_runtime<LOADS>(LOADS * (ahead > 0 ? ahead : 0));
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        stage_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_a(0, kt + 1, 0);                        // past the end: stale, unused
-        read_b(kt + 1, 0);
-        mfmas(1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // Epilogue as in big_tile, each output column's accumulators first
-    // multiplied by its weight rows' scales.
-    constexpr int OC = SWIGLU ? kBig / 2 : kBig;
-    constexpr int CPR = OC / 8;
-    static_assert(kBig * OC * 2 <= KS * STAGE, "output tile fits the stage buffers");
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_barrier();
-    lds_bf16_t* sout = reinterpret_cast<lds_bf16_t*>(smem);
-    const float* sca = P.Sa_r + (size_t)tl.group * ncols;
-    const float* scb = SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : nullptr;
-    {
-        const int orow_l = wm * 128 + (lane & 31);
-        const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (lane >> 5);
-#pragma unroll
-        for (int j = 0; j < (SWIGLU ? HB : NB); ++j) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int ocol = ocol_l + 32 * j + 8 * r4;
-                float fa4[4], fb4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int n = tl.n0 + ocol + e;
-                    fa4[e] = n < ncols ? sca[n] : 0.f;
-                    fb4[e] = SWIGLU && n < ncols ? scb[n] : 0.f;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * r4 + e;
-                        v[e] = SWIGLU ? silu(acc[i][j][r] * fa4[e]) * (acc[i][j + HB][r] * fb4[e])
-                                      : acc[i][j][r] * fa4[e];
-                    }
-                    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    const int orow = orow_l + 32 * i;
-                    const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
-                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(sout + off) = u32x2{lo, hi};
-                }
-            }
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_barrier();
-    {
-        bf16_t* obase = P.O_r;
-        for (int c = tid; c < kBig * CPR; c += 64 * NW) {
-            const int row = c / CPR;
-            const int cc = c - row * CPR;
-            const int col = tl.n0 + cc * 8;
-            if (row < tl.nrows && col < ncols) {
-                const u32x4 v = *reinterpret_cast<lds_u32x4*>(sout + row * OC + ((cc ^ (row % CPR)) << 3));
-                *reinterpret_cast<u32x4*>(obase + (size_t)(grow + row) * ncols + col) = v;
-            }
-        }
-    }
-}
+// LDS of the many-rows tile: five 32 KB operand slots (160 KB).
+constexpr int kBigLdsBytes = 5 * kBig * 64 * 2;
 
 // Many rows per expert with 8-bit routed weights: routed tiles take the
 // 8-bit tile, shared-expert tiles (bf16 weights) the bf16 one.
 template <bool SWIGLU>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_big_q8_kernel(GemmParams P) {
-    // three 48 KB 8-bit stages, or the bf16 tile's five 32 KB slots
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * kBig * 64 * 2];
-    static_assert(3 * (kBig * 64 * 3) <= 5 * kBig * 64 * 2, "the 8-bit stages fit");
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kBigLdsBytes / 2];
     Tile tl;
     if (!fetch_tile(P, tl)) return;
-    if (tl.group < P.E)
-        big_tile_q8<SWIGLU>(P, tl, (__attribute__((address_space(3))) uint8_t*)smem);
-    else
-        big_tile<SWIGLU, 8>(P, tl, (lds_bf16_t*)smem);
+    if (tl.group < P.E) big_tile<SWIGLU, 8, true>(P, tl, (lds_bf16_t*)smem);
+    else big_tile<SWIGLU, 8, false>(P, tl, (lds_bf16_t*)smem);
 }
-
-// LDS of the many-rows bf16 tile: five 32 KB operand slots (160 KB).
-constexpr int kBigLdsBytes = 5 * kBig * 64 * 2;
 
 template <bool SWIGLU, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
