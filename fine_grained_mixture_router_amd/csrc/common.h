@@ -50,6 +50,7 @@ constexpr uint32_t kGateRenorm = 2u;    // shape flag bits of the gating variant
 constexpr uint32_t kGateSigmoid = 4u;
 // Router GEMM tile: 64 tokens x 64 experts, d consumed 64 at a time.
 constexpr int kRouterBT = 64;
+constexpr int kRouterWideT = 256;   // token tile of the router for large batches
 constexpr int kRouterBE = 64;
 
 // One entry of a grouped-GEMM work list.
@@ -73,6 +74,7 @@ struct Plan {
     int Epad;        // E rounded up to the router tile
     int nchunk;      // ceil(T / kChunk)
     int split;       // router split over d
+    int router_wide; // router tiles of kRouterWideT tokens (large batches)
     int rows;        // T*K routed rows + T*Ks shared rows
     GemmCfg g1, g2;
     int max_tiles1, max_tiles2;

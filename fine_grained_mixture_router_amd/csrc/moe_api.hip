@@ -12,6 +12,9 @@ using namespace moe;
 #ifndef MOE_ROUTER_WGS
 #define MOE_ROUTER_WGS 512
 #endif
+#ifndef MOE_ROUTER_WIDE_T
+#define MOE_ROUTER_WIDE_T 8192
+#endif
 #ifndef MOE_ROUTER_MINK
 #define MOE_ROUTER_MINK 4
 #endif
@@ -69,9 +72,17 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
     // so that the launch has about kRouterWGs workgroups (two per CU, which
     // its 80 KB of LDS allows), each split keeping at least kRouterMinK
     // slices of 64.
-    const int rtiles = (s->T + kRouterBT - 1) / kRouterBT;
+    // Batches of MOE_ROUTER_WIDE_T tokens or more take 256-token tiles (one
+    // workgroup per CU, so about half as many workgroups are aimed at).  On
+    // the V3-shape prefill batch (16 384 tokens) that takes the affinities
+    // from 120 to 86 us; at 4 096 tokens the larger split's extra partials
+    // cost the selection what the tiles save.
+    p->router_wide = s->T >= MOE_ROUTER_WIDE_T ? 1 : 0;
+    const int bt = p->router_wide ? kRouterWideT : kRouterBT;
+    const int target = p->router_wide ? MOE_ROUTER_WGS / 2 : MOE_ROUTER_WGS;
+    const int rtiles = (s->T + bt - 1) / bt;
     const int kmax = nk / MOE_ROUTER_MINK > 0 ? nk / MOE_ROUTER_MINK : 1;
-    int split = (MOE_ROUTER_WGS + rtiles - 1) / rtiles;
+    int split = (target + rtiles - 1) / rtiles;
     split = split < 1 ? 1 : (split > kmax ? kmax : split);
     const int kps = (nk + split - 1) / split;
     p->split = (nk + kps - 1) / kps;

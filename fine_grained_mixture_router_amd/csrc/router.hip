@@ -153,6 +153,126 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(
         }
 }
 
+// The same affinities for large batches: tiles of kRouterWideT = 256 tokens
+// by all Epad (<= 256) experts, so the centroids are re-read once per 256
+// tokens rather than per 64 (with 64-token tiles the loads, not the MFMAs,
+// bound the kernel: 40 KB of operands per 512 MFMA cycles of a workgroup).
+// Eight waves, wave (wm, wn) computing tokens 128 wm .. + 127 by experts
+// 64 wn .. + 63 (4 x 2 MFMA 32x32x16 blocks); BK = 64 slices come in by
+// direct-to-LDS buffer loads (one wave instruction fills 8 rows x 128 B)
+// into two LDS stages, swizzled as in swz(); the refill of a stage is
+// issued right after the barrier that ends its reads, a whole stage ahead
+// of its use.
+constexpr int kRouterWideThreads = 512;
+
+__global__ __launch_bounds__(kRouterWideThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void router_logits_wide_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ C,
+                               float* __restrict__ logits, int T, int d, int E, int Epad,
+                               int ksteps_per_split) {
+    constexpr int OPER = kRouterWideT * 64;        // elements of one operand slice
+    constexpr int QI = 4;                          // load instructions per wave per operand
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * 2 * OPER];
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int t0 = blockIdx.x * kRouterWideT;
+    const int nk = d >> 6;
+    const int k_begin = blockIdx.y * ksteps_per_split;
+    const int k_end = min(nk, k_begin + ksteps_per_split);
+    const bool active = 64 * wn < Epad;            // this wave's experts exist
+
+    // Load instruction j = wave + 8 q fills rows 8 j .. 8 j + 7 of a slice;
+    // lane l fills chunk position l % 8 of row 8 j + l / 8.  Rows past T or
+    // E are clamped to the last one (their results are never read).
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * (uint32_t)d * 2u);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (uint32_t)E * (uint32_t)d * 2u);
+    uint32_t aoff[QI], boff[QI];
+#pragma unroll
+    for (int q = 0; q < QI; ++q) {
+        const int row = 8 * (wave + 8 * q) + (lane >> 3);
+        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        aoff[q] = (uint32_t)min(t0 + row, T - 1) * (uint32_t)d * 2u + cb;
+        boff[q] = (uint32_t)min(row, E - 1) * (uint32_t)d * 2u + cb;
+    }
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)(wave * 1024));
+    auto issue = [&](int kt, int buf) {
+        const uint32_t sa = lds_base + (uint32_t)(buf * 2 * OPER * 2);
+        const int kb = kt * 128;
+#pragma unroll
+        for (int q = 0; q < QI; ++q) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(uintptr_t)(sa + q * 8 * 1024), 16,
+                                                     (int)aoff[q], kb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(uintptr_t)(sa + OPER * 2 + q * 8 * 1024),
+                                                     16, (int)boff[q], kb, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    const int lrow = lane & 31;
+    const lds_bf16_t* lsm = (const lds_bf16_t*)smem;
+    if (k_begin < k_end) {
+        issue(k_begin, 0);
+        if (k_begin + 1 < k_end) {
+            issue(k_begin + 1, 1);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        asm volatile("s_barrier" ::: "memory");
+        for (int kt = k_begin; kt < k_end; ++kt) {
+            const int buf = (kt - k_begin) & 1;
+            const lds_bf16_t* sa = lsm + buf * 2 * OPER;
+            const lds_bf16_t* sb = sa + OPER;
+            if (active) {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const int c = 2 * st + (lane >> 5);
+                    bf16x8 a[4], b[2];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + swz(128 * wm + 32 * i + lrow, c));
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        b[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + swz(64 * wn + 32 * j + lrow, c));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                }
+            }
+            // the next slice landed; every wave is done reading this one
+            if (kt + 1 < k_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (kt + 2 < k_end) issue(kt + 2, buf);
+        }
+    }
+
+    // 32x32 accumulator: lane holds column (lane & 31) = expert, rows (tokens)
+    // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
+    if (!active) return;
+    float* outp = logits + (size_t)blockIdx.y * T * Epad;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = 64 * wn + 32 * j + lrow;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = t0 + 128 * wm + 32 * i + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+                if (row < T && col < Epad) outp[(size_t)row * Epad + col] = acc[i][j][r];
+            }
+        }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
@@ -294,8 +414,14 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
 hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st) {
     const int nk = p.d / 64;
     const int kps = (nk + p.split - 1) / p.split;
-    dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.split);
-    router_logits_kernel<<<grid, kRouterThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
+    if (p.router_wide) {
+        dim3 grid((p.T + kRouterWideT - 1) / kRouterWideT, p.split);
+        router_logits_wide_kernel<<<grid, kRouterWideThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E,
+                                                                       p.Epad, kps);
+    } else {
+        dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.split);
+        router_logits_kernel<<<grid, kRouterThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
+    }
     return hipGetLastError();
 }
 

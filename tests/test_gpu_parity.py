@@ -72,6 +72,25 @@ def test_route_parity(name):
     assert exempt < 0.1 * w.T
 
 
+# Batches of 8 192 tokens or more take the router's 256-token tiles: every
+# token's routing at a ragged last tile (T = 8 200), an expert count that is
+# not a multiple of 64 (E = 200) and a slice count that does not divide
+# evenly among the splits (d = 576, 9 slices).
+@pytest.mark.parametrize("T,d,E,K", [(8192, 512, 64, 6), (8200, 576, 200, 8)])
+def test_route_parity_wide_tiles(T, d, E, K):
+    _log(f"[route-wide] T={T} d={d} E={E} K={K}")
+    rng = np.random.default_rng(T + E)
+    x = synth.f32_to_bf16_rne(rng.standard_normal((T, d)).astype(np.float32))
+    C = synth.f32_to_bf16_rne((rng.standard_normal((E, d)) * 0.05).astype(np.float32))
+    bias = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    D = upload(dict(x=x, C=C, bias=bias))
+    idx, gate = moe.route(D["x"], D["C"], K=K, bias=D["bias"])
+    torch.cuda.synchronize()
+    ri, rg, rm = oracle.route(x, C, bias, K)
+    exempt = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), ri, rg, rm, K)
+    assert exempt < 0.1 * T
+
+
 @pytest.mark.parametrize("name,nsample", [("tiny", 128), ("2b", 192), ("16b", 128),
                                           ("16b_zipf", 128)])
 def test_forward_parity(name, nsample):
