@@ -477,9 +477,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmParams P) {
 // slice's last MFMAs.  The order is pinned with scheduling fences.
 // ---------------------------------------------------------------------------
 constexpr int kBig = 256;
-#ifndef MOE_INTERLEAVE
-#define MOE_INTERLEAVE 1
-#endif
 // Configuration of the many-rows tile (measured on MI355X, V3-shape prefill):
 // BK = 64 (128-byte row segments) in a ring of five 32 KB operand slots,
 // 8 waves (two per SIMD, so one issues MFMAs while its sibling waits on
@@ -493,10 +490,6 @@ constexpr int kBig = 256;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;   // bf16 in LDS
 
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, 0, 0, 0);
-}
-
 // Workgroup barrier without the memory fence of __syncthreads(), whose
 // release semantics would wait for every outstanding load (vmcnt(0)) and
 // drain the multi-stage pipeline.  Ordering is kept explicitly: each wave
@@ -508,16 +501,6 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
-
-// Wait until at most n (a multiple of `unit`, n <= 3 * unit) of this wave's
-// loads are in flight.
-template <int UNIT>
-__device__ __forceinline__ void wait_vm_runtime(int n) {
-    if (n >= 3 * UNIT) wait_vm<3 * UNIT>();
-    else if (n >= 2 * UNIT) wait_vm<2 * UNIT>();
-    else if (n >= UNIT) wait_vm<UNIT>();
-    else wait_vm<0>();
-}
 
 // Work-list tile of workgroup blockIdx.x for the many-rows kernels; false
 // when the workgroup has none.  XCD-aware order: workgroup ids are dealt

@@ -24,7 +24,7 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-# the few-rows tile (tiny) and the persistent many-rows tile (16b_zipf)
+# the few-rows tile (tiny) and the many-rows ring tile (16b_zipf)
 @pytest.mark.parametrize("name", ["tiny", "16b_zipf"])
 def test_graph_replay_matches_eager(name):
     w = wl.WORKLOADS[name]
