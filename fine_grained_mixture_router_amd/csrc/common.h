@@ -37,11 +37,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs).
+// fp32 -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+
+// Two fp32 -> two bf16 in one word, the first in the low half: one
+// conversion instruction for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Tokens per routing chunk: one 64-bit lane mask per (chunk, expert).
