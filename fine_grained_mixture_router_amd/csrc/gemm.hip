@@ -740,6 +740,11 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
         constexpr int MF = NA * NB;
         constexpr int RD = NA > 0 ? NA + NB : 0;     // most reads of one step
         constexpr int G = MF > RD ? MF : (RD > 0 ? RD : 1);
+        // The next step's fragment reads go out RPG per group.  Two per group
+        // (all of them in the step's first half, more time to land before the
+        // wait ahead of the barrier) measured 3 % faster on the down GEMM and
+        // 1 % slower on gate/up, so gate/up keeps one per group.
+        constexpr int RPG = SWIGLU ? 1 : 2;
 #pragma unroll
         for (int r = 0; r < RD; ++r) read_one(na_c, 0, 0, 0, r);
         int kt = 0;
@@ -750,7 +755,9 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     if (g < MF) mfma_one(st & 1, g);
-                    if (g < reads_of(NA, st + 1)) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
+#pragma unroll
+                    for (int r = RPG * g; r < RPG * g + RPG; ++r)
+                        if (r < reads_of(NA, st + 1)) read_one(na_c, (st + 1) & 1, kt, st + 1, r);
                     const int t = st * G + g;        // A of slice kt + 2 over steps 0-2
 #pragma unroll
                     for (int q = t * QI / (3 * G); q < (t + 1) * QI / (3 * G); ++q)
@@ -780,7 +787,9 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     if (g < MF) mfma_one(st & 1, g);
-                    if (g < reads_of(NA, st + 1)) read_one(na_c, (st + 1) & 1, kt, st + 1, g);
+#pragma unroll
+                    for (int r = RPG * g; r < RPG * g + RPG; ++r)
+                        if (r < reads_of(NA, st + 1)) read_one(na_c, (st + 1) & 1, kt, st + 1, r);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
