@@ -683,21 +683,27 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     // work shortens every SIMD's share alike.
     bf16x8 fa[2][4], fb[2][NB];
     u32x4 codes[NB];                                // 8-bit: codes of the next step pair
-    // Fragment read r of step st of slice kt: fa[r] for r < NA, then fb[r -
-    // NA] (bf16) or, 8-bit and st even, the codes of blocks r - NA for
-    // steps st and st + 1.
+    // Fragment read r of step st of slice kt: the A fragments fa[0..NA) and
+    // the B fragments fb[0..NB) (bf16) or, 8-bit and st even, the codes of
+    // the B blocks for steps st and st + 1.  Down: A first.  Gate/up: B
+    // first, so that the first MFMAs of the step have their operands
+    // earliest (measured 0.7 % faster there, 1.4 % slower on down).
     auto read_one = [&](auto na_c, int set, int kt, int st, int r) {
         constexpr int NA = decltype(na_c)::value;
-        if (r < NA) {
+        const int nbr = (!Q8 || (st & 1) == 0) ? NB : 0;   // B reads of step st
+        const bool is_a = SWIGLU ? r >= nbr : r < NA;
+        const int ra = SWIGLU ? r - nbr : r;
+        const int rb = SWIGLU ? r : r - NA;
+        if (is_a) {
             const lds_bf16_t* sa = smem + slot(2 * kt) * OPER;
-            fa[set][r] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + r * 32 * BK + cx[st]);
+            fa[set][ra] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + a_row0 + ra * 32 * BK + cx[st]);
         } else if (!Q8) {
             const lds_bf16_t* sb = smem + slot(2 * kt + 1) * OPER;
-            fb[set][r - NA] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[r - NA] + cx[st]);
+            fb[set][rb] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + b_row0[rb] + cx[st]);
         } else {
             const __attribute__((address_space(3))) uint8_t* sb =
                 reinterpret_cast<const __attribute__((address_space(3))) uint8_t*>(smem + slot(2 * kt + 1) * OPER);
-            codes[r - NA] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(sb + qb_row[r - NA] + cq[st >> 1]);
+            codes[rb] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(sb + qb_row[rb] + cq[st >> 1]);
         }
     };
     // reads of step st: the A fragments, and the B fragments (bf16) or the
