@@ -227,6 +227,38 @@ def test_big_tile_ragged_groups(case):
     check_part(out_f64(rout), rref["routed"], "routed")
 
 
+# Gate pre-activations of standard deviation ~60 (W1 scaled up): silu runs
+# deep into both tails, where e^-a overflows fp32 (a < -88) and silu(a) -> 0,
+# or vanishes and silu(a) -> a.  One batch for each tile family.
+SATURATED = [
+    # T, d, E, I, K, Ks, Is
+    (64, 256, 16, 128, 4, 1, 128),      # few rows per expert: the 32-row tile
+    (1024, 256, 8, 128, 2, 1, 128),     # many rows per expert: the 256x256 tile
+]
+
+
+@pytest.mark.parametrize("case", SATURATED, ids=["thin", "big"])
+def test_saturated_swiglu(case):
+    T, d, E, I, K, Ks, Is = case
+    _log(f"[saturated] {case}")
+    L = _rand_layer(700 + T, T, d, E, I, K, Ks, Is)
+    g = np.random.default_rng(800 + T)
+    big = 60.0 / np.sqrt(d)
+    L["w1"] = synth.f32_to_bf16_rne((g.standard_normal((E, I, d)) * big).astype(np.float32))
+    L["ws1"] = synth.f32_to_bf16_rne((g.standard_normal((Ks, Is, d)) * big).astype(np.float32))
+    pre = synth.bf16_to_f64(L["x"][:8]) @ synth.bf16_to_f64(L["w1"][0]).T
+    assert pre.min() < -88 and pre.max() > 88          # both tails reached
+    D = upload(L)
+    out, idx, _ = gpu_forward(D, K, no_residual=True)
+    torch.cuda.synchronize()
+    tok = np.arange(T)
+    ref = oracle.forward(L["x"], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"], L["ws3"],
+                         L["ws2"], K, no_residual=True, forced_idx=idx.cpu().numpy())
+    o = out_f64(out)
+    assert np.all(np.isfinite(o))
+    check_part(o, ref["out"], "delta")
+
+
 def test_errors_leave_output_untouched():
     """Validation errors launch nothing: out keeps its previous contents."""
     w = wl.WORKLOADS["tiny"]
