@@ -23,7 +23,7 @@ __device__ __forceinline__ void add8(float* acc, u32x4 v, float w) {
 }
 
 constexpr int kMaxSrc = 16 + 256;   // Ks + K rows per token at most
-constexpr int kBatch = 8;            // source rows loaded ahead of their adds
+constexpr int kBatch = 16;           // source rows loaded ahead of their adds
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Y, const float* __restrict__ gate,
@@ -51,13 +51,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        if (residual) add8(acc, reinterpret_cast<const u32x4*>(x + (size_t)t * d)[v], 1.0f);
-        for (int b0 = 0; b0 < ns; b0 += kBatch) {
+        // the residual row leaves with the first batch of source rows; every
+        // row here is read once (streaming policy), and so is out written
+        const u32x4 xr = residual ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (size_t)t * d) + v)
+                                  : u32x4{0u, 0u, 0u, 0u};
+        for (int b0 = 0; b0 == 0 || b0 < ns; b0 += kBatch) {   // once at least: ns may be 0
             u32x4 r[kBatch];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
-                if (b0 + b < ns)                    // rows of Y are read once: nontemporal
+                if (b0 + b < ns)
                     r[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Y + (size_t)s_row[b0 + b] * d) + v);
+            if (b0 == 0 && residual) add8(acc, xr, 1.0f);
 #pragma unroll
             for (int b = 0; b < kBatch; ++b)
                 if (b0 + b < ns) add8(acc, r[b], s_w[b0 + b]);
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         o.y = pack_bf16x2(acc[2], acc[3]);
         o.z = pack_bf16x2(acc[4], acc[5]);
         o.w = pack_bf16x2(acc[6], acc[7]);
-        reinterpret_cast<u32x4*>(out + (size_t)t * d)[v] = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (size_t)t * d) + v);
     }
 }
 

@@ -259,6 +259,20 @@ def test_saturated_swiglu(case):
     check_part(o, ref["out"], "delta")
 
 
+def test_no_experts_is_identity():
+    """K = 0 and K_s = 0: the layer is the residual alone, out = x bit for
+    bit; with MOE_FLAG_NO_RESIDUAL, out = 0 (the oracle's special case)."""
+    _log("[identity] K=0 Ks=0")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    x = torch.randn(70, 320, generator=g).to(torch.bfloat16).cuda()
+    out = moe.forward(x, None, None, None, None, K=0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+    z = moe.forward(x, None, None, None, None, K=0, no_residual=True)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(z.view(torch.int16))) == 0
+
+
 def test_errors_leave_output_untouched():
     """Validation errors launch nothing: out keeps its previous contents."""
     w = wl.WORKLOADS["tiny"]
