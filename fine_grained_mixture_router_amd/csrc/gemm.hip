@@ -834,12 +834,18 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     }
 
     // Epilogue: the tile's outputs (bf16; SwiGLU applied in registers) go
-    // through LDS — now free — and leave as whole 16-byte row pieces, one
-    // row segment of OC * 2 bytes per CPR lanes.  In LDS, 16-byte chunk c of
-    // row r sits at position c ^ (r mod CPR), so the 32 rows one write
-    // instruction touches land in 32 different chunks.
+    // through LDS — now free — and leave as whole 16-byte row pieces.
+    // Gate/up (128 output columns per tile, 32 per wave): the workgroup
+    // stages the whole tile, one row segment of OC * 2 bytes per CPR lanes.
+    // Down (256 columns, WCOLS = 64 per wave): each wave stages its own
+    // 128 x WCOLS block in a private region and stores it as whole 128-byte
+    // row segments, with no second barrier (waves that finish early store
+    // early).  In LDS, 16-byte chunk c of row r sits at position c ^ (r mod
+    // chunks per row), so the 32 rows one write instruction touches spread
+    // over the banks.
     constexpr int OC = SWIGLU ? kBig / 2 : kBig;     // output columns of the tile
     constexpr int CPR = OC / 8;                      // 16-byte chunks per row
+    constexpr int RC = WCOLS / 8;                    // down: chunks per region row
     static_assert(kBig * OC <= NSLOT * OPER, "output tile fits the slots");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_barrier();                                 // every wave is done with the slots
@@ -874,24 +880,44 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
                     const uint32_t hi = pack_bf16x2(v[2], v[3]);
                     const int orow = wm * 128 + 32 * i + lrow;
                     const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
-                    const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                    int off;
+                    if (SWIGLU) {
+                        off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                    } else {
+                        const int lr = 32 * i + lrow, lc = ocol - wn * WCOLS;
+                        off = wave * (128 * WCOLS) + lr * WCOLS + (((lc >> 3) ^ (lr % RC)) << 3) + (lc & 4);
+                    }
                     *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) = u32x2{lo, hi};
                 }
             }
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_barrier();
-    {
-        bf16_t* obase = shared ? P.O_s : P.O_r;
-        const int orow0 = SWIGLU ? rrow : grow;
+    bf16_t* obase = shared ? P.O_s : P.O_r;
+    if (SWIGLU) {
+        stage_barrier();
         for (int c = tid; c < kBig * CPR; c += 64 * NW) {
             const int row = c / CPR;
             const int cc = c - row * CPR;
             const int col = tl.n0 + cc * 8;
             if (row < tl.nrows && col < ncols) {
                 const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(smem + row * OC + ((cc ^ (row % CPR)) << 3));
-                *reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col) = v;
+                *reinterpret_cast<u32x4*>(obase + (size_t)(rrow + row) * ncols + col) = v;
+            }
+        }
+    } else {
+        // this wave's own writes have landed (LDS operations of one wave
+        // complete in order, and lgkmcnt(0) above waited for them)
+        const int c0 = tl.n0 + wn * WCOLS;
+#pragma unroll 4
+        for (int it = 0; it < 128 * RC / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int lr = idx / RC, c = idx % RC;
+            const int row = wm * 128 + lr, col = c0 + c * 8;
+            if (row < tl.nrows && col < ncols) {
+                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    smem + wave * (128 * WCOLS) + lr * WCOLS + ((c ^ (lr % RC)) << 3));
+                *reinterpret_cast<u32x4*>(obase + (size_t)(grow + row) * ncols + col) = v;
             }
         }
     }
