@@ -524,7 +524,7 @@ __device__ __forceinline__ bool fetch_tile(const GemmParams& P, Tile& tl) {
     return true;
 }
 
-// One 256 x 256 tile with bf16 weights.
+// One 256 x 256 tile, bf16 weights (or, Q8, 8-bit routed weights).
 //
 // LDS is a ring of five 32 KB slots, each holding one operand half — the
 // A or the B part of one BK = 64 slice; half h (A of slice s: h = 2s, B:
