@@ -9,7 +9,9 @@ d=7168, 256 routed + 1 shared experts of inter 2048, top-8, Zipf(1.2) logit
 bias) — MFMA-bound.  The same layer on a 256-token decode batch (HBM-bound)
 is measured in the same run and reported under "decode", and both batches
 again with 8-bit (E4M3, per-row scaled) routed weights under "prefill_fp8"
-and "decode_fp8".  Inputs are
+and "decode_fp8"; the smaller layer shapes (2B: 63 experts of 896, top-7;
+16B: 64 experts of 1408, top-6, with and without a Zipf(1.1) bias) are
+summarised under "other_configs" with both roofline fractions.  Inputs are
 seeded synthetic data (bf16, N(0,1) activations, N(0,0.006) weights; the
 8-bit codes are drawn as bit fields with per-row scales of a similar size).
 
@@ -69,6 +71,8 @@ def parse():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode",
                     help="second workload on the same layer weights ('' to skip)")
+    ap.add_argument("--configs", default="2b,16b,16b_zipf",
+                    help="smaller layer shapes summarised under other_configs ('' to skip)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the batches with 8-bit routed weights")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -496,6 +500,35 @@ def main():
             del D8
             torch.cuda.empty_cache()
             print(f"[bench] {wd.name} fp8: {ms8:.3f} ms/step", file=sys.stderr, flush=True)
+
+    if args.configs:
+        # the smaller shapes: layer TFLOP/s against the MFMA peak and
+        # algorithmic bytes/s against the HBM peak, both reported
+        others = {}
+        for name in [c for c in args.configs.split(",") if c]:
+            wc = wl.WORKLOADS[name]
+            Lc = wl.gen_all(wc)
+            Dc = {k: (None if v is None else dev(v)) for k, v in Lc.items() if k != "x"}
+            rc = time_workload(wc, Dc, Lc["x"], args.steps, args.warmup)
+            cc = np.bincount(rc["idx"].ravel(), minlength=wc.E)
+            kc = algorithmic(wc, cc)
+            msc = rc["ms_per_step"]
+            tf = kc["layer_flops"] / (msc / 1e3) / 1e12
+            gbs = kc["layer_bytes"] / (msc / 1e3) / 1e9
+            others[name] = {
+                "T": wc.T, "d": wc.d, "E": wc.E, "I": wc.I, "K": wc.K, "Ks": wc.Ks,
+                "zipf_s": wc.zipf_s, "ms_per_step": round(msc, 4),
+                "tokens_per_s": round(wc.T / (msc / 1e3), 1),
+                "tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "roofline_ms": round(layer_roofline_ms(wc, cc), 4),
+                "frac_of_roofline": round(layer_roofline_ms(wc, cc) / msc, 4),
+                "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rc["kernels"].items()},
+            }
+            del Dc, Lc
+            torch.cuda.empty_cache()
+            print(f"[bench] {name}: {msc:.3f} ms/step", file=sys.stderr, flush=True)
+        line["other_configs"] = others
 
     ceil = hbm_read_ceiling()
     line["hbm_read_ceiling"] = ceil
