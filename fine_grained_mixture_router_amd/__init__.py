@@ -68,6 +68,8 @@ _lib.moe_route.argtypes = [ctypes.POINTER(Shape), _vp, _vp, _vp, _vp, _vp, _vp, 
 
 _lib.moe_profile_begin.restype = ctypes.c_int
 _lib.moe_profile_begin.argtypes = [ctypes.c_int32]
+_lib.moe_profile_begin_slots.restype = ctypes.c_int
+_lib.moe_profile_begin_slots.argtypes = [ctypes.c_int32, ctypes.c_uint32]
 _lib.moe_profile_end.restype = ctypes.c_int
 _lib.moe_profile_end.argtypes = [_vp, _vp, ctypes.c_int32]
 _lib.moe_profile_slot_name.restype = ctypes.c_char_p
@@ -78,7 +80,7 @@ _lib.moe_profile_stream_read.restype = ctypes.c_int
 _lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
 EXPORTS = ("moe_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
-           "moe_profile_begin", "moe_profile_end", "moe_profile_slot_name",
+           "moe_profile_begin", "moe_profile_begin_slots", "moe_profile_end", "moe_profile_slot_name",
            "moe_profile_stream_read")
 N_SLOTS = 7
 
@@ -227,9 +229,17 @@ def route(x, centroids, *, K: int, bias=None, renorm: bool = False, sigmoid: boo
     return topk_idx, topk_gate
 
 
-def profile_begin(max_calls: int):
-    """Record HIP events around every kernel of the next max_calls forwards."""
-    _check(_lib.moe_profile_begin(int(max_calls)))
+def profile_begin(max_calls: int, kernels=None):
+    """Record HIP events around every kernel of the next max_calls forwards,
+    or only around the kernels named in `kernels` (slot names)."""
+    if kernels is None:
+        _check(_lib.moe_profile_begin(int(max_calls)))
+        return
+    names = [_lib.moe_profile_slot_name(k).decode() for k in range(N_SLOTS)]
+    mask = 0
+    for name in kernels:
+        mask |= 1 << names.index(name)
+    _check(_lib.moe_profile_begin_slots(int(max_calls), mask))
 
 
 def profile_end() -> dict:

@@ -189,11 +189,12 @@ struct Recorder {
     int max_calls = 0;
     int calls = 0;
     hipEvent_t* ev = nullptr;   // [max_calls][kSlots][2]
+    uint32_t mask = 0;          // kernel slots recorded
     bool used[kSlots] = {};
 } g_rec;
 
 void rec_mark(int slot, int end, hipStream_t s) {
-    if (!g_rec.on || g_rec.calls >= g_rec.max_calls) return;
+    if (!g_rec.on || g_rec.calls >= g_rec.max_calls || !((g_rec.mask >> slot) & 1u)) return;
     (void)hipEventRecord(g_rec.ev[(g_rec.calls * kSlots + slot) * 2 + end], s);
 }
 
@@ -312,7 +313,7 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
         for (int k = 0; k < kSlots; ++k)
-            if (k >= 2 || p.K > 0) g_rec.used[k] = true;
+            if ((k >= 2 || p.K > 0) && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
         ++g_rec.calls;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -366,8 +367,10 @@ __attribute__((visibility("default"))) moe_status_t moe_route(
     return MOE_OK;
 }
 
-__attribute__((visibility("default"))) moe_status_t moe_profile_begin(int32_t max_calls) {
+__attribute__((visibility("default"))) moe_status_t moe_profile_begin_slots(int32_t max_calls,
+                                                                            uint32_t slot_mask) {
     if (max_calls < 1 || max_calls > 100000) return MOE_ERR_SHAPE;
+    if (slot_mask == 0 || (slot_mask >> kSlots) != 0) return MOE_ERR_SHAPE;
     moe_status_t st = device_ok();
     if (st != MOE_OK) return st;
     rec_free();
@@ -381,8 +384,13 @@ __attribute__((visibility("default"))) moe_status_t moe_profile_begin(int32_t ma
         }
     }
     g_rec.max_calls = max_calls;
+    g_rec.mask = slot_mask;
     g_rec.on = true;
     return MOE_OK;
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_profile_begin(int32_t max_calls) {
+    return moe_profile_begin_slots(max_calls, (1u << kSlots) - 1u);
 }
 
 __attribute__((visibility("default"))) moe_status_t moe_profile_end(float* ms, int32_t* launches,

@@ -184,6 +184,15 @@ const char* moe_status_string(moe_status_t status);
  * One process-wide recorder: not thread-safe; do not record from several
  * host threads at once. */
 moe_status_t moe_profile_begin(int32_t max_calls);
+
+/* moe_profile_begin_slots(max_calls, slot_mask): as moe_profile_begin, but
+ * only the kernel slots whose bit is set in slot_mask (bit k = slot k, the
+ * slot numbers below) are recorded; the others report 0 ms and 0 launches.
+ * Each recorded kernel adds two event records to the stream (a few
+ * microseconds each), so a timing run records only the kernel it needs.
+ * Errors as moe_profile_begin, and MOE_ERR_SHAPE for an empty mask or bits
+ * past the last slot. */
+moe_status_t moe_profile_begin_slots(int32_t max_calls, uint32_t slot_mask);
 moe_status_t moe_profile_end(float* ms, int32_t* launches, int32_t n_slots);
 const char* moe_profile_slot_name(int32_t slot);
 

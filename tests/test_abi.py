@@ -146,6 +146,9 @@ def test_profile_validation():
     assert f.moe_profile_end(None, None, 7) == 1          # nothing recording
     assert f.moe_profile_slot_name(4) == b"gemm_gate_up"
     assert f.moe_profile_slot_name(7) == b""
+    assert f.moe_profile_begin_slots(1, 0) == 2           # empty slot mask
+    assert f.moe_profile_begin_slots(1, 1 << 7) == 2      # past the last slot
+    assert f.moe_profile_begin_slots(0, 1 << 4) == 2
 
 
 def test_segment_helper():
