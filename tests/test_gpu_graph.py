@@ -6,6 +6,7 @@ replay must reproduce the eager result bit for bit; replays alternate with
 eager work on the same buffers and with synchronisation, and an input
 changed in place between replays is picked up by the next replay.
 """
+import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -24,21 +25,32 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-# the few-rows tile (tiny) and the many-rows ring tile (16b_zipf)
-@pytest.mark.parametrize("name", ["tiny", "16b_zipf"])
-def test_graph_replay_matches_eager(name):
+# the few-rows tile (tiny) and the many-rows ring tile (16b_zipf), with bf16
+# or 8-bit routed weights
+@pytest.mark.parametrize("name,fp8", [("tiny", False), ("16b_zipf", False), ("tiny", True),
+                                      ("16b_zipf", True)])
+def test_graph_replay_matches_eager(name, fp8):
     w = wl.WORKLOADS[name]
-    print(f"[graph] {name}", flush=True)
+    print(f"[graph] {name} fp8={fp8}", flush=True)
     D = upload(wl.gen_all(w))
+    if fp8:
+        for k, a in zip(("q1", "s1", "q3", "s3", "q2", "s2"), wl.gen_routed_fp8(w)):
+            D[k] = torch.from_numpy(np.ascontiguousarray(a)).cuda()
     shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
     ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
     idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
     gate = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
 
+    def fwd(**kw):
+        if fp8:
+            return moe.forward_fp8(D["x"], D["C"], D["q1"], D["s1"], D["q3"], D["s3"], D["q2"],
+                                   D["s2"], D["ws1"], D["ws3"], D["ws2"], K=w.K, bias=D["bias"], **kw)
+        return moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
+                           K=w.K, bias=D["bias"], **kw)
+
     def run():
-        moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
-                    K=w.K, bias=D["bias"], out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
+        fwd(out=out, topk_idx=idx, topk_gate=gate, workspace=ws)
 
     run()
     torch.cuda.synchronize()
@@ -72,8 +84,7 @@ def test_graph_replay_matches_eager(name):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    want, widx, wgate = moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"],
-                                    D["ws2"], K=w.K, bias=D["bias"], return_routing=True)
+    want, widx, wgate = fwd(return_routing=True)
     torch.cuda.synchronize()
     assert torch.equal(_bits(out), _bits(want))
     assert torch.equal(idx, widx) and torch.equal(gate, wgate)
