@@ -273,6 +273,55 @@ def test_no_experts_is_identity():
     assert int(torch.count_nonzero(z.view(torch.int16))) == 0
 
 
+def test_concurrent_streams_are_independent():
+    """Two forwards in flight at once on two streams, each with its own
+    workspace, give the results each gives alone (the library keeps no state
+    between calls)."""
+    _log("[streams] two batches on two streams")
+    w = wl.WORKLOADS["16b_zipf"]
+    L, D = _inputs(w)
+    x2 = torch.roll(D["x"], shifts=7, dims=0).contiguous()
+    ref1 = gpu_forward(D, w.K)[0].clone()
+    ref2 = gpu_forward(dict(D, x=x2), w.K)[0].clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()        # default priority
+    o1 = torch.empty_like(ref1)
+    o2 = torch.empty_like(ref2)
+    for s in (s1, s2):
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            gpu_forward(D, w.K, out=o1)
+        with torch.cuda.stream(s2):
+            gpu_forward(dict(D, x=x2), w.K, out=o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), ref1.view(torch.int16))
+    assert torch.equal(o2.view(torch.int16), ref2.view(torch.int16))
+
+
+def test_many_token_chunks():
+    """131 072 tokens: 2 048 routing chunks of 64 tokens (the permutation's
+    per-expert scans run over 512 chunks per thread) and about 9 000 tiles
+    in each GEMM list; routing and the output on a token sample."""
+    T, d, E, I, K, Ks, Is = 131072, 512, 64, 256, 8, 1, 256
+    _log(f"[many-chunks] T={T}")
+    L = _rand_layer(4242, T, d, E, I, K, Ks, Is, bias=True)
+    D = upload(L)
+    out, idx, gate = gpu_forward(D, K)
+    torch.cuda.synchronize()
+    tok = _sample(T, 48)
+    ref = oracle.forward(L["x"][tok], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"],
+                         L["ws3"], L["ws2"], K)
+    check_routing(idx.cpu().numpy()[tok], gate.cpu().numpy()[tok], ref["idx"], ref["gate"],
+                  ref["margin"], K)
+    ob = bf16_bits(out)[tok]
+    check_close(synth.bf16_to_f64(ob), ref["out"])
+    check_rounding(ob, ref["out"], ref["shared"], ref["routed"], ref["margin"])
+    # every routing slot used exactly once: the per-expert counts add up
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+    assert counts.sum() == T * K
+
+
 def test_errors_leave_output_untouched():
     """Validation errors launch nothing: out keeps its previous contents."""
     w = wl.WORKLOADS["tiny"]
