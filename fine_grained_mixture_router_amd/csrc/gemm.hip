@@ -13,8 +13,10 @@
 //
 // One kernel template serves both: a work-list entry (group, m0, n0, nrows)
 // names the tile; A rows are gathered through tok_of (G1) or read in place
-// (G2).  Tiles are BM x BN with BK = 64, staged through LDS (double buffer,
-// XOR-swizzled 16-byte chunks) and consumed by v_mfma_f32_32x32x16_bf16.
+// (G2).  Tiles are BM x BN with BK = 64, staged through LDS in XOR-swizzled
+// 16-byte chunks (a double buffer in the few-rows tile, a ring of five
+// operand slots in the many-rows tile) and consumed by
+// v_mfma_f32_32x32x16_bf16.
 // The grid is the work-list bound; workgroups past the device-side count
 // exit at once.  Workgroup ids are dealt round-robin over the 8 XCDs; the
 // many-rows kernels (and the 8-bit few-rows one) remap them so that each
