@@ -60,3 +60,48 @@ def test_multi_gpu_request_exits(monkeypatch):
     with pytest.raises(SystemExit) as e:
         bench.main()
     assert e.value.code == 2
+
+
+def test_algorithmic_work_of_the_v3_batches():
+    """The FLOPs and bytes the roofline lines divide by, from the layer's
+    definition: gate/up does 4·d·I per routed or shared row (8.66 TFLOP at
+    16 384 tokens, top-8 + 1 shared), the layer adds the down GEMM's 2·d·I
+    per row and the router's 2·d·E per token; decode reads W1 and W3 of
+    every touched expert and of the shared one."""
+    import numpy as np
+    from synth import workloads as wl
+    w = wl.WORKLOADS["v3_prefill"]
+    counts = np.zeros(w.E, dtype=np.int64)
+    counts[:43] = 1                                    # 43 touched experts
+    a = bench.algorithmic(w, counts)
+    rows = w.T * (w.K + w.Ks)
+    assert a["g1_flops"] == 4.0 * w.d * w.I * rows == 8658654068736.0
+    assert a["layer_flops"] == 6.0 * w.d * w.I * rows + 2.0 * w.T * w.d * w.E
+    assert a["touched"] == 43
+    wd = wl.WORKLOADS["v3_decode"]
+    cd = np.ones(wd.E, dtype=np.int64)
+    ad = bench.algorithmic(wd, cd)
+    w13 = (wd.E + wd.Ks) * 2 * wd.I * wd.d * 2         # bf16 W1 + W3, routed and shared
+    assert ad["g1_bytes"] == w13 + 2 * wd.T * wd.d + 2 * wd.T * (wd.K + wd.Ks) * wd.I
+    # 8-bit: one byte per routed weight plus a 4-byte scale per weight row
+    a8 = bench.algorithmic_fp8(wd, cd)
+    assert a8["g1_bytes"] == (wd.E * (2 * wd.I * wd.d + 4 * 2 * wd.I) + wd.Ks * 2 * 2 * wd.I * wd.d
+                              + 2 * wd.T * wd.d + 2 * wd.T * (wd.K + wd.Ks) * wd.I)
+
+
+def test_layer_roofline_time_of_one_expert():
+    """An expert of n rows costs max(6·d·I·n / peak, bytes / bandwidth) in
+    the layer roofline: a one-expert, one-token layer is bandwidth-bound by
+    its 3·d·I bf16 weights."""
+    import numpy as np
+    from synth.workloads import Workload
+    import dataclasses
+    base = __import__("synth.workloads", fromlist=["WORKLOADS"]).WORKLOADS["tiny"]
+    w = dataclasses.replace(base, T=1, d=512, E=1, I=256, K=1, Ks=0, Is=256)
+    t = bench.layer_roofline_ms(w, np.array([1]))
+    bw = bench.PEAK_HBM_GBS * 1e9
+    weights = 6.0 * w.d * w.I
+    expect = (max(2.0 * w.d * w.E / (bench.PEAK_BF16_TFLOPS * 1e12), (2.0 * w.d + 2.0 * w.E * w.d) / bw)
+              + (weights + 1 * (2.0 * w.d + 4.0 * w.I + 2.0 * w.d)) / bw
+              + (2 + 1 + 0) * w.d * 2.0 / bw) * 1e3
+    assert abs(t - expect) <= 1e-12 * expect
