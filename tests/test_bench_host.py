@@ -93,10 +93,11 @@ def test_layer_roofline_time_of_one_expert():
     """An expert of n rows costs max(6·d·I·n / peak, bytes / bandwidth) in
     the layer roofline: a one-expert, one-token layer is bandwidth-bound by
     its 3·d·I bf16 weights."""
-    import numpy as np
-    from synth.workloads import Workload
     import dataclasses
-    base = __import__("synth.workloads", fromlist=["WORKLOADS"]).WORKLOADS["tiny"]
+
+    import numpy as np
+    from synth import workloads as wl
+    base = wl.WORKLOADS["tiny"]
     w = dataclasses.replace(base, T=1, d=512, E=1, I=256, K=1, Ks=0, Is=256)
     t = bench.layer_roofline_ms(w, np.array([1]))
     bw = bench.PEAK_HBM_GBS * 1e9
