@@ -244,3 +244,33 @@ def test_fp8_v3_prefill_shape():
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     del D
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,nsample", [("tiny", 96), ("16b_zipf", 96)])
+def test_fp8_v3_style_gate(name, nsample):
+    """8-bit routed weights under the V3-style gate (sigmoid affinities, a
+    selection-only bias, renormalised gates): the router is shared with the
+    bf16 path, so this checks that the 8-bit GEMMs take its gates as given."""
+    w = wl.WORKLOADS[name]
+    kw = dict(renorm=True, sigmoid=True)
+    _log(f"[fp8] {name} sigmoid+renorm")
+    L = _fp8_layer(w)
+    L["bias"] = (np.random.default_rng(w.T + 3).standard_normal(w.E) * 0.02).astype(np.float32)
+    D = _upload(L)
+    out, idx, gate = _gpu(D, w.K, **kw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.T + 11)
+    tok = np.unique(np.r_[0, rng.choice(w.T, min(nsample, w.T), replace=False), w.T - 1])
+    ref = _ref(L, w.K, tok, **kw)
+    gi, gg = idx.cpu().numpy()[tok], gate.cpu().numpy()[tok]
+    # selection keys of the sigmoid gate: score + bias
+    _, _, _, probs = oracle.route(L["x"][tok], L["C"], L["bias"], w.K, return_probs=True, **kw)
+    rows = np.arange(len(tok))[:, None]
+    keys = probs[rows, ref["idx"]] + L["bias"].astype(np.float64)[ref["idx"]]
+    check_routing(gi, gg, ref["idx"], ref["gate"], ref["margin"], w.K, ref_keys=keys)
+    check_close(synth.bf16_to_f64(bf16_bits(out)[tok]), ref["out"])
+    dout, didx, _ = _gpu(D, w.K, no_residual=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(didx, idx)
+    dref = _ref(L, w.K, tok, no_residual=True, forced_idx=gi, **kw)
+    check_part(out_f64(dout)[tok], dref["out"], "delta")
