@@ -57,6 +57,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp = ctypes.c_void_p
 _lib.moe_workspace_size.restype = ctypes.c_size_t
 _lib.moe_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+_lib.moe_route_workspace_size.restype = ctypes.c_size_t
+_lib.moe_route_workspace_size.argtypes = [ctypes.POINTER(Shape)]
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_status_string.argtypes = [ctypes.c_int]
 _lib.moe_forward.restype = ctypes.c_int
@@ -79,7 +81,7 @@ _lib.moe_forward_fp8.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [ctypes.c
 _lib.moe_profile_stream_read.restype = ctypes.c_int
 _lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
-EXPORTS = ("moe_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
+EXPORTS = ("moe_workspace_size", "moe_route_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
            "moe_profile_begin", "moe_profile_begin_slots", "moe_profile_end", "moe_profile_slot_name",
            "moe_profile_stream_read")
 N_SLOTS = 7
@@ -105,13 +107,32 @@ def make_shape(T, d, E, I, K, Ks=0, Is=0, no_residual=False, renorm=False,
     return Shape(T, d, E, I, K, Ks, Is if Ks else 0, flags)
 
 
-def segment(N: int, m: int, I_std: int, K: int, Ks: int = 0) -> dict:
-    """Fine-grained segmentation of N standard experts of inter-dim I_std into
-    E = N*m experts of inter-dim I_std/m ("DeepSeekMoE 深度解读报告" section
-    2.2).  K (routed experts per token) and Ks are passed through."""
+def segment(N: int, m: int, I_std: int, K_std: int, Ks: int = 0,
+            isolate_from_pool: bool = True) -> dict:
+    """Layer shape of DeepSeekMoE's fine-grained segmentation and shared-expert
+    isolation ("DeepSeekMoE 深度解读报告", sections 2.2 and 2.3).
+
+    N standard experts of inter-dim I_std, K_std of them active per token,
+    are each split m ways along the intermediate dimension: N*m experts of
+    inter-dim I_std/m, with m*K_std of them active, so the parameters and the
+    per-token compute stay those of the unsegmented layer (section 2.2).  Ks
+    of the fine-grained experts are then isolated as shared experts that
+    every token uses (section 2.3): with isolate_from_pool they come out of
+    the N*m pool and the routed active count drops by Ks, which keeps both
+    totals fixed (E = N*m - Ks routed, K = m*K_std - Ks); without it the Ks
+    shared experts are added on top (E = N*m, K = m*K_std).  The 2B
+    validation layer is segment(16, 4, 3584, 2, Ks=1): 63 routed experts of
+    inter 896, top-7, plus one shared."""
+    if m < 1 or N < 1 or K_std < 0 or Ks < 0:
+        raise ValueError("N, m >= 1 and K_std, Ks >= 0")
     if I_std % m:
         raise ValueError("I_std must be divisible by m")
-    return dict(E=N * m, I=I_std // m, K=K, Ks=Ks, Is=I_std // m)
+    E, K = N * m, m * K_std
+    if isolate_from_pool:
+        E, K = E - Ks, K - Ks
+        if E < 1 or K < 0:
+            raise ValueError("more shared experts than the segmented pool or active count holds")
+    return dict(E=E, I=I_std // m, K=K, Ks=Ks, Is=I_std // m)
 
 
 def workspace_size(shape: Shape) -> int:
@@ -121,23 +142,130 @@ def workspace_size(shape: Shape) -> int:
     return int(n)
 
 
+def route_workspace_size(shape: Shape) -> int:
+    n = _lib.moe_route_workspace_size(ctypes.byref(shape))
+    if n == 0:
+        raise MoEError(2, status_string(2))
+    return int(n)
+
+
 def _ptr(t):
     return None if t is None else _vp(t.data_ptr())
 
 
-def _stream(device, stream):
-    import torch
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return _vp(s.cuda_stream)
+def _resolve_stream(device, stream):
+    """(stream object, whether it differs from the device's current stream)."""
+    cur = torch.cuda.current_stream(device)
+    if stream is None:
+        return cur, False
+    return stream, stream.cuda_stream != cur.cuda_stream
 
 
-def _shape_of(x, centroids, w1, ws1, K, no_residual, renorm=False, sigmoid=False):
-    T, d = x.shape
-    E = centroids.shape[0] if centroids is not None else (w1.shape[0] if w1 is not None else 1)
-    I = w1.shape[1] if w1 is not None else 64
-    Ks = ws1.shape[0] if ws1 is not None else 0
-    Is = ws1.shape[1] if ws1 is not None and Ks else 0
-    return make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
+def _need(t, name, dtype, shape, device):
+    """Validate a tensor argument before its pointer crosses the ABI: on
+    `device`, of `dtype`, exactly `shape`, contiguous.  A mismatch raises
+    ValueError and nothing is launched."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _absent(t, name):
+    if t is not None:
+        raise ValueError(f"{name} must be None here")
+
+
+class _Alloc:
+    """Allocations made on behalf of the caller.  With an explicit stream
+    other than the current one, every such tensor is marked as used by that
+    stream (record_stream), so torch's caching allocator does not hand its
+    memory to other work before the enqueued kernels are done with it."""
+
+    def __init__(self, device, stream):
+        self.device = device
+        self.stream, self.side = _resolve_stream(device, stream)
+
+    def empty(self, shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=self.device)
+        if self.side:
+            t.record_stream(self.stream)
+        return t
+
+    def handle(self):
+        return _vp(self.stream.cuda_stream)
+
+
+def _x_of(x):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [T, d]")
+    if not x.is_cuda:
+        raise ValueError("x must be a device (HIP) tensor")
+    return x.shape[0], x.shape[1], x.device
+
+
+def _check_routing_args(T, d, E, K, centroids, bias, dev):
+    if K > 0:
+        _need(centroids, "centroids", torch.bfloat16, (E, d), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), dev)
+
+
+def _check_shared(ws1, ws3, ws2, d, dev):
+    if ws1 is None and ws3 is None and ws2 is None:
+        return 0, 0
+    if ws1 is None or ws1.dim() != 3:
+        raise ValueError("ws1 must be [Ks, Is, d] (or all of ws1/ws3/ws2 None)")
+    Ks, Is = ws1.shape[0], ws1.shape[1]
+    _need(ws1, "ws1", torch.bfloat16, (Ks, Is, d), dev)
+    _need(ws3, "ws3", torch.bfloat16, (Ks, Is, d), dev)
+    _need(ws2, "ws2", torch.bfloat16, (Ks, d, Is), dev)
+    return Ks, (Is if Ks else 0)
+
+
+def _routing_outputs(al, T, K, topk_idx, topk_gate, want):
+    if K > 0:
+        if topk_idx is not None:
+            _need(topk_idx, "topk_idx", torch.int32, (T, K), al.device)
+        elif want:
+            topk_idx = al.empty((T, K), torch.int32)
+        if topk_gate is not None:
+            _need(topk_gate, "topk_gate", torch.float32, (T, K), al.device)
+        elif want:
+            topk_gate = al.empty((T, K), torch.float32)
+    else:
+        _absent(topk_idx, "topk_idx (K == 0)")
+        _absent(topk_gate, "topk_gate (K == 0)")
+    return topk_idx, topk_gate
+
+
+def _outputs(al, T, d, K, out, topk_idx, topk_gate, return_routing):
+    if out is None:
+        out = al.empty((T, d), torch.bfloat16)
+    else:
+        _need(out, "out", torch.bfloat16, (T, d), al.device)
+    return (out,) + _routing_outputs(al, T, K, topk_idx, topk_gate, return_routing)
+
+
+def _workspace(al, shape, workspace, size_fn=workspace_size):
+    nbytes = size_fn(shape)
+    if workspace is None:
+        return al.empty((nbytes,), torch.uint8)
+    if workspace.device != al.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"needs {nbytes}")
+    return workspace
 
 
 def forward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, bias=None,
@@ -147,25 +275,31 @@ def forward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, b
     """Layer forward on the GPU.  Tensors are CUDA (HIP) tensors: x [T,d],
     centroids [E,d], w1/w3 [E,I,d], w2 [E,d,I], ws1/ws3 [Ks,Is,d], ws2
     [Ks,d,Is] in bfloat16; bias float32 [E] or None.  renorm / sigmoid select
-    the gating variant (MOE_FLAG_RENORM / MOE_FLAG_SIGMOID).  Returns out
-    [T,d] bfloat16 (and (idx, gate) when return_routing)."""
-    import torch
-    shape = _shape_of(x, centroids, w1, ws1, K, no_residual, renorm, sigmoid)
-    dev = x.device
-    if out is None:
-        out = torch.empty((shape.T, shape.d), dtype=torch.bfloat16, device=dev)
-    if return_routing and K > 0:
-        if topk_idx is None:
-            topk_idx = torch.empty((shape.T, K), dtype=torch.int32, device=dev)
-        if topk_gate is None:
-            topk_gate = torch.empty((shape.T, K), dtype=torch.float32, device=dev)
-    nbytes = workspace_size(shape)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    the gating variant (MOE_FLAG_RENORM / MOE_FLAG_SIGMOID).  Every tensor is
+    checked (device, dtype, shape, contiguity) before anything is launched.
+    Returns out [T,d] bfloat16 (and (idx, gate) when return_routing)."""
+    T, d, dev = _x_of(x)
+    _need(x, "x", torch.bfloat16, (T, d), dev)
+    if K > 0:
+        if w1 is None or w1.dim() != 3:
+            raise ValueError("w1 must be [E, I, d] when K > 0")
+        E, I = w1.shape[0], w1.shape[1]
+        _need(w1, "w1", torch.bfloat16, (E, I, d), dev)
+        _need(w3, "w3", torch.bfloat16, (E, I, d), dev)
+        _need(w2, "w2", torch.bfloat16, (E, d, I), dev)
+    else:
+        E = centroids.shape[0] if centroids is not None else (w1.shape[0] if w1 is not None else 1)
+        I = w1.shape[1] if w1 is not None else 64
+    _check_routing_args(T, d, E, K, centroids, bias, dev)
+    Ks, Is = _check_shared(ws1, ws3, ws2, d, dev)
+    shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
+    al = _Alloc(dev, stream)
+    out, topk_idx, topk_gate = _outputs(al, T, d, K, out, topk_idx, topk_gate, return_routing)
+    workspace = _workspace(al, shape, workspace)
     code = _lib.moe_forward(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(bias), _ptr(w1),
                             _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out),
                             _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace),
-                            workspace.numel() * workspace.element_size(), _stream(dev, stream))
+                            workspace.numel() * workspace.element_size(), al.handle())
     _check(code)
     if return_routing:
         return out, topk_idx, topk_gate
@@ -179,29 +313,32 @@ def forward_fp8(x, centroids, w1q, w1s, w3q, w3s, w2q, w2s, ws1=None, ws3=None, 
     """Layer forward with 8-bit routed weights: w1q/w3q uint8 [E,I,d], w2q
     [E,d,I] (OCP E4M3 codes) with float32 per-row scales w1s/w3s [E,I], w2s
     [E,d]; shared experts ws* in bfloat16; the rest as forward()."""
-    import torch
-    T, d = x.shape
-    E = centroids.shape[0] if centroids is not None else (w1q.shape[0] if w1q is not None else 1)
-    I = w1q.shape[1] if w1q is not None else 64
-    Ks = ws1.shape[0] if ws1 is not None else 0
-    Is = ws1.shape[1] if ws1 is not None and Ks else 0
+    T, d, dev = _x_of(x)
+    _need(x, "x", torch.bfloat16, (T, d), dev)
+    if K > 0:
+        if w1q is None or w1q.dim() != 3:
+            raise ValueError("w1q must be [E, I, d] when K > 0")
+        E, I = w1q.shape[0], w1q.shape[1]
+        _need(w1q, "w1q", torch.uint8, (E, I, d), dev)
+        _need(w3q, "w3q", torch.uint8, (E, I, d), dev)
+        _need(w2q, "w2q", torch.uint8, (E, d, I), dev)
+        _need(w1s, "w1s", torch.float32, (E, I), dev)
+        _need(w3s, "w3s", torch.float32, (E, I), dev)
+        _need(w2s, "w2s", torch.float32, (E, d), dev)
+    else:
+        E = centroids.shape[0] if centroids is not None else (w1q.shape[0] if w1q is not None else 1)
+        I = w1q.shape[1] if w1q is not None else 64
+    _check_routing_args(T, d, E, K, centroids, bias, dev)
+    Ks, Is = _check_shared(ws1, ws3, ws2, d, dev)
     shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
-    dev = x.device
-    if out is None:
-        out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
-    if return_routing and K > 0:
-        if topk_idx is None:
-            topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-        if topk_gate is None:
-            topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
-    nbytes = workspace_size(shape)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    al = _Alloc(dev, stream)
+    out, topk_idx, topk_gate = _outputs(al, T, d, K, out, topk_idx, topk_gate, return_routing)
+    workspace = _workspace(al, shape, workspace)
     code = _lib.moe_forward_fp8(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(bias),
                                 _ptr(w1q), _ptr(w1s), _ptr(w3q), _ptr(w3s), _ptr(w2q), _ptr(w2s),
                                 _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(out), _ptr(topk_idx),
                                 _ptr(topk_gate), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(dev, stream))
+                                workspace.numel() * workspace.element_size(), al.handle())
     _check(code)
     if return_routing:
         return out, topk_idx, topk_gate
@@ -209,22 +346,24 @@ def forward_fp8(x, centroids, w1q, w1s, w3q, w3s, w2q, w2s, ws1=None, ws3=None, 
 
 
 def route(x, centroids, *, K: int, bias=None, renorm: bool = False, sigmoid: bool = False,
-          topk_idx=None, topk_gate=None, workspace=None, I: int = 64, stream=None):
-    """Routing only: returns (idx int32 [T,K], gate float32 [T,K])."""
-    import torch
-    T, d = x.shape
-    shape = make_shape(T, d, centroids.shape[0], I, K, renorm=renorm, sigmoid=sigmoid)
-    dev = x.device
-    if topk_idx is None:
-        topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    if topk_gate is None:
-        topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
-    nbytes = workspace_size(shape)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+          topk_idx=None, topk_gate=None, workspace=None, stream=None):
+    """Routing only: returns (idx int32 [T,K], gate float32 [T,K]).  Needs
+    only the routing scratch (moe_route_workspace_size)."""
+    T, d, dev = _x_of(x)
+    _need(x, "x", torch.bfloat16, (T, d), dev)
+    if centroids is None or centroids.dim() != 2:
+        raise ValueError("centroids must be [E, d]")
+    E = centroids.shape[0]
+    if K < 1:
+        raise ValueError("route needs K >= 1")
+    _check_routing_args(T, d, E, K, centroids, bias, dev)
+    shape = make_shape(T, d, E, 64, K, renorm=renorm, sigmoid=sigmoid)
+    al = _Alloc(dev, stream)
+    topk_idx, topk_gate = _routing_outputs(al, T, K, topk_idx, topk_gate, True)
+    workspace = _workspace(al, shape, workspace, route_workspace_size)
     code = _lib.moe_route(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(bias),
                           _ptr(topk_idx), _ptr(topk_gate), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream(dev, stream))
+                          workspace.numel() * workspace.element_size(), al.handle())
     _check(code)
     return topk_idx, topk_gate
 

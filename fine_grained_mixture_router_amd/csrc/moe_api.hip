@@ -53,8 +53,10 @@ bool shape_ok(const moe_shape_t* s) {
 
 // Fill the shape-derived part of the plan and the workspace offsets (as byte
 // offsets from 0); returns the total workspace size.  q8: the routed weights
-// are 8-bit (the same tile sizes; each has an 8-bit kernel).
-size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
+// are 8-bit (the same tile sizes; each has an 8-bit kernel).  route_only:
+// carve only what routing needs (affinity partials and the chunk masks; the
+// caller passes idx and gate), for moe_route.
+size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false) {
     (void)q8;
     memset(p, 0, sizeof(*p));
     p->T = s->T;
@@ -114,6 +116,10 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
         return o;
     };
     p->logits = (float*)take(s->K > 0 ? (size_t)p->split * s->T * p->Epad * 4 : 0);
+    if (route_only) {
+        p->masks = (uint64_t*)take((size_t)p->nchunk * p->Epad * 8);
+        return off;
+    }
     p->idx = (int32_t*)take((size_t)TK * 4);
     p->gate = (float*)take((size_t)TK * 4);
     p->masks = (uint64_t*)take((size_t)p->nchunk * p->Epad * 8);
@@ -133,6 +139,13 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8) {
 template <class T>
 T* rebase(T* off, char* base) {
     return reinterpret_cast<T*>(base + reinterpret_cast<size_t>(off));
+}
+
+// Route-only plan: the two pieces make_plan(route_only) carved.
+void place_route(Plan* p, void* ws) {
+    char* b = static_cast<char*>(ws);
+    p->logits = rebase(p->logits, b);
+    p->masks = rebase(p->masks, b);
 }
 
 void place(Plan* p, void* ws) {
@@ -208,7 +221,7 @@ void rec_free() {
 
 moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* centroids,
                           const float* bias, void* ws, size_t ws_bytes, Plan* plan,
-                          bool q8 = false) {
+                          bool q8 = false, bool route_only = false) {
     if (!shape) return MOE_ERR_NULL;
     if (!shape_ok(shape)) return MOE_ERR_SHAPE;
     if (!x || !ws) return MOE_ERR_NULL;
@@ -216,7 +229,7 @@ moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* c
     if (!aligned(x, 16) || (centroids && !aligned(centroids, 16))) return MOE_ERR_ALIGN;
     if (bias && !aligned(bias, 4)) return MOE_ERR_ALIGN;
     if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
-    const size_t need = make_plan(shape, plan, q8);
+    const size_t need = make_plan(shape, plan, q8, route_only);
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     return MOE_OK;
 }
@@ -231,6 +244,12 @@ __attribute__((visibility("default"))) size_t moe_workspace_size(const moe_shape
     const size_t a = make_plan(shape, &p, false);
     const size_t b = make_plan(shape, &p, true);   // moe_forward_fp8's plan
     return a > b ? a : b;
+}
+
+__attribute__((visibility("default"))) size_t moe_route_workspace_size(const moe_shape_t* shape) {
+    if (!shape_ok(shape) || shape->K < 1) return 0;
+    Plan p;
+    return make_plan(shape, &p, false, true);
 }
 
 __attribute__((visibility("default"))) const char* moe_status_string(moe_status_t st) {
@@ -349,14 +368,15 @@ __attribute__((visibility("default"))) moe_status_t moe_route(
     const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
     int32_t* topk_idx, float* topk_gate, void* workspace, size_t workspace_bytes, void* stream) {
     Plan p;
-    moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes, &p);
+    moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes,
+                                   &p, false, true);
     if (st != MOE_OK) return st;
     if (shape->K < 1) return MOE_ERR_SHAPE;
     if (!topk_idx || !topk_gate) return MOE_ERR_NULL;
     if (!aligned(topk_idx, 4) || !aligned(topk_gate, 4)) return MOE_ERR_ALIGN;
     st = device_ok();
     if (st != MOE_OK) return st;
-    place(&p, workspace);
+    place_route(&p, workspace);
     p.idx = topk_idx;
     p.gate = topk_gate;
     hipStream_t s = static_cast<hipStream_t>(stream);

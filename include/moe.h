@@ -87,12 +87,17 @@ typedef enum {
     MOE_ERR_HIP = 7          /* a HIP launch failed                         */
 } moe_status_t;
 
-/* Bytes of device workspace moe_forward / moe_forward_fp8 / moe_route need
- * for this shape
+/* Bytes of device workspace moe_forward / moe_forward_fp8 need for this
+ * shape
  * (routing scratch, the token permutation, tile lists, and the bf16
  * intermediates H [T·K·I + T·Ks·Is] and Y [T·(K+Ks), d]).  Pure host
  * arithmetic, no HIP call.  Returns 0 when the shape is invalid. */
 size_t moe_workspace_size(const moe_shape_t* shape);
+
+/* Bytes of device workspace moe_route needs for this shape: the routing
+ * scratch alone (no permutation, tile lists or H / Y).  Pure host
+ * arithmetic.  Returns 0 when the shape is invalid or K == 0. */
+size_t moe_route_workspace_size(const moe_shape_t* shape);
 
 /* Full layer forward (the definition at the top of this file).
  *
@@ -155,7 +160,8 @@ moe_status_t moe_forward_fp8(const moe_shape_t* shape, const void* x, const void
 
 /* Routing only: affinities, softmax (or the flags' gate), top-K
  * ("DeepSeekMoE 深度解读报告", section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both
- * required); same workspace as moe_forward.  K must be >= 1. */
+ * required).  The workspace needs moe_route_workspace_size() bytes (routing
+ * scratch only, far less than a forward's).  K must be >= 1. */
 moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* centroids,
                        const float* expert_bias, int32_t* topk_idx, float* topk_gate,
                        void* workspace, size_t workspace_bytes, void* stream);

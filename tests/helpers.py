@@ -23,6 +23,26 @@ PART_TOL = 5e-2
 PART_RMS_TOL = 1e-2
 
 
+def tile_cover_tokens(idx, E, Ks, T, bm=256):
+    """Tokens whose output rows touch every (group, M-tile) of the grouped
+    GEMMs' work lists: routed group e holds the tokens that chose expert e,
+    in token order (the permutation is stable), cut into tiles of bm rows;
+    each shared group holds every token in order.  One token per tile — the
+    one on the tile's last row, so each group's ragged last tile is among
+    them.  A token's output row spans every N tile, so checking these
+    tokens checks every work-list tile."""
+    idx = np.asarray(idx)
+    picks = set()
+    for e in range(E):
+        toks = np.nonzero((idx == e).any(axis=1))[0]
+        for m0 in range(0, toks.size, bm):
+            picks.add(int(toks[min(m0 + bm, toks.size) - 1]))
+    if Ks > 0:
+        for m0 in range(0, T, bm):
+            picks.add(min(m0 + bm, T) - 1)
+    return np.array(sorted(picks), dtype=np.int64)
+
+
 def to_dev(a, dtype=None):
     import torch
     if a is None:

@@ -152,11 +152,36 @@ def test_profile_validation():
 
 
 def test_segment_helper():
-    # N=16 experts of inter 4096 split m=4 -> 64 experts of inter 1024
-    g = moe.segment(16, 4, 4096, K=8, Ks=1)
-    assert (g["E"], g["I"], g["K"], g["Ks"]) == (64, 1024, 8, 1)
+    """Fine-grained segmentation ("DeepSeekMoE 深度解读报告" section 2.2: N*m
+    experts of inter I/m, m*K active) with shared-expert isolation (section
+    2.3: Ks of them always on, the routed active count cut by Ks): total and
+    active parameters equal those of the unsegmented layer."""
+    from oracle import cost
+    # the 2B validation layer: 16 standard experts of inter 3584, top-2,
+    # segmented m = 4 with one shared expert -> 63 routed of inter 896, top-7
+    g = moe.segment(16, 4, 3584, 2, Ks=1)
+    assert (g["E"], g["I"], g["K"], g["Ks"], g["Is"]) == (63, 896, 7, 1, 896)
+    # the tiny layer adds its shared expert on top of the 16 segments
+    t = moe.segment(4, 4, 1024, 1, Ks=1, isolate_from_pool=False)
+    assert (t["E"], t["I"], t["K"], t["Ks"]) == (16, 256, 4, 1)
+    d = 1280
+    for N, m, I_std, K_std, Ks in [(16, 4, 3584, 2, 1), (8, 2, 1024, 2, 0), (16, 8, 4096, 1, 3)]:
+        g = moe.segment(N, m, I_std, K_std, Ks=Ks)
+        seg = cost.layer_cost(g["E"], g["I"], g["K"], g["Ks"], g["Is"], d)
+        std = cost.layer_cost(N, I_std, K_std, 0, 0, d)
+        assert seg == std, (N, m, seg, std)
     with pytest.raises(ValueError):
-        moe.segment(4, 3, 1000, K=2)
+        moe.segment(4, 3, 1000, 2)
+    with pytest.raises(ValueError):
+        moe.segment(1, 2, 1024, 1, Ks=3)
+
+
+def test_route_workspace_is_routing_scratch_only():
+    s = moe.make_shape(16384, 7168, 256, 2048, 8, 1, 2048)
+    r = moe.route_workspace_size(s)
+    assert 0 < r < moe.workspace_size(s) / 20
+    assert moe.lib().moe_route_workspace_size(ctypes.byref(S(K=0))) == 0
+    assert moe.lib().moe_route_workspace_size(ctypes.byref(S(d=100))) == 0
 
 
 def test_stream_read_validation():

@@ -14,7 +14,8 @@ import oracle
 import synth
 from synth import workloads as wl
 
-from helpers import bf16_bits, check_close, check_part, check_rounding, check_routing, out_f64
+from helpers import (bf16_bits, check_close, check_part, check_rounding, check_routing, out_f64,
+                     tile_cover_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,7 +203,7 @@ def test_fp8_v3_decode_shape():
     torch.cuda.synchronize()
     ri, rg, rm = oracle.route(L["x"], L["C"], L["bias"], w.K)
     check_routing(idx.cpu().numpy(), gate.cpu().numpy(), ri, rg, rm, w.K)
-    tok = np.unique(np.r_[0, np.random.default_rng(5).choice(w.T, 24, replace=False), w.T - 1])
+    tok = np.arange(w.T)                      # every token: each expert's one tile
     ref = _ref(L, w.K, tok)
     ob = bf16_bits(out)[tok]
     check_close(synth.bf16_to_f64(ob), ref["out"])
@@ -219,7 +220,8 @@ def test_fp8_v3_prefill_shape():
     """The V3-shape prefill batch (16384 tokens, Zipf(1.2) bias) with 8-bit
     routed weights: the 256 x 256 tiles of the 8-bit kernel, shared-expert
     tiles in bf16 within the same launch; routing of every token, the output
-    and its delta on a token sample."""
+    and its delta on tokens that put a checked row in every (group, M-tile)
+    of the work lists."""
     w = wl.WORKLOADS["v3_prefill"]
     _log("[fp8] v3_prefill: generating inputs")
     L = _fp8_layer(w)
@@ -230,7 +232,8 @@ def test_fp8_v3_prefill_shape():
     ri, rg, rm = oracle.route(L["x"], L["C"], L["bias"], w.K)
     exempt = check_routing(idx.cpu().numpy(), gate.cpu().numpy(), ri, rg, rm, w.K)
     assert exempt < 0.1 * w.T
-    tok = np.unique(np.r_[0, np.random.default_rng(9).choice(w.T, 32, replace=False), w.T - 1])
+    tok = tile_cover_tokens(idx.cpu().numpy(), w.E, w.Ks, w.T)
+    _log(f"[fp8] v3_prefill: checking {tok.size} tokens, one per (group, M-tile)")
     ref = _ref(L, w.K, tok)
     ob = bf16_bits(out)[tok]
     check_close(synth.bf16_to_f64(ob), ref["out"])

@@ -263,6 +263,28 @@ def test_p9_equal_cost_segmentation(N, m, Kstd, I):
     assert a == b
 
 
+def test_p9_layer_cost_exact_integers():
+    """layer_cost against exact integers fixed elsewhere: one bias-free expert
+    of the youleyou printout (dim 7168, inter 2048) has 3 * 7168 * 2048 =
+    44 040 192 parameters (the printed 44.05 M minus its 2 * 2048 + 7168
+    biases), so the V3-shape layer (256 routed + 1 shared, top-8) holds
+    257 such experts and a token passes through 9 of them, one MAC per
+    parameter.  Dropping d, I, K or the shared term changes these numbers."""
+    one = 44_040_192
+    assert cost.expert_cost(7168, 2048, 1, bias=False)["params"] == one
+    assert cost.expert_cost(7168, 2048, 1, bias=True)["params"] - (2 * 2048 + 7168) == one
+    v3 = cost.layer_cost(256, 2048, 8, 1, 2048, 7168)
+    assert v3 == dict(params=257 * one, token_macs=9 * one)
+    assert v3["params"] == 11_318_329_344
+    # the tiny layer: 16 routed + 1 shared of inter 256 on d = 512, top-4
+    assert cost.layer_cost(16, 256, 4, 1, 256, 512) == dict(params=17 * 393_216,
+                                                            token_macs=5 * 393_216)
+    # shared inter-dim distinct from the routed one, two shared experts
+    assert cost.layer_cost(64, 1408, 6, 2, 704, 2048) == dict(
+        params=64 * 3 * 2048 * 1408 + 2 * 3 * 2048 * 704,
+        token_macs=6 * 3 * 2048 * 1408 + 2 * 3 * 2048 * 704)
+
+
 # ---------------------------------------------------------------- P10
 def test_p10_combinations():
     for c in _gold("combinations.json")["cases"]:
