@@ -63,6 +63,13 @@ def lib():
         L.oracle_forward_fp8.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, vp,
                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_backward.restype = i32
+        L.oracle_backward.argtypes = [ctypes.POINTER(_Shape), vp, i32, vp, vp,
+                                      vp, vp, vp, vp, vp, vp,
+                                      vp, ctypes.c_double, vp,
+                                      vp, i32, vp, i32, i32, i32,
+                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, i32]
         L.oracle_e4m3.restype = ctypes.c_double
         L.oracle_e4m3.argtypes = [ctypes.c_uint8]
         _lib = L
@@ -226,3 +233,71 @@ def forward_fp8(x_rows, C, bias, q1, s1, q3, s3, q2, s2, ws1, ws3, ws2, K, no_re
                                     _ptr(gate), _ptr(margin), int(nthreads))
     return dict(out=out, shared=shared, routed=routed, idx=idx, gate=gate, margin=margin,
                 threads=int(used))
+
+
+def backward(x_all, C, bias, w1, w3, w2, ws1, ws3, ws2, K, dout, *, alpha=0.0, tokens=None,
+             experts=(), want_shared=False, want_dC=False, no_residual=False, forced_idx=None,
+             renorm=False, sigmoid=False, nthreads=0):
+    """Backward of the layer in fp64 (oracle.c, oracle_backward).
+
+    x_all, dout: [T, d] bf16 bits — every token of the batch (the balance
+    statistics and dC need all of them).  Weights as for forward().  alpha
+    weighs the expert-level balance loss.  Returns a dict with, where asked:
+    dx [n_tok, d], dgate [n_tok, K], idx [n_tok, K] for `tokens` (default
+    all); dw1/dw3 [n_exp, I, d], dw2 [n_exp, d, I] for `experts`; dws1/dws3/
+    dws2 for the shared experts (want_shared); dC [E, d] (want_dC); and
+    counts [E], mean_score [E], bal (L_bal) and bal_alpha (alpha * L_bal)."""
+    x_all = np.ascontiguousarray(x_all)
+    T, d = x_all.shape
+    E = C.shape[0]
+    C = _u16(C, (E, d))
+    dout = _u16(dout, (T, d))
+    Ks = 0 if ws1 is None else len(ws1)
+    I = next(a.shape[0] for a in w1 if a is not None) if E else 0
+    Is = ws1[0].shape[0] if Ks else 0
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    keep = []
+    tw = []
+    zero_i = np.zeros((I, d), np.uint16)
+    zero_o = np.zeros((d, I), np.uint16)
+    for stack, shp, z in ((w1, (I, d), zero_i), (w3, (I, d), zero_i), (w2, (d, I), zero_o)):
+        lst = [z if stack[e] is None else stack[e] for e in range(E)]
+        t, k = _ptr_table(lst, E, shp)
+        tw.append(t)
+        keep.append(k)
+    ts = []
+    for stack, shp in ((ws1, (Is, d)), (ws3, (Is, d)), (ws2, (d, Is))):
+        t, k = _ptr_table(stack if Ks else [], Ks, shp)
+        ts.append(t)
+        keep.append(k)
+    tok = np.arange(T, dtype=np.int32) if tokens is None else np.ascontiguousarray(tokens, np.int32)
+    assert tok.size == 0 or (tok.min() >= 0 and tok.max() < T and np.unique(tok).size == tok.size)
+    ex = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    assert ex.size == 0 or (ex.min() >= 0 and ex.max() < E)
+    fi = None
+    if forced_idx is not None:
+        fi = np.ascontiguousarray(forced_idx, dtype=np.int32)
+        assert fi.shape == (T, K)
+    sh = _Shape(T, d, E, I, K, Ks, Is,
+                (NO_RESIDUAL if no_residual else 0) | _gating(renorm, sigmoid))
+    n, m = tok.size, ex.size
+    r = dict(dx=np.zeros((n, d)), dgate=np.zeros((n, K)), idx=np.zeros((n, K), np.int32),
+             dw1=np.zeros((m, I, d)), dw3=np.zeros((m, I, d)), dw2=np.zeros((m, d, I)),
+             dws1=np.zeros((Ks, Is, d)) if want_shared else None,
+             dws3=np.zeros((Ks, Is, d)) if want_shared else None,
+             dws2=np.zeros((Ks, d, Is)) if want_shared else None,
+             dC=np.zeros((E, d)) if want_dC else None,
+             counts=np.zeros(E, np.int64), mean_score=np.zeros(E), bal=np.zeros(2))
+    used = lib().oracle_backward(ctypes.byref(sh), _ptr(x_all), T, _ptr(C), _ptr(b),
+                                 tw[0], tw[1], tw[2], ts[0], ts[1], ts[2],
+                                 _ptr(dout), float(alpha), _ptr(fi),
+                                 _ptr(tok), n, _ptr(ex), m, int(bool(want_shared)),
+                                 int(bool(want_dC)),
+                                 _ptr(r["dx"]), _ptr(r["dgate"]), _ptr(r["idx"]), _ptr(r["dw1"]),
+                                 _ptr(r["dw3"]), _ptr(r["dw2"]), _ptr(r["dws1"]), _ptr(r["dws3"]),
+                                 _ptr(r["dws2"]), _ptr(r["dC"]), _ptr(r["counts"]),
+                                 _ptr(r["mean_score"]), _ptr(r["bal"]), int(nthreads))
+    r["bal_alpha"] = float(r["bal"][1])
+    r["bal"] = float(r["bal"][0])
+    r["threads"] = int(used)
+    return r

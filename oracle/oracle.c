@@ -344,3 +344,389 @@ int32_t oracle_forward_fp8(const oracle_shape* s, const uint16_t* x_rows, int32_
     free(r1); free(r3); free(r2); free(h1); free(h3); free(h2);
     return used;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the layer (the training side), for a given upstream gradient.
+ *
+ * Objective whose gradients are returned:
+ *
+ *   Lambda = sum_{t,j} dout[t,j] * out[t,j]  +  alpha * L_bal
+ *
+ * dout is the upstream gradient dLoss/dout (bf16, as the GPU receives it).
+ * L_bal is the expert-level balance loss of "DeepSeekMoE 深度解读报告"
+ * (sections 2.5 and 3.2): over the batch, each expert's hit rate and mean
+ * gate score are taken, and their agreement with a uniform load is
+ * penalised with a small factor alpha.  The pages name the two statistics
+ * but print no formula; the reading here is
+ *
+ *   f_e = E * count_e / (K * T)         hit rate, 1 for a perfectly even load
+ *   P_e = (1/T) * sum_t s_{t,e}         mean score (the full softmax or
+ *                                       sigmoid score of step 2, before any
+ *                                       renormalisation)
+ *   L_bal = sum_e f_e * P_e
+ *
+ * with f_e held fixed (a count is piecewise constant in the inputs).  The
+ * top-K choice is piecewise constant too, so no gradient flows through it;
+ * gradients reach the affinities through the kept gates (and through every
+ * score via L_bal).  The per-expert logit bias is a fixed input and gets no
+ * gradient.
+ *
+ * Per token t (x = x[t], dO = dout[t]) and per expert with weight
+ * matrices W1, W3 [inter, d], W2 [d, inter] and gate g (1 for a shared
+ * expert), from step 4 of the forward:
+ *
+ *   a = W1 x,  b = W3 x,  h = silu(a) * b,  y = W2 h
+ *   dgate   = <dO, y>                          (routed experts)
+ *   dh      = g * W2^T dO
+ *   silu'(a) = sig(a) * (1 + a * (1 - sig(a))),  sig(a) = 1 / (1 + e^-a)
+ *   da      = dh * b * silu'(a),   db = dh * silu(a)
+ *   dx     += W1^T da + W3^T db
+ *   dW2    += g * dO (x) h,   dW1 += da (x) x,   dW3 += db (x) x
+ *
+ * and for the router, from steps 2 and 3 (s: the E scores of the token):
+ *
+ *   gate -> score:  ds_{e_k} = dgate_k (plain gates), or, with
+ *                   ORACLE_RENORM (gate_k = s_{e_k} / Z, Z = sum_m s_{e_m}),
+ *                   ds_{e_k} = (dgate_k - sum_m dgate_m * gate_m) / Z;
+ *                   0 for experts not kept
+ *   balance:        ds_e += alpha * f_e / T           (every expert)
+ *   score -> affinity:
+ *       softmax     dl_j = s_j * (ds_j - sum_e s_e * ds_e)
+ *       sigmoid     dl_j = s_j * (1 - s_j) * ds_j
+ *   dx += sum_j dl_j C_j,   dC_j += dl_j x            (C: the centroids)
+ *
+ * plus dx += dO for the residual (unless ORACLE_NO_RESIDUAL).
+ * ------------------------------------------------------------------------ */
+
+static double sigm(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* Per (token, expert) pieces of the expert backward: a, b and dh (= g W2^T
+ * dO); dgate_out (if not NULL) = <dO, W2 h>. */
+static void expert_bwd_vectors(int d, int inter, const uint16_t* w1, const uint16_t* w3,
+                               const uint16_t* w2, const double* x_t, const double* dO,
+                               double g, double* a, double* b, double* h, double* dh,
+                               double* dgate_out) {
+    for (int i = 0; i < inter; ++i) {
+        double sa = 0.0, sb = 0.0;
+        for (int j = 0; j < d; ++j) {
+            sa += widen(w1[(size_t)i * d + j]) * x_t[j];
+            sb += widen(w3[(size_t)i * d + j]) * x_t[j];
+        }
+        a[i] = sa;
+        b[i] = sb;
+        h[i] = silu(sa) * sb;
+        dh[i] = 0.0;
+    }
+    double dg = 0.0;
+    for (int o = 0; o < d; ++o) {
+        double y = 0.0;
+        const uint16_t* row = w2 + (size_t)o * inter;
+        for (int i = 0; i < inter; ++i) {
+            const double w = widen(row[i]);
+            y += w * h[i];
+            dh[i] += w * dO[o];
+        }
+        dg += dO[o] * y;
+    }
+    for (int i = 0; i < inter; ++i) dh[i] *= g;
+    if (dgate_out) *dgate_out = dg;
+}
+
+/* da, db from a, b, dh (in place: a -> da, b -> db). */
+static void swiglu_bwd(int inter, double* a, double* b, const double* dh) {
+    for (int i = 0; i < inter; ++i) {
+        const double sg = sigm(a[i]);
+        const double dsilu = sg * (1.0 + a[i] * (1.0 - sg));
+        const double da = dh[i] * b[i] * dsilu;
+        const double db = dh[i] * (a[i] * sg);
+        a[i] = da;
+        b[i] = db;
+    }
+}
+
+/* dx += W1^T da + W3^T db */
+static void expert_dx(int d, int inter, const uint16_t* w1, const uint16_t* w3,
+                      const double* da, const double* db, double* dx) {
+    for (int i = 0; i < inter; ++i) {
+        const uint16_t* r1 = w1 + (size_t)i * d;
+        const uint16_t* r3 = w3 + (size_t)i * d;
+        for (int j = 0; j < d; ++j) dx[j] += widen(r1[j]) * da[i] + widen(r3[j]) * db[i];
+    }
+}
+
+/* Weight gradients of one expert over its tokens (in token order).  xs
+ * [n, d], dOs [n, d] and gs [n] are the tokens' rows, upstream gradients
+ * and gates; dw1, dw3 [inter, d], dw2 [d, inter] are written. */
+static void expert_dw(int d, int inter, const uint16_t* w1, const uint16_t* w3,
+                      const uint16_t* w2, int n, const double* xs, const double* dOs,
+                      const double* gs, double* dw1, double* dw3, double* dw2, int nthreads) {
+    double* A = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * inter);   /* -> da */
+    double* B = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * inter);   /* -> db */
+    double* Hh = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * inter);  /* g * h */
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* dh = malloc(sizeof(double) * (size_t)inter);
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n; ++t) {
+            double* a = A + (size_t)t * inter;
+            double* b = B + (size_t)t * inter;
+            double* h = Hh + (size_t)t * inter;
+            expert_bwd_vectors(d, inter, w1, w3, w2, xs + (size_t)t * d, dOs + (size_t)t * d,
+                               gs[t], a, b, h, dh, NULL);
+            swiglu_bwd(inter, a, b, dh);
+            for (int i = 0; i < inter; ++i) h[i] *= gs[t];
+        }
+        free(dh);
+        /* each output row is owned by one thread; tokens summed in order */
+#pragma omp for schedule(static)
+        for (int i = 0; i < inter; ++i) {
+            double* r1 = dw1 + (size_t)i * d;
+            double* r3 = dw3 + (size_t)i * d;
+            for (int j = 0; j < d; ++j) r1[j] = r3[j] = 0.0;
+            for (int t = 0; t < n; ++t) {
+                const double da = A[(size_t)t * inter + i], db = B[(size_t)t * inter + i];
+                const double* xt = xs + (size_t)t * d;
+                for (int j = 0; j < d; ++j) {
+                    r1[j] += da * xt[j];
+                    r3[j] += db * xt[j];
+                }
+            }
+        }
+#pragma omp for schedule(static)
+        for (int o = 0; o < d; ++o) {
+            double* r2 = dw2 + (size_t)o * inter;
+            for (int i = 0; i < inter; ++i) r2[i] = 0.0;
+            for (int t = 0; t < n; ++t) {
+                const double go = dOs[(size_t)t * d + o];
+                const double* h = Hh + (size_t)t * inter;
+                for (int i = 0; i < inter; ++i) r2[i] += go * h[i];
+            }
+        }
+    }
+    free(A); free(B); free(Hh);
+}
+
+/* Backward of the layer on a batch of T tokens (x_all, dout_all: [T, d]
+ * bf16).  Outputs, each only where asked:
+ *   tok[n_tok]:  dx [n_tok, d], dgate [n_tok, K] (d Lambda / d gate_k),
+ *                idx [n_tok, K] (the routing they were taken under)
+ *   exps[n_exp]: dw1, dw3 [n_exp, I, d], dw2 [n_exp, d, I] of those routed
+ *                experts
+ *   want_shared: dws1, dws3 [Ks, Is, d], dws2 [Ks, d, Is]
+ *   want_dC:     dC [E, d]
+ *   always:      counts [E], mean_score [E] (P_e), bal [2] = {L_bal, alpha * L_bal}
+ * forced_idx ([T, K] or NULL) replaces the selection as in the forward. */
+int32_t oracle_backward(const oracle_shape* s, const uint16_t* x_all, int32_t T,
+                        const uint16_t* C, const float* bias,
+                        const uint16_t* const* w1, const uint16_t* const* w3,
+                        const uint16_t* const* w2,
+                        const uint16_t* const* ws1, const uint16_t* const* ws3,
+                        const uint16_t* const* ws2,
+                        const uint16_t* dout_all, double alpha, const int32_t* forced_idx,
+                        const int32_t* tok, int32_t n_tok, const int32_t* exps, int32_t n_exp,
+                        int32_t want_shared, int32_t want_dC,
+                        double* dx, double* dgate, int32_t* idx_out,
+                        double* dw1, double* dw3, double* dw2,
+                        double* dws1, double* dws3, double* dws2, double* dC,
+                        int64_t* counts, double* mean_score, double* bal, int32_t nthreads) {
+    const int d = s->d, E = s->E, K = s->K, I = s->I, Ks = s->Ks, Is = s->Is;
+    const int ren = (s->flags & ORACLE_RENORM) != 0, sig = (s->flags & ORACLE_SIGMOID) != 0;
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    /* Pass 1: routing of every token (scores, kept experts and gates). */
+    int32_t* idx_all = malloc(sizeof(int32_t) * (size_t)T * (K > 0 ? K : 1));
+    double* gate_all = malloc(sizeof(double) * (size_t)T * (K > 0 ? K : 1));
+    double* prob_all = malloc(sizeof(double) * (size_t)T * E);
+#pragma omp parallel num_threads(nthreads)
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double* xt = malloc(sizeof(double) * (size_t)d);
+        double* key = malloc(sizeof(double) * (size_t)E);
+        uint8_t* tk = malloc((size_t)E);
+        double margin;
+#pragma omp for schedule(dynamic, 4)
+        for (int32_t t = 0; t < T; ++t) {
+            for (int j = 0; j < d; ++j) xt[j] = widen(x_all[(size_t)t * d + j]);
+            int32_t* idx = idx_all + (size_t)t * K;
+            double* gate = gate_all + (size_t)t * K;
+            double* pr = prob_all + (size_t)t * E;
+            route_token(s, xt, C, bias, key, pr, tk, idx, gate, &margin);
+            if (forced_idx) {
+                double z = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    idx[k] = forced_idx[(size_t)t * K + k];
+                    gate[k] = pr[idx[k]];
+                    z += gate[k];
+                }
+                if (ren)
+                    for (int k = 0; k < K; ++k) gate[k] /= z;
+            }
+        }
+        free(xt); free(key); free(tk);
+    }
+    /* balance statistics, summed in token order */
+    double* fe = malloc(sizeof(double) * (size_t)E);
+    for (int e = 0; e < E; ++e) {
+        counts[e] = 0;
+        mean_score[e] = 0.0;
+    }
+    for (int32_t t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) counts[idx_all[(size_t)t * K + k]] += 1;
+        for (int e = 0; e < E; ++e) mean_score[e] += prob_all[(size_t)t * E + e];
+    }
+    double lb = 0.0;
+    for (int e = 0; e < E; ++e) {
+        mean_score[e] /= (double)T;
+        fe[e] = K > 0 ? (double)E * (double)counts[e] / ((double)K * (double)T) : 0.0;
+        lb += fe[e] * mean_score[e];
+    }
+    bal[0] = lb;
+    bal[1] = alpha * lb;
+
+    /* Pass 2: per token — expert backward (dx, dgate) and router backward
+     * (dl).  dl is kept for every token when dC is wanted. */
+    int32_t n_rt = want_dC ? T : n_tok;                  /* tokens taken through pass 2 */
+    int32_t* rt = malloc(sizeof(int32_t) * (size_t)(n_rt > 0 ? n_rt : 1));
+    int32_t* slot = malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));   /* token -> tok[] position */
+    for (int32_t t = 0; t < T; ++t) slot[t] = -1;
+    for (int32_t i = 0; i < n_tok; ++i) slot[tok[i]] = i;
+    for (int32_t i = 0; i < n_rt; ++i) rt[i] = want_dC ? i : tok[i];
+    double* dl_all = want_dC ? malloc(sizeof(double) * (size_t)T * E) : NULL;
+    const int hmax = I > Is ? I : Is;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* xt = malloc(sizeof(double) * (size_t)d);
+        double* dO = malloc(sizeof(double) * (size_t)d);
+        double* acc = malloc(sizeof(double) * (size_t)d);
+        double* a = malloc(sizeof(double) * (size_t)hmax);
+        double* b = malloc(sizeof(double) * (size_t)hmax);
+        double* h = malloc(sizeof(double) * (size_t)hmax);
+        double* dh = malloc(sizeof(double) * (size_t)hmax);
+        double* dg = malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        double* ds = malloc(sizeof(double) * (size_t)E);
+        double* dl = malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t i = 0; i < n_rt; ++i) {
+            const int32_t t = rt[i];
+            const int32_t out_i = slot[t];               /* -1: dl only (for dC) */
+            for (int j = 0; j < d; ++j) {
+                xt[j] = widen(x_all[(size_t)t * d + j]);
+                dO[j] = widen(dout_all[(size_t)t * d + j]);
+                acc[j] = (s->flags & ORACLE_NO_RESIDUAL) ? 0.0 : dO[j];
+            }
+            const int32_t* idx = idx_all + (size_t)t * K;
+            const double* gate = gate_all + (size_t)t * K;
+            const double* pr = prob_all + (size_t)t * E;
+            for (int si = 0; si < Ks && out_i >= 0; ++si) {
+                expert_bwd_vectors(d, Is, ws1[si], ws3[si], ws2[si], xt, dO, 1.0, a, b, h, dh, NULL);
+                swiglu_bwd(Is, a, b, dh);
+                expert_dx(d, Is, ws1[si], ws3[si], a, b, acc);
+            }
+            for (int k = 0; k < K; ++k) {
+                const int e = idx[k];
+                expert_bwd_vectors(d, I, w1[e], w3[e], w2[e], xt, dO, gate[k], a, b, h, dh, &dg[k]);
+                if (out_i >= 0) {
+                    swiglu_bwd(I, a, b, dh);
+                    expert_dx(d, I, w1[e], w3[e], a, b, acc);
+                }
+            }
+            /* router: gates -> scores -> affinities */
+            for (int e = 0; e < E; ++e) ds[e] = K > 0 ? alpha * fe[e] / (double)T : 0.0;
+            if (ren) {
+                double z = 0.0, sg = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    z += pr[idx[k]];
+                    sg += dg[k] * gate[k];
+                }
+                for (int k = 0; k < K; ++k) ds[idx[k]] += (dg[k] - sg) / z;
+            } else {
+                for (int k = 0; k < K; ++k) ds[idx[k]] += dg[k];
+            }
+            if (sig) {
+                for (int e = 0; e < E; ++e) dl[e] = pr[e] * (1.0 - pr[e]) * ds[e];
+            } else {
+                double m = 0.0;
+                for (int e = 0; e < E; ++e) m += pr[e] * ds[e];
+                for (int e = 0; e < E; ++e) dl[e] = pr[e] * (ds[e] - m);
+            }
+            if (K == 0)
+                for (int e = 0; e < E; ++e) dl[e] = 0.0;
+            if (dl_all) memcpy(dl_all + (size_t)t * E, dl, sizeof(double) * (size_t)E);
+            if (out_i >= 0) {
+                for (int e = 0; e < E && K > 0; ++e) {
+                    const uint16_t* c = C + (size_t)e * d;
+                    for (int j = 0; j < d; ++j) acc[j] += dl[e] * widen(c[j]);
+                }
+                memcpy(dx + (size_t)out_i * d, acc, sizeof(double) * (size_t)d);
+                for (int k = 0; k < K; ++k) {
+                    dgate[(size_t)out_i * K + k] = dg[k];
+                    idx_out[(size_t)out_i * K + k] = idx[k];
+                }
+            }
+        }
+        free(xt); free(dO); free(acc); free(a); free(b); free(h); free(dh); free(dg); free(ds);
+        free(dl);
+    }
+
+    /* Pass 3: weight gradients of the requested routed experts and of the
+     * shared experts, each over its tokens in token order. */
+    for (int32_t q = 0; q < n_exp + (want_shared ? Ks : 0); ++q) {
+        const int shared = q >= n_exp;
+        const int e = shared ? q - n_exp : exps[q];
+        const int inter = shared ? Is : I;
+        int n = 0;
+        for (int32_t t = 0; t < T; ++t) {
+            if (shared) { ++n; continue; }
+            for (int k = 0; k < K; ++k) n += idx_all[(size_t)t * K + k] == e;
+        }
+        double* xs = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
+        double* dOs = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
+        double* gs = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        int r = 0;
+        for (int32_t t = 0; t < T; ++t) {
+            double g = -1.0;
+            if (shared) g = 1.0;
+            else
+                for (int k = 0; k < K; ++k)
+                    if (idx_all[(size_t)t * K + k] == e) g = gate_all[(size_t)t * K + k];
+            if (g < 0.0) continue;
+            for (int j = 0; j < d; ++j) {
+                xs[(size_t)r * d + j] = widen(x_all[(size_t)t * d + j]);
+                dOs[(size_t)r * d + j] = widen(dout_all[(size_t)t * d + j]);
+            }
+            gs[r++] = g;
+        }
+        if (shared)
+            expert_dw(d, inter, ws1[e], ws3[e], ws2[e], n, xs, dOs, gs,
+                      dws1 + (size_t)e * inter * d, dws3 + (size_t)e * inter * d,
+                      dws2 + (size_t)e * d * inter, nthreads);
+        else
+            expert_dw(d, inter, w1[e], w3[e], w2[e], n, xs, dOs, gs,
+                      dw1 + (size_t)q * inter * d, dw3 + (size_t)q * inter * d,
+                      dw2 + (size_t)q * d * inter, nthreads);
+        free(xs); free(dOs); free(gs);
+    }
+
+    /* Pass 4: centroid gradients, tokens summed in order. */
+    if (want_dC) {
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+        for (int e = 0; e < E; ++e) {
+            double* row = dC + (size_t)e * d;
+            for (int j = 0; j < d; ++j) row[j] = 0.0;
+            for (int32_t t = 0; t < T; ++t) {
+                const double g = dl_all[(size_t)t * E + e];
+                const uint16_t* xr = x_all + (size_t)t * d;
+                for (int j = 0; j < d; ++j) row[j] += g * widen(xr[j]);
+            }
+        }
+    }
+    free(idx_all); free(gate_all); free(prob_all); free(fe); free(rt); free(slot); free(dl_all);
+    return used;
+}

@@ -40,8 +40,36 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_mistake_fails_a_pin(tmp_path, name, old, new):
+# Mistakes in the backward (oracle_backward); its pins are in their own file.
+BWD_MUTATIONS = [
+    ("silu derivative without the z (1 - sig) term",
+     "const double dsilu = sg * (1.0 + a[i] * (1.0 - sg));", "const double dsilu = sg;"),
+    ("up-projection gradient uses W3 x instead of silu(W1 x)",
+     "const double db = dh[i] * (a[i] * sg);", "const double db = dh[i] * b[i];"),
+    ("dh not scaled by the gate", "    for (int i = 0; i < inter; ++i) dh[i] *= g;\n", "\n"),
+    ("W2^T pairs the wrong output row", "dh[i] += w * dO[o];", "dh[i] += w * dO[(o + 1) % d];"),
+    ("renormalised gate backward drops the common term",
+     "ds[idx[k]] += (dg[k] - sg) / z;", "ds[idx[k]] += dg[k] / z;"),
+    ("softmax backward drops the mean term", "dl[e] = pr[e] * (ds[e] - m);", "dl[e] = pr[e] * ds[e];"),
+    ("sigmoid derivative missing (1 - s)", "dl[e] = pr[e] * (1.0 - pr[e]) * ds[e];",
+     "dl[e] = pr[e] * ds[e];"),
+    ("balance gradient weighted by mean score instead of hit rate",
+     "ds[e] = K > 0 ? alpha * fe[e] / (double)T : 0.0;",
+     "ds[e] = K > 0 ? alpha * mean_score[e] / (double)T : 0.0;"),
+    ("dW2 without the gate", "            for (int i = 0; i < inter; ++i) h[i] *= gs[t];\n", "\n"),
+    ("dW1 from the up-projection gradient", "r1[j] += da * xt[j];", "r1[j] += db * xt[j];"),
+    ("residual gradient dropped", "acc[j] = (s->flags & ORACLE_NO_RESIDUAL) ? 0.0 : dO[j];",
+     "acc[j] = 0.0;"),
+    ("hit rate not divided by K",
+     "fe[e] = K > 0 ? (double)E * (double)counts[e] / ((double)K * (double)T) : 0.0;",
+     "fe[e] = K > 0 ? (double)E * (double)counts[e] / (double)T : 0.0;"),
+    ("centroid gradient from the next token's affinity gradient",
+     "const double g = dl_all[(size_t)t * E + e];",
+     "const double g = dl_all[(size_t)((t + 1) % T) * E + e];"),
+]
+
+
+def _plant(tmp_path, name, old, new, pin_files):
     for sub in ("oracle", "synth", "tests"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
                         ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.o"))
@@ -51,6 +79,16 @@ def test_planted_mistake_fails_a_pin(tmp_path, name, old, new):
     assert old in code, f"mutation site not found: {name}"
     src.write_text(code.replace(old, new, 1))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        *PIN_FILES], cwd=tmp_path, capture_output=True, text=True,
+                        *pin_files], cwd=tmp_path, capture_output=True, text=True,
                        env=dict(os.environ, PYTHONPATH=str(tmp_path)), timeout=600)
     assert r.returncode == 1, f"no pin caught '{name}':\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTATIONS, ids=[m[0] for m in BWD_MUTATIONS])
+def test_planted_backward_mistake_fails_a_pin(tmp_path, name, old, new):
+    _plant(tmp_path, name, old, new, ["tests/test_oracle_backward.py"])
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_fails_a_pin(tmp_path, name, old, new):
+    _plant(tmp_path, name, old, new, PIN_FILES)
