@@ -328,10 +328,19 @@ def test_errors_leave_output_untouched():
     L, D = _inputs(w)
     out = torch.full((w.T, w.d), 3.0, dtype=torch.bfloat16, device="cuda")
     small = torch.empty(64, dtype=torch.uint8, device="cuda")
-    with pytest.raises(moe.MoEError) as e:
+    # the binding refuses the short workspace itself ...
+    with pytest.raises(ValueError):
         moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
                     K=w.K, out=out, workspace=small)
-    assert e.value.code == 4
+    # ... and so does the C ABI, called directly
+    import ctypes
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    vp = ctypes.c_void_p
+    ptr = [vp(D[k].data_ptr()) for k in ("x", "C", "w1", "w3", "w2", "ws1", "ws3", "ws2")]
+    code = moe.lib().moe_forward(ctypes.byref(shape), ptr[0], ptr[1], None, *ptr[2:],
+                                 vp(out.data_ptr()), None, None, vp(small.data_ptr()),
+                                 ctypes.c_size_t(64), None)
+    assert code == 4
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())
     with pytest.raises(moe.MoEError) as e:
