@@ -23,6 +23,7 @@ SIGMOID = 4      # MOE_FLAG_SIGMOID
 STATUS = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
     4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_NO_DEVICE", 6: "MOE_ERR_DEVICE_ARCH", 7: "MOE_ERR_HIP",
+    8: "MOE_ERR_SCRATCH",
 }
 
 
@@ -78,12 +79,16 @@ _lib.moe_profile_slot_name.restype = ctypes.c_char_p
 _lib.moe_profile_slot_name.argtypes = [ctypes.c_int32]
 _lib.moe_forward_fp8.restype = ctypes.c_int
 _lib.moe_forward_fp8.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [ctypes.c_size_t, _vp]
+_lib.moe_forward_noalloc.restype = ctypes.c_int
+_lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 13
+_lib.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
+_lib.moe_noalloc_scratch_bytes.argtypes = []
 _lib.moe_profile_stream_read.restype = ctypes.c_int
 _lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
 EXPORTS = ("moe_workspace_size", "moe_route_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
            "moe_profile_begin", "moe_profile_begin_slots", "moe_profile_end", "moe_profile_slot_name",
-           "moe_profile_stream_read")
+           "moe_profile_stream_read", "moe_forward_noalloc", "moe_noalloc_scratch_bytes")
 N_SLOTS = 7
 
 
@@ -303,6 +308,42 @@ def forward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, b
     _check(code)
     if return_routing:
         return out, topk_idx, topk_gate
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(_lib.moe_noalloc_scratch_bytes())
+
+
+def forward_noalloc(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int,
+                    bias=None, out, topk_idx=None, topk_gate=None, no_residual: bool = False,
+                    renorm: bool = False, sigmoid: bool = False, stream=None):
+    """moe_forward_noalloc: the layer forward with the library's static scratch
+    array as workspace.  Allocates nothing: the caller passes out (and the
+    optional topk_idx / topk_gate).  Calls that overlap on one GPU race on the
+    shared scratch.  Shapes too large for it raise MoEError (MOE_ERR_SCRATCH)."""
+    T, d, dev = _x_of(x)
+    _need(x, "x", torch.bfloat16, (T, d), dev)
+    if K > 0:
+        if w1 is None or w1.dim() != 3:
+            raise ValueError("w1 must be [E, I, d] when K > 0")
+        E, I = w1.shape[0], w1.shape[1]
+        _need(w1, "w1", torch.bfloat16, (E, I, d), dev)
+        _need(w3, "w3", torch.bfloat16, (E, I, d), dev)
+        _need(w2, "w2", torch.bfloat16, (E, d, I), dev)
+    else:
+        E = centroids.shape[0] if centroids is not None else (w1.shape[0] if w1 is not None else 1)
+        I = w1.shape[1] if w1 is not None else 64
+    _check_routing_args(T, d, E, K, centroids, bias, dev)
+    Ks, Is = _check_shared(ws1, ws3, ws2, d, dev)
+    _need(out, "out", torch.bfloat16, (T, d), dev)
+    shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
+    al = _Alloc(dev, stream)
+    topk_idx, topk_gate = _routing_outputs(al, T, K, topk_idx, topk_gate, False)
+    code = _lib.moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(bias),
+                                    _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2),
+                                    _ptr(out), _ptr(topk_idx), _ptr(topk_gate), al.handle())
+    _check(code)
     return out
 
 

@@ -2,6 +2,7 @@
 // launch sequence router -> permutation -> G1 -> G2 -> combine, all enqueued
 // on the caller's stream with no host synchronisation and no allocation.
 #include <atomic>
+#include <mutex>
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -262,6 +263,9 @@ __attribute__((visibility("default"))) const char* moe_status_string(moe_status_
         case MOE_ERR_NO_DEVICE: return "MOE_ERR_NO_DEVICE: no HIP device is available";
         case MOE_ERR_DEVICE_ARCH: return "MOE_ERR_DEVICE_ARCH: the current device is not gfx950";
         case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+        case MOE_ERR_SCRATCH:
+            return "MOE_ERR_SCRATCH: the shape needs more scratch than moe_forward_noalloc's static "
+                   "buffer holds (moe_noalloc_scratch_bytes())";
     }
     return "unknown moe_status_t";
 }
@@ -339,9 +343,62 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     return MOE_OK;
 }
 
+// Allocation-free forward: the workspace is a static device array of
+// kScratchBytes (every GPU the library runs on holds its own copy until the
+// process ends).  Host code never uses the array's name as an address — it
+// is a host-side stand-in there — but the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on the entry point's first call there.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch array, or null (and *err set) if
+// the lookup failed.  The caller has made `dev` current.
+void* scratch_address(int dev, hipError_t* err) {
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+        if (g_scratch_err[dev] != hipSuccess) (void)hipGetLastError();
+    });
+    *err = g_scratch_err[dev];
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+__attribute__((visibility("default"))) moe_status_t moe_forward_noalloc(
+    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
+    const void* w1, const void* w3, const void* w2, const void* ws1, const void* ws3,
+    const void* ws2, void* out, int32_t* topk_idx, float* topk_gate, void* stream) {
+    if (!shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    Plan probe;
+    if (make_plan(shape, &probe, false) > kScratchBytes) return MOE_ERR_SCRATCH;
+    moe_status_t st = device_ok();
+    if (st != MOE_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MOE_ERR_NO_DEVICE;
+    }
+    hipError_t err = hipSuccess;
+    void* ws = scratch_address(dev, &err);
+    if (!ws) return MOE_ERR_HIP;
+    return run_forward(shape, x, centroids, expert_bias, w1, w3, w2, nullptr, ws1, ws3, ws2, out,
+                       topk_idx, topk_gate, ws, kScratchBytes, stream);
+}
+
+__attribute__((visibility("default"))) size_t moe_noalloc_scratch_bytes(void) {
+    return kScratchBytes;
+}
 
 __attribute__((visibility("default"))) moe_status_t moe_forward(
     const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,

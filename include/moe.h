@@ -84,7 +84,9 @@ typedef enum {
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_size() */
     MOE_ERR_NO_DEVICE = 5,   /* no HIP device is visible / current          */
     MOE_ERR_DEVICE_ARCH = 6, /* the current device is not gfx950            */
-    MOE_ERR_HIP = 7          /* a HIP launch failed                         */
+    MOE_ERR_HIP = 7,         /* a HIP launch failed                         */
+    MOE_ERR_SCRATCH = 8      /* moe_forward_noalloc: the shape needs more
+                                scratch than its static buffer holds        */
 } moe_status_t;
 
 /* Bytes of device workspace moe_forward / moe_forward_fp8 need for this
@@ -157,6 +159,32 @@ moe_status_t moe_forward_fp8(const moe_shape_t* shape, const void* x, const void
                              const float* w2_scale, const void* ws1, const void* ws3,
                              const void* ws2, void* out, int32_t* topk_idx, float* topk_gate,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Full layer forward that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory at call time: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, arithmetic, validation and results are those of moe_forward
+ * (bit-identical outputs); the workspace is instead a static device array of
+ * moe_noalloc_scratch_bytes() bytes (64 MiB) that the library's code object
+ * carries: each GPU it runs on holds one copy until the process ends.  Shapes
+ * whose moe_workspace_size() exceeds it are rejected with MOE_ERR_SCRATCH
+ * before anything is launched (the V3-shape 256-token decode batch, 45 MB,
+ * fits; prefill-sized batches do not).  The first call on a device looks up
+ * that device's copy (hipGetSymbolAddress); no call allocates or frees
+ * memory.  Every call on one GPU shares its one copy: calls that overlap in
+ * time on one GPU (on different streams, or from several host threads) race
+ * on it and give undefined results — serialise them.  Nothing in the
+ * scratch needs to start zeroed: every piece of it is written before it is
+ * read within a call. */
+moe_status_t moe_forward_noalloc(const moe_shape_t* shape, const void* x, const void* centroids,
+                                 const float* expert_bias, const void* w1, const void* w3,
+                                 const void* w2, const void* ws1, const void* ws3,
+                                 const void* ws2, void* out, int32_t* topk_idx,
+                                 float* topk_gate, void* stream);
+
+/* Bytes of moe_forward_noalloc's static scratch array (64 MiB). */
+size_t moe_noalloc_scratch_bytes(void);
 
 /* Routing only: affinities, softmax (or the flags' gate), top-K
  * ("DeepSeekMoE 深度解读报告", section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both

@@ -227,3 +227,23 @@ def test_workspace_covers_both_weight_forms():
     # is longer; the one workspace size serves both entry points
     s = moe.make_shape(16384, 7168, 256, 2048, 8, 1, 2048)
     assert moe.workspace_size(s) >= 2.5e9
+
+
+def test_noalloc_scratch_limits():
+    """moe_forward_noalloc's static scratch: 64 MiB, enough for the V3-shape
+    256-token decode batch; larger shapes fail with MOE_ERR_SCRATCH before
+    any device call, smaller ones reach the device check."""
+    cap = moe.noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    dec = moe.make_shape(256, 7168, 256, 2048, 8, 1, 2048)
+    pre = moe.make_shape(16384, 7168, 256, 2048, 8, 1, 2048)
+    assert moe.workspace_size(dec) <= cap < moe.workspace_size(pre)
+    f = moe.lib().moe_forward_noalloc
+    args = [ctypes.c_void_p(4096)] * 13
+    assert f(ctypes.byref(pre), *args) == 8
+    assert f(None, *args) == 1
+    bad = S(d=100)
+    assert f(ctypes.byref(bad), *args) == 2
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() == 0:
+        assert f(ctypes.byref(dec), *args) == 5
