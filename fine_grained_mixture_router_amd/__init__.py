@@ -79,6 +79,15 @@ _lib.moe_profile_slot_name.restype = ctypes.c_char_p
 _lib.moe_profile_slot_name.argtypes = [ctypes.c_int32]
 _lib.moe_forward_fp8.restype = ctypes.c_int
 _lib.moe_forward_fp8.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [ctypes.c_size_t, _vp]
+_lib.moe_train_state_size.restype = ctypes.c_size_t
+_lib.moe_train_state_size.argtypes = [ctypes.POINTER(Shape)]
+_lib.moe_backward_workspace_size.restype = ctypes.c_size_t
+_lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+_lib.moe_forward_train.restype = ctypes.c_int
+_lib.moe_forward_train.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 14 + [ctypes.c_size_t, _vp]
+_lib.moe_backward.restype = ctypes.c_int
+_lib.moe_backward.argtypes = ([ctypes.POINTER(Shape)] + [_vp] * 9 + [ctypes.c_float, _vp,
+                              ctypes.c_size_t] + [_vp] * 10 + [ctypes.c_size_t, _vp])
 _lib.moe_forward_noalloc.restype = ctypes.c_int
 _lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 13
 _lib.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
@@ -88,8 +97,10 @@ _lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
 EXPORTS = ("moe_workspace_size", "moe_route_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
            "moe_profile_begin", "moe_profile_begin_slots", "moe_profile_end", "moe_profile_slot_name",
-           "moe_profile_stream_read", "moe_forward_noalloc", "moe_noalloc_scratch_bytes")
-N_SLOTS = 7
+           "moe_profile_stream_read", "moe_forward_noalloc", "moe_noalloc_scratch_bytes",
+           "moe_train_state_size", "moe_backward_workspace_size", "moe_forward_train",
+           "moe_backward")
+N_SLOTS = 16
 
 
 def lib():
@@ -345,6 +356,123 @@ def forward_noalloc(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K
                                     _ptr(out), _ptr(topk_idx), _ptr(topk_gate), al.handle())
     _check(code)
     return out
+
+
+def train_state_size(shape: Shape) -> int:
+    n = _lib.moe_train_state_size(ctypes.byref(shape))
+    if n == 0:
+        raise MoEError(2, status_string(2))
+    return int(n)
+
+
+def backward_workspace_size(shape: Shape) -> int:
+    n = _lib.moe_backward_workspace_size(ctypes.byref(shape))
+    if n == 0:
+        raise MoEError(2, status_string(2))
+    return int(n)
+
+
+class TrainState:
+    """What moe_forward_train saved for moe_backward: the shape and the state
+    buffer (a uint8 device tensor the caller keeps until the backward)."""
+
+    def __init__(self, shape: Shape, buf):
+        self.shape = shape
+        self.buf = buf
+
+
+def _expert_args(x, centroids, w1, w3, w2, ws1, ws3, ws2, K, bias):
+    T, d, dev = _x_of(x)
+    _need(x, "x", torch.bfloat16, (T, d), dev)
+    if K > 0:
+        if w1 is None or w1.dim() != 3:
+            raise ValueError("w1 must be [E, I, d] when K > 0")
+        E, I = w1.shape[0], w1.shape[1]
+        _need(w1, "w1", torch.bfloat16, (E, I, d), dev)
+        _need(w3, "w3", torch.bfloat16, (E, I, d), dev)
+        _need(w2, "w2", torch.bfloat16, (E, d, I), dev)
+    else:
+        E = centroids.shape[0] if centroids is not None else (w1.shape[0] if w1 is not None else 1)
+        I = w1.shape[1] if w1 is not None else 64
+    _check_routing_args(T, d, E, K, centroids, bias, dev)
+    Ks, Is = _check_shared(ws1, ws3, ws2, d, dev)
+    return T, d, E, I, Ks, Is, dev
+
+
+def forward_train(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, K: int, bias=None,
+                  no_residual: bool = False, renorm: bool = False, sigmoid: bool = False,
+                  out=None, topk_idx=None, topk_gate=None, state=None, stream=None,
+                  return_routing: bool = False, return_stats: bool = False):
+    """moe_forward_train: the forward (same results as forward()) that also
+    writes the training state the backward reads.  Returns (out, TrainState)
+    plus (idx, gate) with return_routing and the balance statistics
+    (f [E], P [E], L_bal) with return_stats."""
+    T, d, E, I, Ks, Is, dev = _expert_args(x, centroids, w1, w3, w2, ws1, ws3, ws2, K, bias)
+    shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
+    al = _Alloc(dev, stream)
+    out, topk_idx, topk_gate = _outputs(al, T, d, K, out, topk_idx, topk_gate, return_routing)
+    stats = al.empty((2 * E + 1,), torch.float32) if (return_stats and K > 0) else None
+    state = _workspace(al, shape, state, train_state_size)
+    code = _lib.moe_forward_train(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(bias),
+                                  _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2),
+                                  _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(stats),
+                                  _ptr(state), state.numel() * state.element_size(), al.handle())
+    _check(code)
+    res = (out, TrainState(shape, state))
+    if return_routing:
+        res += (topk_idx, topk_gate)
+    if return_stats:
+        res += ((stats[:E], stats[E:2 * E], stats[2 * E]) if stats is not None else None,)
+    return res
+
+
+def backward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, dout, state: TrainState,
+             alpha: float = 0.0, dx=None, dw1=None, dw3=None, dw2=None, dws1=None, dws3=None,
+             dws2=None, dC=None, dgate=None, workspace=None, stream=None,
+             return_dgate: bool = False):
+    """moe_backward: gradients of sum(dout * out) + alpha * L_bal for the
+    forward that produced `state` (same inputs).  Returns a dict with dx
+    [T,d], dw1/dw3 [E,I,d], dw2 [E,d,I] (bf16; None without a router),
+    dws1/dws3/dws2 (bf16; None without shared experts), dC [E,d] (fp32) and,
+    with return_dgate, dgate [T,K] (fp32)."""
+    shape = state.shape
+    K = shape.K
+    T, d, E, I, Ks, Is, dev = _expert_args(x, centroids, w1, w3, w2, ws1, ws3, ws2, K, None)
+    if (T, d, E, I, Ks, Is) != (shape.T, shape.d, shape.E, shape.I, shape.Ks, shape.Is):
+        raise ValueError("the tensors do not match the shape of the training forward")
+    _need(dout, "dout", torch.bfloat16, (T, d), dev)
+    if state.buf.device != dev:
+        raise ValueError("state is on another device")
+    al = _Alloc(dev, stream)
+
+    def out_t(t, name, dtype, shp, want):
+        if not want:
+            _absent(t, name)
+            return None
+        if t is None:
+            return al.empty(shp, dtype)
+        return _need(t, name, dtype, shp, dev)
+
+    dx = out_t(dx, "dx", torch.bfloat16, (T, d), True)
+    dw1 = out_t(dw1, "dw1", torch.bfloat16, (E, I, d), K > 0)
+    dw3 = out_t(dw3, "dw3", torch.bfloat16, (E, I, d), K > 0)
+    dw2 = out_t(dw2, "dw2", torch.bfloat16, (E, d, I), K > 0)
+    dws1 = out_t(dws1, "dws1", torch.bfloat16, (Ks, Is, d), Ks > 0)
+    dws3 = out_t(dws3, "dws3", torch.bfloat16, (Ks, Is, d), Ks > 0)
+    dws2 = out_t(dws2, "dws2", torch.bfloat16, (Ks, d, Is), Ks > 0)
+    dC = out_t(dC, "dC", torch.float32, (E, d), K > 0)
+    dgate = out_t(dgate, "dgate", torch.float32, (T, K), K > 0 and (return_dgate or dgate is not None))
+    workspace = _workspace(al, shape, workspace, backward_workspace_size)
+    code = _lib.moe_backward(ctypes.byref(shape), _ptr(x), _ptr(centroids), _ptr(w1), _ptr(w3),
+                             _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(dout),
+                             ctypes.c_float(float(alpha)), _ptr(state.buf),
+                             state.buf.numel() * state.buf.element_size(), _ptr(dx), _ptr(dw1),
+                             _ptr(dw3), _ptr(dw2), _ptr(dws1), _ptr(dws3), _ptr(dws2), _ptr(dC),
+                             _ptr(dgate), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), al.handle())
+    _check(code)
+    return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, dws1=dws1, dws3=dws3, dws2=dws2, dC=dC,
+                dgate=dgate)
 
 
 def forward_fp8(x, centroids, w1q, w1s, w3q, w3s, w2q, w2s, ws1=None, ws3=None, ws2=None, *,

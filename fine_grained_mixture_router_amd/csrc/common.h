@@ -100,6 +100,12 @@ struct Plan {
     int32_t* ntiles;     // [2]
     bf16_t* H;           // routed [T*K, I] then shared [Ks*T, Is]
     bf16_t* Y;           // [rows, d]
+
+    // training forward only (null otherwise): what the backward reads
+    float* scores;       // [T, Epad] every expert's score (softmax / sigmoid), 0 past E
+    float* score_part;   // [nchunk * 4, Epad] score sums of each 16-token quarter chunk
+    float* row_gate;     // [T*K] gate of each routed row
+    bf16_t* Z;           // pre-activations [W1 x | W3 x]: routed [T*K, 2I], shared [Ks*T, 2Is]
 };
 
 // 8-bit routed weights: E4M3 codes with one float scale per output row
@@ -121,6 +127,34 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
 hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
                             const RoutedQ8* q8, hipStream_t st);
 hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st);
+// training forward: balance statistics [2E + 1] = (f_e, P_e, L_bal) from the
+// group offsets and the score sums
+hipError_t launch_balance_stats(const Plan& p, float* stats, hipStream_t st);
+
+// Backward (backward.hip).  The workspace carve-up of one backward call.
+struct BwdPlan {
+    int max_tiles_dh, max_tiles_dx;   // work-list bounds (256 x 256 tiles)
+    int ndh;                          // dgate partials per row (N tiles of the dH GEMM)
+    bf16_t* dZ;       // like Plan::Z
+    bf16_t* gH;       // [T*K, I]
+    float* dgp;       // [rows, ndh]
+    bf16_t* dL;       // [T, Epad]
+    float* R32;       // [T, d]
+    bf16_t* dXr;      // [rows, d]
+    Tile* tiles_dh;
+    Tile* tiles_dx;
+    int32_t* ntiles;  // [2]
+    int32_t* gorder;  // [E + Ks]
+    float* dgate;     // [T, K] when the caller passes none
+};
+struct BwdArgs {
+    const bf16_t *x, *C, *w1, *w3, *w2, *ws1, *ws3, *ws2, *dout;
+    float alpha;
+    bf16_t *dx, *dw1, *dw3, *dw2, *dws1, *dws3, *dws2;
+    float *dC, *dgate;
+};
+hipError_t launch_backward(const Plan& p, const BwdPlan& b, const BwdArgs& a, hipStream_t st,
+                           void (*mark)(int slot, int end, hipStream_t s));
 hipError_t launch_stream_read(const void* buf, size_t bytes, hipStream_t st);
 
 }  // namespace moe

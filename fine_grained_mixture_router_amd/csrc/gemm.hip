@@ -56,6 +56,8 @@ struct GemmParams {
     const float* Sb_r;
     bf16_t* O_r;             // routed output base (G1: H routed, G2: Y)
     bf16_t* O_s;             // shared output base (G1: H shared, G2: Y)
+    bf16_t* Z_r;             // G1 of a training forward: pre-activations [W1 x | W3 x]
+    bf16_t* Z_s;             //   of routed / shared rows (null otherwise)
     int kdim_r, kdim_s;      // reduction length
     int n_r, n_s;            // output columns
     int E, TK;               // routed experts, routed rows (T*K)
@@ -410,8 +412,14 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
                 if (SWIGLU) v = silu(Q8 ? acc[i][j][r] * fa : acc[i][j][r]) *
                                 (Q8 ? acc[i][j + NB / 2][r] * fb : acc[i][j + NB / 2][r]);
                 else v = Q8 ? acc[i][j][r] * fa : acc[i][j][r];
-                if (row < tl.nrows && col < ncols)
+                if (row < tl.nrows && col < ncols) {
                     obase[(size_t)(orow0 + row) * ncols + col] = f32_to_bf16(v);
+                    if (SWIGLU && !Q8 && P.Z_r) {
+                        bf16_t* z = (shared ? P.Z_s : P.Z_r) + (size_t)(orow0 + row) * 2 * ncols + col;
+                        z[0] = f32_to_bf16(acc[i][j][r]);
+                        z[ncols] = f32_to_bf16(acc[i][j + NB / 2][r]);
+                    }
+                }
             }
         }
     }
@@ -541,7 +549,9 @@ __device__ __forceinline__ bool fetch_tile(const GemmParams& P, Tile& tl) {
 // and down 3.63 -> 3.57 ms against two 64 KB stages; running several tiles
 // per workgroup, with the next tile's first slice loading under the
 // epilogue, measured slower than one tile per workgroup with this ring.)
-template <bool SWIGLU, int NW, bool Q8 = false>
+// SAVEZ (gate/up of a training forward): the tile's pre-activations W1 x and
+// W3 x also go out, as bf16, to Z.
+template <bool SWIGLU, int NW, bool Q8 = false, bool SAVEZ = false>
 __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, lds_bf16_t* smem) {
     constexpr int BK = 64;
     constexpr int OPER = kBig * BK;                // elements of one operand half (32 KB)
@@ -882,6 +892,16 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
                     const uint32_t hi = pack_bf16x2(v[2], v[3]);
                     const int orow = wm * 128 + 32 * i + lrow;
                     const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
+                    if (SAVEZ && SWIGLU && orow < tl.nrows && tl.n0 + ocol < ncols) {
+                        bf16_t* z = (shared ? P.Z_s : P.Z_r) + (size_t)(rrow + orow) * 2 * ncols + tl.n0 + ocol;
+                        const int r0 = 4 * r4;
+                        *reinterpret_cast<u32x2*>(z) =
+                            u32x2{pack_bf16x2(acc[i][j][r0], acc[i][j][r0 + 1]),
+                                  pack_bf16x2(acc[i][j][r0 + 2], acc[i][j][r0 + 3])};
+                        *reinterpret_cast<u32x2*>(z + ncols) =
+                            u32x2{pack_bf16x2(acc[i][j + HB][r0], acc[i][j + HB][r0 + 1]),
+                                  pack_bf16x2(acc[i][j + HB][r0 + 2], acc[i][j + HB][r0 + 3])};
+                    }
                     int off;
                     if (SWIGLU) {
                         off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
@@ -940,13 +960,13 @@ void gemm_big_q8_kernel(GemmParams P) {
     else big_tile<SWIGLU, 8, false>(P, tl, (lds_bf16_t*)smem);
 }
 
-template <bool SWIGLU, int NW>
+template <bool SWIGLU, int NW, bool SAVEZ = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_big_kernel(GemmParams P) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kBigLdsBytes / 2];
     Tile tl;
     if (!fetch_tile(P, tl)) return;
-    big_tile<SWIGLU, NW>(P, tl, (lds_bf16_t*)smem);
+    big_tile<SWIGLU, NW, false, SAVEZ>(P, tl, (lds_bf16_t*)smem);
 }
 
 
@@ -998,9 +1018,16 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.TK = p.T * p.K;
     gp.abytes_r = (uint32_t)((size_t)p.T * p.d * 2);
     gp.abytes_s = gp.abytes_r;
+    if (p.Z && !q8) {
+        gp.Z_r = p.Z;
+        gp.Z_s = p.Z + (size_t)p.T * p.K * 2 * p.I;
+    }
     if (p.g1.bm == 256) {
         if (q8)
             gemm_big_q8_kernel<true><<<tile_grid(p.max_tiles1), 512, 0, st>>>(gp);
+        else if (gp.Z_r)
+            gemm_big_kernel<true, MOE_BIG_WAVES, true>
+                <<<tile_grid(p.max_tiles1), 64 * MOE_BIG_WAVES, 0, st>>>(gp);
         else
             gemm_big_kernel<true, MOE_BIG_WAVES>
                 <<<tile_grid(p.max_tiles1), 64 * MOE_BIG_WAVES, 0, st>>>(gp);

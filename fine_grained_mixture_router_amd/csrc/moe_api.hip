@@ -57,7 +57,8 @@ bool shape_ok(const moe_shape_t* s) {
 // are 8-bit (the same tile sizes; each has an 8-bit kernel).  route_only:
 // carve only what routing needs (affinity partials and the chunk masks; the
 // caller passes idx and gate), for moe_route.
-size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false) {
+size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false,
+                 bool train = false) {
     (void)q8;
     memset(p, 0, sizeof(*p));
     p->T = s->T;
@@ -134,6 +135,42 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false
     p->ntiles = (int32_t*)take(16);
     p->H = (bf16_t*)take(((size_t)TK * s->I + (size_t)s->T * s->Ks * p->Is) * 2);
     p->Y = (bf16_t*)take((size_t)p->rows * s->d * 2);
+    if (train) {
+        p->scores = (float*)take(s->K > 0 ? (size_t)s->T * p->Epad * 4 : 0);
+        p->score_part = (float*)take(s->K > 0 ? (size_t)p->nchunk * 4 * p->Epad * 4 : 0);
+        p->row_gate = (float*)take((size_t)TK * 4);
+        p->Z = (bf16_t*)take(((size_t)TK * s->I + (size_t)s->T * s->Ks * p->Is) * 2 * 2);
+    }
+    return off;
+}
+
+// The backward's own workspace: offsets from 0, returns the total size.
+size_t make_bwd_plan(const moe_shape_t* s, const Plan& p, BwdPlan* b) {
+    memset(b, 0, sizeof(*b));
+    const size_t TK = (size_t)s->T * s->K;
+    const int imax = s->I > p.Is ? s->I : p.Is;
+    b->ndh = (imax + 255) / 256;
+    // 256-row tiles: sum over groups of ceil(n_g / 256) <= rows / 256 + groups
+    const long long mt = (long long)p.rows / 256 + s->E + s->Ks;
+    b->max_tiles_dh = (int)(mt * b->ndh);
+    b->max_tiles_dx = (int)(mt * ((s->d + 255) / 256));
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    b->dZ = (bf16_t*)take((TK * s->I + (size_t)s->T * s->Ks * p.Is) * 2 * 2);
+    b->gH = (bf16_t*)take(TK * s->I * 2);
+    b->dgp = (float*)take((size_t)p.rows * b->ndh * 4);
+    b->dL = (bf16_t*)take(s->K > 0 ? (size_t)s->T * p.Epad * 2 : 0);
+    b->R32 = (float*)take(s->K > 0 ? (size_t)s->T * s->d * 4 : 0);
+    b->dXr = (bf16_t*)take((size_t)p.rows * s->d * 2);
+    b->tiles_dh = (Tile*)take((size_t)b->max_tiles_dh * sizeof(Tile));
+    b->tiles_dx = (Tile*)take((size_t)b->max_tiles_dx * sizeof(Tile));
+    b->ntiles = (int32_t*)take(16);
+    b->gorder = (int32_t*)take((size_t)(s->E + s->Ks) * 4);
+    b->dgate = (float*)take(TK * 4);
     return off;
 }
 
@@ -143,6 +180,21 @@ T* rebase(T* off, char* base) {
 }
 
 // Route-only plan: the two pieces make_plan(route_only) carved.
+void place_bwd(BwdPlan* q, void* ws) {
+    char* b = static_cast<char*>(ws);
+    q->dZ = rebase(q->dZ, b);
+    q->gH = rebase(q->gH, b);
+    q->dgp = rebase(q->dgp, b);
+    q->dL = rebase(q->dL, b);
+    q->R32 = rebase(q->R32, b);
+    q->dXr = rebase(q->dXr, b);
+    q->tiles_dh = rebase(q->tiles_dh, b);
+    q->tiles_dx = rebase(q->tiles_dx, b);
+    q->ntiles = rebase(q->ntiles, b);
+    q->gorder = rebase(q->gorder, b);
+    q->dgate = rebase(q->dgate, b);
+}
+
 void place_route(Plan* p, void* ws) {
     char* b = static_cast<char*>(ws);
     p->logits = rebase(p->logits, b);
@@ -151,6 +203,12 @@ void place_route(Plan* p, void* ws) {
 
 void place(Plan* p, void* ws) {
     char* b = static_cast<char*>(ws);
+    if (p->Z) {                                     // a training plan
+        p->scores = rebase(p->scores, b);
+        p->score_part = rebase(p->score_part, b);
+        p->row_gate = rebase(p->row_gate, b);
+        p->Z = rebase(p->Z, b);
+    }
     p->logits = rebase(p->logits, b);
     p->idx = rebase(p->idx, b);
     p->gate = rebase(p->gate, b);
@@ -194,10 +252,14 @@ moe_status_t device_ok() {
 // Benchmark instrumentation: HIP events recorded around every kernel of the
 // next moe_forward calls, on the call's stream.  One global recorder; not
 // thread-safe (documented in moe.h).
-constexpr int kSlots = 7;
+constexpr int kSlots = 16;
+constexpr int kBwdSlot0 = 7;                 // backward kernels: slots 7..15
 const char* const kSlotNames[kSlots] = {"router_logits", "router_select", "perm_scan",
                                         "perm_scatter",  "gemm_gate_up",  "gemm_down",
-                                        "combine"};
+                                        "combine",       "bwd_lists",     "bwd_dh",
+                                        "bwd_router",    "bwd_dx_router", "bwd_dx",
+                                        "bwd_dx_combine", "bwd_dw2",      "bwd_dw13",
+                                        "bwd_dc"};
 struct Recorder {
     bool on = false;
     int max_calls = 0;
@@ -212,6 +274,8 @@ void rec_mark(int slot, int end, hipStream_t s) {
     (void)hipEventRecord(g_rec.ev[(g_rec.calls * kSlots + slot) * 2 + end], s);
 }
 
+void rec_mark_bwd(int slot, int end, hipStream_t s) { rec_mark(kBwdSlot0 + slot, end, s); }
+
 void rec_free() {
     if (g_rec.ev) {
         for (int i = 0; i < g_rec.max_calls * kSlots * 2; ++i) (void)hipEventDestroy(g_rec.ev[i]);
@@ -222,7 +286,7 @@ void rec_free() {
 
 moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* centroids,
                           const float* bias, void* ws, size_t ws_bytes, Plan* plan,
-                          bool q8 = false, bool route_only = false) {
+                          bool q8 = false, bool route_only = false, bool train = false) {
     if (!shape) return MOE_ERR_NULL;
     if (!shape_ok(shape)) return MOE_ERR_SHAPE;
     if (!x || !ws) return MOE_ERR_NULL;
@@ -230,7 +294,7 @@ moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* c
     if (!aligned(x, 16) || (centroids && !aligned(centroids, 16))) return MOE_ERR_ALIGN;
     if (bias && !aligned(bias, 4)) return MOE_ERR_ALIGN;
     if (!aligned(ws, kAlign)) return MOE_ERR_ALIGN;
-    const size_t need = make_plan(shape, plan, q8, route_only);
+    const size_t need = make_plan(shape, plan, q8, route_only, train);
     if (ws_bytes < need) return MOE_ERR_WORKSPACE;
     return MOE_OK;
 }
@@ -245,6 +309,20 @@ __attribute__((visibility("default"))) size_t moe_workspace_size(const moe_shape
     const size_t a = make_plan(shape, &p, false);
     const size_t b = make_plan(shape, &p, true);   // moe_forward_fp8's plan
     return a > b ? a : b;
+}
+
+__attribute__((visibility("default"))) size_t moe_train_state_size(const moe_shape_t* shape) {
+    if (!shape_ok(shape)) return 0;
+    Plan p;
+    return make_plan(shape, &p, false, false, true);
+}
+
+__attribute__((visibility("default"))) size_t moe_backward_workspace_size(const moe_shape_t* shape) {
+    if (!shape_ok(shape)) return 0;
+    Plan p;
+    make_plan(shape, &p, false, false, true);
+    BwdPlan b;
+    return make_bwd_plan(shape, p, &b);
 }
 
 __attribute__((visibility("default"))) size_t moe_route_workspace_size(const moe_shape_t* shape) {
@@ -280,10 +358,11 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
                          const float* expert_bias, const void* w1, const void* w3,
                          const void* w2, const RoutedQ8* q8, const void* ws1, const void* ws3,
                          const void* ws2, void* out, int32_t* topk_idx, float* topk_gate,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         bool train = false, float* stats = nullptr) {
     Plan p;
     moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes,
-                                   &p, q8 != nullptr);
+                                   &p, q8 != nullptr, false, train);
     if (st != MOE_OK) return st;
     if (!out) return MOE_ERR_NULL;
     if (shape->K > 0) {
@@ -300,15 +379,20 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     for (const void* a : a16)
         if (a && !aligned(a, 16)) return MOE_ERR_ALIGN;
     const void* a4[] = {topk_idx, topk_gate, rk && q8 ? q8->s1 : nullptr,
-                        rk && q8 ? q8->s3 : nullptr, rk && q8 ? q8->s2 : nullptr};
+                        rk && q8 ? q8->s3 : nullptr, rk && q8 ? q8->s2 : nullptr, stats};
     for (const void* a : a4)
         if (a && !aligned(a, 4)) return MOE_ERR_ALIGN;
     st = device_ok();
     if (st != MOE_OK) return st;
 
     place(&p, workspace);
-    if (topk_idx) p.idx = topk_idx;
-    if (topk_gate) p.gate = topk_gate;
+    // A training forward keeps the routing in its state (the backward reads
+    // it there) and copies it out afterwards; otherwise the router writes
+    // the caller's arrays directly.
+    if (!train) {
+        if (topk_idx) p.idx = topk_idx;
+        if (topk_gate) p.gate = topk_gate;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* w1b = static_cast<const bf16_t*>(w1);
@@ -328,19 +412,88 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     if (p.K > 0) {
         step(0, [&] { return launch_router_logits(p, xb, static_cast<const bf16_t*>(centroids), s); });
         step(1, [&] { return launch_router_select(p, expert_bias, s); });
+        const size_t rb = (size_t)p.T * p.K * 4;
+        if (train && topk_idx && e == hipSuccess)
+            e = hipMemcpyAsync(topk_idx, p.idx, rb, hipMemcpyDeviceToDevice, s);
+        if (train && topk_gate && e == hipSuccess)
+            e = hipMemcpyAsync(topk_gate, p.gate, rb, hipMemcpyDeviceToDevice, s);
     }
     step(2, [&] { return launch_perm_scan(p, s); });
     step(3, [&] { return launch_perm_scatter(p, s); });
+    if (stats && p.K > 0 && e == hipSuccess) e = launch_balance_stats(p, stats, s);
     step(4, [&] { return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s); });
     step(5, [&] { return launch_gemm_down(p, w2b, ws2b, q, s); });
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
-        for (int k = 0; k < kSlots; ++k)
+        for (int k = 0; k < kBwdSlot0; ++k)
             if ((k >= 2 || p.K > 0) && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
         ++g_rec.calls;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+moe_status_t run_backward(const moe_shape_t* shape, const void* x, const void* centroids,
+                          const void* w1, const void* w3, const void* w2, const void* ws1,
+                          const void* ws3, const void* ws2, const void* dout, float alpha,
+                          const void* state, size_t state_bytes, void* dx, void* dw1, void* dw3,
+                          void* dw2, void* dws1, void* dws3, void* dws2, float* dC, float* dgate,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    if (shape->flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_RENORM | MOE_FLAG_SIGMOID)) return MOE_ERR_SHAPE;
+    if (!(alpha >= 0.f) || !(alpha < 1e30f)) return MOE_ERR_SHAPE;   // also rejects NaN
+    const bool rk = shape->K > 0, sk = shape->Ks > 0;
+    if (!x || !dout || !state || !dx || !workspace) return MOE_ERR_NULL;
+    if (rk && (!centroids || !w1 || !w3 || !w2 || !dw1 || !dw3 || !dw2 || !dC)) return MOE_ERR_NULL;
+    if (sk && (!ws1 || !ws3 || !ws2 || !dws1 || !dws3 || !dws2)) return MOE_ERR_NULL;
+    const void* a16[] = {x, dout, dx, rk ? centroids : nullptr, rk ? w1 : nullptr, rk ? w3 : nullptr,
+                         rk ? w2 : nullptr, rk ? dw1 : nullptr, rk ? dw3 : nullptr, rk ? dw2 : nullptr,
+                         sk ? ws1 : nullptr, sk ? ws3 : nullptr, sk ? ws2 : nullptr,
+                         sk ? dws1 : nullptr, sk ? dws3 : nullptr, sk ? dws2 : nullptr,
+                         rk ? dC : nullptr};
+    for (const void* a : a16)
+        if (a && !aligned(a, 16)) return MOE_ERR_ALIGN;
+    if (dgate && !aligned(dgate, 4)) return MOE_ERR_ALIGN;
+    if (!aligned(state, kAlign) || !aligned(workspace, kAlign)) return MOE_ERR_ALIGN;
+    Plan p;
+    if (state_bytes < make_plan(shape, &p, false, false, true)) return MOE_ERR_WORKSPACE;
+    BwdPlan b;
+    if (workspace_bytes < make_bwd_plan(shape, p, &b)) return MOE_ERR_WORKSPACE;
+    moe_status_t st = device_ok();
+    if (st != MOE_OK) return st;
+    place(&p, const_cast<void*>(state));
+    place_bwd(&b, workspace);
+    BwdArgs a{};
+    a.x = static_cast<const bf16_t*>(x);
+    a.C = static_cast<const bf16_t*>(centroids);
+    a.w1 = static_cast<const bf16_t*>(w1);
+    a.w3 = static_cast<const bf16_t*>(w3);
+    a.w2 = static_cast<const bf16_t*>(w2);
+    a.ws1 = static_cast<const bf16_t*>(ws1);
+    a.ws3 = static_cast<const bf16_t*>(ws3);
+    a.ws2 = static_cast<const bf16_t*>(ws2);
+    a.dout = static_cast<const bf16_t*>(dout);
+    a.alpha = alpha;
+    a.dx = static_cast<bf16_t*>(dx);
+    a.dw1 = static_cast<bf16_t*>(dw1);
+    a.dw3 = static_cast<bf16_t*>(dw3);
+    a.dw2 = static_cast<bf16_t*>(dw2);
+    a.dws1 = static_cast<bf16_t*>(dws1);
+    a.dws3 = static_cast<bf16_t*>(dws3);
+    a.dws2 = static_cast<bf16_t*>(dws2);
+    a.dC = dC;
+    a.dgate = dgate;
+    const hipError_t e = launch_backward(p, b, a, static_cast<hipStream_t>(stream), rec_mark_bwd);
+    if (g_rec.on && g_rec.calls < g_rec.max_calls) {
+        for (int k = kBwdSlot0; k < kSlots; ++k) {
+            const int bs = k - kBwdSlot0;
+            const bool ran = rk || !(bs == 2 || bs == 3 || bs == 8);
+            if (ran && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
+        }
+        ++g_rec.calls;
+    }
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // Allocation-free forward: the workspace is a static device array of
@@ -419,6 +572,26 @@ __attribute__((visibility("default"))) moe_status_t moe_forward_fp8(
                       static_cast<const uint8_t*>(w2q), w1_scale, w3_scale, w2_scale};
     return run_forward(shape, x, centroids, expert_bias, nullptr, nullptr, nullptr, &q8, ws1, ws3,
                        ws2, out, topk_idx, topk_gate, workspace, workspace_bytes, stream);
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_forward_train(
+    const moe_shape_t* shape, const void* x, const void* centroids, const float* expert_bias,
+    const void* w1, const void* w3, const void* w2, const void* ws1, const void* ws3,
+    const void* ws2, void* out, int32_t* topk_idx, float* topk_gate, float* balance_stats,
+    void* state, size_t state_bytes, void* stream) {
+    return run_forward(shape, x, centroids, expert_bias, w1, w3, w2, nullptr, ws1, ws3, ws2, out,
+                       topk_idx, topk_gate, state, state_bytes, stream, true, balance_stats);
+}
+
+__attribute__((visibility("default"))) moe_status_t moe_backward(
+    const moe_shape_t* shape, const void* x, const void* centroids, const void* w1,
+    const void* w3, const void* w2, const void* ws1, const void* ws3, const void* ws2,
+    const void* dout, float alpha, const void* state, size_t state_bytes, void* dx, void* dw1,
+    void* dw3, void* dw2, void* dws1, void* dws3, void* dws2, float* dC, float* dgate,
+    void* workspace, size_t workspace_bytes, void* stream) {
+    return run_backward(shape, x, centroids, w1, w3, w2, ws1, ws3, ws2, dout, alpha, state,
+                        state_bytes, dx, dw1, dw3, dw2, dws1, dws3, dws2, dC, dgate, workspace,
+                        workspace_bytes, stream);
 }
 
 __attribute__((visibility("default"))) moe_status_t moe_route(

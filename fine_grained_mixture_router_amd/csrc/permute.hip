@@ -212,6 +212,7 @@ __global__ __launch_bounds__(kScatterThreads) void perm_scatter_kernel(Plan p, i
             const int slot = p.chunk_base[(size_t)c * p.Epad + e] + __popcll(below);
             p.slot_of[(size_t)t * p.K + (i - tl * p.K)] = slot;
             p.tok_of[slot] = t;
+            if (p.row_gate) p.row_gate[slot] = p.gate[(size_t)t * p.K + (i - tl * p.K)];
         }
     }
     const int tk = p.T * p.K;

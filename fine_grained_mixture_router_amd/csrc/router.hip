@@ -297,11 +297,16 @@ __device__ __forceinline__ float pick4(const float (&a)[4], int j) {
     return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
 }
 
+// scores / score_part (training forward only, else null): every expert's
+// score of every token, and the sums of those scores over each workgroup's
+// 16 tokens, taken in token order (the mean-score statistic of the
+// expert-level balance loss is their sum over workgroups, in order).
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ idx,
     float* __restrict__ gate, uint64_t* __restrict__ masks, int T, int E, int Epad, int K,
-    int split, uint32_t flags) {
+    int split, uint32_t flags, float* __restrict__ scores, float* __restrict__ score_part) {
     __shared__ unsigned smask[256];
+    __shared__ float sscore[kSelectWaves][256];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -360,6 +365,17 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
             for (int j = 0; j < 4; ++j) ps += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
             sum = wave_sum(ps);
         }
+        if (scores) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = lane + 64 * j;
+                if (e < Epad) {
+                    const float sv = e < E ? (sig ? sc[j] : expf(v[j] - mx) / sum) : 0.f;
+                    scores[(size_t)t * Epad + e] = sv;
+                    sscore[wave][e] = sv;
+                }
+            }
+        }
 
         float gk[4] = {0.f, 0.f, 0.f, 0.f};          // renormalised: gate k kept by lane k % 64
         float zsum = 0.f;
@@ -403,7 +419,15 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
             }
         }
     }
+    if (scores && t >= T)
+        for (int e = lane; e < Epad; e += 64) sscore[wave][e] = 0.f;
     __syncthreads();
+    if (score_part)
+        for (int e = tid; e < Epad; e += kSelectThreads) {
+            float acc = 0.f;
+            for (int w = 0; w < kSelectWaves; ++w) acc += sscore[w][e];
+            score_part[(size_t)blockIdx.x * Epad + e] = acc;
+        }
     uint16_t* m16 = reinterpret_cast<uint16_t*>(masks);
     for (int e = tid; e < Epad; e += kSelectThreads)
         m16[((size_t)c * Epad + e) * kSubChunks + q] = (uint16_t)smask[e];
@@ -427,7 +451,8 @@ hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C,
 
 hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st) {
     router_select_kernel<<<p.nchunk * kSubChunks, kSelectThreads, 0, st>>>(
-        p.logits, bias, p.idx, p.gate, p.masks, p.T, p.E, p.Epad, p.K, p.split, p.flags);
+        p.logits, bias, p.idx, p.gate, p.masks, p.T, p.E, p.Epad, p.K, p.split, p.flags,
+        p.scores, p.score_part);
     return hipGetLastError();
 }
 

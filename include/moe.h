@@ -186,6 +186,87 @@ moe_status_t moe_forward_noalloc(const moe_shape_t* shape, const void* x, const 
 /* Bytes of moe_forward_noalloc's static scratch array (64 MiB). */
 size_t moe_noalloc_scratch_bytes(void);
 
+/* ---- Training side: forward that saves what the backward needs, and the
+ * backward itself. ---------------------------------------------------------
+ *
+ * Objective whose gradients moe_backward returns:
+ *
+ *   Lambda = sum_{t,j} dout[t,j] * out[t,j]  +  alpha * L_bal
+ *
+ * dout is the upstream gradient dLoss/dout.  L_bal is the expert-level
+ * balance loss of "DeepSeekMoE 深度解读报告" (sections 2.5 and 3.2), which
+ * takes, over the batch, each expert's hit rate and mean gate score; the
+ * pages print no formula, and the reading here is
+ *
+ *   f_e = E * n_e / (K * T)        n_e = rows routed to expert e
+ *   P_e = (1/T) * sum_t s[t,e]     s = the full score vector of the gate
+ *                                  (softmax or sigmoid, before renormalising)
+ *   L_bal = sum_e f_e * P_e        (f_e held constant: a count has no gradient)
+ *
+ * The top-K choice is piecewise constant, so gradients reach the affinities
+ * only through the kept gates and, via L_bal, through every score.  The
+ * per-expert bias is a fixed input (no gradient).
+ *
+ * Bytes of the training state moe_forward_train writes and moe_backward
+ * reads (the forward's workspace plus every expert's score of every token,
+ * per-row gates, and the pre-activations Z = [W1 x | W3 x] of every row,
+ * bf16).  0 for an invalid shape. */
+size_t moe_train_state_size(const moe_shape_t* shape);
+
+/* Bytes of device workspace moe_backward needs (dZ = [dA | dB] and g * H of
+ * every row, the gate-gradient partials, the affinity gradients, the
+ * per-row input gradients and work lists).  0 for an invalid shape. */
+size_t moe_backward_workspace_size(const moe_shape_t* shape);
+
+/* The layer forward of moe_forward (bit-identical out, topk_idx,
+ * topk_gate), with the training state written to `state`
+ * (moe_train_state_size() bytes, 256-byte aligned, caller-owned; keep it
+ * unchanged until the matching moe_backward).  balance_stats (fp32 [2E + 1]
+ * or NULL): f_e for e < E, P_e at E + e, L_bal at 2E (0 when K == 0).
+ * Errors as for moe_forward, with the state in place of the workspace. */
+moe_status_t moe_forward_train(const moe_shape_t* shape, const void* x, const void* centroids,
+                               const float* expert_bias, const void* w1, const void* w3,
+                               const void* w2, const void* ws1, const void* ws3,
+                               const void* ws2, void* out, int32_t* topk_idx, float* topk_gate,
+                               float* balance_stats, void* state, size_t state_bytes,
+                               void* stream);
+
+/* Backward of the layer for upstream gradient dout (bf16 [T, d]) and
+ * balance factor alpha >= 0, from the state of a moe_forward_train call
+ * with the same shape, x, centroids, bias and weights (not re-checked).
+ * Per row r (token t, routed gate g_r, 1 for a shared expert), with
+ * A = W1 x, B = W3 x, H = silu(A) B:
+ *
+ *   dgate_r = <dout[t], W2 H>             (computed as <W2^T dout[t], H>)
+ *   dH = g_r W2^T dout[t],  dA = dH B silu'(A),  dB = dH silu(A)
+ *   dx[t] += W1^T dA + W3^T dB;  dW2 += g_r dout[t] H^T;
+ *   dW1 += dA x[t]^T;  dW3 += dB x[t]^T
+ *
+ * then gate -> score -> affinity for every token (through the
+ * renormalisation and the softmax or sigmoid of the shape's flags, plus
+ * alpha * f_e / T on every score from L_bal), dx += dL C, dC = dL^T x, and
+ * dx += dout (the residual, unless MOE_FLAG_NO_RESIDUAL).
+ *
+ *   dx          bf16 [T, d]
+ *   dw1, dw3    bf16 [E, I, d];  dw2 bf16 [E, d, I]   (NULL iff K == 0;
+ *               every expert is written, untouched ones with zeros)
+ *   dws1, dws3  bf16 [Ks, Is, d]; dws2 bf16 [Ks, d, Is] (NULL iff Ks == 0)
+ *   dC          fp32 [E, d]      (NULL iff K == 0)
+ *   dgate       fp32 [T, K] or NULL: d Lambda / d gate of each kept expert
+ *   workspace   moe_backward_workspace_size() bytes, 256-byte aligned
+ *
+ * Arithmetic: bf16 MFMA with fp32 accumulation; dZ, g * H, the affinity
+ * gradients and each row's dx contribution stored as bf16; dx summed per
+ * token in fp32 in a fixed order and rounded once.  Bit-identical from run
+ * to run.  Errors: as moe_forward (MOE_ERR_WORKSPACE for a short state or
+ * workspace, MOE_ERR_SHAPE also for alpha < 0 or not finite). */
+moe_status_t moe_backward(const moe_shape_t* shape, const void* x, const void* centroids,
+                          const void* w1, const void* w3, const void* w2, const void* ws1,
+                          const void* ws3, const void* ws2, const void* dout, float alpha,
+                          const void* state, size_t state_bytes, void* dx, void* dw1, void* dw3,
+                          void* dw2, void* dws1, void* dws3, void* dws2, float* dC,
+                          float* dgate, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Routing only: affinities, softmax (or the flags' gate), top-K
  * ("DeepSeekMoE 深度解读报告", section 3.1).  Writes topk_idx [T, K] and topk_gate [T, K] (both
  * required).  The workspace needs moe_route_workspace_size() bytes (routing
@@ -199,10 +280,10 @@ const char* moe_status_string(moe_status_t status);
 
 /* Benchmark instrumentation (not part of the layer's computation).
  *
- * moe_profile_begin(max_calls): the next max_calls (1..100000) moe_forward
- * calls record a HIP event before and after each kernel they launch, on the
- * call's stream.  It creates 14*max_calls HIP events (host-side runtime
- * objects; no device memory).  Errors: MOE_ERR_SHAPE for a bad count,
+ * moe_profile_begin(max_calls): the next max_calls (1..100000) forward or
+ * backward calls record a HIP event before and after each kernel they
+ * launch, on the call's stream.  It creates 32*max_calls HIP events
+ * (host-side runtime objects; no device memory).  Errors: MOE_ERR_SHAPE for a bad count,
  * MOE_ERR_NO_DEVICE / MOE_ERR_DEVICE_ARCH as for moe_forward, MOE_ERR_HIP if
  * event creation fails.
  *
@@ -212,8 +293,10 @@ const char* moe_status_string(moe_status_t status);
  * array; either pointer may be NULL), then releases the events and stops
  * recording.  MOE_ERR_NULL if no recording is active, MOE_ERR_HIP if an event
  * could not be read.  Slots: 0 router_logits, 1 router_select, 2 perm_scan,
- * 3 perm_scatter, 4 gemm_gate_up, 5 gemm_down, 6 combine
- * (moe_profile_slot_name gives the name, "" past the end).
+ * 3 perm_scatter, 4 gemm_gate_up, 5 gemm_down, 6 combine; moe_backward's
+ * 7 bwd_lists, 8 bwd_dh, 9 bwd_router, 10 bwd_dx_router, 11 bwd_dx,
+ * 12 bwd_dx_combine, 13 bwd_dw2, 14 bwd_dw13, 15 bwd_dc (a backward call
+ * counts as a call) (moe_profile_slot_name gives the name, "" past the end).
  *
  * One process-wide recorder: not thread-safe; do not record from several
  * host threads at once. */

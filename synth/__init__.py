@@ -25,6 +25,7 @@ STREAM_X, STREAM_C, STREAM_BIAS, STREAM_W1, STREAM_W3, STREAM_W2 = 0, 1, 2, 3, 4
 STREAM_WS1, STREAM_WS3, STREAM_WS2 = 6, 7, 8
 STREAM_Q1, STREAM_Q3, STREAM_Q2 = 9, 10, 11            # 8-bit routed weight codes
 STREAM_S1, STREAM_S3, STREAM_S2 = 12, 13, 14           # their per-row scales
+STREAM_DOUT = 15                                         # upstream gradient of a backward
 
 
 def build(force: bool = True) -> str:

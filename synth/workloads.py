@@ -19,7 +19,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (STREAM_C, STREAM_Q1, STREAM_Q2, STREAM_Q3, STREAM_S1, STREAM_S2, STREAM_S3,
+from . import (STREAM_C, STREAM_DOUT, STREAM_Q1, STREAM_Q2, STREAM_Q3, STREAM_S1, STREAM_S2, STREAM_S3,
                STREAM_W1, STREAM_W2, STREAM_W3, STREAM_WS1, STREAM_WS2, STREAM_WS3, STREAM_X,
                fp8_codes, normal_bf16, uniform_f32, zipf_bias)
 
@@ -89,6 +89,13 @@ def gen_x_rows(w: Workload, tokens) -> np.ndarray:
     for i, t in enumerate(tokens):
         normal_bf16(w.xseed, STREAM_X, (w.d,), SIGMA_X, offset=int(t) * w.d, out=out[i])
     return out
+
+
+def gen_dout(w: Workload, T: int | None = None) -> np.ndarray:
+    """Upstream gradient dLoss/dout for a backward, N(0, 1) bf16 [T, d], from
+    the activation seed on its own stream."""
+    T = w.T if T is None else T
+    return normal_bf16(w.xseed, STREAM_DOUT, (T, w.d), 1.0)
 
 
 def gen_centroids(w: Workload) -> np.ndarray:

@@ -143,11 +143,13 @@ def test_route_validation():
 def test_profile_validation():
     f = moe.lib()
     assert f.moe_profile_begin(0) == 2
-    assert f.moe_profile_end(None, None, 7) == 1          # nothing recording
+    assert f.moe_profile_end(None, None, 16) == 1         # nothing recording
     assert f.moe_profile_slot_name(4) == b"gemm_gate_up"
-    assert f.moe_profile_slot_name(7) == b""
+    assert f.moe_profile_slot_name(8) == b"bwd_dh"
+    assert f.moe_profile_slot_name(15) == b"bwd_dc"
+    assert f.moe_profile_slot_name(16) == b""
     assert f.moe_profile_begin_slots(1, 0) == 2           # empty slot mask
-    assert f.moe_profile_begin_slots(1, 1 << 7) == 2      # past the last slot
+    assert f.moe_profile_begin_slots(1, 1 << 16) == 2     # past the last slot
     assert f.moe_profile_begin_slots(0, 1 << 4) == 2
 
 
@@ -247,3 +249,46 @@ def test_noalloc_scratch_limits():
     torch = pytest.importorskip("torch")
     if torch.cuda.device_count() == 0:
         assert f(ctypes.byref(dec), *args) == 5
+
+
+def test_training_entry_validation():
+    """moe_forward_train / moe_backward: sizes, and bad arguments refused
+    before any device call."""
+    s = S()
+    st = moe.train_state_size(s)
+    ws = moe.backward_workspace_size(s)
+    assert st > moe.workspace_size(s) and ws > 0 and st % 256 == 0 and ws % 256 == 0
+    assert moe.lib().moe_train_state_size(ctypes.byref(S(d=100))) == 0
+    vp = ctypes.c_void_p
+    ft = moe.lib().moe_forward_train
+    args = [vp(4096)] * 14
+    assert ft(ctypes.byref(s), *args[:12], None, vp(4096), ctypes.c_size_t(st - 1), None) == 4
+    bw = moe.lib().moe_backward
+
+    def call(alpha=0.0, state_bytes=st, ws_bytes=ws, **over):
+        p = dict(x=4096, C=4096, w1=4096, w3=4096, w2=4096, ws1=4096, ws3=4096, ws2=4096,
+                 dout=4096, state=4096, dx=4096, dw1=4096, dw3=4096, dw2=4096, dws1=4096,
+                 dws3=4096, dws2=4096, dC=4096, dgate=None, ws=4096)
+        p.update(over)
+        a = [None if p[k] is None else vp(p[k]) for k in
+             ("x", "C", "w1", "w3", "w2", "ws1", "ws3", "ws2", "dout")]
+        b = [None if p[k] is None else vp(p[k]) for k in
+             ("dx", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2", "dC", "dgate", "ws")]
+        return bw(ctypes.byref(s), *a, ctypes.c_float(alpha), None if p["state"] is None
+                  else vp(p["state"]), ctypes.c_size_t(state_bytes), *b[:9], b[9],
+                  ctypes.c_size_t(ws_bytes), None)
+
+    assert call(dout=None) == 1
+    assert call(dw2=None) == 1
+    assert call(dC=None) == 1
+    assert call(dws3=None) == 1
+    assert call(state=None) == 1
+    assert call(dx=4096 + 8) == 3
+    assert call(state=4096 + 16) == 3
+    assert call(alpha=-1.0) == 2
+    assert call(alpha=float("nan")) == 2
+    assert call(state_bytes=st - 1) == 4
+    assert call(ws_bytes=ws - 1) == 4
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() == 0:
+        assert call() == 5

@@ -98,3 +98,67 @@ def test_v3_parity(v3_layer, name, T):
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(idx2, idx)
+
+
+@pytest.mark.parametrize("name", ["v3_decode", "v3_prefill"])
+def test_v3_backward(v3_layer, name):
+    """The backward at the full V3 shape, through moe_forward_train and
+    moe_backward, against the fp64 backward oracle under the GPU's routing:
+    decode — every token's input and gate gradients, the centroid gradient,
+    the weight gradients of three experts and of the shared expert; prefill —
+    input and gate gradients of tokens that put a checked row in every
+    (group, M-tile) of the dH / dX work lists, and the weight gradients of a
+    middling and the smallest touched expert (the busiest one holds every
+    token: its fp64 reference would take minutes)."""
+    from helpers import check_grad
+    H, D = v3_layer
+    w = wl.WORKLOADS[name]
+    _log(f"[v3-bwd] {name}")
+    x = wl.gen_x(w)
+    bias = wl.gen_bias(w)
+    dout = wl.gen_dout(w)
+    xd, bd, dod = to_dev(x), to_dev(bias), to_dev(dout)
+    args = (xd, D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"])
+    out, st, idx = moe.forward_train(*args, K=w.K, bias=bd, return_routing=True)[:3]
+    g = moe.backward(*args, dout=dod, state=st, return_dgate=True)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    counts = np.bincount(gi.ravel(), minlength=w.E)
+    touched = np.nonzero(counts)[0]
+    order = touched[np.argsort(-counts[touched], kind="stable")]
+    if name == "v3_decode":
+        tok = np.arange(w.T)
+        experts = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+        want_shared = want_dC = True
+    else:
+        tok = tile_cover_tokens(gi, w.E, w.Ks, w.T)
+        experts = sorted({int(order[len(order) // 2]), int(order[-1])})
+        want_shared = want_dC = False
+    _log(f"[v3-bwd] {name}: oracle on {tok.size} tokens, experts {experts} "
+         f"({[int(counts[e]) for e in experts]} rows)")
+    ref = oracle.backward(x, H["C"], bias, H["w1"], H["w3"], H["w2"], H["ws1"], H["ws3"],
+                          H["ws2"], w.K, dout, tokens=tok, experts=experts,
+                          want_shared=want_shared, want_dC=want_dC, forced_idx=gi)
+
+    def f64(t):
+        return out_f64(t) if t.dtype == torch.bfloat16 else t.double().cpu().numpy()
+
+    msg = [f"dx {check_grad(f64(g['dx'])[tok], ref['dx'], 'dx'):.2e}",
+           f"dgate {check_grad(f64(g['dgate'])[tok], ref['dgate'], 'dgate'):.2e}"]
+    sel = torch.as_tensor(np.asarray(experts, dtype=np.int64), device="cuda")
+    for nm in ("dw1", "dw3", "dw2"):
+        msg.append(f"{nm} {check_grad(f64(g[nm][sel]), ref[nm], nm):.2e}")
+    if want_shared:
+        for nm in ("dws1", "dws3", "dws2"):
+            msg.append(f"{nm} {check_grad(f64(g[nm]), ref[nm], nm):.2e}")
+    if want_dC:
+        msg.append(f"dC {check_grad(f64(g['dC']), ref['dC'], 'dC'):.2e}")
+    _log(f"[v3-bwd] {name}: max|err|/max|ref| " + ", ".join(msg))
+    # untouched experts get exact zeros
+    untouched = np.nonzero(counts == 0)[0]
+    if untouched.size:
+        u = torch.as_tensor(untouched, device="cuda")
+        for nm in ("dw1", "dw3", "dw2"):
+            assert not bool((g[nm][u] != 0).any())
+    del g, st
+    torch.cuda.empty_cache()

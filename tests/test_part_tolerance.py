@@ -18,7 +18,7 @@ import synth
 from oracle.ref_np import widen
 from synth import workloads as wl
 
-from helpers import PART_RMS_TOL, PART_TOL, rms
+from helpers import GRAD_RMS_TOL, GRAD_TOL, PART_RMS_TOL, PART_TOL, rms
 
 
 def _bf16(a):
@@ -87,3 +87,101 @@ def test_part_bars_cover_the_specified_roundings(name, n):
     _, ro_bad, _ = _emulate(L, tok, bad, ref["gate"], 0)
     mx, rm = _ratios(ro_bad, ref["routed"])
     assert mx > PART_TOL or rm > PART_RMS_TOL, (name, mx, rm)
+
+
+# ---------------------------------------------------------------------------
+# The backward.  Its specified rounding points: the saved pre-activations
+# Z = [W1 x | W3 x] (bf16), the per-row dZ = [dA | dB] and g*H (bf16), the
+# affinity gradients (bf16), each row's input gradient (bf16), and the bf16
+# results dx, dW1, dW3, dW2; gate gradients and dC stay fp32.  Weight
+# gradients are far more heavy-tailed than layer outputs (max/RMS up to ~9
+# against ~4.5), so their max error is taken relative to max|ref|; the RMS
+# bar is the parts' one.
+
+
+
+def _silu(a):
+    return a / (1.0 + np.exp(-a))
+
+
+def _dsilu(a):
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def _emulate_backward(L, K, idx, gate, probs, experts):
+    """dx, dgate, dW of `experts`, shared dW, dC with the GPU's rounding
+    points (softmax gate, no renormalisation, alpha = 0)."""
+    X, dO = widen(L["x"]), widen(L["dout"])
+    T, d = X.shape
+    E = L["C"].shape[0]
+    dXr_sum = np.zeros((T, d))
+    dgate = np.zeros((T, K))
+    out = {}
+
+    def one(rows, w1, w3, w2, g):
+        Xr, dOr = X[rows], dO[rows]
+        W1, W3, W2 = widen(w1), widen(w3), widen(w2)
+        A, B = _bf16(Xr @ W1.T), _bf16(Xr @ W3.T)
+        dHp = dOr @ W2
+        Hb = _silu(A) * B
+        dg = (dHp * Hb).sum(axis=1)
+        dH = g[:, None] * dHp
+        dA, dB = _bf16(dH * B * _dsilu(A)), _bf16(dH * _silu(A))
+        gH = _bf16(g[:, None] * Hb)
+        return dg, _bf16(dA @ W1 + dB @ W3), (_bf16(dA.T @ Xr), _bf16(dB.T @ Xr), _bf16(dOr.T @ gH))
+
+    for e in range(E):
+        r, k = np.nonzero(idx == e)
+        if r.size == 0:
+            continue
+        dg, dxr, dws = one(r, L["w1"][e], L["w3"][e], L["w2"][e], gate[r, k])
+        dgate[r, k] = dg
+        np.add.at(dXr_sum, r, dxr)
+        if e in experts:
+            out[("dw", e)] = dws
+    for s in range(len(L["ws1"])):
+        _, dxr, dws = one(np.arange(T), L["ws1"][s], L["ws3"][s], L["ws2"][s], np.ones(T))
+        dXr_sum += dxr
+        out[("dws", s)] = dws
+    ds = np.zeros_like(probs)
+    np.put_along_axis(ds, idx, dgate, axis=1)
+    dl = probs * (ds - (probs * ds).sum(axis=1, keepdims=True))
+    dLb = _bf16(dl)
+    out["dx"] = _bf16(dO + dLb @ widen(L["C"]) + dXr_sum)
+    out["dgate"] = dgate
+    out["dC"] = dLb.T @ X
+    return out
+
+
+def _grad_ratios(got, ref):
+    return (float(np.abs(got - ref).max()) / float(np.abs(ref).max()),
+            rms(got - ref) / rms(ref))
+
+
+@pytest.mark.parametrize("name", ["tiny", "2b"])
+def test_grad_bars_cover_the_specified_roundings(name):
+    w = wl.WORKLOADS[name]
+    L = wl.gen_all(w)
+    L["dout"] = wl.gen_dout(w)
+    idx, gate, _, probs = oracle.route(L["x"], L["C"], L["bias"], w.K, return_probs=True)
+    experts = list(range(w.E)) if w.E <= 16 else [0, w.E // 2, w.E - 1]
+    ref = oracle.backward(L["x"], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"],
+                          L["ws3"], L["ws2"], w.K, L["dout"], experts=experts, want_shared=True,
+                          want_dC=True, forced_idx=idx)
+    em = _emulate_backward(L, w.K, idx, gate, probs, set(experts))
+    pairs = [("dx", em["dx"], ref["dx"]), ("dgate", em["dgate"], ref["dgate"]),
+             ("dC", em["dC"], ref["dC"])]
+    for q, e in enumerate(experts):
+        for n, a in zip(("dw1", "dw3", "dw2"), em[("dw", e)]):
+            pairs.append((n, a, ref[n][q]))
+    for n, a in zip(("dws1", "dws3", "dws2"), em[("dws", 0)]):
+        pairs.append((n, a, ref[n][0]))
+    worst_mx = worst_rm = 0.0
+    for n, a, r in pairs:
+        mx, rm = _grad_ratios(a, r)
+        worst_mx, worst_rm = max(worst_mx, mx), max(worst_rm, rm)
+        assert mx <= GRAD_TOL / 2, (name, n, mx)
+        assert rm <= GRAD_RMS_TOL / 2.5, (name, n, rm)
+    # the bars are within a small factor of what the roundings cost
+    assert worst_mx >= GRAD_TOL / 10 and worst_rm >= GRAD_RMS_TOL / 8, (worst_mx, worst_rm)
