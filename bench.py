@@ -10,8 +10,12 @@ bias) — MFMA-bound.  The same layer on a 256-token decode batch (HBM-bound)
 is measured in the same run and reported under "decode", and both batches
 again with 8-bit (E4M3, per-row scaled) routed weights under "prefill_fp8"
 and "decode_fp8"; the smaller layer shapes (2B: 63 experts of 896, top-7;
-16B: 64 experts of 1408, top-6, with and without a Zipf(1.1) bias) are
-summarised under "other_configs" with both roofline fractions.  Inputs are
+16B: 64 experts of 1408, top-6, with and without a Zipf(1.1) bias, and the
+tiny 16-expert layer) are summarised under "other_configs" with both roofline
+fractions.  The training side (moe_forward_train + moe_backward: input,
+weight, centroid and gate gradients for a seeded upstream gradient) is timed
+on the prefill and decode batches under "backward", with the dominant
+backward kernel against its roofline.  Inputs are
 seeded synthetic data (bf16, N(0,1) activations, N(0,0.006) weights; the
 8-bit codes are drawn as bit fields with per-row scales of a similar size).
 
@@ -73,10 +77,12 @@ def parse():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode",
                     help="second workload on the same layer weights ('' to skip)")
-    ap.add_argument("--configs", default="2b,16b,16b_zipf",
+    ap.add_argument("--configs", default="tiny,2b,16b,16b_zipf",
                     help="smaller layer shapes summarised under other_configs ('' to skip)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the batches with 8-bit routed weights")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training-side (backward) measurements")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle CPU baseline (0 to skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -185,6 +191,7 @@ def hit_stats(idx, E):
     p = counts[counts > 0] / counts.sum()
     ent = float(-(p * np.log(p)).sum())
     return dict(touched=int((counts > 0).sum()), max_rows=int(counts.max()),
+                min_rows=int(counts.min()), min_rows_touched=int(counts[counts > 0].min()),
                 mean_rows=float(counts.mean()), entropy_over_lnE=ent / math.log(E) if E > 1 else 1.0,
                 active_ratio=float((counts > 0).mean()))
 
@@ -288,6 +295,116 @@ def time_workload(w, D, host_x, steps, warmup):
                 gate=gate.cpu().numpy())
 
 
+BWD_SLOTS = ("bwd_lists", "bwd_dh", "bwd_router", "bwd_dx_router", "bwd_dx", "bwd_dx_combine",
+             "bwd_dw2", "bwd_dw13", "bwd_dc")
+
+
+def backward_work(w, counts):
+    """Algorithmic FLOPs (and, for the weight-gradient GEMMs, bytes) of one
+    backward.  Per routed (shared) row: dH = dO W2 2·d·I, dX = [dA|dB]
+    [W1;W3] 4·d·I, dW2 2·d·I, dW1+dW3 4·d·I; the router's dL·C and dL^T x
+    2·T·E·d each.  dW13 bytes: the dW1 and dW3 of every expert written once
+    (bf16) plus the rows of dZ and x it reads."""
+    rows_i = w.T * w.K * w.I + w.T * w.Ks * w.Is
+    f = dict(bwd_dh=2.0 * w.d * rows_i, bwd_dx=4.0 * w.d * rows_i, bwd_dw2=2.0 * w.d * rows_i,
+             bwd_dw13=4.0 * w.d * rows_i, bwd_dx_router=2.0 * w.T * w.E * w.d,
+             bwd_dc=2.0 * w.T * w.E * w.d)
+    total = sum(f.values())
+    dw13_bytes = (2 * 2 * (w.E * w.I + w.Ks * w.Is) * w.d            # dW1, dW3 written
+                  + 2 * 2 * rows_i + 2 * w.T * (w.K + w.Ks) * w.d)     # dZ and x rows read
+    return dict(flops=f, total_flops=total, dw13_bytes=float(dw13_bytes))
+
+
+def time_backward(w, D, host_x, steps, warmup):
+    """The training side on one batch: moe_forward_train, then `steps` timed
+    moe_backward calls on its state (a seeded upstream gradient), each
+    backward kernel recorded with HIP events on the call's stream in ten
+    further calls."""
+    import torch
+
+    import fine_grained_mixture_router_amd as moe
+    from synth import workloads as wl
+    x = dev(host_x)
+    dout = dev(wl.gen_dout(w, host_x.shape[0]))
+    bias = D.get("bias")
+    args = (x, D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"])
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    state = torch.empty(moe.train_state_size(shape), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(moe.backward_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+    outs = dict(dx=torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda"),
+                dw1=torch.empty_like(D["w1"]), dw3=torch.empty_like(D["w3"]),
+                dw2=torch.empty_like(D["w2"]), dws1=torch.empty_like(D["ws1"]),
+                dws3=torch.empty_like(D["ws3"]), dws2=torch.empty_like(D["ws2"]),
+                dC=torch.empty((w.E, w.d), dtype=torch.float32, device="cuda"))
+
+    def fwd():
+        return moe.forward_train(*args, K=w.K, bias=bias, out=out, state=state)[1]
+
+    st = fwd()
+    for _ in range(warmup):
+        fwd()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fwd()
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+
+    def bwd():
+        moe.backward(*args, dout=dout, state=st, workspace=ws, **outs)
+
+    for _ in range(warmup):
+        bwd()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / steps
+    split = max(1, min(steps, 10))
+    moe.profile_begin(split, kernels=list(BWD_SLOTS))
+    for _ in range(split):
+        bwd()
+    torch.cuda.synchronize()
+    kern = moe.profile_end()
+    del state, ws, outs
+    torch.cuda.empty_cache()
+    return dict(fwd_train_ms=fwd_ms, bwd_ms=bwd_ms,
+                kernel_ms={k: round(kern[k][0] / max(kern[k][1], 1), 4) for k in BWD_SLOTS
+                           if kern[k][1] > 0})
+
+
+def backward_line(w, r, counts):
+    """The backward's summary for the JSON line: its own throughput and its
+    dominant kernel against the roofline (MFMA for many rows per expert; the
+    weight-gradient writes, HBM, for few)."""
+    bw = backward_work(w, counts)
+    km = r["kernel_ms"]
+    dom = max((k for k in km if k in bw["flops"]), key=lambda k: km[k])
+    t = km[dom] / 1e3
+    if regime(w) == "mfma" or dom != "bwd_dw13":
+        ach = bw["flops"][dom] / t / 1e12
+        roof = dict(kernel=dom, bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    algorithmic_flops=bw["flops"][dom], mean_launch_ms=km[dom])
+    else:
+        ach = bw["dw13_bytes"] / t / 1e9
+        roof = dict(kernel=dom, bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS,
+                    unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), traffic=None,
+                    algorithmic_bytes=bw["dw13_bytes"], mean_launch_ms=km[dom])
+    tf = bw["total_flops"] / (r["bwd_ms"] / 1e3) / 1e12
+    return {"workload": w.name, "T": w.T, "ms_per_backward": round(r["bwd_ms"], 4),
+            "ms_per_forward_train": round(r["fwd_train_ms"], 4),
+            "train_step_tokens_per_s": round(w.T / ((r["bwd_ms"] + r["fwd_train_ms"]) / 1e3), 1),
+            "backward_tflops": round(tf, 1), "backward_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "roofline": roof, "kernel_ms": km}
+
+
 def layer_roofline_ms(w, counts):
     """Lower bound on the layer's time with every piece at the better of its
     two ceilings (2.5 PFLOP/s, 8 TB/s): the router, each routed or shared
@@ -353,23 +470,54 @@ def roofline(kind, work, kernels, workload):
                 unit="GB/s", frac=round(ach / PEAK_HBM_GBS, 4), **common)
 
 
+def tile_cover(idx, w, bm=256):
+    """Tokens whose rows touch every (group, bm-row tile) of the GEMM work
+    lists (the token on each tile's last row), in token order."""
+    import numpy as np
+    picks = set()
+    for e in range(w.E):
+        toks = np.nonzero((idx == e).any(axis=1))[0]
+        for m0 in range(0, toks.size, bm):
+            picks.add(int(toks[min(m0 + bm, toks.size) - 1]))
+    if w.Ks:
+        for m0 in range(0, w.T, bm):
+            picks.add(min(m0 + bm, w.T) - 1)
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def routing_check(w, L, res):
+    """Every token's routing against the oracle: index sets equal wherever
+    the oracle's K-th vs (K+1)-th score margin exceeds 1e-5; the tokens
+    under that margin are counted (exempt), not checked."""
+    import numpy as np
+
+    import oracle
+    ri, _, rm = oracle.route(L["x"], L["C"], L["bias"], w.K)
+    ok = rm > 1e-5
+    gi = np.sort(res["idx"], axis=1)
+    mism = int((np.sort(ri, axis=1) != gi)[ok].any(axis=1).sum())
+    return dict(tokens=int(w.T), margin_exempt=int((~ok).sum()), set_mismatches=mism)
+
+
 def cpu_baseline(w, L, res, seconds):
-    """The fp64 oracle, as it stands, on the first tokens of the same batch
-    for about `seconds` of wall clock; also a spot parity check of the GPU
-    output on those tokens."""
+    """The fp64 oracle, as it stands, timed on the host cores for about
+    `seconds` of wall clock on tokens that put a row in every work-list tile
+    of the GEMMs (in token order; the whole set when the budget allows);
+    also a spot parity check of the GPU output on those tokens."""
     import numpy as np
 
     import oracle
     import synth
     got_bits = res["out"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    order = tile_cover(res["idx"], w)
     done = 0
     errs, mism = [], 0
     t0 = time.time()
     chunk = 16
     threads = 0
     ref_rows = []
-    while done < w.T and (time.time() - t0) < seconds:
-        tok = np.arange(done, min(done + chunk, w.T))
+    while done < order.size and (time.time() - t0) < seconds:
+        tok = order[done:done + chunk]
         r = oracle.forward(L["x"][tok], L["C"], L["bias"], L["w1"], L["w3"], L["w2"], L["ws1"],
                            L["ws3"], L["ws2"], w.K)
         threads = r["threads"]
@@ -385,10 +533,12 @@ def cpu_baseline(w, L, res, seconds):
     got = synth.bf16_to_f64(got_bits[toks])
     rel = float(np.abs(got - ref).max() / np.sqrt(np.mean(ref ** 2)))
     return (dict(value=round(done / dt, 2), unit="tokens/s", cores=int(threads), kind="oracle",
-                 sample=f"first {done} tokens of the {w.name} batch, full layer in fp64 "
-                        f"(routing + {w.K} routed + {w.Ks} shared SwiGLU experts per token), "
+                 sample=f"{done} of the {order.size} tokens of the {w.name} batch that put a row "
+                        f"in every (group, 256-row tile) of the GEMM work lists, full layer in "
+                        f"fp64 (routing + {w.K} routed + {w.Ks} shared SwiGLU experts per token), "
                         f"{dt:.1f} s"),
-            dict(tokens=int(done), max_err_over_rms=rel, routing_set_mismatches=int(mism)))
+            dict(tokens=int(done), tiles_covered=bool(done == order.size),
+                 max_err_over_rms=rel, routing_set_mismatches=int(mism)))
 
 
 def main():
@@ -461,6 +611,9 @@ def main():
             "T": w.T, "value": round(w.T / (msp / 1e3), 1), "unit": "tokens/s",
             "ms_per_step": round(msp, 4), "speedup_vs_bf16": round(ms / msp, 3),
             "mfma_dtype": "bf16 (codes widened exactly before the products)",
+            "note": "8-bit prefill is bound by the bf16 MFMA rate: the codes halve the weight "
+                    "bytes but no FP8 MFMA runs (activations stay bf16), so it gains nothing on "
+                    "the prefill batch; the 8-bit path pays off on the HBM-bound decode batch",
             "roofline": roofline("mfma", kp, rp["kernels"], w.name + "_fp8"),
             "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rp["kernels"].items()},
         }
@@ -513,6 +666,19 @@ def main():
             torch.cuda.empty_cache()
             print(f"[bench] {wd.name} fp8: {ms8:.3f} ms/step", file=sys.stderr, flush=True)
 
+    if not args.no_backward:
+        # the training side on the same batches: forward_train, then backward
+        bl = {}
+        rb = time_backward(w, D, L["x"], args.steps, args.warmup)
+        bl["prefill"] = backward_line(w, rb, counts)
+        print(f"[bench] {w.name} backward: {rb['bwd_ms']:.3f} ms", file=sys.stderr, flush=True)
+        if args.decode:
+            rbd = time_backward(wd, Dd, xd, args.steps, args.warmup)
+            bl["decode"] = backward_line(wd, rbd, cd)
+            print(f"[bench] {wd.name} backward: {rbd['bwd_ms']:.3f} ms", file=sys.stderr,
+                  flush=True)
+        line["backward"] = bl
+
     if args.configs:
         # the smaller shapes: layer TFLOP/s against the MFMA peak and
         # algorithmic bytes/s against the HBM peak, both reported
@@ -554,6 +720,7 @@ def main():
     if args.cpu_seconds > 0:
         base, spot = cpu_baseline(w, L, res, args.cpu_seconds)
         line["cpu_baseline"] = base
+        spot["routing_all_tokens"] = routing_check(w, L, res)
         line["spot_parity"] = spot
     else:
         line["cpu_baseline"] = None

@@ -106,3 +106,35 @@ def test_layer_roofline_time_of_one_expert():
               + (weights + 1 * (2.0 * w.d + 4.0 * w.I + 2.0 * w.d)) / bw
               + (2 + 1 + 0) * w.d * 2.0 / bw) * 1e3
     assert abs(t - expect) <= 1e-12 * expect
+
+
+def test_backward_work_counts():
+    """The backward's algorithmic FLOPs: per routed or shared row 12 d I
+    (dH 2, dX 4, dW2 2, dW1+dW3 4), plus the router's 4 T E d; at the V3
+    prefill shape that is 26.10 TFLOP, twice the forward layer."""
+    import numpy as np
+
+    from synth import workloads as wl
+    w = wl.WORKLOADS["v3_prefill"]
+    bw = bench.backward_work(w, np.zeros(w.E))
+    rows = w.T * (w.K + w.Ks)
+    assert bw["flops"]["bwd_dx"] == 4.0 * w.d * w.I * rows
+    assert bw["total_flops"] == 12.0 * w.d * w.I * rows + 4.0 * w.T * w.E * w.d
+    assert abs(bw["total_flops"] / 1e12 - 26.096) < 0.001
+    assert bw["dw13_bytes"] == 2 * 2 * (w.E + w.Ks) * w.I * w.d + 2 * 2 * rows * w.I + 2 * rows * w.d
+
+
+def test_tile_cover_hits_every_tile():
+    import numpy as np
+
+    from synth import workloads as wl
+    w = wl.WORKLOADS["16b_zipf"]
+    g = np.random.default_rng(0)
+    idx = np.stack([g.choice(w.E, w.K, replace=False, p=None) for _ in range(w.T)]).astype(np.int32)
+    tok = bench.tile_cover(idx, w)
+    for e in range(w.E):
+        rows = np.nonzero((idx == e).any(axis=1))[0]       # the group's rows, in token order
+        for m0 in range(0, rows.size, 256):
+            assert np.intersect1d(rows[m0:m0 + 256], tok).size > 0, (e, m0)
+    for m0 in range(0, w.T, 256):                          # shared groups: every token in order
+        assert np.any((tok >= m0) & (tok < m0 + 256))
