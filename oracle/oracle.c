@@ -148,6 +148,14 @@ double oracle_e4m3(uint8_t q) {
     return sign ? -v : v;
 }
 
+/* The 256 code values, filled from oracle_e4m3() before a forward with
+ * 8-bit weights reads them (a lookup in place of a decode per use). */
+static double e4m3_value[256];
+
+static void e4m3_fill(void) {
+    for (int q = 0; q < 256; ++q) e4m3_value[q] = oracle_e4m3((uint8_t)q);
+}
+
 /* One weight matrix of `cols` columns: bf16 bit patterns, or 8-bit codes
  * with one float scale per row. */
 typedef struct {
@@ -158,7 +166,7 @@ typedef struct {
 
 static double wat(const wmat* w, int row, int cols, int col) {
     const size_t i = (size_t)row * cols + col;
-    return w->bf16 ? widen(w->bf16[i]) : oracle_e4m3(w->q[i]) * (double)w->scale[row];
+    return w->bf16 ? widen(w->bf16[i]) : e4m3_value[w->q[i]] * (double)w->scale[row];
 }
 
 /* Step 4: y = W2 (silu(W1 x) * W3 x) for one token. h: [inter] scratch. */
@@ -336,6 +344,7 @@ int32_t oracle_forward_fp8(const oracle_shape* s, const uint16_t* x_rows, int32_
                            double* out, double* shared_part, double* routed_part,
                            int32_t* idx_out, double* gate_out, double* margin_out,
                            int32_t nthreads) {
+    e4m3_fill();
     wmat *r1 = fp8_mats(q1, s1, s->E), *r3 = fp8_mats(q3, s3, s->E), *r2 = fp8_mats(q2, s2, s->E);
     wmat *h1 = bf16_mats(ws1, s->Ks), *h3 = bf16_mats(ws3, s->Ks), *h2 = bf16_mats(ws2, s->Ks);
     const int32_t used = forward_impl(s, x_rows, n_tokens, C, bias, r1, r3, r2, h1, h3, h2,

@@ -35,8 +35,8 @@ MUTATIONS = [
     ("e4m3 exponent bias 8", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     ("e4m3 subnormals one binade low", "v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
     ("e4m3 mantissa reversed", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)(7 - m) / 8.0, e - 7);"),
-    ("8-bit row scale from the neighbouring row", "oracle_e4m3(w->q[i]) * (double)w->scale[row]",
-     "oracle_e4m3(w->q[i]) * (double)w->scale[row ^ 1]"),
+    ("8-bit row scale from the neighbouring row", "e4m3_value[w->q[i]] * (double)w->scale[row]",
+     "e4m3_value[w->q[i]] * (double)w->scale[row ^ 1]"),
 ]
 
 
