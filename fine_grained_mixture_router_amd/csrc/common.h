@@ -54,9 +54,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kChunk = 64;
 constexpr uint32_t kGateRenorm = 2u;    // shape flag bits of the gating variants
 constexpr uint32_t kGateSigmoid = 4u;
-// Router GEMM tile: 64 tokens x 64 experts, d consumed 64 at a time.
-constexpr int kRouterBT = 64;
-constexpr int kRouterWideT = 256;   // token tile of the router for large batches
+// Router: experts padded to a multiple of 64 (a wavefront's share).
 constexpr int kRouterBE = 64;
 
 // One entry of a grouped-GEMM work list.
@@ -79,14 +77,16 @@ struct Plan {
     uint32_t flags;
     int Epad;        // E rounded up to the router tile
     int nchunk;      // ceil(T / kChunk)
-    int split;       // router split over d
-    int router_wide; // router tiles of kRouterWideT tokens (large batches)
+    int router_bt;   // router tile: 64 tokens (large batches) or 16
+    int split;       // router: d range split this many ways (1: no partials)
+    int kps;         //   slices of 64 per split
     int rows;        // T*K routed rows + T*Ks shared rows
     GemmCfg g1, g2;
     int max_tiles1, max_tiles2;
 
     // workspace carve-up (byte offsets while planning, then pointers)
-    float* logits;       // [split, T, Epad]
+    float* logits;       // [split, T, Epad] partial affinities (split > 1)
+    int32_t* tickets;    // [router tiles] (split > 1)
     int32_t* idx;        // [T, K]
     float* gate;         // [T, K]
     uint64_t* masks;     // [nchunk, Epad]
@@ -117,8 +117,10 @@ struct RoutedQ8 {
 
 // Launchers (each enqueues on `st`; return the launch status).  q8 != null:
 // the routed weights are 8-bit (the plan then uses the thin tiles).
-hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st);
-hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st);
+int router_tiles(const Plan& p);
+hipError_t launch_router_tickets(const Plan& p, hipStream_t st);
+hipError_t launch_router(const Plan& p, const bf16_t* x, const bf16_t* C, const float* bias,
+                         hipStream_t st);
 hipError_t launch_perm_scan(const Plan& p, hipStream_t st);
 hipError_t launch_perm_scatter(const Plan& p, hipStream_t st);
 hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,

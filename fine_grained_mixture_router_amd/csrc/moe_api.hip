@@ -10,14 +10,14 @@
 
 using namespace moe;
 
+// Router tiles: batches of this many tokens or more take 64-token tiles
+// with the whole d range in one workgroup (no partials leave it); smaller
+// ones take 16-token tiles with d split to about one workgroup per CU.
+#ifndef MOE_ROUTER_BIG_T
+#define MOE_ROUTER_BIG_T 4096
+#endif
 #ifndef MOE_ROUTER_WGS
-#define MOE_ROUTER_WGS 512
-#endif
-#ifndef MOE_ROUTER_WIDE_T
-#define MOE_ROUTER_WIDE_T 8192
-#endif
-#ifndef MOE_ROUTER_MINK
-#define MOE_ROUTER_MINK 4
+#define MOE_ROUTER_WGS 256
 #endif
 
 static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID,
@@ -72,24 +72,19 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false
     p->Epad = (s->E + kRouterBE - 1) / kRouterBE * kRouterBE;
     p->nchunk = (s->T + kChunk - 1) / kChunk;
     const int nk = s->d / 64;
-    // Router: a tile covers 64 tokens and every expert; the d range is split
-    // so that the launch has about kRouterWGs workgroups (two per CU, which
-    // its 80 KB of LDS allows), each split keeping at least kRouterMinK
-    // slices of 64.
-    // Batches of MOE_ROUTER_WIDE_T tokens or more take 256-token tiles (one
-    // workgroup per CU, so about half as many workgroups are aimed at).  On
-    // the V3-shape prefill batch (16 384 tokens) that takes the affinities
-    // from 120 to 86 us; at 4 096 tokens the larger split's extra partials
-    // cost the selection what the tiles save.
-    p->router_wide = s->T >= MOE_ROUTER_WIDE_T ? 1 : 0;
-    const int bt = p->router_wide ? kRouterWideT : kRouterBT;
-    const int target = p->router_wide ? MOE_ROUTER_WGS / 2 : MOE_ROUTER_WGS;
-    const int rtiles = (s->T + bt - 1) / bt;
-    const int kmax = nk / MOE_ROUTER_MINK > 0 ? nk / MOE_ROUTER_MINK : 1;
-    int split = (target + rtiles - 1) / rtiles;
-    split = split < 1 ? 1 : (split > kmax ? kmax : split);
-    const int kps = (nk + split - 1) / split;
-    p->split = (nk + kps - 1) / kps;
+    if (s->T >= MOE_ROUTER_BIG_T) {
+        p->router_bt = 64;
+        p->split = 1;
+        p->kps = nk;
+    } else {
+        p->router_bt = 16;
+        const int tiles = p->nchunk * 4;
+        const int kmax = nk / 2 > 1 ? nk / 2 : 1;          // at least two slices per split
+        int split = (MOE_ROUTER_WGS + tiles - 1) / tiles;
+        split = split < 1 ? 1 : (split > kmax ? kmax : split);
+        p->kps = (nk + split - 1) / split;
+        p->split = (nk + p->kps - 1) / p->kps;
+    }
     const long long TK = (long long)s->T * s->K;
     p->rows = (int)(TK + (long long)s->T * s->Ks);
 
@@ -117,7 +112,9 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false
         off = align_up(off + bytes);
         return o;
     };
-    p->logits = (float*)take(s->K > 0 ? (size_t)p->split * s->T * p->Epad * 4 : 0);
+    const bool part = s->K > 0 && p->split > 1;
+    p->logits = (float*)take(part ? (size_t)p->split * s->T * p->Epad * 4 : 0);
+    p->tickets = (int32_t*)take(part ? (size_t)router_tiles(*p) * 4 : 0);
     if (route_only) {
         p->masks = (uint64_t*)take((size_t)p->nchunk * p->Epad * 8);
         return off;
@@ -198,11 +195,13 @@ void place_bwd(BwdPlan* q, void* ws) {
 void place_route(Plan* p, void* ws) {
     char* b = static_cast<char*>(ws);
     p->logits = rebase(p->logits, b);
+    p->tickets = rebase(p->tickets, b);
     p->masks = rebase(p->masks, b);
 }
 
 void place(Plan* p, void* ws) {
     char* b = static_cast<char*>(ws);
+    p->tickets = rebase(p->tickets, b);
     if (p->Z) {                                     // a training plan
         p->scores = rebase(p->scores, b);
         p->score_part = rebase(p->score_part, b);
@@ -254,7 +253,7 @@ moe_status_t device_ok() {
 // thread-safe (documented in moe.h).
 constexpr int kSlots = 16;
 constexpr int kBwdSlot0 = 7;                 // backward kernels: slots 7..15
-const char* const kSlotNames[kSlots] = {"router_logits", "router_select", "perm_scan",
+const char* const kSlotNames[kSlots] = {"router",        "router_tickets", "perm_scan",
                                         "perm_scatter",  "gemm_gate_up",  "gemm_down",
                                         "combine",       "bwd_lists",     "bwd_dh",
                                         "bwd_router",    "bwd_dx_router", "bwd_dx",
@@ -410,8 +409,10 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
         rec_mark(slot, 1, s);
     };
     if (p.K > 0) {
-        step(0, [&] { return launch_router_logits(p, xb, static_cast<const bf16_t*>(centroids), s); });
-        step(1, [&] { return launch_router_select(p, expert_bias, s); });
+        step(1, [&] { return launch_router_tickets(p, s); });
+        step(0, [&] {
+            return launch_router(p, xb, static_cast<const bf16_t*>(centroids), expert_bias, s);
+        });
         const size_t rb = (size_t)p.T * p.K * 4;
         if (train && topk_idx && e == hipSuccess)
             e = hipMemcpyAsync(topk_idx, p.idx, rb, hipMemcpyDeviceToDevice, s);
@@ -425,8 +426,10 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     step(5, [&] { return launch_gemm_down(p, w2b, ws2b, q, s); });
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
-        for (int k = 0; k < kBwdSlot0; ++k)
-            if ((k >= 2 || p.K > 0) && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
+        for (int k = 0; k < kBwdSlot0; ++k) {
+            const bool ran = k >= 2 || (p.K > 0 && (k == 0 || p.split > 1));
+            if (ran && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
+        }
         ++g_rec.calls;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -610,9 +613,9 @@ __attribute__((visibility("default"))) moe_status_t moe_route(
     p.idx = topk_idx;
     p.gate = topk_gate;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_router_logits(p, static_cast<const bf16_t*>(x),
-                             static_cast<const bf16_t*>(centroids), s) != hipSuccess ||
-        launch_router_select(p, expert_bias, s) != hipSuccess)
+    if (launch_router_tickets(p, s) != hipSuccess ||
+        launch_router(p, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(centroids),
+                      expert_bias, s) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -1,4 +1,5 @@
-// Router: token-to-centroid affinities, softmax and top-K selection.
+// Router: token-to-centroid affinities, the gate, top-K selection and the
+// per-chunk expert masks, in one kernel.
 //
 // Definition: the generic top-K gate of "DeepSeekMoE 深度解读报告" section 3.1
 // (softmax over the inner products of the token with every expert centroid,
@@ -9,451 +10,499 @@
 // steers the selection (the youleyou page's auxiliary-loss-free remark; the
 // V3 line in the report's closing notes).
 //
-// Two kernels:
-//   router_logits  bf16 MFMA GEMM x[T,d] . C[E,d]^T -> fp32 partial logits.
-//                  Tiles of 64 tokens x all experts; for small T the d range
-//                  is split so that the launch still covers the chip, and the
-//                  partials are summed in a fixed order by the next kernel.
-//   router_select  one wavefront per token (16 per workgroup): sum partials,
-//                  then the gate — softmax of logit + bias (default), or
-//                  sigmoid of the affinity with the bias added to the
-//                  selection key only — and K rounds of a wavefront arg-max
-//                  over the E<=256 keys (4 per lane; ties go to the lower
-//                  expert id); optionally the K gates are renormalised to sum
-//                  to one.  Per expert it also records the 64-bit
-//                  mask of the tokens of each 64-token chunk that chose that
-//                  expert; the permutation step turns those masks into a
-//                  stable, atomics-free grouping of tokens by expert.
+// One workgroup owns a tile of BT tokens and every expert (E <= 256):
+//   1. affinities x . C^T on bf16 MFMA (fp32 accumulation), BK = 64 slices
+//      of d streamed by direct-to-LDS loads through three LDS stages;
+//   2. fp32 gate per token, one wavefront per token: softmax of logit + bias
+//      (default) or sigmoid of the affinity with the bias in the selection
+//      key only; K rounds of a wavefront arg-max (DPP within rows of 16
+//      lanes, scalar across rows) over the E keys, ceil(E / 64) per lane,
+//      ties to the lower expert id; optional renormalisation;
+//   3. the tile's bits of every expert's 64-token chunk mask, from which the
+//      permutation ranks tokens per expert without atomics.
+// Large batches (the plan's split S = 1) keep the whole reduction over d in
+// the workgroup: the affinities go from the accumulators to LDS and never to
+// memory.  Small batches (decode) cannot fill the chip that way, so the d
+// range is split S ways: each workgroup writes its fp32 partial affinities,
+// takes a ticket (one atomic per workgroup), and the workgroup that takes
+// the last ticket of its tile sums the S partials in split order — a fixed
+// order whatever order the workgroups finish in — and does steps 2-3.  The
+// tickets are cleared by a one-workgroup kernel launched just before.
+//
+// Tiles: 64 tokens (32x32x16 MFMA blocks, one chunk per tile) for large
+// batches; 16 tokens (16x16x32 blocks, a quarter chunk per tile) for small
+// ones, where a 64-token tile's S partials would be too many bytes for the
+// one workgroup that sums them.  Workgroups of 16 waves (see the kernel).
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kRThreads = 1024;  // 16 waves
+constexpr int kRWaves = kRThreads / 64;
+constexpr int kStages = 3;
 
-// Rows of 64 bf16 (one BK = 64 slice), one 16-byte chunk per (row, c),
-// chunk c stored at position c ^ ((row >> 1) & 7).  LDS serves 16 lanes x
-// 16 bytes per cycle; an MFMA fragment read puts 16 lanes on 16 consecutive
-// rows at one logical chunk, and with 128-byte rows those 16 reads then
-// land in 16 distinct 16-byte bank groups.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Rows of 64 bf16 (one BK slice), 16-byte chunk c of row r at position
+// c ^ ((r >> 1) & 7): a fragment read puts 16 lanes on 16 consecutive rows
+// at one logical chunk, and those land in 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
     return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
-// Affinities x . C^T for a tile of kRouterBT = 64 tokens and all Epad (<= 256)
-// experts, over the d range of split blockIdx.y, written as fp32 partials
-// [split, T, Epad].  A tile reads its token rows once and the centroids from
-// L2 (at most 3.7 MB, shared by every tile).  Four waves; wave w computes
-// experts 64 w .. 64 w + 63 for all 64 tokens (2 x 2 MFMA 32x32x16 blocks).
-// Slices of BK = 64 are staged through registers into a double buffer.
-constexpr int kRouterThreads = 256;
-constexpr int kRouterMaxE = 256;
 
-__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ C, float* __restrict__ logits,
-    int T, int d, int E, int Epad, int ksteps_per_split) {
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][kRouterBT * 64];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][kRouterMaxE * 64];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int t0 = blockIdx.x * kRouterBT;
-    const int split = blockIdx.y;
-    const int nk = d >> 6;
-    const int k_begin = split * ksteps_per_split;
-    const int k_end = min(nk, k_begin + ksteps_per_split);
-    const int nbl = Epad / 32;                     // B chunks per thread per slice (<= 8)
-    const bool active = 64 * wave < Epad;          // this wave's experts exist
-
-    // loads: thread moves chunk ch of token rows srow + 32 i and of centroid
-    // rows srow + 32 i; rows past T or E are clamped to the last one (their
-    // results are never read)
-    const int ch = tid & 7;
-    const int srow = tid >> 3;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * (uint32_t)d * 2u);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (uint32_t)E * (uint32_t)d * 2u);
-    uint32_t aoff[2], boff[8];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        aoff[i] = ((uint32_t)min(t0 + srow + 32 * i, T - 1) * (uint32_t)d + ch * 8) * 2u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        boff[i] = ((uint32_t)min(srow + 32 * i, E - 1) * (uint32_t)d + ch * 8) * 2u;
-    const int sx = swz(srow, ch);                  // rows srow + 32 i share the swizzle
-
-    u32x4 ra[2], rb[8];
-    auto gload = [&](int kt) {
-        const uint32_t kb = (uint32_t)kt * 128u;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) ra[i] = buf_load16(rx, aoff[i], kb);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < nbl) rb[i] = buf_load16(rc, boff[i], kb);
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&sA[buf][sx + 32 * i * 64]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < nbl) *reinterpret_cast<u32x4*>(&sB[buf][sx + 32 * i * 64]) = rb[i];
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    const int lrow = lane & 31;
-    if (k_begin < k_end) {
-        gload(k_begin);
-        sstore(0);
-        __syncthreads();
-        for (int kt = k_begin; kt < k_end; ++kt) {
-            const int buf = (kt - k_begin) & 1;
-            const bool more = kt + 1 < k_end;
-            if (more) gload(kt + 1);
-            if (active) {
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const int c = 2 * st + (lane >> 5);
-                    bf16x8 a[2], b[2];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(32 * i + lrow, c)]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        b[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(64 * wave + 32 * j + lrow, c)]);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-                }
-            }
-            if (more) sstore(buf ^ 1);
-            __syncthreads();
-        }
-    }
-
-    // 32x32 accumulator: lane holds column (lane & 31) = expert, rows (tokens)
-    // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
-    if (!active) return;
-    float* outp = logits + (size_t)split * T * Epad;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = 64 * wave + 32 * j + lrow;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = t0 + 32 * i + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-                if (row < T) outp[(size_t)row * Epad + col] = acc[i][j][r];
-            }
-        }
+// Order-preserving unsigned image of a float (-0 taken as +0, so equal
+// values have equal keys); real keys are all above 0, which marks "none".
+__device__ __forceinline__ uint32_t key_of(float v) {
+    const uint32_t b = __float_as_uint(v + 0.f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float float_of_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// The same affinities for large batches: tiles of kRouterWideT = 256 tokens
-// by all Epad (<= 256) experts, so the centroids are re-read once per 256
-// tokens rather than per 64 (with 64-token tiles the loads, not the MFMAs,
-// bound the kernel: 40 KB of operands per 512 MFMA cycles of a workgroup).
-// Eight waves, wave (wm, wn) computing tokens 128 wm .. + 127 by experts
-// 64 wn .. + 63 (4 x 2 MFMA 32x32x16 blocks); BK = 64 slices come in by
-// direct-to-LDS buffer loads (one wave instruction fills 8 rows x 128 B)
-// into two LDS stages, swizzled as in swz(); the refill of a stage is
-// issued right after the barrier that ends its reads, a whole stage ahead
-// of its use.
-constexpr int kRouterWideThreads = 512;
+template <int NE>
+__device__ __forceinline__ uint32_t lane_max(const uint32_t (&u)[NE]) {
+    uint32_t m = u[0];
+#pragma unroll
+    for (int j = 1; j < NE; ++j) m = max(m, u[j]);
+    return m;
+}
 
-__global__ __launch_bounds__(kRouterWideThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void router_logits_wide_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ C,
-                               float* __restrict__ logits, int T, int d, int E, int Epad,
-                               int ksteps_per_split) {
-    constexpr int OPER = kRouterWideT * 64;        // elements of one operand slice
-    constexpr int QI = 4;                          // load instructions per wave per operand
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * 2 * OPER];
-    typedef __attribute__((address_space(3))) void* lds_ptr_t;
-    typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+// Maximum over the wavefront, returned to every lane: DPP within each row
+// of 16 lanes (pair swap, quad swap, half-row mirror, row mirror leave the
+// row's maximum in all 16 lanes), then the four rows through scalar reads.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the wavefront, the same in every lane: the four DPP steps above
+// within each row of 16, then the row sums added in row order.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((a + b) + c) + d;
+}
+
+struct RouterArgs {
+    const bf16_t* x;
+    const bf16_t* C;
+    const float* bias;
+    int T, d, E, Epad, K, S, kps;   // S splits of the d range, kps slices each
+    uint32_t flags;
+    float* part;                    // [S, T, Epad] partial affinities (S > 1)
+    int32_t* tickets;               // [tiles] (S > 1), zero at launch
+    int32_t* idx;                   // [T, K]
+    float* gate;                    // [T, K]
+    uint64_t* masks;                // [nchunk, Epad]
+    float* scores;                  // [T, Epad] or null (training forward)
+    float* score_part;              // [nchunk * 4, Epad] or null
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+template <int BT, int NE>
+struct RouterLds {
+    static constexpr int ROWS = BT + 64 * NE;            // x rows, then centroid rows
+    static constexpr int STAGE = ROWS * 64 * 2;          // bytes of one stage
+    static constexpr int GEMM = kStages * STAGE;
+    static constexpr int LOGITS = BT * 64 * NE * 4;      // fp32 [BT][Epad]
+    static constexpr int BYTES = GEMM > LOGITS ? GEMM : LOGITS;
+};
+
+// BT tokens x (64 NE) experts per workgroup, 16 waves.  The products: with
+// BT = 64, waves 0-7, wave w taking tokens 32 (w / 4) .. + 31 by experts
+// 64 (w % 4) .. + 63 (two 32x32 blocks; 32 accumulators, so four waves fit
+// on a SIMD); with BT = 16, waves 0-3, wave w taking the 16 tokens by
+// experts 64 w .. + 63 (four 16x16 blocks).  Every wave issues loads and
+// every wave selects (4 tokens each for BT = 64, one for BT = 16): the top-K
+// is a chain of dependent cross-lane steps, and 16 waves overlap 16 tokens'
+// chains.
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) float lds_float_t;
+
+template <int BT, int NE>
+__device__ __forceinline__ void router_tile(const RouterArgs& a, lds_char_t* smem, unsigned* smask,
+                                            int& s_last) {
+    typedef RouterLds<BT, NE> L;
+    constexpr int EP = 64 * NE;
+    constexpr int NI = L::ROWS / 8;             // 1 KB load instructions per slice
+    constexpr int NQ = (NI + kRWaves - 1) / kRWaves;   // ... per wave, at most
+    constexpr int LMIN = NI / kRWaves;                 // ... per wave, at least
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
-    const int t0 = blockIdx.x * kRouterWideT;
-    const int nk = d >> 6;
-    const int k_begin = blockIdx.y * ksteps_per_split;
-    const int k_end = min(nk, k_begin + ksteps_per_split);
-    const bool active = 64 * wn < Epad;            // this wave's experts exist
+    const int tile = blockIdx.x;
+    const int z = blockIdx.y;
+    const int t0 = tile * BT;
+    const int nk = a.d >> 6;
+    const int kb = z * a.kps;
+    const int nloc = min(nk, kb + a.kps) - kb;
 
-    // Load instruction j = wave + 8 q fills rows 8 j .. 8 j + 7 of a slice;
-    // lane l fills chunk position l % 8 of row 8 j + l / 8.  Rows past T or
-    // E are clamped to the last one (their results are never read).
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)T * (uint32_t)d * 2u);
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C, (uint32_t)E * (uint32_t)d * 2u);
-    uint32_t aoff[QI], boff[QI];
+    for (int i = tid; i < 2 * EP; i += kRThreads) smask[i] = 0u;
+    // the bias, one value per lane and block of 64 experts, fetched now so
+    // that its latency hides behind the products
+    float bj[NE];
 #pragma unroll
-    for (int q = 0; q < QI; ++q) {
-        const int row = 8 * (wave + 8 * q) + (lane >> 3);
-        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((row >> 1) & 7)) * 16);
-        aoff[q] = (uint32_t)min(t0 + row, T - 1) * (uint32_t)d * 2u + cb;
-        boff[q] = (uint32_t)min(row, E - 1) * (uint32_t)d * 2u + cb;
+    for (int j = 0; j < NE; ++j) {
+        const int e = lane + 64 * j;
+        bj[j] = (a.bias && e < a.E) ? a.bias[e] : 0.f;
     }
-    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)(wave * 1024));
-    auto issue = [&](int kt, int buf) {
-        const uint32_t sa = lds_base + (uint32_t)(buf * 2 * OPER * 2);
-        const int kb = kt * 128;
+
+    // ---- 1. affinities ----
+    // load instruction i = wave + 16 q fills LDS rows 8 i .. 8 i + 7 of a
+    // stage (x rows first, then centroid rows); lane l fills position l % 8
+    // of row 8 i + l / 8.  Rows past T or E are clamped (never read back).
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)a.d * 2u);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C, (uint32_t)a.E * (uint32_t)a.d * 2u);
+    uint32_t off[NQ];
+    bool isx[NQ];
 #pragma unroll
-        for (int q = 0; q < QI; ++q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(uintptr_t)(sa + q * 8 * 1024), 16,
-                                                     (int)aoff[q], kb, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(uintptr_t)(sa + OPER * 2 + q * 8 * 1024),
-                                                     16, (int)boff[q], kb, 0, 0);
+    for (int q = 0; q < NQ; ++q) {
+        const int i = wave + kRWaves * q;
+        const int row = 8 * i + (lane >> 3);
+        const uint32_t cb = (uint32_t)(((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        isx[q] = i < BT / 8;          // whole instruction: wave-uniform, one resource per load
+        const int src = isx[q] ? min(t0 + row, a.T - 1) : min(row - BT, a.E - 1);
+        off[q] = (uint32_t)src * (uint32_t)a.d * 2u + cb;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+    auto issue = [&](int kt, int stage) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int i = wave + kRWaves * q;
+            if (i < NI)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    isx[q] ? rx : rc, (lds_ptr_t)(uintptr_t)(lds0 + stage * L::STAGE + i * 1024), 16,
+                    (int)off[q], kt * 128, 0, 0);
         }
     };
 
-    f32x16 acc[4][2];
+    // this wave's share of the products: token block tb, expert group eg
+    const int tb = BT == 64 ? wave >> 2 : 0;
+    const int eg = BT == 64 ? wave & 3 : wave;
+    const bool active = (BT == 64 ? wave < 8 : wave < 4) && eg < NE;
+    const int lrow32 = lane & 31, lrow16 = lane & 15;
+    // BT 64: acc32[j] 32x32 blocks (tokens 32 tb.., experts 64 eg + 32 j..)
+    // BT 16: acc16[j] 16x16 blocks (tokens 0..15, experts 64 eg + 16 j..)
+    f32x16 acc32[2];
+    f32x4_t acc16[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j) acc32[j] = f32x16{};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    const int lrow = lane & 31;
-    const lds_bf16_t* lsm = (const lds_bf16_t*)smem;
-    if (k_begin < k_end) {
-        issue(k_begin, 0);
-        if (k_begin + 1 < k_end) {
-            issue(k_begin + 1, 1);
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    for (int j = 0; j < 4; ++j) acc16[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int stage) {
+        const lds_bf16_t* sx = (const lds_bf16_t*)smem + stage * (L::STAGE / 2);
+        const lds_bf16_t* sc = sx + BT * 64;
+        if (BT == 64) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int c = 2 * st + (lane >> 5);
+                bf16x8 fb[2];
+                const bf16x8 fa = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                    sx + swz(32 * tb + lrow32, c));
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                        sc + swz(64 * eg + 32 * j + lrow32, c));
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc32[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc32[j], 0, 0, 0);
+            }
         } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        asm volatile("s_barrier" ::: "memory");
-        for (int kt = k_begin; kt < k_end; ++kt) {
-            const int buf = (kt - k_begin) & 1;
-            const lds_bf16_t* sa = lsm + buf * 2 * OPER;
-            const lds_bf16_t* sb = sa + OPER;
-            if (active) {
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const int c = 2 * st + (lane >> 5);
-                    bf16x8 a[4], b[2];
+            for (int kk = 0; kk < 2; ++kk) {
+                const int c = 4 * kk + (lane >> 4);
+                const bf16x8 fa = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                    sx + swz(lrow16, c));
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sa + swz(128 * wm + 32 * i + lrow, c));
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        b[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(sb + swz(64 * wn + 32 * j + lrow, c));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 fb = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                        sc + swz(64 * eg + 16 * j + lrow16, c));
+                    acc16[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc16[j], 0, 0, 0);
                 }
             }
-            // the next slice landed; every wave is done reading this one
-            if (kt + 1 < k_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+    };
+
+    if (nloc > 0) {
+        issue(kb, 0);
+        if (nloc > 1) issue(kb + 1, 1);
+        for (int kt = 0; kt < nloc; ++kt) {
+            if (kt + 1 < nloc) wait_vm<LMIN>();   // this wave's loads of slice kt
+            else wait_vm<0>();
+            // every wave's loads of slice kt landed; every wave is done with slice kt - 1
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (kt + 2 < k_end) issue(kt + 2, buf);
+            if (kt + 2 < nloc) issue(kb + kt + 2, (kt + 2) % kStages);
+            if (active) compute(kt % kStages);
         }
     }
-
-    // 32x32 accumulator: lane holds column (lane & 31) = expert, rows (tokens)
-    // 8*(r/4) + 4*(lane/32) + (r%4) for r = 0..15.
-    if (!active) return;
-    float* outp = logits + (size_t)blockIdx.y * T * Epad;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = 64 * wn + 32 * j + lrow;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = t0 + 128 * wm + 32 * i + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
-                if (row < T && col < Epad) outp[(size_t)row * Epad + col] = acc[i][j][r];
-            }
-        }
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-// One wavefront per token: a workgroup of 16 waves takes 16 consecutive
-// tokens, a quarter of a 64-token chunk, and writes that quarter's 16 bits
-// of every expert's chunk mask (a 16-bit store into the 64-bit word, so the
-// four workgroups of a chunk write disjoint bytes and no mask needs clearing
-// first; quarters past T write zeros).
-constexpr int kSelectWaves = 16;
-constexpr int kSelectThreads = 64 * kSelectWaves;
-constexpr int kSubChunks = kChunk / kSelectWaves;
-static_assert(kSubChunks == 4, "16-bit quarters of the 64-bit chunk mask");
-constexpr int kPartBatch = 8;       // partial logits loaded ahead of their adds
-
-__device__ __forceinline__ float pick4(const float (&a)[4], int j) {
-    return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
-}
-
-// scores / score_part (training forward only, else null): every expert's
-// score of every token, and the sums of those scores over each workgroup's
-// 16 tokens, taken in token order (the mean-score statistic of the
-// expert-level balance loss is their sum over workgroups, in order).
-__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ idx,
-    float* __restrict__ gate, uint64_t* __restrict__ masks, int T, int E, int Epad, int K,
-    int split, uint32_t flags, float* __restrict__ scores, float* __restrict__ score_part) {
-    __shared__ unsigned smask[256];
-    __shared__ float sscore[kSelectWaves][256];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int c = blockIdx.x / kSubChunks;
-    const int q = blockIdx.x % kSubChunks;
-    const bool sig = (flags & kGateSigmoid) != 0;
-    const bool ren = (flags & kGateRenorm) != 0;
-    for (int e = tid; e < Epad; e += kSelectThreads) smask[e] = 0u;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int tl = q * kSelectWaves + wave;          // token within the chunk
-    const int t = c * kChunk + tl;
-    if (t < T) {
-        const float NEG = -INFINITY;
-        // affinities of experts lane + 64 j: the split-K partials summed in
-        // order z = 0, 1, ..., loaded kPartBatch at a time
-        float v[4];
-        int taken = 0;                               // bit j: expert lane + 64j is out
+    // the tile's affinities: lane layout of the accumulators
+    lds_float_t* lg = (lds_float_t*)smem;              // [BT][EP], reusing the stages
+    auto for_each_acc = [&](auto&& f) {               // f(token in tile, expert, value)
+        if (!active) return;
+        if (BT == 64) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[j] = 0.f;
-            if (lane + 64 * j >= E) taken |= 1 << j;
-        }
-        const float* lp = logits + (size_t)t * Epad + lane;
-        const size_t zstride = (size_t)T * Epad;
-        for (int z0 = 0; z0 < split; z0 += kPartBatch) {
-            float pv[kPartBatch][4];
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int b = 0; b < kPartBatch; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pv[b][j] = (z0 + b < split && !((taken >> j) & 1))
-                                   ? lp[(size_t)(z0 + b) * zstride + 64 * j] : 0.f;
-#pragma unroll
-            for (int b = 0; b < kPartBatch; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (z0 + b < split) v[j] += pv[b][j];
-        }
-        // selection keys: softmax gate -> logit + bias (the softmax is
-        // monotone in it); sigmoid gate -> sigmoid(affinity) + bias, the bias
-        // steering the choice only
-        float sc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + 64 * j;
-            const float b = (bias && e < E) ? bias[e] : 0.f;
-            sc[j] = sig ? 1.0f / (1.0f + expf(-v[j])) : 0.f;
-            v[j] = e < E ? (sig ? sc[j] + b : v[j] + b) : NEG;
-        }
-        float mx = 0.f, sum = 1.f;
-        if (!sig) {
-            mx = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-            float ps = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ps += (lane + 64 * j < E) ? expf(v[j] - mx) : 0.f;
-            sum = wave_sum(ps);
-        }
-        if (scores) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = lane + 64 * j;
-                if (e < Epad) {
-                    const float sv = e < E ? (sig ? sc[j] : expf(v[j] - mx) / sum) : 0.f;
-                    scores[(size_t)t * Epad + e] = sv;
-                    sscore[wave][e] = sv;
-                }
-            }
-        }
-
-        float gk[4] = {0.f, 0.f, 0.f, 0.f};          // renormalised: gate k kept by lane k % 64
-        float zsum = 0.f;
-        for (int k = 0; k < K; ++k) {
-            // local best: strictly greater wins, so the lower j (lower e) keeps ties
-            float bv = NEG;
-            int be = 0x7fffffff;
+                for (int r = 0; r < 16; ++r)
+                    f(32 * tb + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3), 64 * eg + 32 * j + lrow32,
+                      acc32[j][r]);
+        } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (!((taken >> j) & 1) && (be == 0x7fffffff || v[j] > bv)) {
-                    bv = v[j];
-                    be = lane + 64 * j;
-                }
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oe = __shfl_xor(be, o, 64);
-                if (ov > bv || (ov == bv && oe < be)) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            if ((be & 63) == lane) taken |= 1 << (be >> 6);
-            const float g = sig ? __shfl(pick4(sc, be >> 6), be & 63, 64) : expf(bv - mx) / sum;
-            if (ren) {
-                zsum += g;                           // every lane, in selection order
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if ((k & 63) == lane && (k >> 6) == j) gk[j] = g;
+                for (int r = 0; r < 4; ++r) f(4 * (lane >> 4) + r, 64 * eg + 16 * j + lrow16, acc16[j][r]);
+        }
+    };
+    if (a.S == 1) {
+        for_each_acc([&](int tl, int e, float v) { lg[tl * EP + e] = v; });
+    } else {
+        // Partial of split z; the last workgroup of the tile to finish sums
+        // them.  The partials pass between workgroups (and XCDs, each with
+        // its own L2) as device-scope relaxed atomic stores and loads, which
+        // the hardware writes through to, and reads from, the device-coherent
+        // level: a fence would write back and invalidate the whole L2 of the
+        // XCD instead, evicting the centroids every other workgroup there is
+        // streaming.  Order: every store of this workgroup has completed
+        // (vmcnt 0, then the barrier) before its ticket is taken, and the
+        // last workgroup reads only after its ticket returned.
+        float* pz = a.part + (size_t)z * a.T * a.Epad;
+        for_each_acc([&](int tl, int e, float v) {
+            if (t0 + tl < a.T)
+                __hip_atomic_store(&pz[(size_t)(t0 + tl) * a.Epad + e], v, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        });
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(&a.tickets[tile], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
+        __syncthreads();
+        if (!s_last) return;
+        // 16-byte loads with the device-coherent policy (sc1, what a
+        // device-scope relaxed atomic load uses), eight splits in flight at a
+        // time, summed in split order whoever finished last
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(a.part, (uint32_t)((size_t)a.S * a.T * a.Epad * 4));
+        const uint32_t zstride = (uint32_t)a.T * (uint32_t)a.Epad * 4u;
+        for (int i = tid; i < BT * EP / 4; i += kRThreads) {
+            const int tl = i / (EP / 4), e = (i % (EP / 4)) * 4;
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            if (t0 + tl < a.T) {
+                const uint32_t base = ((uint32_t)(t0 + tl) * (uint32_t)a.Epad + (uint32_t)e) * 4u;
+                for (int z0 = 0; z0 < a.S; z0 += 8) {
+                    f32x4_t pz[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        pz[q] = __builtin_bit_cast(
+                            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rp, (int)(base + (uint32_t)min(z0 + q, a.S - 1) * zstride), 0, 16));
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (z0 + q < a.S) s += pz[q];
+                }
             }
-            if (lane == 0) {
-                idx[(size_t)t * K + k] = be;
-                if (!ren) gate[(size_t)t * K + k] = g;
-                atomicOr(&smask[be], 1u << wave);
+            *reinterpret_cast<__attribute__((address_space(3))) f32x4_t*>(&lg[tl * EP + e]) = s;
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. gate and top-K, one wavefront per token ----
+    const bool sig = (a.flags & kGateSigmoid) != 0;
+    const bool ren = (a.flags & kGateRenorm) != 0;
+    const float NEG = -INFINITY;
+    for (int tl = wave; tl < BT; tl += kRWaves) {
+        const int t = t0 + tl;
+        if (t >= a.T) {
+            if (a.scores)                                 // rows past T add nothing to the sums
+                for (int e = lane; e < EP; e += 64) lg[tl * EP + e] = 0.f;
+            continue;
+        }
+        float v[NE], sc[NE];
+        uint32_t u[NE];                 // selection keys, 0 once taken or past E
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int e = lane + 64 * j;
+            const float aff = lg[tl * EP + e];
+            sc[j] = sig ? __builtin_amdgcn_rcpf(1.0f + __expf(-aff)) : 0.f;
+            v[j] = e < a.E ? (sig ? sc[j] + bj[j] : aff + bj[j]) : NEG;
+            u[j] = e < a.E ? max(key_of(v[j]), 1u) : 0u;   // (a NaN could map to 0)
+        }
+        // the largest key: the softmax shift (and the first pick)
+        uint32_t m = wave_max_u32(lane_max(u));
+        float g[NE];
+        if (!sig) {                                      // softmax over the routed experts
+            const float vmax = float_of_key(m);
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                g[j] = (lane + 64 * j < a.E) ? __expf(v[j] - vmax) : 0.f;
+                ps += g[j];
+            }
+            const float rs = 1.0f / wave_sum(ps);
+#pragma unroll
+            for (int j = 0; j < NE; ++j) g[j] *= rs;
+        } else {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) g[j] = sc[j];
+        }
+        if (a.scores) {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int e = lane + 64 * j;
+                const float sv = e < a.E ? g[j] : 0.f;
+                a.scores[(size_t)t * a.Epad + e] = sv;
+                lg[tl * EP + e] = sv;                     // this wave's row only
             }
         }
-        if (ren) {
+        // K rounds of a wavefront arg-max: round r takes the largest key
+        // left (ties: the lowest expert id, the lowest block j first, then
+        // the lowest lane) and gives it rank r.  The K gates are summed in
+        // rank order for the renormalisation.
+        int rank[NE];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k = 64 * j + lane;
-                if (k < K) gate[(size_t)t * K + k] = gk[j] / zsum;
+        for (int j = 0; j < NE; ++j) rank[j] = -1;
+        float zs = 0.f;
+        for (int r = 0; r < a.K; ++r) {
+            if (r > 0) m = wave_max_u32(lane_max(u));
+            int js = -1, l = 0;
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const uint64_t b = __ballot(u[j] == m);
+                if (js < 0 && b) { js = j; l = (int)__builtin_ctzll(b); }
+            }
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                if (j == js) {
+                    zs += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g[j]), l));
+                    if (lane == l) { rank[j] = r; u[j] = 0u; }
+                }
+            }
+        }
+        const float rz = ren ? 1.0f / zs : 1.0f;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            if (rank[j] >= 0) {
+                const int e = lane + 64 * j;
+                a.idx[(size_t)t * a.K + rank[j]] = e;
+                a.gate[(size_t)t * a.K + rank[j]] = g[j] * rz;
+                if (BT == 64) atomicOr(&smask[2 * e + (tl >> 5)], 1u << (tl & 31));
+                else atomicOr(&smask[e], 1u << tl);
             }
         }
     }
-    if (scores && t >= T)
-        for (int e = lane; e < Epad; e += 64) sscore[wave][e] = 0.f;
     __syncthreads();
-    if (score_part)
-        for (int e = tid; e < Epad; e += kSelectThreads) {
-            float acc = 0.f;
-            for (int w = 0; w < kSelectWaves; ++w) acc += sscore[w][e];
-            score_part[(size_t)blockIdx.x * Epad + e] = acc;
+
+    // ---- 3. chunk masks (and, training, the score sums per 16 tokens) ----
+    if (BT == 64) {
+        for (int e = tid; e < EP; e += kRThreads)
+            a.masks[(size_t)tile * a.Epad + e] = ((uint64_t)smask[2 * e + 1] << 32) | smask[2 * e];
+    } else {
+        uint16_t* m16 = reinterpret_cast<uint16_t*>(a.masks);
+        for (int e = tid; e < EP; e += kRThreads)
+            m16[((size_t)(tile >> 2) * a.Epad + e) * 4 + (tile & 3)] = (uint16_t)smask[e];
+    }
+    if (a.score_part) {
+        for (int i = tid; i < (BT / 16) * EP; i += kRThreads) {
+            const int q = i / EP, e = i % EP;
+            float s = 0.f;
+            for (int r = 0; r < 16; ++r) s += lg[(16 * q + r) * EP + e];
+            a.score_part[((size_t)tile * (BT / 16) + q) * a.Epad + e] = s;
         }
-    uint16_t* m16 = reinterpret_cast<uint16_t*>(masks);
-    for (int e = tid; e < Epad; e += kSelectThreads)
-        m16[((size_t)c * Epad + e) * kSubChunks + q] = (uint16_t)smask[e];
+    }
+}
+
+// (the body lives in a device function: kept in the kernel itself, with its
+// lambdas and shared arrays, the host pass emitted no launch stub for it)
+template <int BT, int NE>
+__global__ __launch_bounds__(kRThreads) void router_fused_kernel(RouterArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[RouterLds<BT, NE>::BYTES];
+    __shared__ unsigned smask[2 * 64 * NE];
+    __shared__ int s_last;
+    router_tile<BT, NE>(a, (lds_char_t*)smem, smask, s_last);
+}
+
+__global__ void clear_tickets_kernel(int32_t* t, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) t[i] = 0;
+}
+
+template <int BT>
+hipError_t launch_bt(const RouterArgs& a, int tiles, hipStream_t st) {
+    const dim3 grid(tiles, a.S);
+    switch (a.Epad / 64) {
+        case 1: router_fused_kernel<BT, 1><<<grid, kRThreads, 0, st>>>(a); break;
+        case 2: router_fused_kernel<BT, 2><<<grid, kRThreads, 0, st>>>(a); break;
+        case 3: router_fused_kernel<BT, 3><<<grid, kRThreads, 0, st>>>(a); break;
+        default: router_fused_kernel<BT, 4><<<grid, kRThreads, 0, st>>>(a); break;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router_logits(const Plan& p, const bf16_t* x, const bf16_t* C, hipStream_t st) {
-    const int nk = p.d / 64;
-    const int kps = (nk + p.split - 1) / p.split;
-    if (p.router_wide) {
-        dim3 grid((p.T + kRouterWideT - 1) / kRouterWideT, p.split);
-        router_logits_wide_kernel<<<grid, kRouterWideThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E,
-                                                                       p.Epad, kps);
-    } else {
-        dim3 grid((p.T + kRouterBT - 1) / kRouterBT, p.split);
-        router_logits_kernel<<<grid, kRouterThreads, 0, st>>>(x, C, p.logits, p.T, p.d, p.E, p.Epad, kps);
-    }
+int router_tiles(const Plan& p) {
+    // 16-token tiles cover every quarter chunk (the permutation reads all four
+    // quarters of every chunk mask)
+    return p.router_bt == 64 ? p.nchunk : p.nchunk * 4;
+}
+
+hipError_t launch_router_tickets(const Plan& p, hipStream_t st) {
+    if (p.split <= 1) return hipSuccess;
+    clear_tickets_kernel<<<1, 256, 0, st>>>(p.tickets, router_tiles(p));
     return hipGetLastError();
 }
 
-hipError_t launch_router_select(const Plan& p, const float* bias, hipStream_t st) {
-    router_select_kernel<<<p.nchunk * kSubChunks, kSelectThreads, 0, st>>>(
-        p.logits, bias, p.idx, p.gate, p.masks, p.T, p.E, p.Epad, p.K, p.split, p.flags,
-        p.scores, p.score_part);
-    return hipGetLastError();
+hipError_t launch_router(const Plan& p, const bf16_t* x, const bf16_t* C, const float* bias,
+                         hipStream_t st) {
+    RouterArgs a;
+    a.x = x;
+    a.C = C;
+    a.bias = bias;
+    a.T = p.T;
+    a.d = p.d;
+    a.E = p.E;
+    a.Epad = p.Epad;
+    a.K = p.K;
+    a.S = p.split;
+    a.kps = p.kps;
+    a.flags = p.flags;
+    a.part = p.logits;
+    a.tickets = p.tickets;
+    a.idx = p.idx;
+    a.gate = p.gate;
+    a.masks = p.masks;
+    a.scores = p.scores;
+    a.score_part = p.score_part;
+    return p.router_bt == 64 ? launch_bt<64>(a, router_tiles(p), st)
+                             : launch_bt<16>(a, router_tiles(p), st);
 }
 
 }  // namespace moe

@@ -292,7 +292,7 @@ const char* moe_status_string(moe_status_t status);
  * (ms[k], host array) and the number of timed launches (launches[k], host
  * array; either pointer may be NULL), then releases the events and stops
  * recording.  MOE_ERR_NULL if no recording is active, MOE_ERR_HIP if an event
- * could not be read.  Slots: 0 router_logits, 1 router_select, 2 perm_scan,
+ * could not be read.  Slots: 0 router, 1 router_tickets (small batches only), 2 perm_scan,
  * 3 perm_scatter, 4 gemm_gate_up, 5 gemm_down, 6 combine; moe_backward's
  * 7 bwd_lists, 8 bwd_dh, 9 bwd_router, 10 bwd_dx_router, 11 bwd_dx,
  * 12 bwd_dx_combine, 13 bwd_dw2, 14 bwd_dw13, 15 bwd_dc (a backward call
