@@ -10,14 +10,19 @@
 
 using namespace moe;
 
-// Router tiles: batches of this many tokens or more take 64-token tiles
-// with the whole d range in one workgroup (no partials leave it); smaller
-// ones take 16-token tiles with d split to about one workgroup per CU.
+// Router tiles: batches of MOE_ROUTER_BIG_T tokens or more keep the whole d
+// range in one workgroup (no partials leave it), on 16-token tiles while
+// those leave a workgroup per CU or more and re-read the centroids no more
+// than MOE_ROUTER_CBYTES in all, else on 64-token tiles; smaller batches
+// take 16-token tiles with d split to about one workgroup per CU.
 #ifndef MOE_ROUTER_BIG_T
 #define MOE_ROUTER_BIG_T 4096
 #endif
 #ifndef MOE_ROUTER_WGS
 #define MOE_ROUTER_WGS 256
+#endif
+#ifndef MOE_ROUTER_CBYTES
+#define MOE_ROUTER_CBYTES (256LL << 20)
 #endif
 
 static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID,
@@ -73,7 +78,8 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false
     p->nchunk = (s->T + kChunk - 1) / kChunk;
     const int nk = s->d / 64;
     if (s->T >= MOE_ROUTER_BIG_T) {
-        p->router_bt = 64;
+        const long long reread = (long long)s->E * s->d * 2 * (p->nchunk * 4);
+        p->router_bt = (p->nchunk >= MOE_ROUTER_WGS || reread > MOE_ROUTER_CBYTES) ? 64 : 16;
         p->split = 1;
         p->kps = nk;
     } else {

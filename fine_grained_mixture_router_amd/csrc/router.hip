@@ -40,7 +40,6 @@ namespace {
 
 constexpr int kRThreads = 1024;  // 16 waves
 constexpr int kRWaves = kRThreads / 64;
-constexpr int kStages = 3;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
@@ -128,19 +127,29 @@ template <int BT, int NE>
 struct RouterLds {
     static constexpr int ROWS = BT + 64 * NE;            // x rows, then centroid rows
     static constexpr int STAGE = ROWS * 64 * 2;          // bytes of one stage
-    static constexpr int GEMM = kStages * STAGE;
+    // stages: as many as about 150 KB hold, 3 to 8 (slices in flight: one
+    // fewer); each workgroup's products are bound by load latency, so the
+    // depth sets their rate
+    static constexpr int SG0 = (150 * 1024) / STAGE;
+    static constexpr int SG = SG0 < 3 ? 3 : (SG0 > 8 ? 8 : SG0);
+    static constexpr int GEMM = SG * STAGE;
     static constexpr int LOGITS = BT * 64 * NE * 4;      // fp32 [BT][Epad]
     static constexpr int BYTES = GEMM > LOGITS ? GEMM : LOGITS;
 };
 
-// BT tokens x (64 NE) experts per workgroup, 16 waves.  The products: with
-// BT = 64, waves 0-7, wave w taking tokens 32 (w / 4) .. + 31 by experts
-// 64 (w % 4) .. + 63 (two 32x32 blocks; 32 accumulators, so four waves fit
-// on a SIMD); with BT = 16, waves 0-3, wave w taking the 16 tokens by
-// experts 64 w .. + 63 (four 16x16 blocks).  Every wave issues loads and
-// every wave selects (4 tokens each for BT = 64, one for BT = 16): the top-K
-// is a chain of dependent cross-lane steps, and 16 waves overlap 16 tokens'
-// chains.
+// BT tokens x (64 NE) experts per workgroup, 16 waves.  The products run on
+// waves 0-3, one per SIMD.  With BT = 64 and NE >= 3 wave w takes all 64
+// tokens by experts 64 w .. + 63 (four 32x32 blocks); with NE <= 2 wave w
+// takes tokens 32 (w / NE) .. + 31 by experts 64 (w % NE) .. + 63 (two
+// blocks).  With BT = 16 wave w takes the 16 tokens by experts 64 w .. + 63
+// (four 16x16 blocks).  Every operand passes through LDS (written once by
+// the loads, read by each wave that needs it), and LDS bandwidth, not the
+// MFMA rate, bounds this phase: large per-wave tiles keep the reads down
+// (64 KB of reads and 40 KB of writes per 64-deep slice at BT = 64,
+// E = 256, about 800 cycles against 512 of MFMA work per SIMD).  Every wave
+// issues loads and every wave selects (4 tokens each for BT = 64, one for
+// BT = 16): the top-K is a chain of dependent cross-lane steps, and 16
+// waves overlap 16 tokens' chains.
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) float lds_float_t;
 
@@ -152,6 +161,8 @@ __device__ __forceinline__ void router_tile(const RouterArgs& a, lds_char_t* sme
     constexpr int NI = L::ROWS / 8;             // 1 KB load instructions per slice
     constexpr int NQ = (NI + kRWaves - 1) / kRWaves;   // ... per wave, at most
     constexpr int LMIN = NI / kRWaves;                 // ... per wave, at least
+    constexpr int SG = L::SG;
+    constexpr int P = SG - 1;                          // slices in flight
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -201,17 +212,21 @@ __device__ __forceinline__ void router_tile(const RouterArgs& a, lds_char_t* sme
         }
     };
 
-    // this wave's share of the products: token block tb, expert group eg
-    const int tb = BT == 64 ? wave >> 2 : 0;
-    const int eg = BT == 64 ? wave & 3 : wave;
-    const bool active = (BT == 64 ? wave < 8 : wave < 4) && eg < NE;
+    // this wave's share of the products: token blocks tb0 .. tb0 + TBW - 1
+    // of 32, expert group eg of 64; waves 0-3, one per SIMD
+    constexpr int TBW = (BT == 64 && NE >= 3) ? 2 : 1;
+    const int eg = (BT == 64 && TBW == 1) ? wave % NE : wave;
+    const int tb0 = (BT == 64 && TBW == 1) ? wave / NE : 0;
+    const bool active = BT == 64 ? (TBW == 2 ? wave < NE : wave < 2 * NE) : wave < NE;
     const int lrow32 = lane & 31, lrow16 = lane & 15;
-    // BT 64: acc32[j] 32x32 blocks (tokens 32 tb.., experts 64 eg + 32 j..)
+    // BT 64: acc32[b][j] 32x32 blocks (tokens 32 (tb0 + b).., experts 64 eg + 32 j..)
     // BT 16: acc16[j] 16x16 blocks (tokens 0..15, experts 64 eg + 16 j..)
-    f32x16 acc32[2];
+    f32x16 acc32[TBW][2];
     f32x4_t acc16[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc32[j] = f32x16{};
+    for (int b = 0; b < TBW; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc32[b][j] = f32x16{};
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc16[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -222,16 +237,20 @@ __device__ __forceinline__ void router_tile(const RouterArgs& a, lds_char_t* sme
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int c = 2 * st + (lane >> 5);
-                bf16x8 fb[2];
-                const bf16x8 fa = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                    sx + swz(32 * tb + lrow32, c));
+                bf16x8 fa[TBW], fb[2];
+#pragma unroll
+                for (int b = 0; b < TBW; ++b)
+                    fa[b] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                        sx + swz(32 * (tb0 + b) + lrow32, c));
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     fb[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
                         sc + swz(64 * eg + 32 * j + lrow32, c));
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc32[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc32[j], 0, 0, 0);
+                for (int b = 0; b < TBW; ++b)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc32[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b], fb[j], acc32[b][j], 0, 0, 0);
             }
         } else {
 #pragma unroll
@@ -249,16 +268,29 @@ __device__ __forceinline__ void router_tile(const RouterArgs& a, lds_char_t* sme
         }
     };
 
+    // this wave's loads of slice kt have landed once no more than those of
+    // the `ahead` later slices in flight remain outstanding (loads count
+    // down in issue order)
+    const bool more = wave < NI % kRWaves;             // LMIN + 1 loads per slice
+    auto wait_slice = [&](int ahead) {
+        switch (ahead) {
+            case 0: wait_vm<0>(); break;
+#define MOE_WAIT_AHEAD(A) \
+    case A: if (A < P) { if (more) wait_vm<(A < P ? A : 0) * NQ>(); else wait_vm<(A < P ? A : 0) * LMIN>(); } break;
+            MOE_WAIT_AHEAD(1) MOE_WAIT_AHEAD(2) MOE_WAIT_AHEAD(3)
+            MOE_WAIT_AHEAD(4) MOE_WAIT_AHEAD(5) MOE_WAIT_AHEAD(6)
+#undef MOE_WAIT_AHEAD
+            default: break;
+        }
+    };
     if (nloc > 0) {
-        issue(kb, 0);
-        if (nloc > 1) issue(kb + 1, 1);
+        for (int s2 = 0; s2 < P && s2 < nloc; ++s2) issue(kb + s2, s2);
         for (int kt = 0; kt < nloc; ++kt) {
-            if (kt + 1 < nloc) wait_vm<LMIN>();   // this wave's loads of slice kt
-            else wait_vm<0>();
+            wait_slice(min(P - 1, nloc - 1 - kt));
             // every wave's loads of slice kt landed; every wave is done with slice kt - 1
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (kt + 2 < nloc) issue(kb + kt + 2, (kt + 2) % kStages);
-            if (active) compute(kt % kStages);
+            if (kt + P < nloc) issue(kb + kt + P, (kt + P) % SG);
+            if (active) compute(kt % SG);
         }
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -270,11 +302,13 @@ __device__ __forceinline__ void router_tile(const RouterArgs& a, lds_char_t* sme
         if (!active) return;
         if (BT == 64) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int b = 0; b < TBW; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    f(32 * tb + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3), 64 * eg + 32 * j + lrow32,
-                      acc32[j][r]);
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        f(32 * (tb0 + b) + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3),
+                          64 * eg + 32 * j + lrow32, acc32[b][j][r]);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
