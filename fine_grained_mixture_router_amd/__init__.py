@@ -58,6 +58,17 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp = ctypes.c_void_p
 _lib.moe_workspace_size.restype = ctypes.c_size_t
 _lib.moe_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+class Layout(ctypes.Structure):
+    """moe_layout_t: where the forward leaves its token permutation."""
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "gate", "goff", "tok_of", "slot_of",
+                                               "tiles_gate_up", "tiles_down", "ntiles")] + \
+               [(n, ctypes.c_int32) for n in ("rows", "max_tiles_gate_up", "max_tiles_down",
+                                              "tile_rows_gate_up", "tile_cols_gate_up",
+                                              "tile_rows_down", "tile_cols_down")]
+
+
+_lib.moe_workspace_layout.restype = ctypes.c_int
+_lib.moe_workspace_layout.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layout)]
 _lib.moe_route_workspace_size.restype = ctypes.c_size_t
 _lib.moe_route_workspace_size.argtypes = [ctypes.POINTER(Shape)]
 _lib.moe_status_string.restype = ctypes.c_char_p
@@ -95,7 +106,7 @@ _lib.moe_noalloc_scratch_bytes.argtypes = []
 _lib.moe_profile_stream_read.restype = ctypes.c_int
 _lib.moe_profile_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp]
 
-EXPORTS = ("moe_workspace_size", "moe_route_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
+EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_route_workspace_size", "moe_forward", "moe_forward_fp8", "moe_route", "moe_status_string",
            "moe_profile_begin", "moe_profile_begin_slots", "moe_profile_end", "moe_profile_slot_name",
            "moe_profile_stream_read", "moe_forward_noalloc", "moe_noalloc_scratch_bytes",
            "moe_train_state_size", "moe_backward_workspace_size", "moe_forward_train",
@@ -156,6 +167,14 @@ def workspace_size(shape: Shape) -> int:
     if n == 0:
         raise MoEError(2, status_string(2))
     return int(n)
+
+
+def workspace_layout(shape: Shape) -> dict:
+    """moe_workspace_layout as a dict: byte offsets of the permutation arrays
+    in a forward call's workspace, and the work lists' sizes and tile shapes."""
+    lay = Layout()
+    _check(_lib.moe_workspace_layout(ctypes.byref(shape), ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n, _ in Layout._fields_}
 
 
 def route_workspace_size(shape: Shape) -> int:

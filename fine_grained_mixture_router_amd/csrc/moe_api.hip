@@ -27,6 +27,10 @@ using namespace moe;
 
 static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID,
               "gating flag bits");
+static_assert(sizeof(Tile) == sizeof(moe_tile_t) && offsetof(Tile, group) == offsetof(moe_tile_t, group) &&
+                  offsetof(Tile, m0) == offsetof(moe_tile_t, m0) && offsetof(Tile, n0) == offsetof(moe_tile_t, n0) &&
+                  offsetof(Tile, nrows) == offsetof(moe_tile_t, nrows),
+              "work-list entries as the header describes them");
 
 namespace {
 
@@ -307,6 +311,31 @@ moe_status_t check_common(const moe_shape_t* shape, const void* x, const void* c
 }  // namespace
 
 extern "C" {
+
+__attribute__((visibility("default"))) moe_status_t moe_workspace_layout(const moe_shape_t* shape,
+                                                                          moe_layout_t* layout) {
+    if (!layout || !shape) return MOE_ERR_NULL;
+    if (!shape_ok(shape)) return MOE_ERR_SHAPE;
+    Plan p;
+    make_plan(shape, &p, false);
+    auto at = [](const void* off) { return reinterpret_cast<size_t>(off); };
+    layout->idx = at(p.idx);
+    layout->gate = at(p.gate);
+    layout->goff = at(p.goff);
+    layout->tok_of = at(p.tok_of);
+    layout->slot_of = at(p.slot_of);
+    layout->tiles_gate_up = at(p.tiles1);
+    layout->tiles_down = at(p.tiles2);
+    layout->ntiles = at(p.ntiles);
+    layout->rows = p.rows;
+    layout->max_tiles_gate_up = p.max_tiles1;
+    layout->max_tiles_down = p.max_tiles2;
+    layout->tile_rows_gate_up = p.g1.bm;
+    layout->tile_cols_gate_up = p.g1.bn / 2;
+    layout->tile_rows_down = p.g2.bm;
+    layout->tile_cols_down = p.g2.bn;
+    return MOE_OK;
+}
 
 __attribute__((visibility("default"))) size_t moe_workspace_size(const moe_shape_t* shape) {
     if (!shape_ok(shape)) return 0;

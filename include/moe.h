@@ -96,6 +96,42 @@ typedef enum {
  * arithmetic, no HIP call.  Returns 0 when the shape is invalid. */
 size_t moe_workspace_size(const moe_shape_t* shape);
 
+/* One entry of a grouped-GEMM work list: rows m0 .. m0 + nrows - 1 of group
+ * `group` (0..E-1 routed expert, E..E+Ks-1 shared expert) by output columns
+ * n0 .. n0 + tile_cols - 1 (of I or Is for gate/up, of d for down). */
+typedef struct {
+    int32_t group, m0, n0, nrows;
+} moe_tile_t;
+
+/* Where moe_forward and moe_forward_fp8 leave the token permutation (the
+ * step that gathers each expert's tokens after the top-K: eliteato.com
+ * DeepSeek-V2 explainer, section 3.1) inside their workspace: byte offsets
+ * from its start, valid after the call has completed on its stream.
+ *   idx, gate   [T, K] int32 / float32 routing; used (and so filled) only
+ *               when the call's topk_idx / topk_gate are NULL
+ *   goff        [E + Ks + 1] int32: first permuted row of each group,
+ *               goff[E + Ks] = rows; routed groups hold their tokens in
+ *               increasing token order, shared group s holds every token,
+ *               row goff[E + s] + t being token t
+ *   tok_of      [rows] int32: the token of each permuted row
+ *   slot_of     [T, K] int32: the permuted row of (token t, choice k)
+ *   tiles_gate_up, tiles_down  [max_tiles_*] moe_tile_t work lists, their
+ *               first ntiles[0] / ntiles[1] entries filled, in an order of
+ *               the kernels' choosing
+ *   ntiles      [2] int32
+ * Pure host arithmetic.  MOE_ERR_NULL if layout is NULL, MOE_ERR_SHAPE if
+ * the shape is invalid.  For inspection (tests, debugging); the layout may
+ * change between library versions. */
+typedef struct {
+    size_t idx, gate, goff, tok_of, slot_of, tiles_gate_up, tiles_down, ntiles;
+    int32_t rows;                                   /* T K + T Ks */
+    int32_t max_tiles_gate_up, max_tiles_down;
+    int32_t tile_rows_gate_up, tile_cols_gate_up;   /* gate/up tiles read tile_cols rows of W1 and of W3 */
+    int32_t tile_rows_down, tile_cols_down;
+} moe_layout_t;
+
+moe_status_t moe_workspace_layout(const moe_shape_t* shape, moe_layout_t* layout);
+
 /* Bytes of device workspace moe_route needs for this shape: the routing
  * scratch alone (no permutation, tile lists or H / Y).  Pure host
  * arithmetic.  Returns 0 when the shape is invalid or K == 0. */

@@ -57,6 +57,51 @@ def test_workspace_size():
     assert 2.5e9 < v3 < 3.2e9
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(T=1, E=1, K=1, Ks=0), dict(T=4100, E=200, K=8),
+                                dict(T=16384, d=7168, E=256, I=2048, K=8, Ks=1, Is=2048),
+                                dict(T=256, d=7168, E=256, I=2048, K=8, Ks=1, Is=2048)])
+def test_workspace_layout(kw):
+    """The permutation arrays sit inside the workspace, aligned, apart, in
+    the order the header lists them; the work-list bounds hold the tile
+    count of any routing (every expert's ragged last tile included)."""
+    s = S(**kw)
+    lay = moe.workspace_layout(s)
+    n = moe.workspace_size(s)
+    T, E, K, Ks = s.T, s.E, s.K, s.Ks
+    I, Is, d = s.I, (s.Is if Ks else 64), s.d
+    spans = [("idx", T * K * 4), ("gate", T * K * 4), ("goff", (E + Ks + 1) * 4),
+             ("tok_of", lay["rows"] * 4), ("slot_of", T * K * 4),
+             ("tiles_gate_up", lay["max_tiles_gate_up"] * 16), ("tiles_down", lay["max_tiles_down"] * 16),
+             ("ntiles", 8)]
+    end = 0
+    for name, size in spans:
+        off = lay[name]
+        assert off % 16 == 0 and off >= end and off + size <= n, name
+        end = off + size
+    assert lay["rows"] == T * K + T * Ks
+    bm1, bm2 = lay["tile_rows_gate_up"], lay["tile_rows_down"]
+    assert lay["tile_cols_gate_up"] * 2 == 256 and lay["tile_cols_down"] == 256
+    assert bm1 == bm2 == (32 if T * K < 64 * E else 256)
+    # the worst routings for the bound: as many experts with a ragged tile as
+    # possible, or all rows on one expert
+    import numpy as np
+    rng = np.random.default_rng(T)
+    for counts in (np.full(min(E, T * K), 0) + np.bincount(np.arange(T * K) % min(E, T * K)),
+                   np.r_[T * K, np.zeros(E - 1, int)],
+                   np.bincount(rng.integers(0, E, T * K), minlength=E)):
+        counts = np.asarray(counts)
+        mt = (-(-counts // bm1)).sum() + Ks * -(-T // bm1)
+        assert (-(-counts // bm1) * -(-I // 128)).sum() + Ks * -(-T // bm1) * -(-Is // 128) \
+            <= lay["max_tiles_gate_up"]
+        assert (-(-counts // bm2) * -(-d // 256)).sum() + Ks * -(-T // bm2) * -(-d // 256) \
+            <= lay["max_tiles_down"]
+        assert mt > 0
+    bad = S(**kw)
+    bad.K = E + 1
+    with pytest.raises(RuntimeError):
+        moe.workspace_layout(bad)
+
+
 @pytest.mark.parametrize("kw", [
     dict(T=0), dict(d=100), dict(d=32), dict(E=0), dict(E=257), dict(K=17), dict(K=-1),
     dict(I=100), dict(Ks=-1), dict(Ks=17), dict(Ks=1, Is=96), dict(T=(1 << 24) + 1),
