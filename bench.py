@@ -90,6 +90,9 @@ def parse():
                          "scales the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-kernels", metavar="TRACE_DIR",
+                    help="print the per-kernel time table of a rocprofv3 --kernel-trace --stats "
+                         "run and exit")
     return ap.parse_args()
 
 
@@ -166,6 +169,26 @@ def summarize_counters(fetch_dir, write_dir):
     print("```json")
     print(json.dumps(rec, indent=1))
     print("```")
+
+
+def summarize_kernels(trace_dir):
+    """Per-kernel time table (markdown) from the kernel_stats.csv of a
+    rocprofv3 --kernel-trace --stats run."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    print("| kernel | calls | mean us | min us | max us | % of GPU time |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        name = re.sub(r"^void |\(.*$", "", r["Name"].replace("moe::(anonymous namespace)::", ""))
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+              f"{float(r['Percentage']):.2f} |")
 
 
 def recorded_traffic(workload, slot):
@@ -543,6 +566,9 @@ def cpu_baseline(w, L, res, seconds):
 
 def main():
     args = parse()
+    if args.summarize_kernels:
+        summarize_kernels(args.summarize_kernels)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
