@@ -53,7 +53,8 @@ constexpr int kBT = 256;                  // tile rows = tile columns
 constexpr int kBK = 64;                   // k per slice
 constexpr int kNW = 8;                    // waves: 2 along M x 4 along N
 constexpr int kHalf = kBT * kBK;          // elements of one operand slice (32 KB)
-constexpr int kLdsBytes = 2 * 2 * kHalf * 2;   // two stages of A + B
+constexpr int kSlots = 5;                 // LDS ring of operand halves (32 KB each)
+constexpr int kLdsBytes = kSlots * kHalf * 2;
 constexpr int kLoads = kHalf * 2 / 1024 / kNW; // 1 KB load instructions per wave per operand slice
 static_assert(kLoads == 4, "four loads per wave per operand slice");
 
@@ -97,6 +98,47 @@ __device__ __forceinline__ float silu_f(float a) { return a * __builtin_amdgcn_r
 
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// LDS transpose reads (ds_read_b64_tr_b16, byte addresses), issued together
+// and waited for in the same statement.  Written out because the compiler
+// puts a wait for every direct-to-LDS load in flight (vmcnt(0)) in front of
+// each transpose-read builtin, which would stall the operand ring at every
+// fragment read; an ordinary LDS read gets no such wait.  These run after
+// the MFMAs of the previous k16 step have been issued, under them.
+__device__ __forceinline__ void tr_reads4(u32x2v (&r)[4], const uint32_t (&a)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+}
+__device__ __forceinline__ void tr_reads12(u32x2v (&r)[12], const uint32_t (&a)[12]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %12\n\t"
+        "ds_read_b64_tr_b16 %1, %13\n\t"
+        "ds_read_b64_tr_b16 %2, %14\n\t"
+        "ds_read_b64_tr_b16 %3, %15\n\t"
+        "ds_read_b64_tr_b16 %4, %16\n\t"
+        "ds_read_b64_tr_b16 %5, %17\n\t"
+        "ds_read_b64_tr_b16 %6, %18\n\t"
+        "ds_read_b64_tr_b16 %7, %19\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %21\n\t"
+        "ds_read_b64_tr_b16 %10, %22\n\t"
+        "ds_read_b64_tr_b16 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
+        : "memory");
+}
 
 __device__ __forceinline__ uint32_t kmajor_pos(int k, int chunk) {   // byte offset in a K-major slice
     return (uint32_t)(k * (kBT * 2) + ((chunk ^ (4 * (k & 3))) << 4));
@@ -284,62 +326,75 @@ void bwd_gemm_kernel(BwdParams P) {
     }
 
     // ---- loads ----
+    // LDS is a ring of five 32 KB slots, one operand half each: A of slice
+    // s in slot 2s mod 5, B in slot 2s + 1 mod 5.  Iteration kt loads A of
+    // slice kt + 2 over its first three k16 steps (into the slot B of slice
+    // kt - 1 left) and B of slice kt + 2 after the barrier that ends the
+    // reads of slice kt (into A of slice kt's slot), so every load has at
+    // least one slice of MFMA time to land and half of them nearly two.
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)(wave * 1024));
+    auto slot_of = [](int h) { return h % kSlots; };
     // K-major slices: load q of this wave fills rows 2 (wave + 8 q) + l / 32
     // (two 512-byte rows per instruction); lane l fills physical chunk l % 32.
     auto kmajor_row = [&](int q) { return 2 * (wave + kNW * q) + (lane >> 5); };
     const int kchunk = lane & 31;
-    // global row (element index of its first column) of k-row kr of slice kt
-    // for the TN products; returns -1 for rows past the group (read as 0)
-    auto tn_row = [&](int kr, bool for_a) -> int {
+    // TN products: the token of each gathered k row (dO rows for dW2, x
+    // rows for dW13), two sets by the parity of the slice, looked up three
+    // slices ahead of the slice's first load and first used there (a use
+    // right after the lookup would wait for every load in flight).  The
+    // lookup is made for every lane (row clamped), so each fetch issues the
+    // same loads.
+    // gcur: the slice whose loads go out this iteration; gnext: the one
+    // after, rotated in at the top of each iteration (by then its lookups
+    // have had a whole iteration to land)
+    constexpr bool GATHER = KIND == K_DW2 || KIND == K_DW13;
+    int gcur[kLoads], gnext[kLoads];
+    auto fetch_rows = [&](int (&g)[kLoads], int s) {
+        if (!GATHER) return;
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) {
+            const int kr = min(s * kBK + kmajor_row(q), tc.kdim - 1);
+            g[q] = P.tok_of[tc.row0 + kr];
+        }
+    };
+    // global row (element index of its first column) of the k row of load q
+    // of slice s (TN, its lookups in gcur), -1 past the group (read as 0)
+    auto tn_row = [&](int s, int q, bool for_a) -> int {
+        const int kr = s * kBK + kmajor_row(q);
         if (kr >= tc.kdim) return -1;
         if (KIND == K_DC) return kr;
-        const int r = tc.row0 + kr;              // global row
-        if (KIND == K_DW2) return for_a ? P.tok_of[r] : (tc.shared ? r - TK : r);
-        return for_a ? (tc.shared ? r - TK : r) : P.tok_of[r];   // K_DW13
+        const int own = tc.shared ? tc.row0 + kr - TK : tc.row0 + kr;   // row in its region
+        const int tok = GATHER ? gcur[q] : 0;
+        if (KIND == K_DW2) return for_a ? tok : own;
+        return for_a ? own : tok;                                        // K_DW13
     };
-    // the k rows one wave loads for slice kt (TN): looked up a slice ahead
-    int a_rows[kLoads], b_rows[kLoads];
-    auto fetch_rows = [&](int kt) {
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) {
-            const int kr = kt * kBK + kmajor_row(q);
-            a_rows[q] = tn_row(kr, true);
-            b_rows[q] = tn_row(kr, false);
+    auto issue_a = [&](int s, int q) {
+        const uint32_t dst = lds0 + (uint32_t)(slot_of(2 * s) * kHalf * 2) + (uint32_t)(kNW * q * 1024);
+        if (ACONT) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)dst, 16, (int)a_off[q],
+                                                     s * kBK * 2, 0, 0);
+        } else {
+            const int row = tn_row(s, q, true);
+            const int k = kmajor_row(q);
+            const uint32_t c = (uint32_t)(kchunk ^ (4 * (k & 3)));
+            const uint32_t off = row < 0 ? 0x80000000u
+                                         : ((uint32_t)row * (uint32_t)a_ld + (uint32_t)tc.m0) * 2u + c * 16u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)dst, 16, (int)off, 0, 0, 0);
         }
     };
-    auto issue = [&](int kt, int stage) {
-        const uint32_t sa = lds0 + (uint32_t)(stage * 2 * kHalf * 2);
-        const uint32_t sb = sa + (uint32_t)(kHalf * 2);
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) {
-            const uint32_t dst = (uint32_t)(kNW * q * 1024);
-            if (ACONT) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)(sa + dst), 16,
-                                                         (int)a_off[q], kt * kBK * 2, 0, 0);
-            } else {
-                const int row = a_rows[q];
-                const int k = kmajor_row(q);
-                const uint32_t c = (uint32_t)(kchunk ^ (4 * (k & 3)));
-                const uint32_t off = row < 0 ? 0x80000000u
-                                             : ((uint32_t)row * (uint32_t)a_ld + (uint32_t)tc.m0) * 2u + c * 16u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)(sa + dst), 16,
-                                                         (int)off, 0, 0, 0);
-            }
-            {
-                const int k = kmajor_row(q);
-                const uint32_t c = (uint32_t)(kchunk ^ (4 * (k & 3)));
-                int row;
-                if (ACONT) row = kt * kBK + k;     // weight row (dXR: rows >= E are past the resource)
-                else row = b_rows[q];
-                const bool second = ACONT && row >= b_split;
-                const int wr = second ? row - b_split : row;
-                const uint32_t off = row < 0 ? 0x80000000u
-                                             : ((uint32_t)wr * (uint32_t)b_ld + (uint32_t)tc.n0) * 2u + c * 16u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rb2 : rb1, (lds_ptr_t)(uintptr_t)(sb + dst),
-                                                         16, (int)off, 0, 0, 0);
-            }
-        }
+    auto issue_b = [&](int s, int q) {
+        const uint32_t dst = lds0 + (uint32_t)(slot_of(2 * s + 1) * kHalf * 2) + (uint32_t)(kNW * q * 1024);
+        const int k = kmajor_row(q);
+        const uint32_t c = (uint32_t)(kchunk ^ (4 * (k & 3)));
+        int row;
+        if (ACONT) row = s * kBK + k;              // weight row (dXR: rows >= E are past the resource)
+        else row = tn_row(s, q, false);
+        const bool second = ACONT && row >= b_split;
+        const int wr = second ? row - b_split : row;
+        const uint32_t off = row < 0 ? 0x80000000u
+                                     : ((uint32_t)wr * (uint32_t)b_ld + (uint32_t)tc.n0) * 2u + c * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rb2 : rb1, (lds_ptr_t)(uintptr_t)dst, 16,
+                                                 (int)off, 0, 0, 0);
     };
 
     // ---- fragments ----
@@ -356,19 +411,16 @@ void bwd_gemm_kernel(BwdParams P) {
     const int lrow = lane & 31;
     const int g16 = lane >> 4, i16 = lane & 15;
     // transpose read of a K-major slice: 4 k of column block cb for step st, half h
-    auto tr_read = [&](const lds_bf16_t* base, int cb, int st, int h) -> v4i16 {
+    // byte address of transpose read h (k 4h .. 4h + 3 of the lane's 8) of
+    // the fragment of column block cb, step st: lane 4e + q of each 16-lane
+    // group reads row k0 + e at columns 4q .. 4q + 3
+    auto tr_addr = [&](const lds_bf16_t* base, int cb, int st, int h) -> uint32_t {
         const int k = 16 * st + 8 * (g16 >> 1) + 4 * h + (i16 >> 2);
         const int c = (cb >> 3) + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-        const uint32_t b = kmajor_pos(k, c) + 8u * (uint32_t)(i16 & 1);
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) char*)base + b));
+        return (uint32_t)(uintptr_t)base + kmajor_pos(k, c) + 8u * (uint32_t)(i16 & 1);
     };
-    auto frag_kmajor = [&](const lds_bf16_t* base, int cb, int st) -> bf16x8 {
-        const v4i16 lo = tr_read(base, cb, st, 0);
-        const v4i16 hi = tr_read(base, cb, st, 1);
-        const v4i16 v0 = lo, v1 = hi;
-        typedef short v8i16 __attribute__((ext_vector_type(8)));
-        const v8i16 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    auto frag_of = [](u32x2v lo, u32x2v hi) -> bf16x8 {
+        const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
         return __builtin_bit_cast(bf16x8, v);
     };
     auto frag_kcontig = [&](const lds_bf16_t* base, int row, int st) -> bf16x8 {
@@ -376,46 +428,119 @@ void bwd_gemm_kernel(BwdParams P) {
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
             base + row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3));
     };
-    auto compute = [&](int stage) {
-        const lds_bf16_t* sa = (const lds_bf16_t*)smem + stage * 2 * kHalf;
-        const lds_bf16_t* sb = sa + kHalf;
+    // fragments of step st of slice s into register set `set`; the MFMAs of a set
+    bf16x8 fa[2][4], fb[2][2];
+    auto read_frags = [&](auto set_c, int s, int st) {
+        constexpr int SET = decltype(set_c)::value;
+        const lds_bf16_t* sa = (const lds_bf16_t*)smem + slot_of(2 * s) * kHalf;
+        const lds_bf16_t* sb = (const lds_bf16_t*)smem + slot_of(2 * s + 1) * kHalf;
+        if (ACONT) {
 #pragma unroll
-        for (int st = 0; st < kBK / 16; ++st) {
-            bf16x8 fa[4], fb[2];
+            for (int i = 0; i < 4; ++i) fa[SET][i] = frag_kcontig(sa, wm * 128 + 32 * i + lrow, st);
+            uint32_t ad[4];
+            u32x2v r[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = frag_kmajor(sb, wn * 64 + 32 * j, st);
+            for (int j = 0; j < 2; ++j) {
+                ad[2 * j] = tr_addr(sb, wn * 64 + 32 * j, st, 0);
+                ad[2 * j + 1] = tr_addr(sb, wn * 64 + 32 * j, st, 1);
+            }
+            tr_reads4(r, ad);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (ACONT) fa[i] = frag_kcontig(sa, wm * 128 + 32 * i + lrow, st);
-                else fa[i] = frag_kmajor(sa, wm * 128 + 32 * i, st);
+            for (int j = 0; j < 2; ++j) fb[SET][j] = frag_of(r[2 * j], r[2 * j + 1]);
+        } else {
+            uint32_t ad[12];
+            u32x2v r[12];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                ad[2 * j] = tr_addr(sb, wn * 64 + 32 * j, st, 0);
+                ad[2 * j + 1] = tr_addr(sb, wn * 64 + 32 * j, st, 1);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                ad[4 + 2 * i] = tr_addr(sa, wm * 128 + 32 * i, st, 0);
+                ad[5 + 2 * i] = tr_addr(sa, wm * 128 + 32 * i, st, 1);
+            }
+            tr_reads12(r, ad);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 2; ++j) fb[SET][j] = frag_of(r[2 * j], r[2 * j + 1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[SET][i] = frag_of(r[4 + 2 * i], r[5 + 2 * i]);
         }
     };
+    auto mfmas = [&](auto set_c) {
+        constexpr int SET = decltype(set_c)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[SET][j], fa[SET][i], acc[i][j], 0, 0, 0);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
 
-    // ---- main loop: two stages, one barrier per slice ----
+    // ---- main loop over the ring ----
+    // Order of this wave's vector-memory instructions (they complete in
+    // order for the waits): the row lookups of slice kt + 3 (TN), then A of
+    // slice kt + 2 over steps 0-2; the wait before the barrier lets only
+    // those A loads stay in flight, so slice kt + 1 has landed.
     const int nk = (tc.kdim + kBK - 1) / kBK;
     if (nk > 0) {
-        if (!ACONT) fetch_rows(0);
-        issue(0, 0);
+        fetch_rows(gcur, 0);
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) issue_a(0, q);
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) issue_b(0, q);
         if (nk > 1) {
-            if (!ACONT) fetch_rows(1);
-            issue(1, 1);
-            wait_vm<2 * kLoads>();
+            fetch_rows(gcur, 1);
+            fetch_rows(gnext, 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < kLoads; ++q) issue_a(1, q);
+#pragma unroll
+            for (int q = 0; q < kLoads; ++q) issue_b(1, q);
+            wait_vm<2 * kLoads>();                     // slice 0 landed
         } else {
             wait_vm<0>();
         }
         asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(S0{}, 0, 0);
         for (int kt = 0; kt < nk; ++kt) {
-            if (!ACONT && kt + 2 < nk) fetch_rows(kt + 2);   // row indices a slice ahead
-            compute(kt & 1);
-            if (kt + 1 < nk) wait_vm<0>();                   // this wave's loads of slice kt + 1
+            const bool more = kt + 2 < nk;
+            if (GATHER) {                              // (unconditional: rows past the group clamp)
+#pragma unroll
+                for (int q = 0; q < kLoads; ++q) gcur[q] = gnext[q];   // slice kt + 2
+                fetch_rows(gnext, kt + 3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int st = 0; st < 3; ++st) {
+                if (st & 1) {                          // the MFMAs first: the reads wait under them
+                    mfmas(S1{});
+                    read_frags(S0{}, kt, st + 1);
+                } else {
+                    mfmas(S0{});
+                    read_frags(S1{}, kt, st + 1);
+                }
+                if (more)
+#pragma unroll
+                    for (int q = st * kLoads / 3; q < (st + 1) * kLoads / 3; ++q) issue_a(kt + 2, q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kt + 1 < nk) {
+                if (more) wait_vm<kLoads>();           // slice kt + 1 landed (A of kt + 2 may not)
+                else wait_vm<0>();
+            }
+            // this wave's reads of slice kt have returned before the barrier
+            // after which A of slice kt's slot is refilled
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (kt + 2 < nk) issue(kt + 2, kt & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(S1{});                               // step 3
+            if (more)
+#pragma unroll
+                for (int q = 0; q < kLoads; ++q) issue_b(kt + 2, q);
+            if (kt + 1 < nk) read_frags(S0{}, kt + 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
