@@ -250,6 +250,34 @@ void bwd_gemm_kernel(BwdParams P) {
     const int rrow0 = tc.shared ? tc.row0 - TK : tc.row0;   // first row within its region
     const int sidx = tc.g - P.E;                             // shared expert index
 
+    // bf16 outputs (dX rows, dW2, dW1 | dW3): the start of output row m of
+    // the tile (column n0); every output width is a multiple of 64, so a
+    // tile row is whole 16-byte pieces
+    constexpr bool STAGED = KIND == K_DX || KIND == K_DW2 || KIND == K_DW13;
+    auto out_row = [&](int m) -> bf16_t* {
+        const int row = tc.m0 + m;
+        if (KIND == K_DX) return P.dXr + (size_t)(tc.row0 + row) * P.d + tc.n0;
+        if (KIND == K_DW2) {
+            bf16_t* o = tc.shared ? P.dws2 + (size_t)sidx * P.d * P.Is : P.dw2 + (size_t)tc.g * P.d * P.I;
+            return o + (size_t)row * inter + tc.n0;
+        }
+        const bool up = row >= inter;                          // K_DW13
+        bf16_t* o = tc.shared ? (up ? P.dws3 : P.dws1) + (size_t)sidx * P.Is * P.d
+                              : (up ? P.dw3 : P.dw1) + (size_t)tc.g * P.I * P.d;
+        return o + (size_t)(up ? row - inter : row) * P.d + tc.n0;
+    };
+    // an expert no row chose: its weight gradients are zero, written as
+    // whole rows (32 lanes per 512-byte tile row), nothing else to do
+    if ((KIND == K_DW2 || KIND == K_DW13) && tc.kdim == 0) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const int cpr = tc.ncols >> 3;
+        for (int idx = tid; idx < tc.mrows * 32; idx += 64 * kNW) {
+            const int m = idx >> 5, c = idx & 31;
+            if (c < cpr) __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(out_row(m) + 8 * c));
+        }
+        return;
+    }
+
     // ---- operand A ----
     // K-contiguous (NN): rows of the tile; the slice's k offset in the scalar offset.
     // K-major (TN): rows are k (the group's rows), columns m0 .. m0 + 255.
@@ -612,6 +640,38 @@ void bwd_gemm_kernel(BwdParams P) {
             const float v = ((red[tid] + red[kBT + tid]) + red[2 * kBT + tid]) + red[3 * kBT + tid];
             const int ntile = (P.I > P.Is ? P.I : P.Is) / kBT + ((P.I > P.Is ? P.I : P.Is) % kBT != 0);
             P.dgp[(size_t)(tc.row0 + tc.m0 + tid) * ntile + tc.n0 / kBT] = v;
+        }
+        return;
+    }
+    if (STAGED) {
+        // the tile (256 x 256 bf16, 128 KB) through the free ring: 16-byte
+        // chunk c of row r at position c ^ (r mod 32), then out as whole rows
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        lds_bf16_t* stile = (lds_bf16_t*)smem;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int m = mbase + 32 * i;
+                    const int n = nbase + 32 * j + 8 * r4;
+                    const int off = m * kBT + (((n >> 3) ^ (m & 31)) << 3) + (n & 4);
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stile + off) =
+                        u32x2{pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]),
+                              pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3])};
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int cpr = tc.ncols >> 3;
+        for (int idx = tid; idx < tc.mrows * 32; idx += 64 * kNW) {
+            const int m = idx >> 5, c = idx & 31;
+            if (c < cpr) {
+                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    stile + m * kBT + ((c ^ (m & 31)) << 3));
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out_row(m) + 8 * c));
+            }
         }
         return;
     }
