@@ -458,13 +458,18 @@ void bwd_gemm_kernel(BwdParams P) {
     };
     // fragments of step st of slice s into register set `set`; the MFMAs of a set
     bf16x8 fa[2][4], fb[2][2];
-    auto read_frags = [&](auto set_c, int s, int st) {
+    // NA: this wave's 32-row blocks of A that hold rows of the tile (NN
+    // products; a compile-time constant per main-loop instance): a ragged
+    // tile skips the reads and MFMAs of its padding blocks
+    auto read_frags = [&](auto na_c, auto set_c, int s, int st) {
+        constexpr int NA = decltype(na_c)::value;
         constexpr int SET = decltype(set_c)::value;
         const lds_bf16_t* sa = (const lds_bf16_t*)smem + slot_of(2 * s) * kHalf;
         const lds_bf16_t* sb = (const lds_bf16_t*)smem + slot_of(2 * s + 1) * kHalf;
         if (ACONT) {
+            if (NA == 0) return;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[SET][i] = frag_kcontig(sa, wm * 128 + 32 * i + lrow, st);
+            for (int i = 0; i < NA; ++i) fa[SET][i] = frag_kcontig(sa, wm * 128 + 32 * i + lrow, st);
             uint32_t ad[4];
             u32x2v r[4];
 #pragma unroll
@@ -495,10 +500,11 @@ void bwd_gemm_kernel(BwdParams P) {
             for (int i = 0; i < 4; ++i) fa[SET][i] = frag_of(r[4 + 2 * i], r[5 + 2 * i]);
         }
     };
-    auto mfmas = [&](auto set_c) {
+    auto mfmas = [&](auto na_c, auto set_c) {
+        constexpr int NA = decltype(na_c)::value;
         constexpr int SET = decltype(set_c)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[SET][j], fa[SET][i], acc[i][j], 0, 0, 0);
@@ -512,7 +518,8 @@ void bwd_gemm_kernel(BwdParams P) {
     // slice kt + 2 over steps 0-2; the wait before the barrier lets only
     // those A loads stay in flight, so slice kt + 1 has landed.
     const int nk = (tc.kdim + kBK - 1) / kBK;
-    if (nk > 0) {
+    auto main_loop = [&](auto na_c) {
+        if (nk <= 0) return;
         fetch_rows(gcur, 0);
 #pragma unroll
         for (int q = 0; q < kLoads; ++q) issue_a(0, q);
@@ -532,7 +539,7 @@ void bwd_gemm_kernel(BwdParams P) {
         }
         asm volatile("s_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(S0{}, 0, 0);
+        read_frags(na_c, S0{}, 0, 0);
         for (int kt = 0; kt < nk; ++kt) {
             const bool more = kt + 2 < nk;
             if (GATHER) {                              // (unconditional: rows past the group clamp)
@@ -544,11 +551,11 @@ void bwd_gemm_kernel(BwdParams P) {
 #pragma unroll
             for (int st = 0; st < 3; ++st) {
                 if (st & 1) {                          // the MFMAs first: the reads wait under them
-                    mfmas(S1{});
-                    read_frags(S0{}, kt, st + 1);
+                    mfmas(na_c, S1{});
+                    read_frags(na_c, S0{}, kt, st + 1);
                 } else {
-                    mfmas(S0{});
-                    read_frags(S1{}, kt, st + 1);
+                    mfmas(na_c, S0{});
+                    read_frags(na_c, S1{}, kt, st + 1);
                 }
                 if (more)
 #pragma unroll
@@ -563,13 +570,24 @@ void bwd_gemm_kernel(BwdParams P) {
             // after which A of slice kt's slot is refilled
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(S1{});                               // step 3
+            mfmas(na_c, S1{});                         // step 3
             if (more)
 #pragma unroll
                 for (int q = 0; q < kLoads; ++q) issue_b(kt + 2, q);
-            if (kt + 1 < nk) read_frags(S0{}, kt + 1, 0);
+            if (kt + 1 < nk) read_frags(na_c, S0{}, kt + 1, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    if constexpr (!ACONT) {
+        main_loop(std::integral_constant<int, 4>{});
+    } else {
+        // the instance for this wave's live blocks (wave-uniform)
+        const int na = (tc.mrows - wm * 128 + 31) >> 5;
+        if (na >= 4) main_loop(std::integral_constant<int, 4>{});
+        else if (na == 3) main_loop(std::integral_constant<int, 3>{});
+        else if (na == 2) main_loop(std::integral_constant<int, 2>{});
+        else if (na == 1) main_loop(std::integral_constant<int, 1>{});
+        else main_loop(std::integral_constant<int, 0>{});
     }
 
     // ---- epilogues ----
