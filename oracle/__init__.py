@@ -25,6 +25,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 NO_RESIDUAL = 1
 RENORM = 2      # gates divided by their sum over the K selected experts
 SIGMOID = 4     # sigmoid affinities; the bias enters the selection only
+ACT8 = 8        # routed gate/up take 8-bit activations (per-token power-of-two scales)
 
 
 def build(force: bool = True) -> str:
@@ -72,6 +73,12 @@ def lib():
                                       vp, vp, vp, i32]
         L.oracle_e4m3.restype = ctypes.c_double
         L.oracle_e4m3.argtypes = [ctypes.c_uint8]
+        L.oracle_act8_exponent.restype = i32
+        L.oracle_act8_exponent.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_nearest.restype = ctypes.c_uint8
+        L.oracle_e4m3_nearest.argtypes = [ctypes.c_double]
+        L.oracle_quantize_act8.restype = None
+        L.oracle_quantize_act8.argtypes = [vp, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -103,6 +110,29 @@ def _ptr_table(stack, n, shape, dtype=np.uint16):
 def e4m3(code: int) -> float:
     """Value of an OCP FP8 E4M3 code (NaN for 0x7F / 0xFF)."""
     return float(lib().oracle_e4m3(int(code)))
+
+
+def act8_exponent(amax: float) -> int:
+    """Scale exponent of a row of 8-bit activations: the smallest integer e
+    with amax <= 448 * 2^e (0 for amax = 0)."""
+    return int(lib().oracle_act8_exponent(float(amax)))
+
+
+def e4m3_nearest(y: float) -> int:
+    """E4M3 code nearest to y (|y| <= 448), ties to the even code."""
+    return int(lib().oracle_e4m3_nearest(float(y)))
+
+
+def quantize_act8(x_rows):
+    """8-bit activations of bf16 rows (uint16 bits [n, d]): (codes uint8
+    [n, d], scale exponents int32 [n]); row t's values are e4m3(codes) *
+    2^exps[t]."""
+    x_rows = np.ascontiguousarray(x_rows, dtype=np.uint16)
+    n, d = x_rows.shape
+    codes = np.zeros((n, d), np.uint8)
+    exps = np.zeros(n, np.int32)
+    lib().oracle_quantize_act8(_ptr(x_rows), n, d, _ptr(codes), _ptr(exps))
+    return codes, exps
 
 
 def _gating(renorm, sigmoid):
@@ -187,7 +217,7 @@ def forward(x_rows, C, bias, w1, w3, w2, ws1, ws3, ws2, K, no_residual=False,
 
 
 def forward_fp8(x_rows, C, bias, q1, s1, q3, s3, q2, s2, ws1, ws3, ws2, K, no_residual=False,
-                forced_idx=None, nthreads=0, renorm=False, sigmoid=False):
+                forced_idx=None, nthreads=0, renorm=False, sigmoid=False, act8=False):
     """Layer forward with 8-bit routed weights, in fp64: q1/q3 uint8 [E, I, d]
     and q2 [E, d, I] E4M3 codes, s1/s3 float32 [E, I] and s2 [E, d] per-row
     scales (weight = e4m3(q) * scale); shared experts ws* in bf16 as for
@@ -219,7 +249,7 @@ def forward_fp8(x_rows, C, bias, q1, s1, q3, s3, q2, s2, ws1, ws3, ws2, K, no_re
         fi = np.ascontiguousarray(forced_idx, dtype=np.int32)
         assert fi.shape == (n, K)
     sh = _Shape(n, d, E, I, K, Ks, Is,
-                (NO_RESIDUAL if no_residual else 0) | _gating(renorm, sigmoid))
+                (NO_RESIDUAL if no_residual else 0) | _gating(renorm, sigmoid) | (ACT8 if act8 else 0))
     out = np.zeros((n, d), np.float64)
     shared = np.zeros((n, d), np.float64)
     routed = np.zeros((n, d), np.float64)

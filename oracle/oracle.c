@@ -50,6 +50,18 @@
  * field 0 holds the subnormals m/8 * 2^-6, and 0x7F / 0xFF are NaN.  Every
  * finite value and every product with a float scale is exact in double.
  *
+ * 8-bit activations (ORACLE_ACT8, with 8-bit routed weights the layer's
+ * products can then run on 8-bit multipliers): each token's row x gets the
+ * power-of-two scale 2^e, e the smallest integer with max_j |x_j| <= 448 *
+ * 2^e (448 being E4M3's largest finite value; e = 0 for an all-zero row),
+ * and the codes q_j = nearest E4M3 value of x_j * 2^-e, ties to the even
+ * code.  The routed experts' W1 x and W3 x take the dequantised row
+ * e4m3(q_j) * 2^e; the shared experts and the down projection keep the
+ * 16-bit activations.  The pages only advise low-bit routed experts with
+ * per-channel or per-group scales (eliteato DeepSeek-V2 explainer, section
+ * 5.5); per-token power-of-two scales are the plainest reading that keeps
+ * every quantised value, and its product with any weight, exact.
+ *
  * Tokens are independent; OpenMP runs them on separate threads without
  * changing any token's order of operations.
  */
@@ -64,6 +76,7 @@
 #define ORACLE_NO_RESIDUAL 1u
 #define ORACLE_RENORM 2u
 #define ORACLE_SIGMOID 4u
+#define ORACLE_ACT8 8u
 
 typedef struct {
     int32_t T, d, E, I, K, Ks, Is;
@@ -146,6 +159,49 @@ double oracle_e4m3(uint8_t q) {
     if (e == 0) v = ldexp((double)m / 8.0, -6);
     else v = ldexp(1.0 + (double)m / 8.0, e - 7);
     return sign ? -v : v;
+}
+
+/* Scale exponent of a row of 8-bit activations: the smallest integer e
+ * with amax <= 448 * 2^e (0 when amax is 0). */
+int32_t oracle_act8_exponent(double amax) {
+    if (!(amax > 0.0)) return 0;
+    int e = (int)ceil(log2(amax / 448.0));
+    while (ldexp(448.0, e) < amax) ++e;
+    while (ldexp(448.0, e - 1) >= amax) --e;
+    return e;
+}
+
+/* The E4M3 code nearest to y (|y| <= 448), ties to the even code: the
+ * non-negative finite codes 0x00..0x7E scanned in increasing value. */
+uint8_t oracle_e4m3_nearest(double y) {
+    const double a = fabs(y);
+    int best = 0;
+    double bd = INFINITY;
+    for (int q = 0; q <= 0x7E; ++q) {
+        const double dd = fabs(oracle_e4m3((uint8_t)q) - a);
+        if (dd < bd || (dd == bd && (q & 1) == 0)) {
+            bd = dd;
+            best = q;
+        }
+    }
+    return (uint8_t)(signbit(y) ? (best | 0x80) : best);
+}
+
+/* 8-bit activations of n rows (bf16 bits [n, d]): codes [n, d] and the
+ * scale exponents [n]. */
+void oracle_quantize_act8(const uint16_t* x_rows, int32_t n, int32_t d, uint8_t* codes,
+                          int32_t* exps) {
+    for (int32_t i = 0; i < n; ++i) {
+        double amax = 0.0;
+        for (int j = 0; j < d; ++j) {
+            const double v = fabs(widen(x_rows[(size_t)i * d + j]));
+            if (v > amax) amax = v;
+        }
+        const int e = oracle_act8_exponent(amax);
+        exps[i] = e;
+        for (int j = 0; j < d; ++j)
+            codes[(size_t)i * d + j] = oracle_e4m3_nearest(ldexp(widen(x_rows[(size_t)i * d + j]), -e));
+    }
 }
 
 /* The 256 code values, filled from oracle_e4m3() before a forward with
@@ -250,6 +306,8 @@ static int32_t forward_impl(const oracle_shape* s, const uint16_t* x_rows, int32
         used = omp_get_num_threads();
 #endif
         double* xt = malloc(sizeof(double) * (size_t)d);
+        double* xr = malloc(sizeof(double) * (size_t)d);   /* the routed experts' input */
+        uint8_t* q = malloc((size_t)d);
         double* y = malloc(sizeof(double) * (size_t)d);
         double* h = malloc(sizeof(double) * (size_t)(hmax > 0 ? hmax : 1));
         double* lg = malloc(sizeof(double) * (size_t)s->E);
@@ -262,6 +320,13 @@ static int32_t forward_impl(const oracle_shape* s, const uint16_t* x_rows, int32
             double* sh = shared_part + (size_t)i * d;
             double* ro = routed_part + (size_t)i * d;
             for (int j = 0; j < d; ++j) xt[j] = widen(x_rows[(size_t)i * d + j]);
+            if (s->flags & ORACLE_ACT8) {
+                int32_t e;
+                oracle_quantize_act8(x_rows + (size_t)i * d, 1, d, q, &e);
+                for (int j = 0; j < d; ++j) xr[j] = ldexp(oracle_e4m3(q[j]), e);
+            } else {
+                for (int j = 0; j < d; ++j) xr[j] = xt[j];
+            }
 
             route_token(s, xt, C, bias, lg, pr, tk, idx, gate, margin_out + i);
             if (forced_idx) {
@@ -283,13 +348,13 @@ static int32_t forward_impl(const oracle_shape* s, const uint16_t* x_rows, int32
             for (int j = 0; j < d; ++j) ro[j] = 0.0;
             for (int k = 0; k < K; ++k) {
                 const int e = idx[k];
-                expert_ffn(d, s->I, &rw1[e], &rw3[e], &rw2[e], xt, h, y);
+                expert_ffn(d, s->I, &rw1[e], &rw3[e], &rw2[e], xr, h, y);
                 for (int j = 0; j < d; ++j) ro[j] += gate[k] * y[j];
             }
             const double res = (s->flags & ORACLE_NO_RESIDUAL) ? 0.0 : 1.0;
             for (int j = 0; j < d; ++j) out[(size_t)i * d + j] = res * xt[j] + sh[j] + ro[j];
         }
-        free(xt); free(y); free(h); free(lg); free(pr); free(tk);
+        free(xt); free(xr); free(q); free(y); free(h); free(lg); free(pr); free(tk);
     }
     return used;
 }

@@ -94,3 +94,113 @@ def test_down_scale_acts_on_its_output_row():
     others = np.delete(np.arange(w.d), o)
     assert np.all(diff[:, others] == 0)
     assert np.any(diff[:, o] != 0)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit activations (ACT8): per-token power-of-two scale, nearest-even E4M3
+# codes, used by the routed experts' gate/up products only.
+# ---------------------------------------------------------------------------
+
+def test_act8_exponent_is_the_smallest_fitting_power_of_two():
+    """A1: e is the smallest integer with amax <= 448 * 2^e: exact at
+    448 * 2^k, one more just above it; a zero row takes e = 0."""
+    for k in range(-20, 12):
+        top = 448.0 * 2.0 ** k
+        assert oracle.act8_exponent(top) == k
+        assert oracle.act8_exponent(np.nextafter(top, np.inf)) == k + 1
+        assert oracle.act8_exponent(np.nextafter(top, 0.0)) == k
+        assert oracle.act8_exponent(224.0 * 2.0 ** k) == k - 1       # the binade below fits one lower
+        assert oracle.act8_exponent(np.nextafter(224.0 * 2.0 ** k, np.inf)) == k
+    assert oracle.act8_exponent(0.0) == 0
+    rng = np.random.default_rng(3)
+    for a in np.exp(rng.uniform(-30, 20, 500)):
+        e = oracle.act8_exponent(a)
+        assert a <= 448.0 * 2.0 ** e and a > 448.0 * 2.0 ** (e - 1)
+
+
+def test_e4m3_nearest_even():
+    """A2: every finite E4M3 value maps to its own code; midpoints between
+    neighbours go to the even code, values beside them to the nearer one;
+    the sign bit follows the sign (also of zero)."""
+    pos = E4M3[:0x7F]
+    for q in range(0x7F):
+        assert oracle.e4m3_nearest(pos[q]) == q
+        assert oracle.e4m3_nearest(-pos[q]) == q | 0x80
+    for q in range(0x7E):
+        mid = 0.5 * (pos[q] + pos[q + 1])
+        even = q if q % 2 == 0 else q + 1
+        assert oracle.e4m3_nearest(mid) == even
+        assert oracle.e4m3_nearest(np.nextafter(mid, 0.0)) == q
+        assert oracle.e4m3_nearest(np.nextafter(mid, np.inf)) == q + 1
+    assert oracle.e4m3_nearest(0.0) == 0x00 and oracle.e4m3_nearest(-0.0) == 0x80
+    assert oracle.e4m3_nearest(448.0) == 0x7E
+
+
+def test_act8_rows_error_bound_and_top_binade():
+    """A3: every dequantised value is within half a code step of the input
+    (the step of E4M3 at that magnitude times 2^e), each row's largest
+    magnitude, scaled, lies in (224, 448] and so codes to a value in [224,
+    448] (e is not larger than needed), and a row of already representable
+    values comes back exactly."""
+    rng = np.random.default_rng(5)
+    x = synth.f32_to_bf16_rne((rng.standard_normal((16, 512)) * np.exp(rng.uniform(-8, 8, (16, 1))))
+                              .astype(np.float32))
+    codes, exps = oracle.quantize_act8(x)
+    xv = synth.bf16_to_f64(x)
+    deq = E4M3[codes] * np.ldexp(1.0, exps)[:, None]
+    y = np.abs(xv) * np.ldexp(1.0, -exps)[:, None]
+    step = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(deq - xv) <= 0.5 * step * np.ldexp(1.0, exps)[:, None])
+    top = np.abs(E4M3[codes]).max(axis=1)
+    assert np.all((top >= 224.0) & (top <= 448.0))
+    assert np.all(np.abs(xv).max(axis=1) * np.ldexp(1.0, -exps) > 224.0)
+    # representable rows: codes times a power of two, the row max at 448 * 2^e
+    q = rng.integers(0, 0x7E, size=(4, 64)).astype(np.uint8)
+    q[:, 0] = 0x7E
+    for t, e in enumerate([-3, 0, 5, -12]):
+        row = E4M3[q[t]] * 2.0 ** e
+        bits = synth.f32_to_bf16_rne(row.astype(np.float32))
+        c2, e2 = oracle.quantize_act8(bits[None, :])
+        assert e2[0] == e and np.array_equal(c2[0], q[t])
+
+
+def _act8_layer(seed, representable):
+    w, L = _layer(seed, T=16, d=128)
+    if representable:                               # rows already on the 8-bit grid
+        rng = np.random.default_rng(seed + 1)
+        q = rng.integers(0, 0x7E, size=(w.T, w.d)).astype(np.uint8)
+        q[:, 3] = 0x7E
+        sign = np.where(rng.random((w.T, w.d)) < 0.5, -1.0, 1.0)
+        e = rng.integers(-10, -5, size=(w.T, 1))
+        L["x"] = synth.f32_to_bf16_rne((sign * E4M3[q] * np.ldexp(1.0, e)).astype(np.float32))
+    return w, L
+
+
+def _fp8(w, L, **kw):
+    return oracle.forward_fp8(L["x"], L["C"], L["bias"], L["q1"], L["s1"], L["q3"], L["s3"],
+                              L["q2"], L["s2"], L["ws1"], L["ws3"], L["ws2"], w.K, **kw)
+
+
+def test_act8_layer_on_representable_rows_equals_the_fp8_layer():
+    """A4: when every row is already an 8-bit row (codes times a power of
+    two, its largest magnitude at 448 * 2^e), quantising changes nothing:
+    the ACT8 layer equals the 8-bit-weight layer to the last bit."""
+    w, L = _act8_layer(31, True)
+    a, b = _fp8(w, L), _fp8(w, L, act8=True)
+    for k in ("out", "routed", "shared", "gate", "margin"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["idx"], b["idx"])
+
+
+def test_act8_touches_only_the_routed_experts():
+    """A5: on ordinary rows, ACT8 leaves the routing and the shared experts'
+    part unchanged to the last bit and moves the routed part by about the
+    size of the activation rounding (and no more)."""
+    w, L = _act8_layer(32, False)
+    a, b = _fp8(w, L), _fp8(w, L, act8=True)
+    for k in ("shared", "gate", "margin"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["idx"], b["idx"])
+    d = b["routed"] - a["routed"]
+    rel = np.sqrt((d ** 2).mean()) / np.sqrt((a["routed"] ** 2).mean())
+    assert 1e-4 < rel < 0.1

@@ -37,6 +37,15 @@ MUTATIONS = [
     ("e4m3 mantissa reversed", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)(7 - m) / 8.0, e - 7);"),
     ("8-bit row scale from the neighbouring row", "e4m3_value[w->q[i]] * (double)w->scale[row]",
      "e4m3_value[w->q[i]] * (double)w->scale[row ^ 1]"),
+    ("8-bit activation ties away from zero", "if (dd < bd || (dd == bd && (q & 1) == 0)) {",
+     "if (dd < bd || dd == bd) {"),
+    ("8-bit activation scale one binade high", "    while (ldexp(448.0, e - 1) >= amax) --e;\n    return e;",
+     "    while (ldexp(448.0, e - 1) >= amax) --e;\n    return e + 1;"),
+    ("8-bit activation scale not applied", "for (int j = 0; j < d; ++j) xr[j] = ldexp(oracle_e4m3(q[j]), e);",
+     "for (int j = 0; j < d; ++j) xr[j] = oracle_e4m3(q[j]) + 0 * e;"),
+    ("8-bit activations also fed to the shared experts",
+     "expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xt, h, y);",
+     "expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xr, h, y);"),
 ]
 
 
