@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 NO_RESIDUAL = 1
 RENORM = 2       # MOE_FLAG_RENORM
 SIGMOID = 4      # MOE_FLAG_SIGMOID
+ACT8 = 8         # MOE_FLAG_ACT8 (moe_forward_fp8 only)
 
 STATUS = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
@@ -61,7 +62,8 @@ _lib.moe_workspace_size.argtypes = [ctypes.POINTER(Shape)]
 class Layout(ctypes.Structure):
     """moe_layout_t: where the forward leaves its token permutation."""
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "gate", "goff", "tok_of", "slot_of",
-                                               "tiles_gate_up", "tiles_down", "ntiles")] + \
+                                               "tiles_gate_up", "tiles_down", "ntiles",
+                                               "act8_codes", "act8_exps")] + \
                [(n, ctypes.c_int32) for n in ("rows", "max_tiles_gate_up", "max_tiles_down",
                                               "tile_rows_gate_up", "tile_cols_gate_up",
                                               "tile_rows_down", "tile_cols_down")]
@@ -128,9 +130,9 @@ def _check(code: int):
 
 
 def make_shape(T, d, E, I, K, Ks=0, Is=0, no_residual=False, renorm=False,
-               sigmoid=False) -> Shape:
+               sigmoid=False, act8=False) -> Shape:
     flags = ((NO_RESIDUAL if no_residual else 0) | (RENORM if renorm else 0)
-             | (SIGMOID if sigmoid else 0))
+             | (SIGMOID if sigmoid else 0) | (ACT8 if act8 else 0))
     return Shape(T, d, E, I, K, Ks, Is if Ks else 0, flags)
 
 
@@ -496,11 +498,14 @@ def backward(x, centroids, w1, w3, w2, ws1=None, ws3=None, ws2=None, *, dout, st
 
 def forward_fp8(x, centroids, w1q, w1s, w3q, w3s, w2q, w2s, ws1=None, ws3=None, ws2=None, *,
                 K: int, bias=None, no_residual: bool = False, renorm: bool = False,
-                sigmoid: bool = False, out=None, topk_idx=None, topk_gate=None, workspace=None,
-                stream=None, return_routing: bool = False):
+                sigmoid: bool = False, act8: bool = False, out=None, topk_idx=None, topk_gate=None,
+                workspace=None, stream=None, return_routing: bool = False):
     """Layer forward with 8-bit routed weights: w1q/w3q uint8 [E,I,d], w2q
     [E,d,I] (OCP E4M3 codes) with float32 per-row scales w1s/w3s [E,I], w2s
-    [E,d]; shared experts ws* in bfloat16; the rest as forward()."""
+    [E,d]; shared experts ws* in bfloat16; the rest as forward().  act8
+    (MOE_FLAG_ACT8): the routed gate/up products take 8-bit activations
+    (per-token power-of-two scale, nearest-even E4M3 codes) on the FP8
+    matrix cores."""
     T, d, dev = _x_of(x)
     _need(x, "x", torch.bfloat16, (T, d), dev)
     if K > 0:
@@ -518,7 +523,7 @@ def forward_fp8(x, centroids, w1q, w1s, w3q, w3s, w2q, w2s, ws1=None, ws3=None, 
         I = w1q.shape[1] if w1q is not None else 64
     _check_routing_args(T, d, E, K, centroids, bias, dev)
     Ks, Is = _check_shared(ws1, ws3, ws2, d, dev)
-    shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid)
+    shape = make_shape(T, d, E, I, K, Ks, Is, no_residual, renorm, sigmoid, act8)
     al = _Alloc(dev, stream)
     out, topk_idx, topk_gate = _outputs(al, T, d, K, out, topk_idx, topk_gate, return_routing)
     workspace = _workspace(al, shape, workspace)

@@ -1,0 +1,102 @@
+// 8-bit activations for the routed gate/up products (MOE_FLAG_ACT8).
+//
+// Each token row x gets the scale 2^e, e the smallest integer with
+// max_j |x_j| <= 448 * 2^e (448: the largest finite E4M3 value; e = 0 for an
+// all-zero row), and the codes are the nearest E4M3 values of x * 2^-e, ties
+// to the even code.  The pages only advise low-bit routed experts with
+// per-channel or per-group scales (eliteato DeepSeek-V2 explainer, section
+// 5.5); a power-of-two per-token scale makes x * 2^-e exact, so the codes
+// depend on nothing but round-to-nearest-even, which the hardware conversion
+// (v_cvt_pk_fp8_f32) performs.
+//
+// e from the row maximum a = f * 2^E2, f in [0.5, 1) (frexp, exact):
+// a <= 448 * 2^e = 0.875 * 2^(9 + e) holds for e = E2 - 9 when f <= 0.875 and
+// needs e = E2 - 8 otherwise; one less never holds (f >= 0.5 > 0.4375).
+//
+// One workgroup per token row: the row maximum over 16-byte pieces (a
+// wavefront reduction, then one across the four waves), then the codes, four
+// per 32-bit store, and for batches off the FP8 tile (decode-size tiles, or d
+// not a multiple of its 128-deep slices) the dequantised row in bf16
+// (exact: an E4M3 value times a power of two fits bf16's 8-bit significand).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(kQThreads) void act8_quant_kernel(const bf16_t* __restrict__ x, int d,
+                                                               uint8_t* __restrict__ xq,
+                                                               int32_t* __restrict__ xe,
+                                                               bf16_t* __restrict__ xd) {
+    const int t = blockIdx.x;
+    const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * d);
+    const int nv = d >> 3;                          // 16-byte pieces (8 values)
+    float amax = 0.f;
+    for (int v = threadIdx.x; v < nv; v += kQThreads) {
+        const u32x4 p = row[v];
+        const uint32_t u[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(u[i])), fabsf(bf16_hi(u[i]))));
+    }
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    __shared__ float s_max[kQThreads / 64];
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, s_max[w]);
+    int e = 0;
+    if (amax > 0.f) {
+        int e2;
+        const float f = frexpf(amax, &e2);
+        e = e2 - 9 + (f > 0.875f ? 1 : 0);
+    }
+    if (threadIdx.x == 0) xe[t] = e;
+    uint32_t* qrow = reinterpret_cast<uint32_t*>(xq + (size_t)t * d);
+    u32x4* drow = xd ? reinterpret_cast<u32x4*>(xd + (size_t)t * d) : nullptr;
+    for (int v = threadIdx.x; v < nv; v += kQThreads) {
+        const u32x4 p = row[v];
+        const uint32_t u[4] = {p.x, p.y, p.z, p.w};
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[2 * i] = ldexpf(bf16_lo(u[i]), -e);   // exact: a power-of-two rescale
+            y[2 * i + 1] = ldexpf(bf16_hi(u[i]), -e);
+        }
+        uint32_t c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h], y[4 * h + 1], 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2], y[4 * h + 3], w, true);
+            c[h] = (uint32_t)w;
+        }
+        qrow[2 * v] = c[0];
+        qrow[2 * v + 1] = c[1];
+        if (drow) {
+            uint32_t o[4];
+            typedef float f32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // two codes at a time -> two floats (exact), times 2^e, to bf16 (exact)
+                const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], false);
+                const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], true);
+                o[2 * h] = pack_bf16x2(ldexpf(lo.x, e), ldexpf(lo.y, e));
+                o[2 * h + 1] = pack_bf16x2(ldexpf(hi.x, e), ldexpf(hi.y, e));
+            }
+            drow[v] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_act8_quant(const Plan& p, const bf16_t* x, hipStream_t st) {
+    act8_quant_kernel<<<p.T, kQThreads, 0, st>>>(x, p.d, p.xq, p.xe, p.xd);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -54,6 +54,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kChunk = 64;
 constexpr uint32_t kGateRenorm = 2u;    // shape flag bits of the gating variants
 constexpr uint32_t kGateSigmoid = 4u;
+constexpr uint32_t kAct8 = 8u;         // 8-bit activations for the routed gate/up
 // Router: experts padded to a multiple of 64 (a wavefront's share).
 constexpr int kRouterBE = 64;
 
@@ -98,6 +99,9 @@ struct Plan {
     Tile* tiles1;        // [max_tiles1]
     Tile* tiles2;        // [max_tiles2]
     int32_t* ntiles;     // [2]
+    uint8_t* xq;         // 8-bit activations (MOE_FLAG_ACT8): codes [T, d]
+    int32_t* xe;         //   their scale exponents [T]
+    bf16_t* xd;          //   the dequantised rows [T, d] (batches off the FP8 tile only)
     bf16_t* H;           // routed [T*K, I] then shared [Ks*T, Is]
     bf16_t* Y;           // [rows, d]
 
@@ -129,6 +133,9 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
 hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
                             const RoutedQ8* q8, hipStream_t st);
 hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st);
+// MOE_FLAG_ACT8: the 8-bit activations of x (codes, exponents, and for the
+// decode-size tiles the dequantised rows)
+hipError_t launch_act8_quant(const Plan& p, const bf16_t* x, hipStream_t st);
 // training forward: balance statistics [2E + 1] = (f_e, P_e, L_bal) from the
 // group offsets and the score sums
 hipError_t launch_balance_stats(const Plan& p, float* stats, hipStream_t st);

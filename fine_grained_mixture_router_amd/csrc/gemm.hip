@@ -54,6 +54,8 @@ struct GemmParams {
     const uint8_t* Qb_r;     // 8-bit routed W3 (G1 only)
     const float* Sa_r;       // their per-row scales [E, n_r]
     const float* Sb_r;
+    const uint8_t* Xq;       // G1 with 8-bit activations: codes of x [T, d], or null
+    const int32_t* Xe;       //   their per-token scale exponents [T]
     bf16_t* O_r;             // routed output base (G1: H routed, G2: Y)
     bf16_t* O_s;             // shared output base (G1: H shared, G2: Y)
     bf16_t* Z_r;             // G1 of a training forward: pre-activations [W1 x | W3 x]
@@ -945,6 +947,202 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     }
 }
 
+// One 256 x 256 gate/up tile of a routed expert with 8-bit activations and
+// 8-bit weights (MOE_FLAG_ACT8), on the FP8 matrix cores:
+// v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation), twice the
+// bf16 rate per k.  A slice is 128 codes of k, so an operand half (256 rows x
+// 128 bytes, 32 KB) loads exactly like a bf16 half of 64 values: the same
+// ring of five slots, the same load assignment and swizzle as big_tile, with
+// two k64 MFMA steps per slice instead of four k16 steps.  Fragment of a
+// 32-row block: lane l holds row l % 32 and the 32 codes k = 32 (l / 32) ..
+// + 31 of the step (two 16-byte LDS reads); on this instruction a lane's
+// half (l / 32) and byte position pair A and B codes of equal k, and lane l
+// addresses row / column l % 32 of the operand (measured on MI355X).  The
+// epilogue scales each output by 2^e of its token and the weight row's scale
+// (exact power-of-two step first), then applies SwiGLU as big_tile.
+// One fragment set: the next step's reads are issued after this step's MFMAs
+// (the MFMAs read their operands as they issue), and land under them.
+__device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds_bf16_t* smem) {
+    constexpr int BKB = 128;                       // codes (bytes) of k per slice
+    constexpr int OPER = kBig * BKB / 2;           // bf16-sized elements of one operand half
+    constexpr int NSLOT = 5;
+    constexpr int NW = 8;
+    constexpr int CH = BKB / 16;                   // 16-byte chunks per row
+    constexpr int RI = 1024 / BKB;                 // rows per load instruction
+    constexpr int R = 256 / BKB;                   // rows per 256 bytes of LDS
+    constexpr int QI = kBig / RI / NW;             // load instructions per wave per half
+    constexpr int WN = NW / 2;                     // waves along the B rows (2 along M)
+    constexpr int WCOLS = kBig / WN;               // B-rows per wave: 32 of W1, 32 of W3
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    static_assert(QI == 4, "four load instructions per wave per half");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int kdim = P.kdim_r;                     // d: codes per activation / weight row
+    const int ncols = P.n_r;
+    const int grow = P.goff[tl.group] + tl.m0;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(P.Xq, P.abytes_r / 2);   // T d codes
+    const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim;
+    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(P.Qa_r + (size_t)tl.group * wbytes, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(P.Qb_r + (size_t)tl.group * wbytes, wbytes);
+    uint32_t aoff[QI], boff[QI];
+#pragma unroll
+    for (int q = 0; q < QI; ++q) {
+        const int row = RI * (wave + NW * q) + lane / CH;
+        const uint32_t cbytes = (uint32_t)(((lane % CH) ^ ((row / R) % CH)) * 16);
+        const int rr = row < tl.nrows ? row : 0;
+        aoff[q] = (uint32_t)P.tok_of[grow + rr] * (uint32_t)kdim + cbytes;
+        int n = tl.n0 + (q >= QI / 2 ? row - kBig / 2 : row);   // B rows 0..127 W1, 128..255 W3
+        n = n < ncols ? n : ncols - 1;
+        boff[q] = (uint32_t)n * (uint32_t)kdim + cbytes;
+    }
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)smem + (uint32_t)(wave * RI * BKB));
+    auto slot = [](int h) { return h % NSLOT; };
+    auto load_one = [&](int h, int q) {            // half h: A (even) or B (odd) of slice h / 2
+        const uint32_t sa = lds_base + (uint32_t)(slot(h) * OPER * 2) + (uint32_t)(NW * q * 1024);
+        if ((h & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)sa, 16, (int)aoff[q],
+                                                     (h >> 1) * BKB, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(q >= QI / 2 ? rw3 : rw1, (lds_ptr_t)(uintptr_t)sa, 16,
+                                                     (int)boff[q], (h >> 1) * BKB, 0, 0);
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    const int lrow = lane & 31, hh = lane >> 5;
+    i32x8 fa[4], fb[2];
+    // fragments of k64 step st of slice kt: chunks 4 st + 2 hh and + 1 of the row
+    auto read_frags = [&](int kt, int st) {
+        const lds_bf16_t* sa = smem + slot(2 * kt) * OPER;
+        const lds_bf16_t* sb = smem + slot(2 * kt + 1) * OPER;
+        auto frag = [&](const lds_bf16_t* base, int row) -> i32x8 {
+            const int c0 = 4 * st + 2 * hh, f = (row / R) % CH;
+            const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                base + row * (BKB / 2) + ((c0 ^ f) << 3));
+            const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                base + row * (BKB / 2) + (((c0 + 1) ^ f) << 3));
+            return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = frag(sb, (j == 0 ? 0 : kBig / 2) + wn * (WCOLS / 2) + lrow);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = frag(sa, wm * 128 + 32 * i + lrow);
+    };
+    auto mfmas = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                            0, 0, 0);
+    };
+
+    const int nk = kdim / BKB;
+#pragma unroll
+    for (int q = 0; q < QI; ++q) load_one(0, q);
+#pragma unroll
+    for (int q = 0; q < QI; ++q) load_one(1, q);
+    if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < QI; ++q) load_one(2, q);
+#pragma unroll
+        for (int q = 0; q < QI; ++q) load_one(3, q);
+        wait_vm<2 * QI>();                         // slice 0 landed
+    } else {
+        wait_vm<0>();
+    }
+    stage_barrier();
+    read_frags(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 2 < nk;
+        mfmas();                                   // step 0
+        read_frags(kt, 1);
+        if (more)
+#pragma unroll
+            for (int q = 0; q < QI; ++q) load_one(2 * (kt + 2), q);   // A of slice kt + 2 (slot of B of kt - 1)
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) {
+            if (more) wait_vm<QI>();               // slice kt + 1 landed (A of kt + 2 may not)
+            else wait_vm<0>();
+        }
+        // this wave's reads of slice kt have returned before the barrier after
+        // which A of slice kt's slot is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas();                                   // step 1
+        if (more)
+#pragma unroll
+            for (int q = 0; q < QI; ++q) load_one(2 * (kt + 2) + 1, q);   // B of slice kt + 2
+        if (kt + 1 < nk) read_frags(kt + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue (as big_tile's gate/up): each output times 2^e of its token
+    // and its weight row's scale, SwiGLU in registers, the tile staged
+    // through the free slots and stored as 16-byte row pieces.
+    constexpr int OC = kBig / 2;                   // 128 output columns
+    constexpr int CPR = OC / 8;
+    int ex[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = wm * 128 + 32 * i + lrow;
+        ex[i] = m < tl.nrows ? P.Xe[P.tok_of[grow + m]] : 0;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();                               // every wave is done with the slots
+    {
+        const int ocol_l = wn * (WCOLS / 2) + 4 * hh;
+        const float* sca = P.Sa_r + (size_t)tl.group * ncols;
+        const float* scb = P.Sb_r + (size_t)tl.group * ncols;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float fa4[4], fb4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = tl.n0 + ocol_l + 8 * r4 + e;
+                fa4[e] = n < ncols ? sca[n] : 0.f;
+                fb4[e] = n < ncols ? scb[n] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * r4 + e;
+                    const float a = ldexpf(acc[i][0][r], ex[i]) * fa4[e];
+                    const float b = ldexpf(acc[i][1][r], ex[i]) * fb4[e];
+                    v[e] = silu(a) * b;
+                }
+                const int orow = wm * 128 + 32 * i + lrow;
+                const int ocol = ocol_l + 8 * r4;
+                const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_barrier();
+    for (int c = tid; c < kBig * CPR; c += 64 * NW) {
+        const int row = c / CPR;
+        const int cc = c - row * CPR;
+        const int col = tl.n0 + cc * 8;
+        if (row < tl.nrows && col < ncols) {
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                smem + row * OC + ((cc ^ (row % CPR)) << 3));
+            *reinterpret_cast<u32x4*>(P.O_r + (size_t)(grow + row) * ncols + col) = v;
+        }
+    }
+}
+
 // LDS of the many-rows tile: five 32 KB operand slots (160 KB).
 constexpr int kBigLdsBytes = 5 * kBig * 64 * 2;
 
@@ -956,8 +1154,17 @@ void gemm_big_q8_kernel(GemmParams P) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kBigLdsBytes / 2];
     Tile tl;
     if (!fetch_tile(P, tl)) return;
-    if (tl.group < P.E) big_tile<SWIGLU, 8, true>(P, tl, (lds_bf16_t*)smem);
-    else big_tile<SWIGLU, 8, false>(P, tl, (lds_bf16_t*)smem);
+    if (tl.group < P.E) {
+        if constexpr (SWIGLU) {
+            if (P.Xq) {                            // 8-bit activations: the FP8 matrix cores
+                f8_tile(P, tl, (lds_bf16_t*)smem);
+                return;
+            }
+        }
+        big_tile<SWIGLU, 8, true>(P, tl, (lds_bf16_t*)smem);
+    } else {
+        big_tile<SWIGLU, 8, false>(P, tl, (lds_bf16_t*)smem);
+    }
 }
 
 template <bool SWIGLU, int NW, bool SAVEZ = false>
@@ -1002,7 +1209,11 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
     gp.ntiles = p.ntiles;
     gp.goff = p.goff;
     gp.tok_of = p.tok_of;
-    gp.A_r = x;
+    gp.A_r = p.xd ? p.xd : x;                       // 8-bit activations off the FP8 tile: dequantised rows
+    if (q8 && p.xq && !p.xd) {
+        gp.Xq = p.xq;
+        gp.Xe = p.xe;
+    }
     gp.A_s = x;
     gp.Ba_r = w1;
     gp.Bb_r = w3;

@@ -25,8 +25,9 @@ using namespace moe;
 #define MOE_ROUTER_CBYTES (256LL << 20)
 #endif
 
-static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID,
-              "gating flag bits");
+static_assert(kGateRenorm == MOE_FLAG_RENORM && kGateSigmoid == MOE_FLAG_SIGMOID &&
+                  kAct8 == MOE_FLAG_ACT8,
+              "flag bits");
 static_assert(sizeof(Tile) == sizeof(moe_tile_t) && offsetof(Tile, group) == offsetof(moe_tile_t, group) &&
                   offsetof(Tile, m0) == offsetof(moe_tile_t, m0) && offsetof(Tile, n0) == offsetof(moe_tile_t, n0) &&
                   offsetof(Tile, nrows) == offsetof(moe_tile_t, nrows),
@@ -47,7 +48,8 @@ bool shape_ok(const moe_shape_t* s) {
     if (s->I < 64 || s->I > 65536 || s->I % 64) return false;
     if (s->Ks < 0 || s->Ks > 16) return false;
     if (s->Ks > 0 && (s->Is < 64 || s->Is > 65536 || s->Is % 64)) return false;
-    if (s->flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_RENORM | MOE_FLAG_SIGMOID)) return false;
+    if (s->flags & ~(MOE_FLAG_NO_RESIDUAL | MOE_FLAG_RENORM | MOE_FLAG_SIGMOID | MOE_FLAG_ACT8))
+        return false;
     const long long rows = (long long)s->T * (s->K + s->Ks);
     if (rows > (1LL << 30)) return false;
     // The GEMM kernels address x, H and one expert's weights with 32-bit
@@ -140,6 +142,13 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false
     p->tiles1 = (Tile*)take((size_t)p->max_tiles1 * sizeof(Tile));
     p->tiles2 = (Tile*)take((size_t)p->max_tiles2 * sizeof(Tile));
     p->ntiles = (int32_t*)take(16);
+    const bool act8 = (s->flags & MOE_FLAG_ACT8) && s->K > 0;
+    p->xq = (uint8_t*)take(act8 ? (size_t)s->T * s->d : 0);
+    p->xe = (int32_t*)take(act8 ? (size_t)s->T * 4 : 0);
+    // the FP8 tile takes 256-row tiles with d a multiple of its 128-deep
+    // slices; other batches feed the dequantised rows to the 8-bit-weight tiles
+    const bool f8 = p->g1.bm == 256 && s->d % 128 == 0;
+    p->xd = (bf16_t*)take(act8 && !f8 ? (size_t)s->T * s->d * 2 : 0);
     p->H = (bf16_t*)take(((size_t)TK * s->I + (size_t)s->T * s->Ks * p->Is) * 2);
     p->Y = (bf16_t*)take((size_t)p->rows * s->d * 2);
     if (train) {
@@ -230,6 +239,10 @@ void place(Plan* p, void* ws) {
     p->tiles1 = rebase(p->tiles1, b);
     p->tiles2 = rebase(p->tiles2, b);
     p->ntiles = rebase(p->ntiles, b);
+    const bool act8 = (p->flags & kAct8) && p->K > 0;
+    p->xq = act8 ? rebase(p->xq, b) : nullptr;
+    p->xe = act8 ? rebase(p->xe, b) : nullptr;
+    p->xd = act8 && !(p->g1.bm == 256 && p->d % 128 == 0) ? rebase(p->xd, b) : nullptr;
     p->H = rebase(p->H, b);
     p->Y = rebase(p->Y, b);
 }
@@ -327,6 +340,9 @@ __attribute__((visibility("default"))) moe_status_t moe_workspace_layout(const m
     layout->tiles_gate_up = at(p.tiles1);
     layout->tiles_down = at(p.tiles2);
     layout->ntiles = at(p.ntiles);
+    const bool act8 = (shape->flags & MOE_FLAG_ACT8) && shape->K > 0;
+    layout->act8_codes = act8 ? at(p.xq) : 0;
+    layout->act8_exps = act8 ? at(p.xe) : 0;
     layout->rows = p.rows;
     layout->max_tiles_gate_up = p.max_tiles1;
     layout->max_tiles_down = p.max_tiles2;
@@ -398,6 +414,7 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     moe_status_t st = check_common(shape, x, centroids, expert_bias, workspace, workspace_bytes,
                                    &p, q8 != nullptr, false, train);
     if (st != MOE_OK) return st;
+    if ((shape->flags & MOE_FLAG_ACT8) && !q8) return MOE_ERR_SHAPE;   // 8-bit weights only
     if (!out) return MOE_ERR_NULL;
     if (shape->K > 0) {
         if (q8 ? (!q8->q1 || !q8->q3 || !q8->q2 || !q8->s1 || !q8->s3 || !q8->s2)
@@ -457,7 +474,13 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     step(2, [&] { return launch_perm_scan(p, s); });
     step(3, [&] { return launch_perm_scatter(p, s); });
     if (stats && p.K > 0 && e == hipSuccess) e = launch_balance_stats(p, stats, s);
-    step(4, [&] { return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s); });
+    step(4, [&] {                           // (with 8-bit activations, their quantisation too)
+        if (p.xq) {
+            const hipError_t qe = launch_act8_quant(p, xb, s);
+            if (qe != hipSuccess) return qe;
+        }
+        return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s);
+    });
     step(5, [&] { return launch_gemm_down(p, w2b, ws2b, q, s); });
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {

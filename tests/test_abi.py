@@ -116,12 +116,29 @@ def test_bad_shapes(kw):
 
 def test_bad_flags():
     s = S()
-    for f in (8, 16, 1 << 31):
+    for f in (16, 32, 1 << 31):
         s.flags = f
         assert moe.lib().moe_workspace_size(ctypes.byref(s)) == 0
-    for f in (0, 1, 2, 4, 7):                    # NO_RESIDUAL, RENORM, SIGMOID and combinations
+    for f in (0, 1, 2, 4, 7, 8, 15):             # NO_RESIDUAL, RENORM, SIGMOID, ACT8 and combinations
         s.flags = f
         assert moe.lib().moe_workspace_size(ctypes.byref(s)) > 0
+
+
+def test_act8_only_with_8bit_weights():
+    """MOE_FLAG_ACT8 needs 8-bit routed weights: the bf16 forward and the
+    training entry points refuse it before touching a device; its workspace
+    holds the codes and exponents, placed apart from the rest."""
+    s = S(T=300, d=512)
+    s.flags = moe.ACT8
+    assert _fwd(s) == 2                                   # MOE_ERR_SHAPE
+    plain = moe.make_shape(300, 512, 16, 256, 4, 1, 256)
+    lay, lay0 = moe.workspace_layout(s), moe.workspace_layout(plain)
+    assert lay0["act8_codes"] == 0 and lay0["act8_exps"] == 0
+    n = moe.workspace_size(s)
+    assert lay["act8_codes"] >= lay["ntiles"] + 16
+    assert lay["act8_exps"] >= lay["act8_codes"] + 300 * 512
+    assert lay["act8_exps"] + 300 * 4 <= n
+    assert n > moe.workspace_size(plain)
 
 
 def _fwd(shape, ws_bytes=1 << 40, **over):

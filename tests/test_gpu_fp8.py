@@ -277,3 +277,119 @@ def test_fp8_v3_style_gate(name, nsample):
     assert torch.equal(didx, idx)
     dref = _ref(L, w.K, tok, no_residual=True, forced_idx=gi, **kw)
     check_part(out_f64(dout)[tok], dref["out"], "delta")
+
+
+# ---------------------------------------------------------------------------
+# 8-bit activations (MOE_FLAG_ACT8): the routed gate/up products on the FP8
+# matrix cores (256-row tiles) or, for decode-size batches, on the bf16 tile
+# fed the dequantised rows.
+# ---------------------------------------------------------------------------
+
+def _act8_codes(D, L, K, shape_kw):
+    """Run the 8-bit forward with a workspace of our own and read back the
+    activation codes and exponents it wrote."""
+    T, d = L["x"].shape
+    E, I = L["q1"].shape[0], L["q1"].shape[1]
+    Ks = L["ws1"].shape[0]
+    shape = moe.make_shape(T, d, E, I, K, Ks, L["ws1"].shape[1] if Ks else 0, act8=True, **shape_kw)
+    lay = moe.workspace_layout(shape)
+    ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out, idx, gate = _gpu(D, K, act8=True, workspace=ws, **shape_kw)
+    torch.cuda.synchronize()
+    codes = ws[lay["act8_codes"]:lay["act8_codes"] + T * d].cpu().numpy().reshape(T, d)
+    exps = ws[lay["act8_exps"]:lay["act8_exps"] + 4 * T].view(torch.int32).cpu().numpy()
+    return out, idx, gate, codes, exps
+
+
+@pytest.mark.parametrize("name", ["tiny", "2b"])
+def test_act8_codes_bit_exact(name):
+    """Every activation code and exponent equals the oracle's (an integer
+    decision: bit-exact), on rows of every magnitude, an all-zero row and
+    a row of bf16 subnormals."""
+    w = wl.WORKLOADS[name]
+    _log(f"[fp8] act8 codes {name}")
+    L = _fp8_layer(w)
+    rng = np.random.default_rng(11)
+    x = synth.bf16_to_f64(L["x"]) * np.exp(rng.uniform(-12, 12, (w.T, 1)))
+    x[1] = 0.0
+    x[2] = x[2] * 2.0 ** -130                       # subnormal row
+    L["x"] = synth.f32_to_bf16_rne(x.astype(np.float32))
+    D = _upload(L)
+    _, _, _, codes, exps = _act8_codes(D, L, w.K, {})
+    rc, re_ = oracle.quantize_act8(L["x"])
+    assert np.array_equal(exps, re_)
+    assert np.array_equal(codes, rc)
+
+
+@pytest.mark.parametrize("name,nsample", [("tiny", 128), ("2b", 96), ("16b_zipf", 96)])
+def test_act8_layer_parity(name, nsample):
+    """The layer with 8-bit activations against the oracle's ACT8 layer:
+    routing, output and the residual-free delta under the GPU's routing
+    (tiny takes the decode-size tiles, 2B and 16B the FP8 256-row tiles)."""
+    w = wl.WORKLOADS[name]
+    _log(f"[fp8] act8 {name}")
+    L = _fp8_layer(w)
+    D = _upload(L)
+    out, idx, gate = _gpu(D, w.K, act8=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.T + 9)
+    tok = np.unique(np.r_[0, rng.choice(w.T, min(nsample, w.T), replace=False), w.T - 1])
+    ref = _ref(L, w.K, tok, act8=True)
+    gi, gg = idx.cpu().numpy()[tok], gate.cpu().numpy()[tok]
+    check_routing(gi, gg, ref["idx"], ref["gate"], ref["margin"], w.K)
+    ob = bf16_bits(out)[tok]
+    check_close(synth.bf16_to_f64(ob), ref["out"])
+    dout, didx, _ = _gpu(D, w.K, act8=True, no_residual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(didx, idx)
+    dref = _ref(L, w.K, tok, act8=True, no_residual=True, forced_idx=gi)
+    check_part(out_f64(dout)[tok], dref["out"], "delta")
+    rout, ridx, _ = _gpu(D, w.K, Ks=0, act8=True, no_residual=True)
+    torch.cuda.synchronize()
+    rref = _ref(L, w.K, tok, Ks=0, act8=True, no_residual=True, forced_idx=ridx.cpu().numpy()[tok])
+    check_part(out_f64(rout)[tok], rref["routed"], "routed")
+    out2, _, _ = _gpu(D, w.K, act8=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", [
+    (67, 576, 13, 192, 3, 2, 320),
+    (700, 1024, 5, 512, 1, 3, 128),
+    (2048, 256, 6, 128, 2, 1, 192),
+], ids=lambda c: "T%dd%dE%dI%dK%dKs%dIs%d" % c)
+def test_act8_edge_shapes(case):
+    T, d, E, I, K, Ks, Is = case
+    _log(f"[fp8] act8 edge {case}")
+    w = wl.Workload("edge", T=T, d=d, E=E, I=I, K=K, Ks=Ks, Is=Is, wseed=T + d, xseed=T + E)
+    L = _fp8_layer(w)
+    D = _upload(L)
+    dout, idx, _ = _gpu(D, K, act8=True, no_residual=True)
+    torch.cuda.synchronize()
+    tok = np.unique(np.r_[0, np.random.default_rng(d).choice(T, min(T, 64), replace=False), T - 1])
+    ref = _ref(L, K, tok, act8=True, no_residual=True, forced_idx=idx.cpu().numpy()[tok])
+    check_part(out_f64(dout)[tok], ref["out"], "delta")
+
+
+def test_act8_v3_prefill_shape():
+    """The V3-shape prefill batch with 8-bit weights and activations: routing
+    of every token, and the output on tokens that put a checked row in every
+    (group, 256-row tile) of the gate/up work list."""
+    w = wl.WORKLOADS["v3_prefill"]
+    _log("[fp8] act8 v3_prefill: generating inputs")
+    L = _fp8_layer(w)
+    D = _upload(L)
+    out, idx, gate = _gpu(D, w.K, act8=True)
+    torch.cuda.synchronize()
+    ri, rg, rm = oracle.route(L["x"], L["C"], L["bias"], w.K)
+    check_routing(idx.cpu().numpy(), gate.cpu().numpy(), ri, rg, rm, w.K)
+    tok = tile_cover_tokens(idx.cpu().numpy(), w.E, w.Ks, w.T)
+    _log(f"[fp8] act8 v3_prefill: checking {tok.size} tokens")
+    dout, _, _ = _gpu(D, w.K, act8=True, no_residual=True)
+    torch.cuda.synchronize()
+    dref = _ref(L, w.K, tok, act8=True, no_residual=True, forced_idx=idx.cpu().numpy()[tok])
+    check_part(out_f64(dout)[tok], dref["out"], "delta")
+    ob = bf16_bits(out)[tok]
+    check_close(synth.bf16_to_f64(ob), dref["out"] + synth.bf16_to_f64(L["x"][tok]))
+    del D
+    torch.cuda.empty_cache()
