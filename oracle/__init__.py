@@ -25,7 +25,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 NO_RESIDUAL = 1
 RENORM = 2      # gates divided by their sum over the K selected experts
 SIGMOID = 4     # sigmoid affinities; the bias enters the selection only
-ACT8 = 8        # routed gate/up take 8-bit activations (per-token power-of-two scales)
+ACT8 = 8        # routed products take 8-bit activations (per-row power-of-two scales)
 
 
 def build(force: bool = True) -> str:
@@ -77,6 +77,8 @@ def lib():
         L.oracle_act8_exponent.argtypes = [ctypes.c_double]
         L.oracle_e4m3_nearest.restype = ctypes.c_uint8
         L.oracle_e4m3_nearest.argtypes = [ctypes.c_double]
+        L.oracle_bf16_nearest.restype = ctypes.c_uint16
+        L.oracle_bf16_nearest.argtypes = [ctypes.c_double]
         L.oracle_quantize_act8.restype = None
         L.oracle_quantize_act8.argtypes = [vp, i32, i32, vp, vp]
         _lib = L
@@ -121,6 +123,11 @@ def act8_exponent(amax: float) -> int:
 def e4m3_nearest(y: float) -> int:
     """E4M3 code nearest to y (|y| <= 448), ties to the even code."""
     return int(lib().oracle_e4m3_nearest(float(y)))
+
+
+def bf16_nearest(v: float) -> int:
+    """Bits of the bf16 value nearest to v, ties to the even significand."""
+    return int(lib().oracle_bf16_nearest(float(v)))
 
 
 def quantize_act8(x_rows):
@@ -221,7 +228,10 @@ def forward_fp8(x_rows, C, bias, q1, s1, q3, s3, q2, s2, ws1, ws3, ws2, K, no_re
     """Layer forward with 8-bit routed weights, in fp64: q1/q3 uint8 [E, I, d]
     and q2 [E, d, I] E4M3 codes, s1/s3 float32 [E, I] and s2 [E, d] per-row
     scales (weight = e4m3(q) * scale); shared experts ws* in bf16 as for
-    forward().  Returns the same dict as forward()."""
+    forward().  act8: the routed experts' products take 8-bit activations —
+    x quantised per token, h = silu(W1 x) * W3 x rounded to bf16 and
+    quantised per (token, expert) row (quantize_act8's rule) before W2.
+    Returns the same dict as forward()."""
     x_rows = np.ascontiguousarray(x_rows)
     n, d = x_rows.shape
     E = C.shape[0]

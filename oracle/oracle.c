@@ -56,11 +56,17 @@
  * 2^e (448 being E4M3's largest finite value; e = 0 for an all-zero row),
  * and the codes q_j = nearest E4M3 value of x_j * 2^-e, ties to the even
  * code.  The routed experts' W1 x and W3 x take the dequantised row
- * e4m3(q_j) * 2^e; the shared experts and the down projection keep the
- * 16-bit activations.  The pages only advise low-bit routed experts with
- * per-channel or per-group scales (eliteato DeepSeek-V2 explainer, section
- * 5.5); per-token power-of-two scales are the plainest reading that keeps
- * every quantised value, and its product with any weight, exact.
+ * e4m3(q_j) * 2^e.  Their down projection's input is treated the same way:
+ * h = silu(W1 x) * W3 x is first rounded to bf16 (nearest, ties to even;
+ * the 16-bit format the layer holds h in between its two products), then
+ * each (token, expert) row of h gets its own power-of-two scale and
+ * nearest-even codes by the same rule, and W2 takes the dequantised row.
+ * The shared experts keep 16-bit activations throughout.  The pages only
+ * advise low-bit routed experts with per-channel or per-group scales
+ * (eliteato DeepSeek-V2 explainer, section 5.5); per-row power-of-two scales
+ * are the plainest reading that keeps every quantised value, and its
+ * product with any weight, exact, and quantising both inputs of the routed
+ * products lets all of them run on 8-bit multipliers.
  *
  * Tokens are independent; OpenMP runs them on separate threads without
  * changing any token's order of operations.
@@ -204,6 +210,27 @@ void oracle_quantize_act8(const uint16_t* x_rows, int32_t n, int32_t d, uint8_t*
     }
 }
 
+/* v rounded to the nearest bf16 value, ties to the even significand (v
+ * finite and below bf16's overflow threshold); returned as bf16 bits.
+ * bf16 keeps 8 significant bits for |v| >= 2^-126 and a fixed step of
+ * 2^-133 below. */
+uint16_t oracle_bf16_nearest(double v) {
+    double r;
+    if (v == 0.0) {
+        r = v;
+    } else if (fabs(v) >= ldexp(1.0, -126)) {
+        int e2;
+        const double f = frexp(v, &e2);            /* |f| in [0.5, 1) */
+        r = ldexp(nearbyint(ldexp(f, 8)), e2 - 8);
+    } else {
+        r = ldexp(nearbyint(ldexp(v, 133)), -133);
+    }
+    const float fr = (float)r;                     /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &fr, 4);
+    return (uint16_t)(u >> 16);
+}
+
 /* The 256 code values, filled from oracle_e4m3() before a forward with
  * 8-bit weights reads them (a lookup in place of a decode per use). */
 static double e4m3_value[256];
@@ -225,9 +252,11 @@ static double wat(const wmat* w, int row, int cols, int col) {
     return w->bf16 ? widen(w->bf16[i]) : e4m3_value[w->q[i]] * (double)w->scale[row];
 }
 
-/* Step 4: y = W2 (silu(W1 x) * W3 x) for one token. h: [inter] scratch. */
+/* Step 4: y = W2 (silu(W1 x) * W3 x) for one token. h: [inter] scratch.
+ * hq (bf16 bits [inter]) and q (codes [inter]) non-NULL: 8-bit activations
+ * into W2, h rounded to bf16 and quantised as one row (see the header). */
 static void expert_ffn(int d, int inter, const wmat* w1, const wmat* w3, const wmat* w2,
-                       const double* x_t, double* h, double* y) {
+                       const double* x_t, double* h, double* y, uint16_t* hq, uint8_t* q) {
     for (int i = 0; i < inter; ++i) {
         double a = 0.0, b = 0.0;
         for (int j = 0; j < d; ++j) {
@@ -235,6 +264,12 @@ static void expert_ffn(int d, int inter, const wmat* w1, const wmat* w3, const w
             b += wat(w3, i, d, j) * x_t[j];
         }
         h[i] = silu(a) * b;
+    }
+    if (hq) {
+        int32_t e;
+        for (int i = 0; i < inter; ++i) hq[i] = oracle_bf16_nearest(h[i]);
+        oracle_quantize_act8(hq, 1, inter, q, &e);
+        for (int i = 0; i < inter; ++i) h[i] = ldexp(oracle_e4m3(q[i]), e);
     }
     for (int o = 0; o < d; ++o) {
         double acc = 0.0;
@@ -307,7 +342,8 @@ static int32_t forward_impl(const oracle_shape* s, const uint16_t* x_rows, int32
 #endif
         double* xt = malloc(sizeof(double) * (size_t)d);
         double* xr = malloc(sizeof(double) * (size_t)d);   /* the routed experts' input */
-        uint8_t* q = malloc((size_t)d);
+        uint8_t* q = malloc((size_t)(d > hmax ? d : hmax));
+        uint16_t* hq = malloc(sizeof(uint16_t) * (size_t)(hmax > 0 ? hmax : 1));
         double* y = malloc(sizeof(double) * (size_t)d);
         double* h = malloc(sizeof(double) * (size_t)(hmax > 0 ? hmax : 1));
         double* lg = malloc(sizeof(double) * (size_t)s->E);
@@ -342,19 +378,20 @@ static int32_t forward_impl(const oracle_shape* s, const uint16_t* x_rows, int32
 
             for (int j = 0; j < d; ++j) sh[j] = 0.0;
             for (int si = 0; si < s->Ks; ++si) {
-                expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xt, h, y);
+                expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xt, h, y, NULL, NULL);
                 for (int j = 0; j < d; ++j) sh[j] += y[j];
             }
             for (int j = 0; j < d; ++j) ro[j] = 0.0;
             for (int k = 0; k < K; ++k) {
                 const int e = idx[k];
-                expert_ffn(d, s->I, &rw1[e], &rw3[e], &rw2[e], xr, h, y);
+                const int a8 = (s->flags & ORACLE_ACT8) != 0;
+                expert_ffn(d, s->I, &rw1[e], &rw3[e], &rw2[e], xr, h, y, a8 ? hq : NULL, q);
                 for (int j = 0; j < d; ++j) ro[j] += gate[k] * y[j];
             }
             const double res = (s->flags & ORACLE_NO_RESIDUAL) ? 0.0 : 1.0;
             for (int j = 0; j < d; ++j) out[(size_t)i * d + j] = res * xt[j] + sh[j] + ro[j];
         }
-        free(xt); free(xr); free(q); free(y); free(h); free(lg); free(pr); free(tk);
+        free(xt); free(xr); free(q); free(hq); free(y); free(h); free(lg); free(pr); free(tk);
     }
     return used;
 }

@@ -164,39 +164,72 @@ def test_act8_rows_error_bound_and_top_binade():
         assert e2[0] == e and np.array_equal(c2[0], q[t])
 
 
-def _act8_layer(seed, representable):
-    w, L = _layer(seed, T=16, d=128)
-    if representable:                               # rows already on the 8-bit grid
-        rng = np.random.default_rng(seed + 1)
-        q = rng.integers(0, 0x7E, size=(w.T, w.d)).astype(np.uint8)
-        q[:, 3] = 0x7E
-        sign = np.where(rng.random((w.T, w.d)) < 0.5, -1.0, 1.0)
-        e = rng.integers(-10, -5, size=(w.T, 1))
-        L["x"] = synth.f32_to_bf16_rne((sign * E4M3[q] * np.ldexp(1.0, e)).astype(np.float32))
-    return w, L
-
-
 def _fp8(w, L, **kw):
     return oracle.forward_fp8(L["x"], L["C"], L["bias"], L["q1"], L["s1"], L["q3"], L["s3"],
                               L["q2"], L["s2"], L["ws1"], L["ws3"], L["ws2"], w.K, **kw)
 
 
-def test_act8_layer_on_representable_rows_equals_the_fp8_layer():
-    """A4: when every row is already an 8-bit row (codes times a power of
-    two, its largest magnitude at 448 * 2^e), quantising changes nothing:
-    the ACT8 layer equals the 8-bit-weight layer to the last bit."""
-    w, L = _act8_layer(31, True)
-    a, b = _fp8(w, L), _fp8(w, L, act8=True)
-    for k in ("out", "routed", "shared", "gate", "margin"):
-        assert np.array_equal(a[k], b[k]), k
-    assert np.array_equal(a["idx"], b["idx"])
+def test_bf16_nearest():
+    """A6: h is rounded to bf16 before its codes are taken.  Every finite
+    bf16 value maps to its own bits (both zeros, subnormals, the largest
+    finite), the midpoint of two neighbours to the one with the even
+    significand, values just beside a midpoint to the nearer neighbour."""
+    bits = np.arange(0x8000, dtype=np.uint32)
+    bits = bits[(bits & 0x7F80) != 0x7F80].astype(np.uint16)          # finite, non-negative
+    val = synth.bf16_to_f64(bits)
+    for b, v in zip(bits[::7], val[::7]):
+        assert oracle.bf16_nearest(v) == b
+        assert oracle.bf16_nearest(-v) == b | 0x8000
+    for b in list(range(0, 40)) + list(range(0x3F70, 0x3F90)) + list(range(0x7F00, 0x7F7F)):
+        lo, hi = val[b], val[b + 1]
+        mid = 0.5 * (lo + hi)                      # exact in double
+        assert oracle.bf16_nearest(mid) == (b if b % 2 == 0 else b + 1)
+        assert oracle.bf16_nearest(np.nextafter(mid, 0.0)) == b
+        assert oracle.bf16_nearest(np.nextafter(mid, np.inf)) == b + 1
+        assert oracle.bf16_nearest(-mid) == (b if b % 2 == 0 else b + 1) | 0x8000
+
+
+def test_act8_down_input_is_the_quantised_bf16_h():
+    """A4: the routed experts' down projection takes 8-bit activations made
+    from h rounded to bf16.  With rows already on the 8-bit grid (so the x
+    quantisation changes nothing), one expert per token with gate 1
+    (renormalised K = 1) and W2 the identity (d = I), the 8-bit-weight
+    layer's routed part is h itself, and the ACT8 layer's must be exactly
+    e4m3(codes) * 2^e of quantize_act8(bf16(h)) row by row.  The instance
+    is one where skipping the bf16 rounding would change some codes."""
+    T, d, E = 16, 128, 6
+    w = wl.Workload("t", T=T, d=d, E=E, I=d, K=1, Ks=1, Is=64, wseed=41, xseed=41)
+    rng = np.random.default_rng(41)
+    q1, _, q3, _, _, _ = wl.gen_routed_fp8(w)
+    pw = lambda *s: np.ldexp(1.0, -rng.integers(3, 6, size=s)).astype(np.float32)
+    q2 = np.zeros((E, d, d), np.uint8)
+    q2[:, np.arange(d), np.arange(d)] = 0x38                           # e4m3 1.0 on the diagonal
+    L = dict(C=wl.gen_centroids(w), q1=q1, q3=q3, q2=q2, s1=pw(E, d), s3=pw(E, d),
+             s2=np.ones((E, d), np.float32), bias=np.zeros(E, np.float32))
+    L["ws1"], L["ws3"], L["ws2"] = wl.gen_shared(w)
+    q = rng.integers(0, 0x7E, size=(T, d)).astype(np.uint8)
+    q[:, 5] = 0x7E
+    sign = np.where(rng.random((T, d)) < 0.5, -1.0, 1.0)
+    L["x"] = synth.f32_to_bf16_rne((sign * E4M3[q] * np.ldexp(1.0, rng.integers(-4, 0, size=(T, 1))))
+                                   .astype(np.float32))
+    a = _fp8(w, L, renorm=True)
+    b = _fp8(w, L, renorm=True, act8=True)
+    assert np.all(a["gate"] == 1.0)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["shared"], b["shared"])
+    h = a["routed"]
+    hb = np.array([[oracle.bf16_nearest(v) for v in row] for row in h], np.uint16)
+    codes, exps = oracle.quantize_act8(hb)
+    want = E4M3[codes] * np.ldexp(1.0, exps)[:, None]
+    assert np.array_equal(b["routed"], want)
+    direct = np.array([[oracle.e4m3_nearest(v * 2.0 ** -e) for v in row] for row, e in zip(h, exps)])
+    assert (direct != codes).any()                 # the bf16 step matters here
 
 
 def test_act8_touches_only_the_routed_experts():
     """A5: on ordinary rows, ACT8 leaves the routing and the shared experts'
     part unchanged to the last bit and moves the routed part by about the
     size of the activation rounding (and no more)."""
-    w, L = _act8_layer(32, False)
+    w, L = _layer(32, T=16, d=128)
     a, b = _fp8(w, L), _fp8(w, L, act8=True)
     for k in ("shared", "gate", "margin"):
         assert np.array_equal(a[k], b[k]), k

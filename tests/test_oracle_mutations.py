@@ -43,9 +43,15 @@ MUTATIONS = [
      "    while (ldexp(448.0, e - 1) >= amax) --e;\n    return e + 1;"),
     ("8-bit activation scale not applied", "for (int j = 0; j < d; ++j) xr[j] = ldexp(oracle_e4m3(q[j]), e);",
      "for (int j = 0; j < d; ++j) xr[j] = oracle_e4m3(q[j]) + 0 * e;"),
+    ("8-bit activations into W2 skipped", "        oracle_quantize_act8(hq, 1, inter, q, &e);\n        for (int i = 0; i < inter; ++i) h[i] = ldexp(oracle_e4m3(q[i]), e);",
+     "        (void)e;"),
+    ("h truncated to bf16 before its codes", "hq[i] = oracle_bf16_nearest(h[i]);",
+     "{ const float f = (float)h[i]; uint32_t u; memcpy(&u, &f, 4); hq[i] = (uint16_t)(u >> 16); }"),
+    ("bf16 rounding ties away from zero", "r = ldexp(nearbyint(ldexp(f, 8)), e2 - 8);", "r = ldexp(round(ldexp(f, 8)), e2 - 8);"),
+    ("h of the shared experts quantised too", "&sw2[si], xt, h, y, NULL, NULL);", "&sw2[si], xt, h, y, hq, q);"),
     ("8-bit activations also fed to the shared experts",
-     "expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xt, h, y);",
-     "expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xr, h, y);"),
+     "expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xt, h, y, NULL, NULL);",
+     "expert_ffn(d, s->Is, &sw1[si], &sw3[si], &sw2[si], xr, h, y, NULL, NULL);"),
 ]
 
 
