@@ -267,15 +267,16 @@ def dev(a):
     return t.cuda()
 
 
-def time_workload(w, D, host_x, steps, warmup):
+def time_workload(w, D, host_x, steps, warmup, act8=False):
     """Warm up, then time exactly `steps` forwards with HIP events around the
-    whole region and around every kernel.  Returns timings and routing."""
+    whole region and around every kernel.  Returns timings and routing.
+    act8: the 8-bit-weight forward with 8-bit activations (MOE_FLAG_ACT8)."""
     import torch
 
     import fine_grained_mixture_router_amd as moe
     x = dev(host_x)
     bias = None if D.get("bias") is None else D["bias"]
-    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is, act8=act8)
     ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
     idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
@@ -284,7 +285,7 @@ def time_workload(w, D, host_x, steps, warmup):
     def step():
         if "q1" in D:
             moe.forward_fp8(x, D["C"], D["q1"], D["s1"], D["q3"], D["s3"], D["q2"], D["s2"],
-                            D["ws1"], D["ws3"], D["ws2"], K=w.K, bias=bias, out=out,
+                            D["ws1"], D["ws3"], D["ws2"], K=w.K, bias=bias, act8=act8, out=out,
                             topk_idx=idx, topk_gate=gate, workspace=ws)
         else:
             moe.forward(x, D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
@@ -637,14 +638,42 @@ def main():
             "T": w.T, "value": round(w.T / (msp / 1e3), 1), "unit": "tokens/s",
             "ms_per_step": round(msp, 4), "speedup_vs_bf16": round(ms / msp, 3),
             "mfma_dtype": "bf16 (codes widened exactly before the products)",
-            "note": "8-bit prefill is bound by the bf16 MFMA rate: the codes halve the weight "
-                    "bytes but no FP8 MFMA runs (activations stay bf16), so it gains nothing on "
-                    "the prefill batch; the 8-bit path pays off on the HBM-bound decode batch",
+            "note": "with bf16 activations the 8-bit weights only halve the bytes each tile "
+                    "moves, and the products still run on the bf16 MFMA; prefill_fp8_act8 adds "
+                    "8-bit activations and runs the routed gate/up on the FP8 MFMA",
             "roofline": roofline("mfma", kp, rp["kernels"], w.name + "_fp8"),
             "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rp["kernels"].items()},
         }
+        # the same with 8-bit activations (MOE_FLAG_ACT8): the routed gate/up
+        # and down products on the FP8 MFMA (32x32x64, E4M3 x E4M3), the
+        # shared expert bf16
+        ra = time_workload(w, P8, L["x"], args.steps, args.warmup, act8=True)
+        msa = ra["ms_per_step"]
+        g1r = 4.0 * w.d * w.I * w.T * w.K                 # routed gate/up FLOPs (FP8)
+        g1s = 4.0 * w.d * w.Is * w.T * w.Ks               # shared gate/up FLOPs (bf16)
+        mixed_peak = (g1r + g1s) / (g1r / (2 * PEAK_BF16_TFLOPS) + g1s / PEAK_BF16_TFLOPS)
+        ga_ms, ga_n = ra["kernels"]["gemm_gate_up"]
+        ga_s = ga_ms / max(ga_n, 1) / 1e3
+        ach = (g1r + g1s) / ga_s / 1e12
+        line["prefill_fp8_act8"] = {
+            "workload": w.name + " (8-bit E4M3 routed weights and activations: per-row "
+                                 "power-of-two activation scales for x and h; shared expert bf16)",
+            "T": w.T, "value": round(w.T / (msa / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(msa, 4), "speedup_vs_bf16": round(ms / msa, 3),
+            "mfma_dtype": "fp8 (routed gate/up and down, v_mfma_f32_32x32x64_f8f6f4); bf16 for "
+                          "the shared expert",
+            "roofline": dict(kernel="gemm_gate_up", bound="mfma", achieved=round(ach, 1),
+                             peak=round(mixed_peak, 1), unit="TFLOP/s",
+                             frac=round(ach / mixed_peak, 4), traffic=None,
+                             peak_note="routed FLOPs at the 5.0 PF FP8 peak, the shared expert's "
+                                       "at the 2.5 PF bf16 peak; the time includes the "
+                                       "activation quantisation of x",
+                             mean_launch_ms=round(ga_s * 1e3, 4), launches=ga_n),
+            "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in ra["kernels"].items()},
+        }
         del P8
-        print(f"[bench] {w.name} fp8: {msp:.3f} ms/step", file=sys.stderr, flush=True)
+        print(f"[bench] {w.name} fp8: {msp:.3f} ms/step, with 8-bit activations {msa:.3f} ms/step",
+              file=sys.stderr, flush=True)
 
     if args.decode:
         wd = wl.WORKLOADS[args.decode]

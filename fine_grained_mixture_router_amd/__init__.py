@@ -63,7 +63,8 @@ class Layout(ctypes.Structure):
     """moe_layout_t: where the forward leaves its token permutation."""
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "gate", "goff", "tok_of", "slot_of",
                                                "tiles_gate_up", "tiles_down", "ntiles",
-                                               "act8_codes", "act8_exps")] + \
+                                               "act8_codes", "act8_exps", "h",
+                                               "act8_h_codes", "act8_h_exps")] + \
                [(n, ctypes.c_int32) for n in ("rows", "max_tiles_gate_up", "max_tiles_down",
                                               "tile_rows_gate_up", "tile_cols_gate_up",
                                               "tile_rows_down", "tile_cols_down")]

@@ -1,11 +1,12 @@
-// 8-bit activations for the routed gate/up products (MOE_FLAG_ACT8).
+// 8-bit activations for the routed products (MOE_FLAG_ACT8): the token rows
+// x before W1 / W3, the routed rows of h (bf16) before W2.
 //
-// Each token row x gets the scale 2^e, e the smallest integer with
+// Each row gets the scale 2^e, e the smallest integer with
 // max_j |x_j| <= 448 * 2^e (448: the largest finite E4M3 value; e = 0 for an
 // all-zero row), and the codes are the nearest E4M3 values of x * 2^-e, ties
 // to the even code.  The pages only advise low-bit routed experts with
 // per-channel or per-group scales (eliteato DeepSeek-V2 explainer, section
-// 5.5); a power-of-two per-token scale makes x * 2^-e exact, so the codes
+// 5.5); a power-of-two per-row scale makes x * 2^-e exact, so the codes
 // depend on nothing but round-to-nearest-even, which the hardware conversion
 // (v_cvt_pk_fp8_f32) performs.
 //
@@ -13,11 +14,14 @@
 // a <= 448 * 2^e = 0.875 * 2^(9 + e) holds for e = E2 - 9 when f <= 0.875 and
 // needs e = E2 - 8 otherwise; one less never holds (f >= 0.5 > 0.4375).
 //
-// One workgroup per token row: the row maximum over 16-byte pieces (a
-// wavefront reduction, then one across the four waves), then the codes, four
-// per 32-bit store, and for batches off the FP8 tile (decode-size tiles, or d
-// not a multiple of its 128-deep slices) the dequantised row in bf16
-// (exact: an E4M3 value times a power of two fits bf16's 8-bit significand).
+// One workgroup per row: the row maximum over 16-byte pieces (a wavefront
+// reduction, then one across the four waves), then the codes, four per
+// 32-bit store, and where the FP8 tiles do not apply (decode-size tiles, or
+// a reduction length that is not a multiple of their 128-deep slices) the
+// dequantised row in bf16 (exact: an E4M3 value times a power of two fits
+// bf16's 8-bit significand).  The dequantised row may overwrite the input:
+// each thread writes only the pieces it has itself read, after the
+// workgroup-wide maximum (and so every read of the first pass) is complete.
 #include "common.h"
 
 namespace moe {
@@ -28,10 +32,10 @@ constexpr int kQThreads = 256;
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-__global__ __launch_bounds__(kQThreads) void act8_quant_kernel(const bf16_t* __restrict__ x, int d,
+__global__ __launch_bounds__(kQThreads) void act8_quant_kernel(const bf16_t* x, int d,
                                                                uint8_t* __restrict__ xq,
                                                                int32_t* __restrict__ xe,
-                                                               bf16_t* __restrict__ xd) {
+                                                               bf16_t* xd) {
     const int t = blockIdx.x;
     const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * d);
     const int nv = d >> 3;                          // 16-byte pieces (8 values)
@@ -55,8 +59,8 @@ __global__ __launch_bounds__(kQThreads) void act8_quant_kernel(const bf16_t* __r
         const float f = frexpf(amax, &e2);
         e = e2 - 9 + (f > 0.875f ? 1 : 0);
     }
-    if (threadIdx.x == 0) xe[t] = e;
-    uint32_t* qrow = reinterpret_cast<uint32_t*>(xq + (size_t)t * d);
+    if (xe && threadIdx.x == 0) xe[t] = e;
+    uint32_t* qrow = xq ? reinterpret_cast<uint32_t*>(xq + (size_t)t * d) : nullptr;
     u32x4* drow = xd ? reinterpret_cast<u32x4*>(xd + (size_t)t * d) : nullptr;
     for (int v = threadIdx.x; v < nv; v += kQThreads) {
         const u32x4 p = row[v];
@@ -74,8 +78,10 @@ __global__ __launch_bounds__(kQThreads) void act8_quant_kernel(const bf16_t* __r
             w = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2], y[4 * h + 3], w, true);
             c[h] = (uint32_t)w;
         }
-        qrow[2 * v] = c[0];
-        qrow[2 * v + 1] = c[1];
+        if (qrow) {
+            qrow[2 * v] = c[0];
+            qrow[2 * v + 1] = c[1];
+        }
         if (drow) {
             uint32_t o[4];
             typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -94,8 +100,11 @@ __global__ __launch_bounds__(kQThreads) void act8_quant_kernel(const bf16_t* __r
 
 }  // namespace
 
-hipError_t launch_act8_quant(const Plan& p, const bf16_t* x, hipStream_t st) {
-    act8_quant_kernel<<<p.T, kQThreads, 0, st>>>(x, p.d, p.xq, p.xe, p.xd);
+hipError_t launch_act8_quant(const bf16_t* x, int rows, int d, uint8_t* codes, int32_t* exps,
+                             bf16_t* deq, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (d % 8) return hipErrorInvalidValue;
+    act8_quant_kernel<<<rows, kQThreads, 0, st>>>(x, d, codes, exps, deq);
     return hipGetLastError();
 }
 

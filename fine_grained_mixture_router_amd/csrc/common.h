@@ -54,7 +54,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kChunk = 64;
 constexpr uint32_t kGateRenorm = 2u;    // shape flag bits of the gating variants
 constexpr uint32_t kGateSigmoid = 4u;
-constexpr uint32_t kAct8 = 8u;         // 8-bit activations for the routed gate/up
+constexpr uint32_t kAct8 = 8u;         // 8-bit activations for the routed products
 // Router: experts padded to a multiple of 64 (a wavefront's share).
 constexpr int kRouterBE = 64;
 
@@ -102,6 +102,8 @@ struct Plan {
     uint8_t* xq;         // 8-bit activations (MOE_FLAG_ACT8): codes [T, d]
     int32_t* xe;         //   their scale exponents [T]
     bf16_t* xd;          //   the dequantised rows [T, d] (batches off the FP8 tile only)
+    uint8_t* hq;         // 8-bit activations of the routed rows of H: codes [T*K, I] and
+    int32_t* he;         //   exponents [T*K] (FP8 down tiles only; else H is dequantised in place)
     bf16_t* H;           // routed [T*K, I] then shared [Ks*T, Is]
     bf16_t* Y;           // [rows, d]
 
@@ -133,9 +135,14 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
 hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
                             const RoutedQ8* q8, hipStream_t st);
 hipError_t launch_combine(const Plan& p, const bf16_t* x, bf16_t* out, hipStream_t st);
-// MOE_FLAG_ACT8: the 8-bit activations of x (codes, exponents, and for the
-// decode-size tiles the dequantised rows)
-hipError_t launch_act8_quant(const Plan& p, const bf16_t* x, hipStream_t st);
+// MOE_FLAG_ACT8: the 8-bit activations of `rows` bf16 rows of width d
+// (d a multiple of 8): codes [rows, d] and exponents [rows] (each may be
+// null) and the dequantised rows (deq, may be null or equal to x)
+hipError_t launch_act8_quant(const bf16_t* x, int rows, int d, uint8_t* codes, int32_t* exps,
+                             bf16_t* deq, hipStream_t st);
+// the FP8 tiles: 256-row tiles and a reduction length of whole 128-deep slices
+inline bool f8_gate_up(const Plan& p) { return p.g1.bm == 256 && p.d % 128 == 0; }
+inline bool f8_down(const Plan& p) { return p.g2.bm == 256 && p.I % 128 == 0; }
 // training forward: balance statistics [2E + 1] = (f_e, P_e, L_bal) from the
 // group offsets and the score sums
 hipError_t launch_balance_stats(const Plan& p, float* stats, hipStream_t st);

@@ -54,8 +54,9 @@ struct GemmParams {
     const uint8_t* Qb_r;     // 8-bit routed W3 (G1 only)
     const float* Sa_r;       // their per-row scales [E, n_r]
     const float* Sb_r;
-    const uint8_t* Xq;       // G1 with 8-bit activations: codes of x [T, d], or null
-    const int32_t* Xe;       //   their per-token scale exponents [T]
+    const uint8_t* Xq;       // 8-bit activations: codes of the routed A rows (G1: x [T, d],
+                             //   G2: h [T*K, I]), or null
+    const int32_t* Xe;       //   their per-row scale exponents
     bf16_t* O_r;             // routed output base (G1: H routed, G2: Y)
     bf16_t* O_s;             // shared output base (G1: H shared, G2: Y)
     bf16_t* Z_r;             // G1 of a training forward: pre-activations [W1 x | W3 x]
@@ -947,21 +948,26 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     }
 }
 
-// One 256 x 256 gate/up tile of a routed expert with 8-bit activations and
-// 8-bit weights (MOE_FLAG_ACT8), on the FP8 matrix cores:
-// v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation), twice the
-// bf16 rate per k.  A slice is 128 codes of k, so an operand half (256 rows x
-// 128 bytes, 32 KB) loads exactly like a bf16 half of 64 values: the same
-// ring of five slots, the same load assignment and swizzle as big_tile, with
-// two k64 MFMA steps per slice instead of four k16 steps.  Fragment of a
-// 32-row block: lane l holds row l % 32 and the 32 codes k = 32 (l / 32) ..
-// + 31 of the step (two 16-byte LDS reads); on this instruction a lane's
-// half (l / 32) and byte position pair A and B codes of equal k, and lane l
-// addresses row / column l % 32 of the operand (measured on MI355X).  The
-// epilogue scales each output by 2^e of its token and the weight row's scale
-// (exact power-of-two step first), then applies SwiGLU as big_tile.
-// One fragment set: the next step's reads are issued after this step's MFMAs
-// (the MFMAs read their operands as they issue), and land under them.
+// One 256 x 256 tile of a routed expert with 8-bit activations and 8-bit
+// weights (MOE_FLAG_ACT8), on the FP8 matrix cores: v_mfma_f32_32x32x64_f8f6f4
+// (E4M3 x E4M3, fp32 accumulation), twice the bf16 rate per k.  Gate/up
+// (SWIGLU): A = codes of the gathered token rows, B = 128 rows of W1 then the
+// same 128 rows of W3.  Down: A = codes of the tile's rows of h (contiguous),
+// B = 256 rows of W2.  A slice is 128 codes of k, so an operand half (256
+// rows x 128 bytes, 32 KB) loads exactly like a bf16 half of 64 values: the
+// same ring of five slots, load assignment and swizzle as big_tile, with two
+// k64 MFMA steps per slice instead of four k16 steps.  Fragment of a 32-row
+// block: lane l holds row l % 32 and the 32 codes k = 32 (l / 32) .. + 31 of
+// the step (two 16-byte LDS reads); on this instruction a lane's half
+// (l / 32) and byte position pair A and B codes of equal k, and lane l
+// addresses row / column l % 32 of the operand (measured on MI355X).
+// Each wave owns 128 rows x 64 B-rows (gate/up: 32 of W1 and the same 32 of
+// W3).  As in big_tile, each step is a sequence of fenced groups — one MFMA,
+// one fragment read of the next step into the other register set, a share of
+// the loads — so reads and loads issue under running MFMAs.  The epilogue
+// scales each output by 2^e of its activation row and its weight row's scale
+// (the exact power-of-two step first), then gate/up applies SwiGLU.
+template <bool SWIGLU>
 __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds_bf16_t* smem) {
     constexpr int BKB = 128;                       // codes (bytes) of k per slice
     constexpr int OPER = kBig * BKB / 2;           // bf16-sized elements of one operand half
@@ -972,7 +978,9 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
     constexpr int R = 256 / BKB;                   // rows per 256 bytes of LDS
     constexpr int QI = kBig / RI / NW;             // load instructions per wave per half
     constexpr int WN = NW / 2;                     // waves along the B rows (2 along M)
-    constexpr int WCOLS = kBig / WN;               // B-rows per wave: 32 of W1, 32 of W3
+    constexpr int WCOLS = kBig / WN;               // B-rows per wave
+    constexpr int MF = 8;                          // MFMAs per step: 4 row blocks x 2 B blocks
+    constexpr int RD = 6;                          // fragment reads per step: 2 B, then 4 A
     typedef int i32x8 __attribute__((ext_vector_type(8)));
     static_assert(QI == 4, "four load instructions per wave per half");
 
@@ -980,21 +988,23 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const int kdim = P.kdim_r;                     // d: codes per activation / weight row
+    const int kdim = P.kdim_r;                     // codes per activation / weight row
     const int ncols = P.n_r;
     const int grow = P.goff[tl.group] + tl.m0;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(P.Xq, P.abytes_r / 2);   // T d codes
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(P.Xq, P.abytes_r / 2);   // codes: half the bf16 bytes
     const uint32_t wbytes = (uint32_t)ncols * (uint32_t)kdim;
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(P.Qa_r + (size_t)tl.group * wbytes, wbytes);
-    const __amdgpu_buffer_rsrc_t rw3 = make_rsrc(P.Qb_r + (size_t)tl.group * wbytes, wbytes);
+    const __amdgpu_buffer_rsrc_t rw3 =
+        SWIGLU ? make_rsrc(P.Qb_r + (size_t)tl.group * wbytes, wbytes) : rw1;
     uint32_t aoff[QI], boff[QI];
 #pragma unroll
     for (int q = 0; q < QI; ++q) {
         const int row = RI * (wave + NW * q) + lane / CH;
         const uint32_t cbytes = (uint32_t)(((lane % CH) ^ ((row / R) % CH)) * 16);
         const int rr = row < tl.nrows ? row : 0;
-        aoff[q] = (uint32_t)P.tok_of[grow + rr] * (uint32_t)kdim + cbytes;
-        int n = tl.n0 + (q >= QI / 2 ? row - kBig / 2 : row);   // B rows 0..127 W1, 128..255 W3
+        const uint32_t arow = SWIGLU ? (uint32_t)P.tok_of[grow + rr] : (uint32_t)(grow + rr);
+        aoff[q] = arow * (uint32_t)kdim + cbytes;
+        int n = tl.n0 + ((SWIGLU && q >= QI / 2) ? row - kBig / 2 : row);   // gate/up: W1 rows, then W3
         n = n < ncols ? n : ncols - 1;
         boff[q] = (uint32_t)n * (uint32_t)kdim + cbytes;
     }
@@ -1007,8 +1017,9 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(uintptr_t)sa, 16, (int)aoff[q],
                                                      (h >> 1) * BKB, 0, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(q >= QI / 2 ? rw3 : rw1, (lds_ptr_t)(uintptr_t)sa, 16,
-                                                     (int)boff[q], (h >> 1) * BKB, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && q >= QI / 2) ? rw3 : rw1,
+                                                     (lds_ptr_t)(uintptr_t)sa, 16, (int)boff[q],
+                                                     (h >> 1) * BKB, 0, 0);
     };
 
     f32x16 acc[4][2];
@@ -1017,31 +1028,33 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
     const int lrow = lane & 31, hh = lane >> 5;
-    i32x8 fa[4], fb[2];
-    // fragments of k64 step st of slice kt: chunks 4 st + 2 hh and + 1 of the row
-    auto read_frags = [&](int kt, int st) {
-        const lds_bf16_t* sa = smem + slot(2 * kt) * OPER;
-        const lds_bf16_t* sb = smem + slot(2 * kt + 1) * OPER;
-        auto frag = [&](const lds_bf16_t* base, int row) -> i32x8 {
-            const int c0 = 4 * st + 2 * hh, f = (row / R) % CH;
-            const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                base + row * (BKB / 2) + ((c0 ^ f) << 3));
-            const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                base + row * (BKB / 2) + (((c0 + 1) ^ f) << 3));
-            return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        };
+    int b_row[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fb[j] = frag(sb, (j == 0 ? 0 : kBig / 2) + wn * (WCOLS / 2) + lrow);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = frag(sa, wm * 128 + 32 * i + lrow);
+    for (int j = 0; j < 2; ++j)
+        b_row[j] = SWIGLU ? (j == 0 ? 0 : kBig / 2) + wn * (WCOLS / 2) + lrow : wn * WCOLS + 32 * j + lrow;
+    i32x8 fa[2][4], fb[2][2];
+    // fragment read r of step st of slice kt into register set `set`: the
+    // two B fragments first, then the four A fragments (chunks 4 st + 2 hh
+    // and + 1 of the row)
+    auto read_one = [&](int set, int kt, int st, int r) {
+        const bool is_b = r < 2;
+        const lds_bf16_t* base = smem + slot(2 * kt + (is_b ? 1 : 0)) * OPER;
+        const int row = is_b ? b_row[r] : wm * 128 + 32 * (r - 2) + lrow;
+        const int c0 = 4 * st + 2 * hh, f = (row / R) % CH;
+        const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            base + row * (BKB / 2) + ((c0 ^ f) << 3));
+        const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            base + row * (BKB / 2) + (((c0 + 1) ^ f) << 3));
+        const i32x8 v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if (is_b) fb[set][r] = v;
+        else fa[set][r - 2] = v;
     };
-    auto mfmas = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
-                                                                            0, 0, 0);
+    // The weight fragment is the first operand, so lane l of the
+    // accumulator holds activation row l % 32 (as in big_tile)
+    auto mfma_one = [&](int set, int m) {
+        const int i = m / 2, j = m % 2;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0,
+                                                                    0, 0, 0);
     };
 
     const int nk = kdim / BKB;
@@ -1059,86 +1072,132 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
         wait_vm<0>();
     }
     stage_barrier();
-    read_frags(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 2 < nk;
-        mfmas();                                   // step 0
-        read_frags(kt, 1);
-        if (more)
 #pragma unroll
-            for (int q = 0; q < QI; ++q) load_one(2 * (kt + 2), q);   // A of slice kt + 2 (slot of B of kt - 1)
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nk) {
-            if (more) wait_vm<QI>();               // slice kt + 1 landed (A of kt + 2 may not)
-            else wait_vm<0>();
+    for (int r = 0; r < RD; ++r) read_one(0, 0, 0, r);
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {                    // steady state: slice kt + 2 to issue
+#pragma unroll
+        for (int g = 0; g < MF; ++g) {             // step 0, step 1's reads, A of slice kt + 2
+            mfma_one(0, g);
+            if (g < RD) read_one(1, kt, 1, g);
+            if (g % 2 == 1) load_one(2 * (kt + 2), g / 2);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        wait_vm<QI>();                             // slice kt + 1 landed (A of kt + 2 may not)
         // this wave's reads of slice kt have returned before the barrier after
-        // which A of slice kt's slot is refilled
+        // which slice kt's A slot is refilled
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        mfmas();                                   // step 1
-        if (more)
 #pragma unroll
-            for (int q = 0; q < QI; ++q) load_one(2 * (kt + 2) + 1, q);   // B of slice kt + 2
-        if (kt + 1 < nk) read_frags(kt + 1, 0);
+        for (int g = 0; g < MF; ++g) {             // step 1, B of slice kt + 2, slice kt + 1's first reads
+            mfma_one(1, g);
+            if (g % 2 == 1) load_one(2 * (kt + 2) + 1, g / 2);
+            if (g < RD) read_one(0, kt + 1, 0, g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    for (; kt < nk; ++kt) {                        // tail: nothing left to issue
+#pragma unroll
+        for (int g = 0; g < MF; ++g) {
+            mfma_one(0, g);
+            if (g < RD) read_one(1, kt, 1, g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more_k = kt + 1 < nk;
+#pragma unroll
+        for (int g = 0; g < MF; ++g) {
+            mfma_one(1, g);
+            if (g < RD && more_k) read_one(0, kt + 1, 0, g);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Epilogue (as big_tile's gate/up): each output times 2^e of its token
-    // and its weight row's scale, SwiGLU in registers, the tile staged
-    // through the free slots and stored as 16-byte row pieces.
-    constexpr int OC = kBig / 2;                   // 128 output columns
-    constexpr int CPR = OC / 8;
+    // Epilogue: each output times 2^e of its activation row and its weight
+    // row's scale; gate/up applies SwiGLU and stages the whole 256 x 128
+    // tile through the free slots, down stages each wave's 128 x 64 block in
+    // a region of its own (as big_tile); both leave as 16-byte row pieces.
     int ex[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + 32 * i + lrow;
-        ex[i] = m < tl.nrows ? P.Xe[P.tok_of[grow + m]] : 0;
+        ex[i] = m < tl.nrows ? P.Xe[SWIGLU ? P.tok_of[grow + m] : grow + m] : 0;
     }
+    constexpr int OC = SWIGLU ? kBig / 2 : kBig;   // output columns of the tile
+    constexpr int CPR = OC / 8;
+    constexpr int RC = WCOLS / 8;                  // down: chunks per region row
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_barrier();                               // every wave is done with the slots
     {
-        const int ocol_l = wn * (WCOLS / 2) + 4 * hh;
+        const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * hh;
         const float* sca = P.Sa_r + (size_t)tl.group * ncols;
-        const float* scb = P.Sb_r + (size_t)tl.group * ncols;
+        const float* scb = SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : sca;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            float fa4[4], fb4[4];
+        for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = tl.n0 + ocol_l + 8 * r4 + e;
-                fa4[e] = n < ncols ? sca[n] : 0.f;
-                fb4[e] = n < ncols ? scb[n] : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v[4];
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float fa4[4], fb4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e;
-                    const float a = ldexpf(acc[i][0][r], ex[i]) * fa4[e];
-                    const float b = ldexpf(acc[i][1][r], ex[i]) * fb4[e];
-                    v[e] = silu(a) * b;
+                    const int n = tl.n0 + ocol_l + 32 * j + 8 * r4 + e;
+                    fa4[e] = n < ncols ? sca[n] : 0.f;
+                    fb4[e] = SWIGLU && n < ncols ? scb[n] : 0.f;
                 }
-                const int orow = wm * 128 + 32 * i + lrow;
-                const int ocol = ocol_l + 8 * r4;
-                const int off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
-                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) =
-                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        const float a = ldexpf(acc[i][j][r], ex[i]) * fa4[e];
+                        v[e] = SWIGLU ? silu(a) * (ldexpf(acc[i][1][r], ex[i]) * fb4[e]) : a;
+                    }
+                    const int orow = wm * 128 + 32 * i + lrow;
+                    const int ocol = ocol_l + 32 * j + 8 * r4;      // multiple of 4
+                    int off;
+                    if (SWIGLU) {
+                        off = orow * OC + (((ocol >> 3) ^ (orow % CPR)) << 3) + (ocol & 4);
+                    } else {
+                        const int lr = 32 * i + lrow, lc = ocol - wn * WCOLS;
+                        off = wave * (128 * WCOLS) + lr * WCOLS + (((lc >> 3) ^ (lr % RC)) << 3) + (lc & 4);
+                    }
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(smem + off) =
+                        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                }
             }
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_barrier();
-    for (int c = tid; c < kBig * CPR; c += 64 * NW) {
-        const int row = c / CPR;
-        const int cc = c - row * CPR;
-        const int col = tl.n0 + cc * 8;
-        if (row < tl.nrows && col < ncols) {
-            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                smem + row * OC + ((cc ^ (row % CPR)) << 3));
-            *reinterpret_cast<u32x4*>(P.O_r + (size_t)(grow + row) * ncols + col) = v;
+    if (SWIGLU) {
+        stage_barrier();
+        for (int c = tid; c < kBig * CPR; c += 64 * NW) {
+            const int row = c / CPR;
+            const int cc = c - row * CPR;
+            const int col = tl.n0 + cc * 8;
+            if (row < tl.nrows && col < ncols) {
+                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    smem + row * OC + ((cc ^ (row % CPR)) << 3));
+                *reinterpret_cast<u32x4*>(P.O_r + (size_t)(grow + row) * ncols + col) = v;
+            }
+        }
+    } else {
+        // this wave's own writes have landed (LDS operations of one wave
+        // complete in order, and lgkmcnt(0) above waited for them)
+        const int c0 = tl.n0 + wn * WCOLS;
+#pragma unroll 4
+        for (int it = 0; it < 128 * RC / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int lr = idx / RC, c = idx % RC;
+            const int row = wm * 128 + lr, col = c0 + c * 8;
+            if (row < tl.nrows && col < ncols) {
+                const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    smem + wave * (128 * WCOLS) + lr * WCOLS + ((c ^ (lr % RC)) << 3));
+                *reinterpret_cast<u32x4*>(P.O_r + (size_t)(grow + row) * ncols + col) = v;
+            }
         }
     }
 }
@@ -1155,11 +1214,9 @@ void gemm_big_q8_kernel(GemmParams P) {
     Tile tl;
     if (!fetch_tile(P, tl)) return;
     if (tl.group < P.E) {
-        if constexpr (SWIGLU) {
-            if (P.Xq) {                            // 8-bit activations: the FP8 matrix cores
-                f8_tile(P, tl, (lds_bf16_t*)smem);
-                return;
-            }
+        if (P.Xq) {                                // 8-bit activations: the FP8 matrix cores
+            f8_tile<SWIGLU>(P, tl, (lds_bf16_t*)smem);
+            return;
         }
         big_tile<SWIGLU, 8, true>(P, tl, (lds_bf16_t*)smem);
     } else {
@@ -1264,6 +1321,10 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
     gp.Bb_r = nullptr;
     gp.Ba_s = ws2;
     gp.Bb_s = nullptr;
+    if (q8 && p.hq) {                               // 8-bit activations on the FP8 tile
+        gp.Xq = p.hq;
+        gp.Xe = p.he;
+    }
     gp.O_r = p.Y;
     gp.O_s = p.Y;
     gp.kdim_r = p.I;

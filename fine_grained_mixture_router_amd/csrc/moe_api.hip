@@ -147,8 +147,9 @@ size_t make_plan(const moe_shape_t* s, Plan* p, bool q8, bool route_only = false
     p->xe = (int32_t*)take(act8 ? (size_t)s->T * 4 : 0);
     // the FP8 tile takes 256-row tiles with d a multiple of its 128-deep
     // slices; other batches feed the dequantised rows to the 8-bit-weight tiles
-    const bool f8 = p->g1.bm == 256 && s->d % 128 == 0;
-    p->xd = (bf16_t*)take(act8 && !f8 ? (size_t)s->T * s->d * 2 : 0);
+    p->xd = (bf16_t*)take(act8 && !f8_gate_up(*p) ? (size_t)s->T * s->d * 2 : 0);
+    p->hq = (uint8_t*)take(act8 && f8_down(*p) ? (size_t)TK * s->I : 0);
+    p->he = (int32_t*)take(act8 && f8_down(*p) ? (size_t)TK * 4 : 0);
     p->H = (bf16_t*)take(((size_t)TK * s->I + (size_t)s->T * s->Ks * p->Is) * 2);
     p->Y = (bf16_t*)take((size_t)p->rows * s->d * 2);
     if (train) {
@@ -242,7 +243,9 @@ void place(Plan* p, void* ws) {
     const bool act8 = (p->flags & kAct8) && p->K > 0;
     p->xq = act8 ? rebase(p->xq, b) : nullptr;
     p->xe = act8 ? rebase(p->xe, b) : nullptr;
-    p->xd = act8 && !(p->g1.bm == 256 && p->d % 128 == 0) ? rebase(p->xd, b) : nullptr;
+    p->xd = act8 && !f8_gate_up(*p) ? rebase(p->xd, b) : nullptr;
+    p->hq = act8 && f8_down(*p) ? rebase(p->hq, b) : nullptr;
+    p->he = act8 && f8_down(*p) ? rebase(p->he, b) : nullptr;
     p->H = rebase(p->H, b);
     p->Y = rebase(p->Y, b);
 }
@@ -343,6 +346,9 @@ __attribute__((visibility("default"))) moe_status_t moe_workspace_layout(const m
     const bool act8 = (shape->flags & MOE_FLAG_ACT8) && shape->K > 0;
     layout->act8_codes = act8 ? at(p.xq) : 0;
     layout->act8_exps = act8 ? at(p.xe) : 0;
+    layout->h = at(p.H);
+    layout->act8_h_codes = act8 && f8_down(p) ? at(p.hq) : 0;
+    layout->act8_h_exps = act8 && f8_down(p) ? at(p.he) : 0;
     layout->rows = p.rows;
     layout->max_tiles_gate_up = p.max_tiles1;
     layout->max_tiles_down = p.max_tiles2;
@@ -474,14 +480,23 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     step(2, [&] { return launch_perm_scan(p, s); });
     step(3, [&] { return launch_perm_scatter(p, s); });
     if (stats && p.K > 0 && e == hipSuccess) e = launch_balance_stats(p, stats, s);
-    step(4, [&] {                           // (with 8-bit activations, their quantisation too)
+    // with 8-bit activations each GEMM's slot also times the quantisation of
+    // its routed input rows (x; the routed rows of H)
+    step(4, [&] {
         if (p.xq) {
-            const hipError_t qe = launch_act8_quant(p, xb, s);
+            const hipError_t qe = launch_act8_quant(xb, p.T, p.d, p.xq, p.xe, p.xd, s);
             if (qe != hipSuccess) return qe;
         }
         return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s);
     });
-    step(5, [&] { return launch_gemm_down(p, w2b, ws2b, q, s); });
+    step(5, [&] {
+        if (p.xq) {
+            const hipError_t qe = p.hq ? launch_act8_quant(p.H, p.T * p.K, p.I, p.hq, p.he, nullptr, s)
+                                       : launch_act8_quant(p.H, p.T * p.K, p.I, nullptr, nullptr, p.H, s);
+            if (qe != hipSuccess) return qe;
+        }
+        return launch_gemm_down(p, w2b, ws2b, q, s);
+    });
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
         for (int k = 0; k < kBwdSlot0; ++k) {

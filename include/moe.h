@@ -76,16 +76,17 @@ typedef struct {
 #define MOE_FLAG_RENORM 2u
 #define MOE_FLAG_SIGMOID 4u
 /* MOE_FLAG_ACT8 (moe_forward_fp8 only; other entry points reject it with
- * MOE_ERR_SHAPE): the routed experts' gate/up products take 8-bit
- * activations.  Each token row x gets the scale 2^e, e the smallest integer
- * with max_j |x_j| <= 448 * 2^e (448: E4M3's largest finite value; e = 0
- * for an all-zero row), and the codes are the nearest E4M3 values of
- * x * 2^-e, ties to the even code; W1 x and W3 x are then computed from
- * those codes and the 8-bit weights on the FP8 matrix cores.  The shared
- * experts and the down projection keep bf16 activations.  (The pages only
- * advise low-bit routed experts with per-channel or per-group scales,
- * eliteato DeepSeek-V2 explainer section 5.5; power-of-two per-token scales
- * keep every quantised value and every product exact.) */
+ * MOE_ERR_SHAPE): the routed experts' products take 8-bit activations.
+ * Each token row x gets the scale 2^e, e the smallest integer with
+ * max_j |x_j| <= 448 * 2^e (448: E4M3's largest finite value; e = 0 for an
+ * all-zero row), and the codes are the nearest E4M3 values of x * 2^-e,
+ * ties to the even code; W1 x and W3 x are then computed from those codes
+ * and the 8-bit weights on the FP8 matrix cores.  Each routed row of
+ * h = silu(W1 x) * W3 x, held in bf16, is quantised by the same rule before
+ * W2.  The shared experts keep bf16 activations.  (The pages only advise
+ * low-bit routed experts with per-channel or per-group scales, eliteato
+ * DeepSeek-V2 explainer section 5.5; power-of-two per-row scales keep every
+ * quantised value and every product exact.) */
 #define MOE_FLAG_ACT8 8u
 
 typedef enum {
@@ -138,6 +139,11 @@ typedef struct {
     size_t idx, gate, goff, tok_of, slot_of, tiles_gate_up, tiles_down, ntiles;
     size_t act8_codes, act8_exps;   /* MOE_FLAG_ACT8 and K > 0: uint8 [T, d] codes and int32 [T]
                                        scale exponents of the 8-bit activations (else 0) */
+    size_t h;                       /* bf16 [T K, I]: h of the routed rows, in permuted row order */
+    size_t act8_h_codes, act8_h_exps;  /* MOE_FLAG_ACT8, K > 0 and the FP8 down tiles in use
+                                       (tile_rows_down 256, I a multiple of 128): uint8 [T K, I]
+                                       codes and int32 [T K] exponents of those rows (else 0;
+                                       then h itself is replaced by its dequantised value) */
     int32_t rows;                                   /* T K + T Ks */
     int32_t max_tiles_gate_up, max_tiles_down;
     int32_t tile_rows_gate_up, tile_cols_gate_up;   /* gate/up tiles read tile_cols rows of W1 and of W3 */

@@ -127,7 +127,8 @@ def test_bad_flags():
 def test_act8_only_with_8bit_weights():
     """MOE_FLAG_ACT8 needs 8-bit routed weights: the bf16 forward and the
     training entry points refuse it before touching a device; its workspace
-    holds the codes and exponents, placed apart from the rest."""
+    holds the codes and exponents of x and (on the FP8 down tiles) of h,
+    placed apart from the rest."""
     s = S(T=300, d=512)
     s.flags = moe.ACT8
     assert _fwd(s) == 2                                   # MOE_ERR_SHAPE
@@ -139,6 +140,21 @@ def test_act8_only_with_8bit_weights():
     assert lay["act8_exps"] >= lay["act8_codes"] + 300 * 512
     assert lay["act8_exps"] + 300 * 4 <= n
     assert n > moe.workspace_size(plain)
+    # 256-row tiles and I = 256: h's routed rows get codes and exponents of
+    # their own (the FP8 down tiles), apart from everything else
+    TK, I = 300 * 4, 256
+    assert lay["tile_rows_down"] == 256 and lay0["act8_h_codes"] == lay0["act8_h_exps"] == 0
+    spans = sorted([(lay["act8_codes"], 300 * 512), (lay["act8_exps"], 300 * 4),
+                    (lay["act8_h_codes"], TK * I), (lay["act8_h_exps"], TK * 4),
+                    (lay["h"], (TK * I + 300 * 256) * 2), (lay["ntiles"], 8)])
+    for (o1, n1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 % 16 == 0 and o1 + n1 <= o2
+    assert spans[-1][0] + spans[-1][1] <= n
+    # decode-size tiles (32 rows): no code buffer for h (it is dequantised in place)
+    small = moe.make_shape(8, 512, 16, 256, 4, 1, 256, act8=True)
+    ls = moe.workspace_layout(small)
+    assert ls["tile_rows_down"] == 32 and ls["act8_h_codes"] == 0 and ls["act8_h_exps"] == 0
+    assert ls["act8_codes"] > 0 and ls["h"] > 0
 
 
 def _fwd(shape, ws_bytes=1 << 40, **over):

@@ -25,6 +25,8 @@ if not torch.cuda.is_available():
 
 import fine_grained_mixture_router_amd as moe  # noqa: E402
 
+E4M3 = np.array([oracle.e4m3(c) for c in range(256)])
+
 CODE_1 = 0x38          # 1.0
 CODE_448 = 0x7E        # 448, the largest finite value
 
@@ -319,6 +321,38 @@ def test_act8_codes_bit_exact(name):
     rc, re_ = oracle.quantize_act8(L["x"])
     assert np.array_equal(exps, re_)
     assert np.array_equal(codes, rc)
+
+
+@pytest.mark.parametrize("name", ["tiny", "2b", "16b_zipf"])
+def test_act8_h_codes(name):
+    """The down projection's 8-bit input: on the FP8 down tiles (2B, 16B)
+    every code and exponent of h's routed rows equals the oracle's
+    quantisation of the bf16 h the call left in its workspace (bit-exact);
+    on the decode-size tiles (tiny) h is replaced by its dequantised rows,
+    which the quantisation maps back to themselves exactly."""
+    w = wl.WORKLOADS[name]
+    _log(f"[fp8] act8 h codes {name}")
+    L = _fp8_layer(w)
+    D = _upload(L)
+    T, d, K, I = w.T, w.d, w.K, w.I
+    shape = moe.make_shape(T, d, w.E, I, K, w.Ks, w.Is, act8=True)
+    lay = moe.workspace_layout(shape)
+    ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    _gpu(D, K, act8=True, workspace=ws)
+    torch.cuda.synchronize()
+    h = ws[lay["h"]:lay["h"] + T * K * I * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(T * K, I)
+    if lay["act8_h_codes"]:
+        codes = ws[lay["act8_h_codes"]:lay["act8_h_codes"] + T * K * I].cpu().numpy().reshape(T * K, I)
+        exps = ws[lay["act8_h_exps"]:lay["act8_h_exps"] + 4 * T * K].view(torch.int32).cpu().numpy()
+        rc, re_ = oracle.quantize_act8(h)
+        assert np.array_equal(exps, re_)
+        assert np.array_equal(codes, rc)
+        assert (exps != 0).any() and (codes != 0).any()
+    else:
+        assert name == "tiny"
+        rc, re_ = oracle.quantize_act8(h)
+        deq = E4M3[rc] * np.ldexp(1.0, re_)[:, None]
+        assert np.array_equal(deq, synth.bf16_to_f64(h))
 
 
 @pytest.mark.parametrize("name,nsample", [("tiny", 128), ("2b", 96), ("16b_zipf", 96)])
