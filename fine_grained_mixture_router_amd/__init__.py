@@ -114,7 +114,7 @@ EXPORTS = ("moe_workspace_size", "moe_workspace_layout", "moe_route_workspace_si
            "moe_profile_stream_read", "moe_forward_noalloc", "moe_noalloc_scratch_bytes",
            "moe_train_state_size", "moe_backward_workspace_size", "moe_forward_train",
            "moe_backward")
-N_SLOTS = 16
+N_SLOTS = 18
 
 
 def lib():

@@ -1206,19 +1206,17 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
 constexpr int kBigLdsBytes = 5 * kBig * 64 * 2;
 
 // Many rows per expert with 8-bit routed weights: routed tiles take the
-// 8-bit tile, shared-expert tiles (bf16 weights) the bf16 one.
-template <bool SWIGLU>
+// 8-bit tile (A8: with 8-bit activations, the FP8 tile), shared-expert tiles
+// (bf16 weights) the bf16 one.
+template <bool SWIGLU, bool A8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_big_q8_kernel(GemmParams P) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kBigLdsBytes / 2];
     Tile tl;
     if (!fetch_tile(P, tl)) return;
     if (tl.group < P.E) {
-        if (P.Xq) {                                // 8-bit activations: the FP8 matrix cores
-            f8_tile<SWIGLU>(P, tl, (lds_bf16_t*)smem);
-            return;
-        }
-        big_tile<SWIGLU, 8, true>(P, tl, (lds_bf16_t*)smem);
+        if constexpr (A8) f8_tile<SWIGLU>(P, tl, (lds_bf16_t*)smem);
+        else big_tile<SWIGLU, 8, true>(P, tl, (lds_bf16_t*)smem);
     } else {
         big_tile<SWIGLU, 8, false>(P, tl, (lds_bf16_t*)smem);
     }
@@ -1291,8 +1289,10 @@ hipError_t launch_gemm_gate_up(const Plan& p, const bf16_t* x, const bf16_t* w1,
         gp.Z_s = p.Z + (size_t)p.T * p.K * 2 * p.I;
     }
     if (p.g1.bm == 256) {
-        if (q8)
-            gemm_big_q8_kernel<true><<<tile_grid(p.max_tiles1), 512, 0, st>>>(gp);
+        if (q8 && gp.Xq)
+            gemm_big_q8_kernel<true, true><<<tile_grid(p.max_tiles1), 512, 0, st>>>(gp);
+        else if (q8)
+            gemm_big_q8_kernel<true, false><<<tile_grid(p.max_tiles1), 512, 0, st>>>(gp);
         else if (gp.Z_r)
             gemm_big_kernel<true, MOE_BIG_WAVES, true>
                 <<<tile_grid(p.max_tiles1), 64 * MOE_BIG_WAVES, 0, st>>>(gp);
@@ -1336,8 +1336,10 @@ hipError_t launch_gemm_down(const Plan& p, const bf16_t* w2, const bf16_t* ws2,
     gp.abytes_r = (uint32_t)((size_t)p.T * p.K * p.I * 2);
     gp.abytes_s = (uint32_t)((size_t)p.T * p.Ks * p.Is * 2);
     if (p.g2.bm == 256) {
-        if (q8)
-            gemm_big_q8_kernel<false><<<tile_grid(p.max_tiles2), 512, 0, st>>>(gp);
+        if (q8 && gp.Xq)
+            gemm_big_q8_kernel<false, true><<<tile_grid(p.max_tiles2), 512, 0, st>>>(gp);
+        else if (q8)
+            gemm_big_q8_kernel<false, false><<<tile_grid(p.max_tiles2), 512, 0, st>>>(gp);
         else
             gemm_big_kernel<false, MOE_BIG_WAVES>
                 <<<tile_grid(p.max_tiles2), 64 * MOE_BIG_WAVES, 0, st>>>(gp);

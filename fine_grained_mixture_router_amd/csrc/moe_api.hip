@@ -277,14 +277,15 @@ moe_status_t device_ok() {
 // Benchmark instrumentation: HIP events recorded around every kernel of the
 // next moe_forward calls, on the call's stream.  One global recorder; not
 // thread-safe (documented in moe.h).
-constexpr int kSlots = 16;
+constexpr int kSlots = 18;
 constexpr int kBwdSlot0 = 7;                 // backward kernels: slots 7..15
+constexpr int kAct8Slot0 = 16;               // 8-bit activations: quantisation of x, of h
 const char* const kSlotNames[kSlots] = {"router",        "router_tickets", "perm_scan",
                                         "perm_scatter",  "gemm_gate_up",  "gemm_down",
                                         "combine",       "bwd_lists",     "bwd_dh",
                                         "bwd_router",    "bwd_dx_router", "bwd_dx",
                                         "bwd_dx_combine", "bwd_dw2",      "bwd_dw13",
-                                        "bwd_dc"};
+                                        "bwd_dc",         "act8_x",       "act8_h"};
 struct Recorder {
     bool on = false;
     int max_calls = 0;
@@ -480,29 +481,25 @@ moe_status_t run_forward(const moe_shape_t* shape, const void* x, const void* ce
     step(2, [&] { return launch_perm_scan(p, s); });
     step(3, [&] { return launch_perm_scatter(p, s); });
     if (stats && p.K > 0 && e == hipSuccess) e = launch_balance_stats(p, stats, s);
-    // with 8-bit activations each GEMM's slot also times the quantisation of
-    // its routed input rows (x; the routed rows of H)
-    step(4, [&] {
-        if (p.xq) {
-            const hipError_t qe = launch_act8_quant(xb, p.T, p.d, p.xq, p.xe, p.xd, s);
-            if (qe != hipSuccess) return qe;
-        }
-        return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s);
-    });
-    step(5, [&] {
-        if (p.xq) {
-            const hipError_t qe = p.hq ? launch_act8_quant(p.H, p.T * p.K, p.I, p.hq, p.he, nullptr, s)
-                                       : launch_act8_quant(p.H, p.T * p.K, p.I, nullptr, nullptr, p.H, s);
-            if (qe != hipSuccess) return qe;
-        }
-        return launch_gemm_down(p, w2b, ws2b, q, s);
-    });
+    // 8-bit activations: each GEMM's routed input rows (x; the routed rows
+    // of H) are quantised just before it
+    if (p.xq) step(kAct8Slot0, [&] { return launch_act8_quant(xb, p.T, p.d, p.xq, p.xe, p.xd, s); });
+    step(4, [&] { return launch_gemm_gate_up(p, xb, w1b, w3b, ws1b, ws3b, q, s); });
+    if (p.xq) {
+        step(kAct8Slot0 + 1, [&] {
+            return p.hq ? launch_act8_quant(p.H, p.T * p.K, p.I, p.hq, p.he, nullptr, s)
+                        : launch_act8_quant(p.H, p.T * p.K, p.I, nullptr, nullptr, p.H, s);
+        });
+    }
+    step(5, [&] { return launch_gemm_down(p, w2b, ws2b, q, s); });
     step(6, [&] { return launch_combine(p, xb, static_cast<bf16_t*>(out), s); });
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
         for (int k = 0; k < kBwdSlot0; ++k) {
             const bool ran = k >= 2 || (p.K > 0 && (k == 0 || p.split > 1));
             if (ran && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
         }
+        for (int k = kAct8Slot0; k < kSlots; ++k)
+            if (p.xq && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;
         ++g_rec.calls;
     }
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -562,7 +559,7 @@ moe_status_t run_backward(const moe_shape_t* shape, const void* x, const void* c
     a.dgate = dgate;
     const hipError_t e = launch_backward(p, b, a, static_cast<hipStream_t>(stream), rec_mark_bwd);
     if (g_rec.on && g_rec.calls < g_rec.max_calls) {
-        for (int k = kBwdSlot0; k < kSlots; ++k) {
+        for (int k = kBwdSlot0; k < kAct8Slot0; ++k) {
             const int bs = k - kBwdSlot0;
             const bool ran = rk || !(bs == 2 || bs == 3 || bs == 8);
             if (ran && ((g_rec.mask >> k) & 1u)) g_rec.used[k] = true;

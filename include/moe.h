@@ -338,7 +338,7 @@ const char* moe_status_string(moe_status_t status);
  *
  * moe_profile_begin(max_calls): the next max_calls (1..100000) forward or
  * backward calls record a HIP event before and after each kernel they
- * launch, on the call's stream.  It creates 32*max_calls HIP events
+ * launch, on the call's stream.  It creates 36*max_calls HIP events
  * (host-side runtime objects; no device memory).  Errors: MOE_ERR_SHAPE for a bad count,
  * MOE_ERR_NO_DEVICE / MOE_ERR_DEVICE_ARCH as for moe_forward, MOE_ERR_HIP if
  * event creation fails.
@@ -352,7 +352,9 @@ const char* moe_status_string(moe_status_t status);
  * 3 perm_scatter, 4 gemm_gate_up, 5 gemm_down, 6 combine; moe_backward's
  * 7 bwd_lists, 8 bwd_dh, 9 bwd_router, 10 bwd_dx_router, 11 bwd_dx,
  * 12 bwd_dx_combine, 13 bwd_dw2, 14 bwd_dw13, 15 bwd_dc (a backward call
- * counts as a call) (moe_profile_slot_name gives the name, "" past the end).
+ * counts as a call); with MOE_FLAG_ACT8 16 act8_x, 17 act8_h (the
+ * quantisation of x and of h's routed rows) (moe_profile_slot_name gives
+ * the name, "" past the end).
  *
  * One process-wide recorder: not thread-safe; do not record from several
  * host threads at once. */

@@ -225,9 +225,11 @@ def test_profile_validation():
     assert f.moe_profile_slot_name(4) == b"gemm_gate_up"
     assert f.moe_profile_slot_name(8) == b"bwd_dh"
     assert f.moe_profile_slot_name(15) == b"bwd_dc"
-    assert f.moe_profile_slot_name(16) == b""
+    assert f.moe_profile_slot_name(16) == b"act8_x"
+    assert f.moe_profile_slot_name(17) == b"act8_h"
+    assert f.moe_profile_slot_name(18) == b""
     assert f.moe_profile_begin_slots(1, 0) == 2           # empty slot mask
-    assert f.moe_profile_begin_slots(1, 1 << 16) == 2     # past the last slot
+    assert f.moe_profile_begin_slots(1, 1 << 18) == 2     # past the last slot
     assert f.moe_profile_begin_slots(0, 1 << 4) == 2
 
 
