@@ -102,7 +102,7 @@ def test_down_scale_acts_on_its_output_row():
 # ---------------------------------------------------------------------------
 
 def test_act8_exponent_is_the_smallest_fitting_power_of_two():
-    """A1: e is the smallest integer with amax <= 448 * 2^e: exact at
+    """Q1: e is the smallest integer with amax <= 448 * 2^e: exact at
     448 * 2^k, one more just above it; a zero row takes e = 0."""
     for k in range(-20, 12):
         top = 448.0 * 2.0 ** k
@@ -119,7 +119,7 @@ def test_act8_exponent_is_the_smallest_fitting_power_of_two():
 
 
 def test_e4m3_nearest_even():
-    """A2: every finite E4M3 value maps to its own code; midpoints between
+    """Q2: every finite E4M3 value maps to its own code; midpoints between
     neighbours go to the even code, values beside them to the nearer one;
     the sign bit follows the sign (also of zero)."""
     pos = E4M3[:0x7F]
@@ -137,7 +137,7 @@ def test_e4m3_nearest_even():
 
 
 def test_act8_rows_error_bound_and_top_binade():
-    """A3: every dequantised value is within half a code step of the input
+    """Q3: every dequantised value is within half a code step of the input
     (the step of E4M3 at that magnitude times 2^e), each row's largest
     magnitude, scaled, lies in (224, 448] and so codes to a value in [224,
     448] (e is not larger than needed), and a row of already representable
@@ -170,7 +170,7 @@ def _fp8(w, L, **kw):
 
 
 def test_bf16_nearest():
-    """A6: h is rounded to bf16 before its codes are taken.  Every finite
+    """Q6: h is rounded to bf16 before its codes are taken.  Every finite
     bf16 value maps to its own bits (both zeros, subnormals, the largest
     finite), the midpoint of two neighbours to the one with the even
     significand, values just beside a midpoint to the nearer neighbour."""
@@ -190,7 +190,7 @@ def test_bf16_nearest():
 
 
 def test_act8_down_input_is_the_quantised_bf16_h():
-    """A4: the routed experts' down projection takes 8-bit activations made
+    """Q4: the routed experts' down projection takes 8-bit activations made
     from h rounded to bf16.  With rows already on the 8-bit grid (so the x
     quantisation changes nothing), one expert per token with gate 1
     (renormalised K = 1) and W2 the identity (d = I), the 8-bit-weight
@@ -226,7 +226,7 @@ def test_act8_down_input_is_the_quantised_bf16_h():
 
 
 def test_act8_touches_only_the_routed_experts():
-    """A5: on ordinary rows, ACT8 leaves the routing and the shared experts'
+    """Q5: on ordinary rows, ACT8 leaves the routing and the shared experts'
     part unchanged to the last bit and moves the routed part by about the
     size of the activation rounding (and no more)."""
     w, L = _layer(32, T=16, d=128)
