@@ -1008,6 +1008,18 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
         n = n < ncols ? n : ncols - 1;
         boff[q] = (uint32_t)n * (uint32_t)kdim + cbytes;
     }
+    const int lrow = lane & 31, hh = lane >> 5;
+    // the scale exponents of this lane's four output rows, for the epilogue
+    // (gate/up: two dependent loads through tok_of, issued under the last
+    // slice's MFMAs)
+    int ex[4];
+    auto fetch_ex = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = wm * 128 + 32 * i + lrow;
+            ex[i] = m < tl.nrows ? P.Xe[SWIGLU ? P.tok_of[grow + m] : grow + m] : 0;
+        }
+    };
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)smem + (uint32_t)(wave * RI * BKB));
     auto slot = [](int h) { return h % NSLOT; };
@@ -1027,7 +1039,6 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    const int lrow = lane & 31, hh = lane >> 5;
     int b_row[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -1109,6 +1120,8 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const bool more_k = kt + 1 < nk;
+        if constexpr (SWIGLU)
+            if (!more_k) fetch_ex();
 #pragma unroll
         for (int g = 0; g < MF; ++g) {
             mfma_one(1, g);
@@ -1119,33 +1132,42 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
 
     // Epilogue: each output times 2^e of its activation row and its weight
     // row's scale; gate/up applies SwiGLU and stages the whole 256 x 128
-    // tile through the free slots, down stages each wave's 128 x 64 block in
-    // a region of its own (as big_tile); both leave as 16-byte row pieces.
-    int ex[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = wm * 128 + 32 * i + lrow;
-        ex[i] = m < tl.nrows ? P.Xe[SWIGLU ? P.tok_of[grow + m] : grow + m] : 0;
-    }
+    // tile in LDS, down stages each wave's 128 x 64 block in a region of its
+    // own (as big_tile); both leave as 16-byte row pieces.  No barrier before
+    // the staging: after the main loop's last barrier no wave reads the
+    // slots again and no load into them is in flight.
     constexpr int OC = SWIGLU ? kBig / 2 : kBig;   // output columns of the tile
     constexpr int CPR = OC / 8;
     constexpr int RC = WCOLS / 8;                  // down: chunks per region row
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_barrier();                               // every wave is done with the slots
+    constexpr int NJ = SWIGLU ? 1 : 2;
+    typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
     {
         const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * hh;
         const float* sca = P.Sa_r + (size_t)tl.group * ncols;
         const float* scb = SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : sca;
+        // the weight-row scales of the lane's output columns, all loads
+        // issued before any is used: runs of four consecutive columns (ncols
+        // and the run starts are multiples of 4, so a run is wholly inside
+        // or wholly past the matrix)
+        f32x4 sa4[NJ][4], sb4[4];
+        if constexpr (!SWIGLU) fetch_ex();
 #pragma unroll
-        for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int n = tl.n0 + ocol_l + 32 * j + 8 * r4;
+                sa4[j][r4] = n < ncols ? (f32x4)*reinterpret_cast<const f32x4a4*>(sca + n) : f32x4{};
+                if (SWIGLU) sb4[r4] = n < ncols ? (f32x4)*reinterpret_cast<const f32x4a4*>(scb + n) : f32x4{};
+            }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 float fa4[4], fb4[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int n = tl.n0 + ocol_l + 32 * j + 8 * r4 + e;
-                    fa4[e] = n < ncols ? sca[n] : 0.f;
-                    fb4[e] = SWIGLU && n < ncols ? scb[n] : 0.f;
+                    fa4[e] = sa4[j][r4][e];
+                    fb4[e] = SWIGLU ? sb4[r4][e] : 0.f;
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
