@@ -862,8 +862,9 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     constexpr int CPR = OC / 8;                      // 16-byte chunks per row
     constexpr int RC = WCOLS / 8;                    // down: chunks per region row
     static_assert(kBig * OC <= NSLOT * OPER, "output tile fits the slots");
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stage_barrier();                                 // every wave is done with the slots
+    // No barrier before the staging: the main loop's last barrier comes
+    // after every wave's last fragment read and after the last load into
+    // the slots has landed; only MFMAs on registers follow it.
     {
         const int ocol_l = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + 4 * (lane >> 5);   // + 32 j + 8 r4
         // 8-bit: each output column's accumulators times its weight rows' scales
