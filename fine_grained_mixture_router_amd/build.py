@@ -1,6 +1,11 @@
 """Build libmoe.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
     python fine_grained_mixture_router_amd/build.py
+    python fine_grained_mixture_router_amd/build.py --phase
+
+--phase builds a separate measurement copy, libmoe_phase.so (objects in
+_build/phase), with -DMOE_PHASE_STAMPS: per-tile timestamps of the
+many-rows GEMM tiles, read by phase_timing.py.  libmoe.so is not touched.
 """
 from __future__ import annotations
 
@@ -25,31 +30,38 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, obj_dir: str = OBJ, defines=()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+PHASE_DIR = os.path.join(OBJ, "phase")
+PHASE_LIB = os.path.join(HERE, "libmoe_phase.so")
+
+
+def build(verbose: bool = False, phase: bool = False) -> str:
+    obj_dir = PHASE_DIR if phase else OBJ
+    lib = PHASE_LIB if phase else LIB
+    defines = ("-DMOE_PHASE_STAMPS",) if phase else ()
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, defines), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, phase="--phase" in sys.argv[1:])
     sys.exit(0)

@@ -26,6 +26,39 @@
 
 #include <type_traits>
 
+// Phase timestamps (built only with -DMOE_PHASE_STAMPS, by
+// `build.py --phase`; the library itself carries none of this): per
+// workgroup of the many-rows GEMM tiles, the shader clock (s_memtime) at the
+// tile's start, after its first slice has landed, after its main loop and
+// after its epilogue's stores have been issued, and the hardware id of the
+// wave.  Four regions of kPhaseWgs workgroups: bf16 gate/up, bf16 down, FP8
+// gate/up, FP8 down; a later launch of the same kind overwrites.
+#ifdef MOE_PHASE_STAMPS
+constexpr int kPhaseWgs = 32768;
+__device__ unsigned long long g_phase[4 * kPhaseWgs * 5];
+extern "C" __attribute__((visibility("default"))) int moe_phase_read(unsigned long long* host, int n) {
+    if (n < 0 || n > 4 * kPhaseWgs * 5) return 1;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase), (size_t)n * 8, 0, hipMemcpyDeviceToHost);
+}
+extern "C" __attribute__((visibility("default"))) int moe_phase_slots() { return 4 * kPhaseWgs * 5; }
+#define PHASE_STAMP(kind, k)                                                                   \
+    do {                                                                                       \
+        if (threadIdx.x == 0 && blockIdx.x < (unsigned)kPhaseWgs) {                            \
+            const size_t at_ = ((size_t)(kind) * kPhaseWgs + blockIdx.x) * 5;                  \
+            g_phase[at_ + (k)] = __builtin_amdgcn_s_memtime();                                 \
+            if ((k) == 0) {                                                                    \
+                unsigned hw_;                                                                  \
+                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw_));              \
+                g_phase[at_ + 4] = hw_;                                                        \
+            }                                                                                  \
+        }                                                                                      \
+    } while (0)
+#else
+#define PHASE_STAMP(kind, k) \
+    do {                     \
+    } while (0)
+#endif
+
 namespace moe {
 namespace {
 
@@ -578,6 +611,8 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
     static_assert(QI >= 2 && QI % 2 == 0 && QB >= 2 && QB % 2 == 0, "W1 / W3 halves of the load list");
 
     const int tid = threadIdx.x;
+    constexpr int kPhaseKind = SWIGLU ? 0 : 1;
+    PHASE_STAMP(kPhaseKind, 0);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wm = wave / WN, wn = wave % WN;
@@ -838,6 +873,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
         wait_vm<0>();
     }
     stage_barrier();
+    PHASE_STAMP(kPhaseKind, 1);
     // the instance for this wave's share of the tile's rows (wave-uniform)
     {
         const int na = (tl.nrows - wm * 128 + 31) >> 5;
@@ -847,6 +883,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
         else if (na == 1) main_loop(std::integral_constant<int, 1>{}, nk);
         else main_loop(std::integral_constant<int, 0>{}, nk);
     }
+    PHASE_STAMP(kPhaseKind, 2);
 
     // Epilogue: the tile's outputs (bf16; SwiGLU applied in registers) go
     // through LDS — now free — and leave as whole 16-byte row pieces.
@@ -947,6 +984,7 @@ __device__ __forceinline__ void big_tile(const GemmParams& P, const Tile& tl, ld
             }
         }
     }
+    PHASE_STAMP(kPhaseKind, 3);
 }
 
 // One 256 x 256 tile of a routed expert with 8-bit activations and 8-bit
@@ -986,6 +1024,8 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
     static_assert(QI == 4, "four load instructions per wave per half");
 
     const int tid = threadIdx.x;
+    constexpr int kPhaseKind = SWIGLU ? 2 : 3;
+    PHASE_STAMP(kPhaseKind, 0);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
@@ -1084,6 +1124,7 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
         wait_vm<0>();
     }
     stage_barrier();
+    PHASE_STAMP(kPhaseKind, 1);
 #pragma unroll
     for (int r = 0; r < RD; ++r) read_one(0, 0, 0, r);
     int kt = 0;
@@ -1131,6 +1172,7 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    PHASE_STAMP(kPhaseKind, 2);
     // Epilogue: each output times 2^e of its activation row and its weight
     // row's scale; gate/up applies SwiGLU and stages the whole 256 x 128
     // tile in LDS, down stages each wave's 128 x 64 block in a region of its
@@ -1223,6 +1265,7 @@ __device__ __forceinline__ void f8_tile(const GemmParams& P, const Tile& tl, lds
             }
         }
     }
+    PHASE_STAMP(kPhaseKind, 3);
 }
 
 // LDS of the many-rows tile: five 32 KB operand slots (160 KB).
