@@ -52,7 +52,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
         // the residual row leaves with the first batch of source rows; every
-        // row here is read once (streaming policy), and so is out written
+        // row here is read once (streaming policy); out is written with plain
+        // stores (mixed with this read stream, a read probe of the same
+        // traffic ran 6 % faster with them than with streaming stores)
         const u32x4 xr = residual ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (size_t)t * d) + v)
                                   : u32x4{0u, 0u, 0u, 0u};
         for (int b0 = 0; b0 == 0 || b0 < ns; b0 += kBatch) {   // once at least: ns may be 0
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
         o.y = pack_bf16x2(acc[2], acc[3]);
         o.z = pack_bf16x2(acc[4], acc[5]);
         o.w = pack_bf16x2(acc[6], acc[7]);
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (size_t)t * d) + v);
+        reinterpret_cast<u32x4*>(out + (size_t)t * d)[v] = o;
     }
 }
 
