@@ -426,16 +426,25 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
     }
 
     // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and
-    // rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.
+    // rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.  The outputs go through
+    // LDS (free: every wave passed the main loop's last barrier after its
+    // last fragment read) and leave as whole 16-byte pieces of each row.
+    // Stored straight from the accumulators, each store instruction wrote
+    // 2-byte values to two 64-byte row pieces; on the decode down GEMM those
+    // stores cost 8 % of its time (measured without them).
     bf16_t* obase = shared ? P.O_s : P.O_r;
     const int orow0 = SWIGLU ? rrow : grow;
     const float* sca = Q8 ? P.Sa_r + (size_t)tl.group * ncols : nullptr;
     const float* scb = Q8 && SWIGLU ? P.Sb_r + (size_t)tl.group * ncols : nullptr;
+    constexpr int OC = SWIGLU ? BN / 2 : BN;       // output columns of the tile
+    static_assert(BM * OC <= 2 * BN * kBK, "the output tile fits the B buffers");
+    bf16_t* const stage = sB;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
         for (int j = 0; j < (SWIGLU ? NB / 2 : NB); ++j) {
-            const int col = tl.n0 + (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + j * 32 + (lane & 31);
+            const int lcol = (SWIGLU ? wn * (WCOLS / 2) : wn * WCOLS) + j * 32 + (lane & 31);
+            const int col = tl.n0 + lcol;
             float fa = 1.f, fb = 1.f;
             if (Q8 && col < ncols) {
                 fa = sca[col];
@@ -448,16 +457,23 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
                 if (SWIGLU) v = silu(Q8 ? acc[i][j][r] * fa : acc[i][j][r]) *
                                 (Q8 ? acc[i][j + NB / 2][r] * fb : acc[i][j + NB / 2][r]);
                 else v = Q8 ? acc[i][j][r] * fa : acc[i][j][r];
-                if (row < tl.nrows && col < ncols) {
-                    obase[(size_t)(orow0 + row) * ncols + col] = f32_to_bf16(v);
-                    if (SWIGLU && !Q8 && P.Z_r) {
-                        bf16_t* z = (shared ? P.Z_s : P.Z_r) + (size_t)(orow0 + row) * 2 * ncols + col;
-                        z[0] = f32_to_bf16(acc[i][j][r]);
-                        z[ncols] = f32_to_bf16(acc[i][j + NB / 2][r]);
-                    }
+                stage[row * OC + lcol] = f32_to_bf16(v);
+                if (SWIGLU && !Q8 && P.Z_r && row < tl.nrows && col < ncols) {
+                    bf16_t* z = (shared ? P.Z_s : P.Z_r) + (size_t)(orow0 + row) * 2 * ncols + col;
+                    z[0] = f32_to_bf16(acc[i][j][r]);
+                    z[ncols] = f32_to_bf16(acc[i][j + NB / 2][r]);
                 }
             }
         }
+    }
+    bar();
+    for (int idx = tid; idx < BM * (OC / 8); idx += kThreads) {
+        const int row = idx / (OC / 8);
+        const int c = idx - row * (OC / 8);
+        const int col = tl.n0 + c * 8;                // ncols is a multiple of 8: whole pieces
+        if (row < tl.nrows && col < ncols)
+            *reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col) =
+                *reinterpret_cast<const u32x4*>(stage + row * OC + c * 8);
     }
 }
 
