@@ -26,17 +26,19 @@ def _bits(t):
 
 
 # the few-rows tile (tiny) and the many-rows ring tile (16b_zipf), with bf16
-# or 8-bit routed weights
-@pytest.mark.parametrize("name,fp8", [("tiny", False), ("16b_zipf", False), ("tiny", True),
-                                      ("16b_zipf", True)])
-def test_graph_replay_matches_eager(name, fp8):
+# or 8-bit routed weights, and with 8-bit activations (the quantisation
+# kernels and, on 16b_zipf, the FP8 tiles)
+@pytest.mark.parametrize("name,fp8,act8", [("tiny", False, False), ("16b_zipf", False, False),
+                                           ("tiny", True, False), ("16b_zipf", True, False),
+                                           ("tiny", True, True), ("16b_zipf", True, True)])
+def test_graph_replay_matches_eager(name, fp8, act8):
     w = wl.WORKLOADS[name]
-    print(f"[graph] {name} fp8={fp8}", flush=True)
+    print(f"[graph] {name} fp8={fp8} act8={act8}", flush=True)
     D = upload(wl.gen_all(w))
     if fp8:
         for k, a in zip(("q1", "s1", "q3", "s3", "q2", "s2"), wl.gen_routed_fp8(w)):
             D[k] = torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is, act8=act8)
     ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
     idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
@@ -45,7 +47,8 @@ def test_graph_replay_matches_eager(name, fp8):
     def fwd(**kw):
         if fp8:
             return moe.forward_fp8(D["x"], D["C"], D["q1"], D["s1"], D["q3"], D["s3"], D["q2"],
-                                   D["s2"], D["ws1"], D["ws3"], D["ws2"], K=w.K, bias=D["bias"], **kw)
+                                   D["s2"], D["ws1"], D["ws3"], D["ws2"], K=w.K, bias=D["bias"],
+                                   act8=act8, **kw)
         return moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], D["ws1"], D["ws3"], D["ws2"],
                            K=w.K, bias=D["bias"], **kw)
 
