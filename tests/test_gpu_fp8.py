@@ -387,6 +387,31 @@ def test_act8_layer_parity(name, nsample):
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["tiny", "2b"])
+def test_act8_v3_style_gate(name):
+    """8-bit activations under the V3-style gate (sigmoid scores, the bias in
+    the selection only, renormalised gates): routing, the residual-free
+    delta under the GPU's routing, and the full output against the oracle."""
+    w = wl.WORKLOADS[name]
+    _log(f"[fp8] act8 sigmoid+renorm {name}")
+    L = _fp8_layer(w)
+    if L.get("bias") is None:
+        L["bias"] = (np.random.default_rng(w.T).standard_normal(w.E) * 0.5).astype(np.float32)
+    D = _upload(L)
+    kw = dict(act8=True, sigmoid=True, renorm=True)
+    out, idx, gate = _gpu(D, w.K, **kw)
+    torch.cuda.synchronize()
+    tok = np.unique(np.r_[0, np.random.default_rng(w.T + 3).choice(w.T, min(96, w.T), replace=False), w.T - 1])
+    ref = _ref(L, w.K, tok, **kw)
+    gi, gg = idx.cpu().numpy()[tok], gate.cpu().numpy()[tok]
+    check_routing(gi, gg, ref["idx"], ref["gate"], ref["margin"], w.K)
+    check_close(synth.bf16_to_f64(bf16_bits(out)[tok]), ref["out"])
+    dout, _, _ = _gpu(D, w.K, no_residual=True, **kw)
+    torch.cuda.synchronize()
+    dref = _ref(L, w.K, tok, no_residual=True, forced_idx=gi, **kw)
+    check_part(out_f64(dout)[tok], dref["out"], "delta")
+
+
 @pytest.mark.parametrize("case", [
     (67, 576, 13, 192, 3, 2, 320),
     (700, 1024, 5, 512, 1, 3, 128),
