@@ -471,9 +471,9 @@ __device__ __forceinline__ void thin_tile(const GemmParams& P, const Tile& tl, b
         const int row = idx / (OC / 8);
         const int c = idx - row * (OC / 8);
         const int col = tl.n0 + c * 8;                // ncols is a multiple of 8: whole pieces
-        if (row < tl.nrows && col < ncols)
-            *reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col) =
-                *reinterpret_cast<const u32x4*>(stage + row * OC + c * 8);
+        if (row < tl.nrows && col < ncols)                // streaming stores: 4 % faster decode down
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stage + row * OC + c * 8),
+                                        reinterpret_cast<u32x4*>(obase + (size_t)(orow0 + row) * ncols + col));
     }
 }
 
