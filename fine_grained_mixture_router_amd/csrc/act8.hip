@@ -15,10 +15,10 @@
 // needs e = E2 - 8 otherwise; one less never holds (f >= 0.5 > 0.4375).
 //
 // One wave per row: the row maximum over 16-byte pieces (a wavefront
-// reduction), then the codes, eight per 64-bit store, and where the FP8 tiles do not apply (decode-size tiles, or
-// a reduction length that is not a multiple of their 128-deep slices) the
-// dequantised row in bf16 (exact: an E4M3 value times a power of two fits
-// bf16's 8-bit significand).  The dequantised row may overwrite the input:
+// reduction), then the codes, eight per 64-bit store, and where the FP8
+// tiles do not apply (decode-size tiles, or a reduction length that is not
+// a multiple of their 128-deep slices) the dequantised row in bf16 (exact:
+// an E4M3 value times a power of two fits bf16's 8-bit significand).  The dequantised row may overwrite the input:
 // each lane writes only the pieces it has itself read, after the wave-wide
 // maximum (and so every read of the first pass) is complete.
 #include "common.h"
