@@ -416,6 +416,8 @@ def test_act8_v3_style_gate(name):
     (67, 576, 13, 192, 3, 2, 320),
     (700, 1024, 5, 512, 1, 3, 128),
     (2048, 256, 6, 128, 2, 1, 192),
+    (2048, 320, 4, 192, 2, 1, 192),   # 256-row tiles with d, I not multiples of 128: dequantised rows
+    (1, 128, 4, 128, 4, 1, 64),       # one token, every expert
 ], ids=lambda c: "T%dd%dE%dI%dK%dKs%dIs%d" % c)
 def test_act8_edge_shapes(case):
     T, d, E, I, K, Ks, Is = case
