@@ -33,8 +33,9 @@
 // copy of any weight or activation.
 //
 // Tile: 256 x 256 outputs, eight waves (2 along M, 4 along N) of 128 x 64,
-// BK = 64, two LDS stages of 64 KB (A half, B half), direct-to-LDS buffer
-// loads, one barrier per slice.  Layouts in LDS:
+// BK = 64, a ring of five 32 KB LDS slots holding one operand half (the A or
+// the B part of a slice) each, direct-to-LDS buffer loads, one barrier per
+// slice.  Layouts in LDS:
 //   K-contiguous operand: [256 rows][64 k], 16-byte chunk c of row r at
 //     position c ^ ((r / 2) mod 8) (conflict-free ds_read_b128 fragments)
 //   K-major operand: [64 k][256 cols], 16-byte chunk c of row k at
