@@ -744,7 +744,8 @@ void bwd_gemm_kernel(BwdParams P) {
 // the group's inter-dim; dX: N = d), in blocks of 4 M-tiles x all N-tiles
 // (consecutive entries share A rows or weight rows), and the groups in
 // descending row count (ties: lower id) for the weight-gradient products, so
-// the longest reductions start first.  One workgroup.
+// the longest reductions start first, with the groups no row chose spread
+// among them (routed layers).  One workgroup.
 // ---------------------------------------------------------------------------
 constexpr int kListThreads = 1024;
 constexpr int kMaxGroups = 256 + 16;
@@ -799,8 +800,9 @@ __device__ void emit_tiles(Tile* out, int total, const int* s_off, const int* s_
 __global__ __launch_bounds__(kListThreads) void bwd_lists_kernel(const int32_t* goff, int E, int G,
                                                                  int I, int Is, int d, Tile* tdh,
                                                                  Tile* tdx, int32_t* ntiles,
-                                                                 int32_t* gorder) {
-    __shared__ int s_cnt[kMaxGroups], s_o1[kMaxGroups], s_o2[kMaxGroups];
+                                                                 int32_t* gorder, int spread) {
+    __shared__ int s_cnt[kMaxGroups], s_o1[kMaxGroups], s_o2[kMaxGroups], s_rows[kMaxGroups];
+    __shared__ long long s_cum[kMaxGroups + 1];
     __shared__ int swave[kListThreads / 64];
     const int tid = threadIdx.x;
     int cnt = 0, t1 = 0, t2 = 0;
@@ -823,13 +825,54 @@ __global__ __launch_bounds__(kListThreads) void bwd_lists_kernel(const int32_t* 
         ntiles[1] = tot2;
     }
     __syncthreads();
+    // Groups with rows take ranks 0 .. nc - 1 (most rows first); the nz
+    // empty ones (zero gradients: stores only) are spread among them in
+    // proportion to the rows before them, so that their stores run while
+    // other CUs still compute: empty group j goes right after the last group
+    // whose rows start at or before (j + 1) / (nz + 1) of all rows.  Every
+    // group with rows keeps its rank order, so the positions form a
+    // bijection onto 0 .. G - 1.
+    int rank = 0, nc = 0;
     if (tid < G) {
-        int rank = 0;
         for (int h = 0; h < G; ++h) {
             const int c = s_cnt[h];
             rank += (c > cnt) || (c == cnt && h < tid);
+            nc += c > 0;
         }
-        gorder[rank] = tid;
+        if (cnt > 0) s_rows[rank] = cnt;
+    }
+    __syncthreads();
+    if (tid == 0) {                                     // rows before each rank
+        long long a = 0;
+        for (int i = 0; i < nc; ++i) {
+            const long long v = s_rows[i];
+            s_cum[i] = a;
+            a += v;
+        }
+        s_cum[nc] = a;
+    }
+    __syncthreads();
+    if (tid < G) {
+        const int nz = G - nc;
+        int pos = rank;
+        if (spread && nc > 0 && nz > 0) {
+            const long long total = s_cum[nc];
+            if (cnt > 0) {                              // + empty groups placed before it
+                const long long S = s_cum[rank] * (nz + 1);
+                pos = rank + (int)(S == 0 ? 0 : min((long long)nz, (S - 1) / total));
+            } else {
+                const int j = rank - nc;
+                const long long thr = ((long long)(j + 1) * total) / (nz + 1);
+                int lo = 0, hi = nc - 1;                // last group starting at or before thr
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_cum[mid] <= thr) lo = mid;
+                    else hi = mid - 1;
+                }
+                pos = lo + 1 + j;
+            }
+        }
+        gorder[pos] = tid;
     }
     emit_tiles(tdh, tot1, s_o1, s_cnt, G, E, I, Is);
     emit_tiles(tdx, tot2, s_o2, s_cnt, G, E, d, d);
@@ -1063,7 +1106,7 @@ hipError_t launch_backward(const Plan& p, const BwdPlan& b, const BwdArgs& a, hi
     float* dgate = a.dgate ? a.dgate : b.dgate;
     step(0, [&] {
         bwd_lists_kernel<<<1, kListThreads, 0, st>>>(p.goff, p.E, G, p.I, p.Is, p.d, b.tiles_dh,
-                                                     b.tiles_dx, b.ntiles, b.gorder);
+                                                     b.tiles_dx, b.ntiles, b.gorder, routed ? 1 : 0);
     });
     P.tiles = b.tiles_dh;
     P.ntiles = b.ntiles;
