@@ -33,6 +33,15 @@ def _f64(t):
     return out_f64(t) if t.dtype == torch.bfloat16 else t.detach().double().cpu().numpy()
 
 
+def _nan_like(t):
+    o = torch.empty_like(t)
+    if o.dtype == torch.bfloat16:
+        o.view(torch.int16).fill_(0x7FC0)           # a bf16 NaN
+    else:
+        o.fill_(float("nan"))
+    return o
+
+
 def _run(L, K, alpha=0.0, **flags):
     D = {k: to_dev(v) for k, v in L.items() if v is not None}
     ws = (D["ws1"], D["ws3"], D["ws2"]) if L["ws1"] is not None and len(L["ws1"]) else (None,) * 3
@@ -41,7 +50,11 @@ def _run(L, K, alpha=0.0, **flags):
                                                   return_routing=True, return_stats=True, **flags)
     ref_out = moe.forward(*args, K=K, bias=D.get("bias"), **flags)
     g = moe.backward(*args, dout=D["dout"], state=st, alpha=alpha, return_dgate=K > 0)
-    g2 = moe.backward(*args, dout=D["dout"], state=st, alpha=alpha, return_dgate=K > 0)
+    # the second call writes into outputs filled with NaN, so the bit-equality
+    # below also shows that every element of every output (each expert's
+    # weight gradients, computed or zero) is written
+    g2 = moe.backward(*args, dout=D["dout"], state=st, alpha=alpha, return_dgate=K > 0,
+                      **{k: _nan_like(v) for k, v in g.items() if v is not None})
     torch.cuda.synchronize()
     # the training forward is the forward; the backward is deterministic
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
