@@ -897,8 +897,8 @@ __device__ __forceinline__ float wsum(float v) {
 __global__ __launch_bounds__(64 * kRbWaves) void router_bwd_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ goff, const float* __restrict__ dgp,
-    int ndh, float alpha, int T, int E, int Epad, int K, uint32_t flags, float* __restrict__ dgate,
-    bf16_t* __restrict__ dL) {
+    int ndh, int nrt, float alpha, int T, int E, int Epad, int K, uint32_t flags,
+    float* __restrict__ dgate, bf16_t* __restrict__ dL) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRbWaves + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -911,7 +911,10 @@ __global__ __launch_bounds__(64 * kRbWaves) void router_bwd_kernel(
         sc[j] = e < Epad ? scores[(size_t)t * Epad + e] : 0.f;
         ds[j] = e < E ? bal * (float)(goff[e + 1] - goff[e]) : 0.f;
     }
-    // gate gradients: lane k holds dg_k (k < 64), taken in dH tile order
+    // gate gradients: lane k holds dg_k (k < 64), taken in dH tile order —
+    // the nrt partials of a routed row (its N tiles over I; the row stride
+    // ndh is the larger of the routed and shared counts, and a routed row's
+    // entries past nrt are never written)
     float dgl[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -919,7 +922,7 @@ __global__ __launch_bounds__(64 * kRbWaves) void router_bwd_kernel(
         if (k < K) {
             const float* pp = dgp + (size_t)slot_of[(size_t)t * K + k] * ndh;
             float a = 0.f;
-            for (int n = 0; n < ndh; ++n) a += pp[n];
+            for (int n = 0; n < nrt; ++n) a += pp[n];
             dgl[j] = a;
             dgate[(size_t)t * K + k] = a;
         }
@@ -1114,7 +1117,8 @@ hipError_t launch_backward(const Plan& p, const BwdPlan& b, const BwdArgs& a, hi
     if (routed) {
         step(2, [&] {
             router_bwd_kernel<<<(p.T + kRbWaves - 1) / kRbWaves, 64 * kRbWaves, 0, st>>>(
-                p.scores, p.idx, p.gate, p.slot_of, p.goff, b.dgp, b.ndh, a.alpha, p.T, p.E, p.Epad,
+                p.scores, p.idx, p.gate, p.slot_of, p.goff, b.dgp, b.ndh, (p.I + kBT - 1) / kBT, a.alpha,
+                p.T, p.E, p.Epad,
                 p.K, p.flags, dgate, b.dL);
         });
         const int g3 = ((p.T + kBT - 1) / kBT) * ((p.d + kBT - 1) / kBT);

@@ -132,6 +132,13 @@ def _gpu(D, K, Ks=None, **kw):
                            *ws, K=K, bias=D.get("bias"), return_routing=True, **kw)
 
 
+def _junk_ws(w, act8=False):
+    """A workspace filled with 0xFF bytes: a rerun in it must match the first
+    run bit for bit, so no kernel relies on a cleared workspace."""
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is, act8=act8)
+    return torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
 def _ref(L, K, tok, Ks=None, **kw):
     ws = (L["ws1"][:0], L["ws3"][:0], L["ws2"][:0]) if Ks == 0 else (L["ws1"], L["ws3"], L["ws2"])
     return oracle.forward_fp8(L["x"][tok], L["C"], L["bias"], L["q1"], L["s1"], L["q3"], L["s3"],
@@ -166,7 +173,7 @@ def test_fp8_layer_parity(name, nsample):
     rref = _ref(L, w.K, tok, Ks=0, no_residual=True, forced_idx=ridx.cpu().numpy()[tok])
     check_part(out_f64(rout)[tok], rref["routed"], "routed")
 
-    out2, idx2, gate2 = _gpu(D, w.K)
+    out2, idx2, gate2 = _gpu(D, w.K, workspace=_junk_ws(w))
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
@@ -382,7 +389,7 @@ def test_act8_layer_parity(name, nsample):
     torch.cuda.synchronize()
     rref = _ref(L, w.K, tok, Ks=0, act8=True, no_residual=True, forced_idx=ridx.cpu().numpy()[tok])
     check_part(out_f64(rout)[tok], rref["routed"], "routed")
-    out2, _, _ = _gpu(D, w.K, act8=True)
+    out2, _, _ = _gpu(D, w.K, act8=True, workspace=_junk_ws(w, act8=True))
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
 

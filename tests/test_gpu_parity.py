@@ -126,8 +126,16 @@ def test_forward_parity(name, nsample):
     sref = _oracle(L, w, tok, K=0, no_residual=True)
     check_part(out_f64(sout)[tok], sref["shared"], "shared")
 
-    # determinism: a second run is bit-identical
-    out2, idx2, gate2 = gpu_forward(D, w.K)
+    # determinism: a second run is bit-identical — into NaN / -1 filled
+    # outputs and a workspace filled with 0xFF bytes, so every output element
+    # is written and nothing relies on a cleared workspace
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    ws = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(out)
+    o2.view(torch.int16).fill_(0x7FC0)
+    i2 = torch.full_like(idx, -1)
+    g2 = torch.full_like(gate, float("nan"))
+    out2, idx2, gate2 = gpu_forward(D, w.K, out=o2, topk_idx=i2, topk_gate=g2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
