@@ -66,6 +66,12 @@ def test_route_variant(name, variant):
     assert exempt < 0.1 * w.T
     if kw.get("renorm"):
         assert np.allclose(gg.sum(axis=1), 1.0, rtol=0, atol=1e-5)
+    # a rerun in a routing scratch of 0xFF bytes is bit-identical
+    shape = moe.make_shape(w.T, w.d, w.E, 64, w.K, **kw)
+    junk = torch.full((moe.route_workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    idx2, gate2 = moe.route(D["x"], D["C"], K=w.K, bias=D["bias"], workspace=junk, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
@@ -95,7 +101,10 @@ def test_forward_variant(name, nsample, variant):
                           L["ws3"], L["ws2"], w.K, no_residual=True, forced_idx=gi, **kw)
     check_part(out_f64(dout)[tok], dref["out"], "delta")
 
-    out2, idx2, gate2 = gpu_forward(D, w.K, **kw)
+    # a rerun in a workspace of 0xFF bytes is bit-identical
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, w.K, w.Ks, w.Is, **kw)
+    junk = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    out2, idx2, gate2 = gpu_forward(D, w.K, workspace=junk, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(idx2, idx) and torch.equal(gate2, gate)

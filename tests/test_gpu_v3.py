@@ -93,8 +93,11 @@ def test_v3_parity(v3_layer, name, T):
                           H["ws2"], w.K, no_residual=True, forced_idx=gi_all[tok])
     check_part(out_f64(dout)[tok], dref["out"], "delta")
 
-    # determinism at full size
-    out2, idx2, _ = run()
+    # determinism at full size, the rerun in a workspace of 0xFF bytes
+    shape = moe.make_shape(nt, w.d, w.E, w.I, w.K, w.Ks, w.Is)
+    junk = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    out2, idx2, _ = run(workspace=junk)
+    del junk
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(idx2, idx)
@@ -160,5 +163,25 @@ def test_v3_backward(v3_layer, name):
         u = torch.as_tensor(untouched, device="cuda")
         for nm in ("dw1", "dw3", "dw2"):
             assert not bool((g[nm][u] != 0).any())
-    del g, st
+    # a rerun in a workspace of 0xFF bytes, into NaN-filled outputs, is
+    # bit-identical: every gradient element of every expert is written and
+    # nothing relies on a cleared workspace
+    junk = torch.full((moe.backward_workspace_size(st.shape),), 0xFF, dtype=torch.uint8,
+                      device="cuda")
+    outs = {}
+    for k, v in g.items():
+        if v is not None:
+            o = torch.empty_like(v)
+            if o.dtype == torch.bfloat16:
+                o.view(torch.int16).fill_(0x7FC0)
+            else:
+                o.fill_(float("nan"))
+            outs[k] = o
+    g2 = moe.backward(*args, dout=dod, state=st, workspace=junk, **outs)
+    torch.cuda.synchronize()
+    for k, v in g.items():
+        if v is not None:
+            bits = (lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32))
+            assert torch.equal(bits(v), bits(g2[k])), k
+    del g, g2, outs, junk, st
     torch.cuda.empty_cache()
