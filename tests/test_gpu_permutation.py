@@ -74,7 +74,8 @@ def _check(L, K, flags, what):
     D = {k: to_dev(v) for k, v in L.items()}
     shape = moe.make_shape(T, d, E, I, K, Ks, Is, **flags)
     lay = moe.workspace_layout(shape)
-    ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    # filled with 0xFF bytes: every array read back below must have been written
+    ws = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
     ws_args = (D["ws1"], D["ws3"], D["ws2"]) if Ks else (None, None, None)
     _, idx, _ = moe.forward(D["x"], D["C"], D["w1"], D["w3"], D["w2"], *ws_args, K=K,
                             bias=D["bias"], workspace=ws, return_routing=True, **flags)
@@ -158,7 +159,8 @@ def test_permutation_shared_only():
     D = {k: to_dev(v) for k, v in L.items()}
     shape = moe.make_shape(200, 128, 1, 64, 0, 2, 64)   # the binding's shape without routed experts
     lay = moe.workspace_layout(shape)
-    ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    # filled with 0xFF bytes: every array read back below must have been written
+    ws = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
     moe.forward(D["x"], None, None, None, None, D["ws1"], D["ws3"], D["ws2"], K=0, workspace=ws)
     torch.cuda.synchronize()
     goff = _read(ws, lay["goff"], 1 + 2 + 1, torch.int32)
