@@ -50,13 +50,17 @@ def _run(L, K, alpha=0.0, **flags):
                                                   return_routing=True, return_stats=True, **flags)
     ref_out = moe.forward(*args, K=K, bias=D.get("bias"), **flags)
     g = moe.backward(*args, dout=D["dout"], state=st, alpha=alpha, return_dgate=K > 0)
-    # the second call writes into outputs filled with NaN (and works in a
-    # workspace of 0xFF bytes), so the bit-equality below also shows that
-    # every element of every output (each expert's weight gradients,
-    # computed or zero) is written
+    # the second backward starts from a training forward into a state buffer
+    # of 0xFF bytes, works in a workspace of 0xFF bytes and writes into
+    # outputs filled with NaN, so the bit-equality below also shows that
+    # nothing relies on cleared state or workspace and that every element of
+    # every output (each expert's weight gradients, computed or zero) is written
+    junk_state = torch.full((moe.train_state_size(st.shape),), 0xFF, dtype=torch.uint8,
+                            device="cuda")
+    _, stj = moe.forward_train(*args, K=K, bias=D.get("bias"), state=junk_state, **flags)
     junk = torch.full((moe.backward_workspace_size(st.shape),), 0xFF, dtype=torch.uint8,
-                      device="cuda")                 # nothing may rely on a cleared workspace
-    g2 = moe.backward(*args, dout=D["dout"], state=st, alpha=alpha, return_dgate=K > 0,
+                      device="cuda")
+    g2 = moe.backward(*args, dout=D["dout"], state=stj, alpha=alpha, return_dgate=K > 0,
                       workspace=junk, **{k: _nan_like(v) for k, v in g.items() if v is not None})
     torch.cuda.synchronize()
     # the training forward is the forward; the backward is deterministic
