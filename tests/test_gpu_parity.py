@@ -154,6 +154,21 @@ def _rand_layer(seed, T, d, E, I, K, Ks, Is, sc=0.02, bias=False):
     return L
 
 
+def _rerun_in_junk(D, T, d, E, I, K, Ks, Is, out, idx, gate):
+    """The same call again, in a workspace of 0xFF bytes and into NaN / -1
+    filled outputs: bit-identical, so every output element is written and
+    nothing relies on a cleared workspace."""
+    shape = moe.make_shape(T, d, E, I, K, Ks, Is if Ks else 0)
+    ws = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(out)
+    o2.view(torch.int16).fill_(0x7FC0)
+    out2, idx2, gate2 = gpu_forward(D, K, Ks=None if Ks else 0, out=o2, topk_idx=torch.full_like(idx, -1),
+                                    topk_gate=torch.full_like(gate, float("nan")), workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(idx2, idx) and torch.equal(gate2, gate)
+
+
 EDGE = [
     # T, d, E, I, K, Ks, Is, bias   — ragged token chunks, ragged N tiles in
     # both GEMMs (I=192, d=576), E not a multiple of 64, K=E, Ks=0, I != Is
@@ -192,6 +207,7 @@ def test_edge_shapes(case):
                           forced_idx=didx.cpu().numpy()[tok])
     if rms(dref["out"]) > 0:
         check_part(out_f64(dout)[tok], dref["out"], "delta")
+    _rerun_in_junk(D, T, d, E, I, K, Ks, Is, out, idx, gate)
 
 
 # The many-rows tile (T*K >= 64 E) with expert row counts skewed by a strong
@@ -233,6 +249,7 @@ def test_big_tile_ragged_groups(case):
                           L["ws3"][:0], L["ws2"][:0], K, no_residual=True,
                           forced_idx=ridx.cpu().numpy()[tok])
     check_part(out_f64(rout), rref["routed"], "routed")
+    _rerun_in_junk(D, T, d, E, I, K, Ks, Is, out, idx, gate)
 
 
 # Gate pre-activations of standard deviation ~60 (W1 scaled up): silu runs
