@@ -139,6 +139,19 @@ def _junk_ws(w, act8=False):
     return torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
 
 
+def _rerun_in_junk(D, w, K, out, idx, act8=False, **kw):
+    """The same call again in a workspace of 0xFF bytes, into a NaN-filled
+    output: bit-identical."""
+    shape = moe.make_shape(w.T, w.d, w.E, w.I, K, w.Ks, w.Is, act8=act8, **kw)
+    ws = torch.full((moe.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(out)
+    o2.view(torch.int16).fill_(0x7FC0)
+    out2, idx2, _ = _gpu(D, K, act8=act8, workspace=ws, out=o2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(idx2, idx)
+
+
 def _ref(L, K, tok, Ks=None, **kw):
     ws = (L["ws1"][:0], L["ws3"][:0], L["ws2"][:0]) if Ks == 0 else (L["ws1"], L["ws3"], L["ws2"])
     return oracle.forward_fp8(L["x"][tok], L["C"], L["bias"], L["q1"], L["s1"], L["q3"], L["s3"],
@@ -198,6 +211,7 @@ def test_fp8_edge_shapes(case):
     tok = np.unique(np.r_[0, np.random.default_rng(d).choice(T, min(T, 48), replace=False), T - 1])
     ref = _ref(L, K, tok, no_residual=True, forced_idx=idx.cpu().numpy()[tok])
     check_part(out_f64(dout)[tok], ref["out"], "delta")
+    _rerun_in_junk(D, w, K, dout, idx, no_residual=True)
 
 
 def test_fp8_v3_decode_shape():
@@ -437,6 +451,7 @@ def test_act8_edge_shapes(case):
     tok = np.unique(np.r_[0, np.random.default_rng(d).choice(T, min(T, 64), replace=False), T - 1])
     ref = _ref(L, K, tok, act8=True, no_residual=True, forced_idx=idx.cpu().numpy()[tok])
     check_part(out_f64(dout)[tok], ref["out"], "delta")
+    _rerun_in_junk(D, w, K, dout, idx, act8=True, no_residual=True)
 
 
 def test_act8_v3_prefill_shape():
