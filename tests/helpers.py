@@ -1,4 +1,4 @@
-"""Shared pieces of the GPU parity tests: upload of seeded inputs, the judged
+"""Shared pieces of the GPU parity tests: upload of seeded inputs, the parity
 comparisons (routing under the 1e-5 score-margin rule, max |err| <= 2e-2 *
 RMS(out)) and the stricter component checks."""
 from __future__ import annotations
@@ -17,7 +17,7 @@ OUT_TOL = 2e-2
 # error of 2.1-3.1 % of RMS and an RMS error of 0.29 % of RMS at the tiny,
 # 2B, 16B and 16B-Zipf shapes.  So a part must meet max|err| <= 5e-2 * RMS
 # and RMS(err) <= 1e-2 * RMS — the second is far more sensitive to a wrong
-# expert, gate or row than any max bound.  The judged bar on the layer
+# expert, gate or row than any max bound.  The bar on the layer
 # output (whose RMS includes the residual) stays 2e-2.
 PART_TOL = 5e-2
 PART_RMS_TOL = 1e-2
