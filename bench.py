@@ -577,7 +577,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X and has "
+        print("bench.py measures one GPU: the library runs the layer on a single MI355X and has "
               "no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
