@@ -36,6 +36,10 @@ def _swap_library(moe):
     path = os.path.join(HERE, "libmoe_phase.so")
     if not os.path.exists(path):
         raise SystemExit(f"{path} is missing: run build.py --phase first")
+    csrc = os.path.join(HERE, "csrc")
+    newest = max(os.path.getmtime(os.path.join(csrc, f)) for f in os.listdir(csrc))
+    if newest > os.path.getmtime(path):
+        raise SystemExit(f"{path} is older than the sources: run build.py --phase again")
     lib = ctypes.CDLL(path)
     for name in moe.EXPORTS:
         f0, f1 = getattr(moe._lib, name), getattr(lib, name)
