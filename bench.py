@@ -269,6 +269,12 @@ def dev(a):
     return t.cuda()
 
 
+def per_launch_ms(kernels):
+    """{kernel: mean ms per launch} of the kernels that ran (a layer launches
+    only the kernels its shape and flags need)."""
+    return {k: round(ms / n, 4) for k, (ms, n) in kernels.items() if n > 0}
+
+
 def time_workload(w, D, host_x, steps, warmup, act8=False):
     """Warm up, then time exactly `steps` forwards with HIP events around the
     whole region and around every kernel.  Returns timings and routing.
@@ -617,7 +623,7 @@ def main():
         "roofline": roofline(regime(w), work, res["kernels"], w.name),
         "layer": {"tflops": round(work["layer_flops"] / (ms / 1e3) / 1e12, 1),
                   "mfma_frac": round(work["layer_flops"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                  "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in res["kernels"].items()},
+                  "kernel_ms": per_launch_ms(res["kernels"]),
                   "roofline_ms": round(layer_roofline_ms(w, counts), 4),
                   "frac_of_roofline": round(layer_roofline_ms(w, counts) / ms, 4),
                   "load": hit_stats(res["idx"], w.E)},
@@ -644,7 +650,7 @@ def main():
                     "moves, and the products still run on the bf16 MFMA; prefill_fp8_act8 adds "
                     "8-bit activations and runs the routed gate/up on the FP8 MFMA",
             "roofline": roofline("mfma", kp, rp["kernels"], w.name + "_fp8"),
-            "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rp["kernels"].items()},
+            "kernel_ms": per_launch_ms(rp["kernels"]),
         }
         # the same with 8-bit activations (MOE_FLAG_ACT8): the routed gate/up
         # and down products on the FP8 MFMA (32x32x64, E4M3 x E4M3), the
@@ -673,7 +679,7 @@ def main():
                                        "at the 2.5 PF bf16 peak; the quantisation of x is its "
                                        "own kernel (act8_x in kernel_ms)",
                              mean_launch_ms=round(ga_s * 1e3, 4), launches=ga_n),
-            "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in ra["kernels"].items()},
+            "kernel_ms": per_launch_ms(ra["kernels"]),
         }
         del P8
         print(f"[bench] {w.name} fp8: {msp:.3f} ms/step, with 8-bit activations {msa:.3f} ms/step",
@@ -694,7 +700,7 @@ def main():
             "roofline": roofline(regime(wd), wk, rd["kernels"], wd.name),
             "layer_gbs": round(wk["layer_bytes"] / (msd / 1e3) / 1e9, 1),
             "layer_hbm_frac": round(wk["layer_bytes"] / (msd / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rd["kernels"].items()},
+            "kernel_ms": per_launch_ms(rd["kernels"]),
             "roofline_ms": round(layer_roofline_ms(wd, cd), 4),
             "frac_of_roofline": round(layer_roofline_ms(wd, cd) / msd, 4),
             "load": hit_stats(rd["idx"], wd.E),
@@ -719,7 +725,7 @@ def main():
                 "roofline": roofline(regime(wd), k8, r8["kernels"], wd.name + "_fp8"),
                 "layer_gbs": round(k8["layer_bytes"] / (ms8 / 1e3) / 1e9, 1),
                 "layer_hbm_frac": round(k8["layer_bytes"] / (ms8 / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in r8["kernels"].items()},
+                "kernel_ms": per_launch_ms(r8["kernels"]),
             }
             del D8
             torch.cuda.empty_cache()
@@ -760,7 +766,7 @@ def main():
                 "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                 "roofline_ms": round(layer_roofline_ms(wc, cc), 4),
                 "frac_of_roofline": round(layer_roofline_ms(wc, cc) / msc, 4),
-                "kernel_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rc["kernels"].items()},
+                "kernel_ms": per_launch_ms(rc["kernels"]),
             }
             del Dc, Lc
             torch.cuda.empty_cache()
