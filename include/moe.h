@@ -182,8 +182,9 @@ moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* ce
                          void* out, int32_t* topk_idx, float* topk_gate, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Full layer forward with 8-bit routed-expert weights (the survey's next
- * step for decode: it halves the bytes every routed weight costs).
+/* Full layer forward with 8-bit routed-expert weights (for decode, where
+ * reading the weights bounds the layer: it halves the bytes every routed
+ * weight costs).
  *
  * Routed experts are stored as OCP FP8 E4M3 codes (sign bit 7, exponent
  * bits 6-3 with bias 7, mantissa bits 2-0; codes 0x7F / 0xFF are NaN and
