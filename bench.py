@@ -57,17 +57,24 @@ CALIB_BYTES = 1 << 30         # the calibration copy: 1 GiB read + 1 GiB written
 # kernel-name prefix -> (workload, slot) in a default run (prefill on the
 # 256x256 tile, decode on the 32x256 tile, the 8-bit batches on the 8-bit
 # instances of each)
-COUNTER_KERNELS = {
-    "gemm_big_kernel<true": ("v3_prefill", "gemm_gate_up"),
-    "gemm_big_kernel<false": ("v3_prefill", "gemm_down"),
+COUNTER_KERNELS = {                 # kernel instance -> (workload, slot); names match whole
+    "gemm_big_kernel<true, 8, false>": ("v3_prefill", "gemm_gate_up"),
+    "gemm_big_kernel<false, 8, false>": ("v3_prefill", "gemm_down"),
     "grouped_gemm_kernel<32, 256, 1, 4, true, false>": ("v3_decode", "gemm_gate_up"),
     "grouped_gemm_kernel<32, 256, 1, 4, false, false>": ("v3_decode", "gemm_down"),
     "grouped_gemm_kernel<32, 256, 1, 4, true, true>": ("v3_decode_fp8", "gemm_gate_up"),
     "grouped_gemm_kernel<32, 256, 1, 4, false, true>": ("v3_decode_fp8", "gemm_down"),
-    "gemm_big_q8_kernel<true, false": ("v3_prefill_fp8", "gemm_gate_up"),
-    "gemm_big_q8_kernel<false, false": ("v3_prefill_fp8", "gemm_down"),
-    "gemm_big_q8_kernel<true, true": ("v3_prefill_fp8_act8", "gemm_gate_up"),
-    "gemm_big_q8_kernel<false, true": ("v3_prefill_fp8_act8", "gemm_down"),
+    "gemm_big_q8_kernel<true, false>": ("v3_prefill_fp8", "gemm_gate_up"),
+    "gemm_big_q8_kernel<false, false>": ("v3_prefill_fp8", "gemm_down"),
+    "gemm_big_q8_kernel<true, true>": ("v3_prefill_fp8_act8", "gemm_gate_up"),
+    "gemm_big_q8_kernel<false, true>": ("v3_prefill_fp8_act8", "gemm_down"),
+    # the backward of the prefill batch (counter runs take it on that batch only)
+    "bwd_gemm_kernel<0>": ("v3_prefill_bwd", "bwd_dh"),
+    "bwd_gemm_kernel<1>": ("v3_prefill_bwd", "bwd_dx"),
+    "bwd_gemm_kernel<2>": ("v3_prefill_bwd", "bwd_dx_router"),
+    "bwd_gemm_kernel<3>": ("v3_prefill_bwd", "bwd_dw2"),
+    "bwd_gemm_kernel<4>": ("v3_prefill_bwd", "bwd_dw13"),
+    "bwd_gemm_kernel<5>": ("v3_prefill_bwd", "bwd_dc"),
 }
 
 
@@ -85,6 +92,9 @@ def parse():
                     help="skip the batches with 8-bit routed weights")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training-side (backward) measurements")
+    ap.add_argument("--backward-on", default="prefill,decode",
+                    help="batches whose training step is measured (the counter runs take "
+                         "'prefill' alone, so that each backward kernel's counters are one size's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle CPU baseline (0 to skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -98,7 +108,7 @@ def parse():
     return ap.parse_args()
 
 
-DIGEST_SOURCES = ("common.h", "gemm.hip", "permute.hip")   # the GEMMs and their tile order
+DIGEST_SOURCES = ("common.h", "gemm.hip", "permute.hip", "backward.hip")   # the GEMMs, their tile order
 
 
 def source_digest():
@@ -149,14 +159,14 @@ def summarize_counters(fetch_dir, write_dir):
     kern = {}
     for name in set(fetch) | set(write):
         short = re.sub(r"^void |\(.*$", "", name.replace("moe::(anonymous namespace)::", ""))
-        for pre, (wl_name, slot) in COUNTER_KERNELS.items():
-            if short.startswith(pre):
-                fk = sum(fetch.get(name, [0])) / max(len(fetch.get(name, [])), 1)
-                wk = sum(write.get(name, [0])) / max(len(write.get(name, [])), 1)
-                kern.setdefault(wl_name, {})[slot] = dict(
-                    kernel=short, dispatches=len(fetch.get(name, [])), fetch_kib=round(fk, 1),
-                    write_kib=round(wk, 1),
-                    bytes=round(fk * 1024 * f_fetch + wk * 1024 * f_write))
+        if short not in COUNTER_KERNELS:
+            continue
+        wl_name, slot = COUNTER_KERNELS[short]
+        fk = sum(fetch.get(name, [0])) / max(len(fetch.get(name, [])), 1)
+        wk = sum(write.get(name, [0])) / max(len(write.get(name, [])), 1)
+        kern.setdefault(wl_name, {})[slot] = dict(
+            kernel=short, dispatches=len(fetch.get(name, [])), fetch_kib=round(fk, 1),
+            write_kib=round(wk, 1), bytes=round(fk * 1024 * f_fetch + wk * 1024 * f_write))
     rec = dict(source_digest=source_digest(),
                calibration=dict(copy_bytes=CALIB_BYTES, fetch_scale=round(f_fetch, 4),
                                 write_scale=round(f_write, 4)),
@@ -420,10 +430,16 @@ def backward_line(w, r, counts):
     dom = max((k for k in km if k in bw["flops"]), key=lambda k: km[k])
     t = km[dom] / 1e3
     if regime(w) == "mfma" or dom != "bwd_dw13":
+        # traffic: HBM bytes per launch from the counter runs (taken on the
+        # prefill batch's backward; none for other batches)
+        tr = recorded_traffic(w.name + "_bwd", dom)
         ach = bw["flops"][dom] / t / 1e12
         roof = dict(kernel=dom, bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4),
+                    traffic=None if tr is None else round(tr),
                     algorithmic_flops=bw["flops"][dom], mean_launch_ms=km[dom])
+        if dom == "bwd_dw13":
+            roof["algorithmic_bytes"] = bw["dw13_bytes"]
     else:
         ach = bw["dw13_bytes"] / t / 1e9
         roof = dict(kernel=dom, bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS,
@@ -737,7 +753,7 @@ def main():
         rb = time_backward(w, D, L["x"], args.steps, args.warmup)
         bl["prefill"] = backward_line(w, rb, counts)
         print(f"[bench] {w.name} backward: {rb['bwd_ms']:.3f} ms", file=sys.stderr, flush=True)
-        if args.decode:
+        if args.decode and "decode" in args.backward_on.split(","):
             rbd = time_backward(wd, Dd, xd, args.steps, args.warmup)
             bl["decode"] = backward_line(wd, rbd, cd)
             print(f"[bench] {wd.name} backward: {rbd['bwd_ms']:.3f} ms", file=sys.stderr,

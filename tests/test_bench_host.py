@@ -22,7 +22,7 @@ def _write_counters(d, counter, rows):
 
 
 def test_summary_scales_by_the_calibration_copy(tmp_path):
-    g1 = "void moe::(anonymous namespace)::gemm_big_kernel<true, 64, 2, 8>(moe::(anonymous namespace)::GemmParams)"
+    g1 = "void moe::(anonymous namespace)::gemm_big_kernel<true, 8, false>(moe::(anonymous namespace)::GemmParams)"
     cp = "__amd_rocclr_copyBuffer"
     # the copy reads 1 GiB but FETCH_SIZE shows half of it; a smaller copy is ignored
     _write_counters(tmp_path / "f", "FETCH_SIZE", [(cp, 10.0), (g1, 1000.0), (g1, 3000.0),
@@ -138,3 +138,25 @@ def test_tile_cover_hits_every_tile():
             assert np.intersect1d(rows[m0:m0 + 256], tok).size > 0, (e, m0)
     for m0 in range(0, w.T, 256):                          # shared groups: every token in order
         assert np.any((tok >= m0) & (tok < m0 + 256))
+
+
+def test_summary_keeps_instances_apart(tmp_path):
+    """The training forward's gate/up instance (it also writes the
+    pre-activations) does not land in the forward's slot, and the backward
+    kinds map to their own slots."""
+    ns = "void moe::(anonymous namespace)::"
+    g1 = ns + "gemm_big_kernel<true, 8, false>(moe::(anonymous namespace)::GemmParams)"
+    g1z = ns + "gemm_big_kernel<true, 8, true>(moe::(anonymous namespace)::GemmParams)"
+    dw13 = ns + "bwd_gemm_kernel<4>(moe::(anonymous namespace)::BwdParams)"
+    cp = "__amd_rocclr_copyBuffer"
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [(cp, 524288.0), (g1, 100.0), (g1z, 900.0),
+                                                   (dw13, 40.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [(cp, 1048576.0), (g1, 10.0), (g1z, 90.0),
+                                                   (dw13, 4.0)])
+    buf = io.StringIO()
+    with redirect_stdout(buf):
+        bench.summarize_counters(str(tmp_path / "f"), str(tmp_path / "w"))
+    rec = json.loads(re.search(r"```json\n(.*?)\n```", buf.getvalue(), re.S).group(1))
+    assert rec["kernels"]["v3_prefill"]["gemm_gate_up"]["bytes"] == 100 * 1024 * 2 + 10 * 1024
+    assert rec["kernels"]["v3_prefill_bwd"]["bwd_dw13"]["bytes"] == 40 * 1024 * 2 + 4 * 1024
+    assert set(rec["kernels"]) == {"v3_prefill", "v3_prefill_bwd"}
